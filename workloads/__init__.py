@@ -1,0 +1,196 @@
+"""Seeded synthetic inputs for the Kimi Delta Attention (KDA) layer.
+
+This module is shared by the oracle's tests, the GPU parity tests and
+``bench.py``. It holds random draws and nothing of the method's arithmetic:
+the input distributions are the ones the workloads define (q, k, v, z ~ N(0,1),
+g = -softplus(N(0,1)) per key channel, beta = sigmoid(N(0,1)) per head),
+followed by round-to-nearest-even to the activation dtype where the workload
+asks for bf16 inputs.
+
+Every token-indexed tensor is drawn in blocks of ``BLOCK_TOKENS`` tokens with
+``numpy.random.default_rng([seed, tensor_id, block])``, so a tensor's values do
+not depend on how many blocks are generated at once or in which order.
+
+Arrays come back as numpy float32 (bf16 activations are float32 arrays whose
+values are exactly representable in bf16), int32 or int64. Layouts:
+  q, k, g   [T][H][dk]        v, z   [T][H][dv]        beta [T][H]
+  conv_w    [H][2*dk+dv][W]   (per head: q channels, then k, then v)
+  norm_w    [dv]
+  state     [S][H][dk][dv]    conv_state [S][H][2*dk+dv][W-1] (index 0 = oldest)
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+BLOCK_TOKENS = 65536
+
+# Tensor ids for the seed sequence; fixed forever so stored inputs stay valid.
+TID = {
+    "q": 1, "k": 2, "v": 3, "z": 4, "g": 5, "beta": 6,
+    "conv_w": 7, "norm_w": 8, "state": 9, "conv_state": 10,
+    "lengths": 11, "slots": 12, "resume": 13,
+}
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even); return float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    b = x.view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
+    return b.astype(np.uint32).view(np.float32).reshape(x.shape)
+
+
+def _softplus(x: np.ndarray) -> np.ndarray:
+    return np.logaddexp(np.float32(0.0), x).astype(np.float32)
+
+
+def _sigmoid(x: np.ndarray) -> np.ndarray:
+    return (1.0 / (1.0 + np.exp(-x.astype(np.float64)))).astype(np.float32)
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def draw_tokens(seed: int, tid: int, T: int, inner: tuple, kind: str = "normal",
+                std: float = 1.0) -> np.ndarray:
+    """Draw a [T, *inner] float32 tensor block by block (see module docstring)."""
+    out = np.empty((T,) + tuple(inner), dtype=np.float32)
+    nblk = (T + BLOCK_TOKENS - 1) // BLOCK_TOKENS
+
+    def one(b):
+        lo, hi = b * BLOCK_TOKENS, min(T, (b + 1) * BLOCK_TOKENS)
+        rng = np.random.default_rng([seed, tid, b])
+        blk = rng.standard_normal((hi - lo,) + tuple(inner), dtype=np.float32)
+        if std != 1.0:
+            blk *= np.float32(std)
+        out[lo:hi] = blk
+
+    if nblk <= 1:
+        for b in range(nblk):
+            one(b)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(one, range(nblk)))
+    return out
+
+
+def draw_plain(seed: int, tid: int, shape: tuple, std: float = 1.0) -> np.ndarray:
+    rng = np.random.default_rng([seed, tid, 0])
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return x
+
+
+@dataclass
+class LayerShape:
+    """Head geometry of one KDA layer on one GPU."""
+    H: int
+    dk: int
+    dv: int
+    W: int = 4
+    act: str = "bf16"            # dtype of q, k, v, z, out and the conv state
+
+    @property
+    def C(self) -> int:          # conv channels per head
+        return 2 * self.dk + self.dv
+
+
+@dataclass
+class Inputs:
+    shape: LayerShape
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    z: np.ndarray
+    g: np.ndarray
+    beta: np.ndarray
+    conv_w: np.ndarray
+    norm_w: np.ndarray
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def T(self) -> int:
+        return self.q.shape[0]
+
+
+def token_inputs(seed: int, shape: LayerShape, T: int, *, g_scale: float = 1.0,
+                 norm_w: str = "ones", conv_w_std: float = 0.5) -> Inputs:
+    """Per-token activations and gates for T tokens, plus conv and norm weights.
+
+    g_scale multiplies the drawn log-decay (1.0 is the workloads' gate; small
+    values give the weak-decay stress inputs, 0.0 gives the pure delta rule).
+    norm_w is "ones" (the workloads' RMSNorm weight) or "random" (a positive
+    non-unit weight that exposes indexing mistakes).
+    """
+    H, dk, dv = shape.H, shape.dk, shape.dv
+    rnd = round_bf16 if shape.act == "bf16" else (lambda a: a)
+    q = rnd(draw_tokens(seed, TID["q"], T, (H, dk)))
+    k = rnd(draw_tokens(seed, TID["k"], T, (H, dk)))
+    v = rnd(draw_tokens(seed, TID["v"], T, (H, dv)))
+    z = rnd(draw_tokens(seed, TID["z"], T, (H, dv)))
+    g = -_softplus(draw_tokens(seed, TID["g"], T, (H, dk)))
+    if g_scale != 1.0:
+        g = (g * np.float32(g_scale)).astype(np.float32)
+    beta = _sigmoid(draw_tokens(seed, TID["beta"], T, (H,)))
+    conv_w = draw_plain(seed, TID["conv_w"], (H, shape.C, shape.W), std=conv_w_std)
+    if norm_w == "ones":
+        nw = np.ones((dv,), np.float32)
+    else:
+        nw = (0.5 + np.abs(draw_plain(seed, TID["norm_w"], (dv,)))).astype(np.float32)
+    return Inputs(shape, q, k, v, z, g, beta, conv_w, nw)
+
+
+def states(seed: int, shape: LayerShape, nslots: int, state_std: float = 0.02,
+           conv_std: float = 1.0):
+    """Random recurrent state (fp32) and conv state (activation dtype) pools."""
+    S = draw_plain(seed, TID["state"], (nslots, shape.H, shape.dk, shape.dv), std=state_std)
+    X = draw_plain(seed, TID["conv_state"], (nslots, shape.H, shape.C, shape.W - 1), std=conv_std)
+    if shape.act == "bf16":
+        X = round_bf16(X)
+    return S, X
+
+
+def loguniform_lengths(seed: int, n: int, lo: int, hi: int) -> np.ndarray:
+    """n lengths floor(exp(U(ln lo, ln hi))) (the varlen workload's length mix)."""
+    rng = np.random.default_rng([seed, TID["lengths"], 0])
+    u = rng.uniform(math.log(lo), math.log(hi), size=n)
+    return np.floor(np.exp(u)).astype(np.int64)
+
+
+def cu_seqlens(lengths) -> np.ndarray:
+    lengths = np.asarray(lengths, dtype=np.int64)
+    cu = np.zeros(len(lengths) + 1, dtype=np.int64)
+    np.cumsum(lengths, out=cu[1:])
+    return cu
+
+
+def slot_permutation(seed: int, nslots: int, n: int) -> np.ndarray:
+    """n distinct slot ids drawn from a pool of nslots."""
+    rng = np.random.default_rng([seed, TID["slots"], 0])
+    return rng.permutation(nslots)[:n].astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# The five workloads (tiny recurrent, batched decode, chunked prefill, varlen
+# prefill with checkpoints, long context).  Each returns a plain description;
+# the inputs themselves come from the functions above.
+# ---------------------------------------------------------------------------
+
+WORKLOADS = {
+    "tiny_f32": dict(seed=0, shape=LayerShape(H=2, dk=32, dv=32, act="f32"), B=1, T=64),
+    "decode_b64": dict(seed=1, shape=LayerShape(H=32, dk=128, dv=128, act="bf16"),
+                       B=64, steps=256, pool=80, state_std=0.02, conv_std=1.0),
+    "prefill_4x8k": dict(seed=2, shape=LayerShape(H=32, dk=128, dv=128, act="bf16"),
+                         lengths=[8192] * 4),
+    "varlen_ckpt": dict(seed=3, shape=LayerShape(H=32, dk=128, dv=128, act="bf16"),
+                        n=16, lo=1024, hi=65536, interval=4096),
+    "long_1m": dict(seed=4, shape=LayerShape(H=8, dk=128, dv=128, act="bf16"),
+                    lengths=[1 << 20], interval=32768, decode_B=256, decode_steps=512),
+}

@@ -1,0 +1,211 @@
+"""Benchmark of the KDA layer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one pass of the batched decode workload: 64 sequences advanced by
+256 single-token decode steps (H=32, dk=dv=128, bf16 activations, fp32
+state), i.e. 256 launches of the fused decode kernel over inputs that are
+already resident in HBM.  `value` is decode tokens/s (64*256 tokens per
+step).  The line also carries:
+  roofline      the decode kernel's achieved algorithmic HBM bandwidth
+                (bytes per launch / mean launch duration from HIP events)
+                against the 8 TB/s peak, and the HBM traffic measured by
+                rocprofv3 counters when those were taken on this kernel source
+  prefill       the chunked prefill workload (4 x 8192 tokens) when the
+                prefill kernel is available: tokens/s, HBM and MFMA fractions
+  cpu_baseline  the fp64 oracle timed on this host on a bounded sample of the
+                decode workload
+Only one GPU is supported: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA decode tok/s @B=64 (% HBM peak); prefill tok/s (% bf16 MFMA peak)"
+HBM_PEAK = 8.0e12            # bytes/s
+BF16_PEAK = 2.5e15           # dense FLOP/s
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "decode_b64_traffic.json")
+DECODE_SOURCES = ["linear_attention_recurrence_decode_amd/csrc/decode.hip",
+                  "linear_attention_recurrence_decode_amd/csrc/kda_device.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes_per_launch(B, H, dk, dv, act_bytes=2):
+    """Algorithmic HBM bytes of one decode launch: per (sequence, head) the
+    fp32 state read + written, the conv state read + written, q/k/v/z in,
+    g and beta in, out; plus the conv and norm weights and the slot ids."""
+    C = 2 * dk + dv
+    per = (2 * dk * dv * 4 + 2 * C * 3 * act_bytes + (2 * dk + 2 * dv) * act_bytes
+           + dk * 4 + 4 + dv * act_bytes)
+    return B * H * per + H * C * 4 * 4 + dv * 4 + B * 4
+
+
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary, or None when it is missing or was taken on other kernel code."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha") != source_sha(DECODE_SOURCES):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def bench_decode(args):
+    import torch
+    import linear_attention_recurrence_decode_amd as kda
+    import workloads as wl
+
+    w = wl.WORKLOADS["decode_b64"]
+    shape, B, nsteps, pool = w["shape"], w["B"], w["steps"], w["pool"]
+    H, dk, dv = shape.H, shape.dk, shape.dv
+    cfg = kda.Config(H, dk, dv, kda.KDA_BF16)
+    act = cfg.torch_act
+    log(f"[bench] generating decode inputs B={B} steps={nsteps} H={H} d={dk}")
+    inp = wl.token_inputs(w["seed"], shape, B * nsteps)
+    S, X = wl.states(w["seed"], shape, pool, state_std=w["state_std"], conv_std=w["conv_std"])
+    slots = wl.slot_permutation(w["seed"], pool, B)
+    r = lambda a: torch.from_numpy(a.reshape((nsteps, B) + a.shape[1:]))
+    q, k, v, z = (r(a).to(act).cuda() for a in (inp.q, inp.k, inp.v, inp.z))
+    g, beta = r(inp.g).cuda(), r(inp.beta).cuda()
+    conv_w, norm_w = torch.from_numpy(inp.conv_w).cuda(), torch.from_numpy(inp.norm_w).cuda()
+    Sd = torch.from_numpy(S).cuda()
+    Xd = torch.from_numpy(X).to(act).cuda()
+    slot_d = torch.from_numpy(slots).cuda()
+    out = torch.empty((nsteps, B, H, dv), dtype=act, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def one_pass():
+        for s in range(nsteps):
+            kda.kda_decode_step(cfg, q[s], k[s], v[s], z[s], g[s], beta[s], conv_w, norm_w, Sd, Xd,
+                                slot_d, out[s], stream=stream)
+
+    log(f"[bench] warmup {args.warmup} passes")
+    for _ in range(args.warmup):
+        one_pass()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K passes, bracketed by synchronisation
+    log(f"[bench] timing {args.steps} passes")
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        one_pass()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+
+    # mean duration of one decode launch: the timed region's HIP-event time on
+    # the launch stream divided by the number of launches (the launches are
+    # back to back, so this is the kernel's own duration plus dispatch gaps)
+    launch_s = total_ms * 1e-3 / (args.steps * nsteps)
+
+    tokens = B * nsteps * args.steps
+    ms_per_step = total_ms / args.steps
+    nbytes = decode_bytes_per_launch(B, H, dk, dv)
+    achieved = nbytes / launch_s
+    traffic = measured_traffic()
+    res = {
+        "value": tokens / (total_ms * 1e-3),
+        "ms_per_step": ms_per_step,
+        "wall_s": wall,
+        "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK, "traffic": traffic,
+                     "kernel": "decode_kernel<128,128,bf16,256>",
+                     "bytes_per_launch": nbytes, "mean_launch_us": launch_s * 1e6},
+    }
+    return res
+
+
+def cpu_baseline(sample_steps: int):
+    """The fp64 oracle on the first `sample_steps` steps of the decode
+    workload (all 64 sequences, all 32 heads), timed on this host."""
+    import oracle
+    import workloads as wl
+
+    w = wl.WORKLOADS["decode_b64"]
+    shape, B, pool = w["shape"], w["B"], w["pool"]
+    inp = wl.token_inputs(w["seed"], shape, B * sample_steps)
+    S, X = wl.states(w["seed"], shape, pool, state_std=w["state_std"], conv_std=w["conv_std"])
+    slots = wl.slot_permutation(w["seed"], pool, B)
+    r = lambda a: a.reshape((sample_steps, B) + a.shape[1:])
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.decode_steps(r(inp.q), r(inp.k), r(inp.v), r(inp.z), r(inp.g), r(inp.beta),
+                        inp.conv_w, inp.norm_w, S[slots], X[slots])
+    dt = time.perf_counter() - t0
+    return {"value": B * sample_steps / dt, "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": f"decode workload, first {sample_steps} of 256 steps, 64 sequences x 32 heads, "
+                      f"fp64 token-by-token, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-sample-steps", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the KDA layer shards by heads or by sequences with no exchange between GPUs, "
+              "so one GPU's throughput is the figure that matters here)", file=sys.stderr)
+        sys.exit(2)
+
+    res = bench_decode(args)
+    line = {
+        "metric": METRIC,
+        "value": res["value"],
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode_b64: 64 seqs x 256 single-token steps, H=32, dk=dv=128, "
+                               "bf16 activations, fp32 state", "global_batch": 64, "seq_len": 256,
+                   "parallelism": "single GPU"},
+        "roofline": res["roofline"],
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_sample_steps} decode steps")
+        line["cpu_baseline"] = cpu_baseline(args.cpu_sample_steps)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

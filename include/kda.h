@@ -1,0 +1,197 @@
+/*
+ * kda.h -- C ABI of libkda, the MI355X (gfx950) implementation of the Kimi
+ * Delta Attention (KDA) layer's inference hot path: a fused single-launch
+ * decode step, a chunked varlen prefill that writes recurrent-state
+ * checkpoints, and the copy-on-write state copies used to resume from them.
+ *
+ * The layer, per sequence and head (dk key channels, dv value channels):
+ *   a   = SiLU(causal depthwise conv of width 4 over the raw q | k | v channels)
+ *   q^  = a_q / sqrt(|a_q|^2 + l2_eps),  k^ = a_k / sqrt(|a_k|^2 + l2_eps),  v^ = a_v
+ *   S_t = (I - beta_t k^ k^T) Diag(exp g_t) S_{t-1} + beta_t k^ v^T     (dk x dv, fp32)
+ *   o_t = S_t^T q^
+ *   y_t = o_t / sqrt(mean(o_t^2) + rms_eps) * norm_w * sigmoid(z_t)
+ * The pages this follows: vLLM blog "A Preview of Production-Scale Kimi K3
+ * Support on vLLM" (sections "The Hardest Part: Prefix Caching for KDA" and
+ * "KDA prefill and decode") and agentlenshq "vLLM Kimi K3 Support" (sections
+ * "Hybrid KV-Cache Management", "Fused Kernels and Metadata Optimization" and
+ * "Agentic Cache Retention Policies").  They describe the parts (recurrent
+ * state plus short conv state per layer, a decode fusing conv, state update,
+ * output gate and normalisation into one launch, a prefill that gathers the
+ * initial states in one operation, checkpoints at fixed intervals and at
+ * prompt ends, copy-on-write on a prefix hit); the equation above is the
+ * gated delta rule with per-channel decay that they name.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Ownership: the caller owns every buffer.  The library allocates nothing,
+ *   keeps no pointer after a call returns, and holds no global mutable state
+ *   apart from a thread-local error message.
+ * Execution: every call enqueues its kernels on `stream` (a hipStream_t; NULL
+ *   means the null stream) and returns without synchronising.  A fault inside
+ *   a kernel surfaces at the caller's next synchronisation.
+ * Errors: calls return a kda_status.  All argument checks run on the host
+ *   before the first launch; on any error nothing is launched and
+ *   kda_last_error() describes the problem.  Slot ids are device data and are
+ *   checked inside the kernels: an out-of-range id is skipped (its outputs are
+ *   filled with NaN where the call has outputs) instead of being dereferenced.
+ * Pointers: all device pointers must be 16-byte aligned.
+ * Layouts (row-major, innermost last; T = tokens of the call, S = slots):
+ *   q, k      [T][H][dk]   activation dtype       v, z, out [T][H][dv]  activation dtype
+ *   g         [T][H][dk]   fp32 (log decay, <= 0) beta      [T][H]      fp32
+ *   conv_w    [H][2dk+dv][4] fp32 (per head: q channels, then k, then v;
+ *             tap 3 multiplies the current token, tap 0 the token 3 back)
+ *   norm_w    [dv] fp32, shared by all heads
+ *   state     [S][H][dk][dv] fp32      (pool of recurrent states; also the
+ *                                       checkpoint format)
+ *   conv      [S][H][2dk+dv][3] activation dtype (raw inputs of the last 3
+ *                                       tokens, index 0 = oldest)
+ * Supported shapes: dk == dv in {32, 64, 128}; conv width 4; H >= 1.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1,  /* NULL / misaligned pointer, bad size or count */
+    KDA_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement */
+    KDA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
+    KDA_ERR_HIP = 4           /* the HIP runtime refused a launch */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+typedef struct {
+    int32_t num_heads;   /* H: heads handled by this call (one GPU's share) */
+    int32_t head_k;      /* dk */
+    int32_t head_v;      /* dv */
+    int32_t conv_width;  /* must be 4 */
+    int32_t act_dtype;   /* kda_dtype of q, k, v, z, out and the conv state;
+                            the recurrent state is always fp32 */
+    float l2_eps;        /* eps inside the q/k L2 norm (1e-6 by convention) */
+    float rms_eps;       /* eps inside the output RMSNorm (1e-6 by convention) */
+} kda_config;
+
+/*
+ * One decode step for B sequences, one token each, in ONE kernel launch.
+ * [vLLM blog, "KDA prefill and decode": decode fuses the short convolution,
+ *  the state update, the output gate and the normalisation instead of
+ *  launching them separately; agentlenshq, "Fused Kernels and Metadata
+ *  Optimization": one launch, no intermediate tensors, the state is read and
+ *  written once.]
+ *
+ * q, k, v, z, g, beta: this step's inputs, layouts above with T = B.
+ * state_pool, conv_pool: pools of num_slots slots; sequence b reads and
+ *   updates slot slot[b] in place (state and conv state).
+ * slot: [B] int32 device array.  Ids must be distinct within a call; an id
+ *   outside [0, num_slots) makes the kernel skip that sequence and write NaN
+ *   to its out row.
+ * out: [B][H][dv] activation dtype.
+ * B == 0 is a no-op.
+ */
+kda_status kda_decode_step(const kda_config* cfg, int32_t B,
+                           const void* q, const void* k, const void* v, const void* z,
+                           const float* g, const float* beta,
+                           const float* conv_w, const float* norm_w,
+                           float* state_pool, void* conv_pool, int32_t num_slots,
+                           const int32_t* slot, void* out, void* stream);
+
+/*
+ * Chunked prefill of num_seqs packed sequences (chunk = 64 tokens).
+ * [vLLM blog, "KDA prefill and decode": the prefill gathers each request's
+ *  initial recurrent state in one operation; "The Hardest Part": a resumable
+ *  state must exist at the exact prefix boundary; agentlenshq, "Agentic Cache
+ *  Retention Policies": states are kept at fixed intervals and at prompt ends.]
+ *
+ * cu_seqlens: [num_seqs+1] int32 device array, cu_seqlens[0] == 0, non-
+ *   decreasing, cu_seqlens[num_seqs] == total_tokens.  Sequence n owns packed
+ *   tokens [cu_seqlens[n], cu_seqlens[n+1]).  Empty sequences are allowed.
+ * start_pos: [num_seqs] int64 device array or NULL (all zero): the absolute
+ *   position of each sequence's first token.  Chunks are aligned to absolute
+ *   multiples of 64, so a sequence resumed at a multiple of 64 computes the
+ *   same bits as the run that went straight through.
+ * init_slot: [num_seqs] int32: slot of the initial state and conv state in
+ *   the pools, or -1 for a zero state.
+ * final_slot: [num_seqs] int32: slot that receives the final state and conv
+ *   state, or -1 for none.  init_slot[n] == final_slot[n] (in place) is
+ *   allowed; final slots must be distinct and must not be another sequence's
+ *   init slot.
+ * ckpt_interval: 0 = no checkpoints; otherwise a positive multiple of 64.
+ *   Sequence n then writes a checkpoint at every absolute position p with
+ *   p % ckpt_interval == 0 strictly inside (start, start+len), and at its end
+ *   p = start+len (once if both); kda_num_checkpoints() gives the count.  Its
+ *   j-th checkpoint goes to checkpoint slot ckpt_base[n] + j of ckpt_state /
+ *   ckpt_conv (pools of num_ckpt_slots slots, same layout as the live pools).
+ *   A checkpoint at p holds the state after the tokens before position p.
+ * out: [total_tokens][H][dv] activation dtype.
+ * workspace: device scratch of at least kda_prefill_workspace_bytes(...)
+ *   bytes; its contents on entry do not matter.
+ * Precondition on the gate: within any 32 consecutive tokens of a chunk the
+ *   accumulated log-decay of every channel stays above -80 (for instance
+ *   g >= -2.5 everywhere); the intra-chunk decay factors are formed relative
+ *   to the middle of the chunk and would leave the fp32 range otherwise.
+ */
+kda_status kda_prefill_varlen(const kda_config* cfg, int32_t num_seqs, int64_t total_tokens,
+                              const int32_t* cu_seqlens, const int64_t* start_pos,
+                              const void* q, const void* k, const void* v, const void* z,
+                              const float* g, const float* beta,
+                              const float* conv_w, const float* norm_w,
+                              float* state_pool, void* conv_pool, int32_t num_slots,
+                              const int32_t* init_slot, const int32_t* final_slot,
+                              int32_t ckpt_interval, float* ckpt_state, void* ckpt_conv,
+                              int32_t num_ckpt_slots, const int32_t* ckpt_base,
+                              void* out, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * Copy n (state, conv state) slot pairs from the live pools to checkpoint
+ * slots: ckpt[dst_ckpt[i]] = pool[src_slot[i]], bit for bit, all heads.
+ * [vLLM blog, "The Hardest Part": the state registered at a boundary is kept
+ *  apart from the request that goes on extending it.]
+ * Ids outside their pool are skipped.  Destinations must be distinct.
+ */
+kda_status kda_state_checkpoint(const kda_config* cfg, int32_t n,
+                                const float* state_pool, const void* conv_pool, int32_t num_slots,
+                                const int32_t* src_slot,
+                                float* ckpt_state, void* ckpt_conv, int32_t num_ckpt_slots,
+                                const int32_t* dst_ckpt, void* stream);
+
+/*
+ * Copy-on-write resume: pool[dst_slot[i]] = ckpt[src_ckpt[i]], bit for bit.
+ * The checkpoint stays untouched, so one checkpoint can seed many slots.
+ * [vLLM blog, "The Hardest Part": a hit on a cached boundary copies the
+ *  cached state into a private destination before the request extends it,
+ *  and reuse within the same step waits until the copy is safe.]
+ * Ordering: the copy is enqueued on `stream`; a kernel that reads a
+ * destination slot must be enqueued after it on the same stream (or wait on
+ * an event recorded after it).  Ids outside their pool are skipped.
+ */
+kda_status kda_resume(const kda_config* cfg, int32_t n,
+                      const float* ckpt_state, const void* ckpt_conv, int32_t num_ckpt_slots,
+                      const int32_t* src_ckpt,
+                      float* state_pool, void* conv_pool, int32_t num_slots,
+                      const int32_t* dst_slot, void* stream);
+
+/* Workspace bytes kda_prefill_varlen needs for these sizes (0 on a config
+ * error; kda_last_error() then says why). */
+size_t kda_prefill_workspace_bytes(const kda_config* cfg, int32_t num_seqs, int64_t total_tokens);
+
+/* Number of checkpoints kda_prefill_varlen writes for one sequence: the
+ * multiples of interval strictly inside (start, start+len) plus its end; 0
+ * when interval <= 0 or len <= 0.  Host function. */
+int64_t kda_num_checkpoints(int64_t start, int64_t len, int32_t interval);
+
+/* Message of the last error on this thread ("" if none). */
+const char* kda_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,232 @@
+"""Python binding of libkda, the gfx950 KDA layer library (include/kda.h).
+
+The functions here carry the C-ABI names and only marshal arguments: they
+check that torch tensors have the expected device, dtype, shape and
+contiguity, pass their device pointers and the current HIP stream to the
+library, and raise KdaError when the library returns an error.  Every step of
+the computation runs in the library's HIP kernels; there is no fallback.  If
+libkda.so has not been built, importing this package works but every call
+raises KdaLibraryMissing.
+
+Build with ``python -m linear_attention_recurrence_decode_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
+KDA_F32, KDA_BF16 = 0, 1
+
+# every symbol include/kda.h declares
+EXPORTS = (
+    "kda_decode_step", "kda_prefill_varlen", "kda_state_checkpoint", "kda_resume",
+    "kda_prefill_workspace_bytes", "kda_num_checkpoints", "kda_last_error",
+)
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"kda status {status}: {message}")
+        self.status = status
+
+
+class KdaLibraryMissing(RuntimeError):
+    pass
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("head_k", ctypes.c_int32),
+                ("head_v", ctypes.c_int32), ("conv_width", ctypes.c_int32),
+                ("act_dtype", ctypes.c_int32), ("l2_eps", ctypes.c_float),
+                ("rms_eps", ctypes.c_float)]
+
+
+@dataclass
+class Config:
+    num_heads: int
+    head_k: int
+    head_v: int
+    act_dtype: int = KDA_BF16
+    conv_width: int = 4
+    l2_eps: float = 1e-6
+    rms_eps: float = 1e-6
+
+    @property
+    def torch_act(self):
+        return torch.bfloat16 if self.act_dtype == KDA_BF16 else torch.float32
+
+    @property
+    def conv_channels(self):
+        return 2 * self.head_k + self.head_v
+
+    def c(self) -> _Config:
+        return _Config(self.num_heads, self.head_k, self.head_v, self.conv_width,
+                       self.act_dtype, self.l2_eps, self.rms_eps)
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libkda.so (ctypes.CDLL) with argument types set."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise KdaLibraryMissing(f"{LIB_PATH} is not built; run "
+                                "`python -m linear_attention_recurrence_decode_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    CP = ctypes.POINTER(_Config)
+    L.kda_decode_step.argtypes = [CP, I32] + [P] * 8 + [P, P, I32, P, P, P]
+    L.kda_prefill_varlen.argtypes = ([CP, I32, I64, P, P] + [P] * 8 + [P, P, I32, P, P, I32, P, P, I32, P,
+                                     P, P, ctypes.c_size_t, P])
+    L.kda_state_checkpoint.argtypes = [CP, I32, P, P, I32, P, P, P, I32, P, P]
+    L.kda_resume.argtypes = [CP, I32, P, P, I32, P, P, P, I32, P, P]
+    L.kda_prefill_workspace_bytes.argtypes = [CP, I32, I64]
+    L.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
+    L.kda_num_checkpoints.argtypes = [I64, I64, I32]
+    L.kda_num_checkpoints.restype = I64
+    L.kda_last_error.restype = ctypes.c_char_p
+    for f in ("kda_decode_step", "kda_prefill_varlen", "kda_state_checkpoint", "kda_resume"):
+        getattr(L, f).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return lib().kda_last_error().decode()
+
+
+def _check(status: int):
+    if status != KDA_OK:
+        raise KdaError(status, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _want(t, name, dtype, shape=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device (got {t.device})")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+
+
+def kda_num_checkpoints(start: int, length: int, interval: int) -> int:
+    return int(lib().kda_num_checkpoints(int(start), int(length), int(interval)))
+
+
+def kda_prefill_workspace_bytes(cfg: Config, num_seqs: int, total_tokens: int) -> int:
+    n = int(lib().kda_prefill_workspace_bytes(ctypes.byref(cfg.c()), int(num_seqs), int(total_tokens)))
+    if n == 0 and last_error():
+        raise KdaError(KDA_ERR_INVALID_ARG, last_error())
+    return n
+
+
+def kda_decode_step(cfg: Config, q, k, v, z, g, beta, conv_w, norm_w, state_pool, conv_pool,
+                    slot, out, stream=None):
+    """One fused decode step for B = slot.numel() sequences (see include/kda.h)."""
+    B, H, dk, dv, C = slot.numel(), cfg.num_heads, cfg.head_k, cfg.head_v, cfg.conv_channels
+    act = cfg.torch_act
+    S = state_pool.shape[0]
+    _want(q, "q", act, (B, H, dk)); _want(k, "k", act, (B, H, dk))
+    _want(v, "v", act, (B, H, dv)); _want(z, "z", act, (B, H, dv))
+    _want(g, "g", torch.float32, (B, H, dk)); _want(beta, "beta", torch.float32, (B, H))
+    _want(conv_w, "conv_w", torch.float32, (H, C, 4)); _want(norm_w, "norm_w", torch.float32, (dv,))
+    _want(state_pool, "state_pool", torch.float32, (S, H, dk, dv))
+    _want(conv_pool, "conv_pool", act, (S, H, C, 3))
+    _want(slot, "slot", torch.int32, (B,)); _want(out, "out", act, (B, H, dv))
+    _check(lib().kda_decode_step(ctypes.byref(cfg.c()), B, _ptr(q), _ptr(k), _ptr(v), _ptr(z),
+                                 _ptr(g), _ptr(beta), _ptr(conv_w), _ptr(norm_w), _ptr(state_pool),
+                                 _ptr(conv_pool), S, _ptr(slot), _ptr(out), _stream(stream)))
+    return out
+
+
+def kda_prefill_varlen(cfg: Config, cu_seqlens, q, k, v, z, g, beta, conv_w, norm_w,
+                       state_pool, conv_pool, init_slot, final_slot, out, workspace,
+                       start_pos=None, ckpt_interval: int = 0, ckpt_state=None, ckpt_conv=None,
+                       ckpt_base=None, stream=None):
+    """Chunked varlen prefill (see include/kda.h)."""
+    N = cu_seqlens.numel() - 1
+    T = q.shape[0]
+    H, dk, dv, C = cfg.num_heads, cfg.head_k, cfg.head_v, cfg.conv_channels
+    act = cfg.torch_act
+    S = state_pool.shape[0]
+    _want(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
+    _want(start_pos, "start_pos", torch.int64, (N,))
+    _want(q, "q", act, (T, H, dk)); _want(k, "k", act, (T, H, dk))
+    _want(v, "v", act, (T, H, dv)); _want(z, "z", act, (T, H, dv))
+    _want(g, "g", torch.float32, (T, H, dk)); _want(beta, "beta", torch.float32, (T, H))
+    _want(conv_w, "conv_w", torch.float32, (H, C, 4)); _want(norm_w, "norm_w", torch.float32, (dv,))
+    _want(state_pool, "state_pool", torch.float32, (S, H, dk, dv))
+    _want(conv_pool, "conv_pool", act, (S, H, C, 3))
+    _want(init_slot, "init_slot", torch.int32, (N,)); _want(final_slot, "final_slot", torch.int32, (N,))
+    _want(out, "out", act, (T, H, dv))
+    nck = 0
+    if ckpt_interval:
+        nck = ckpt_state.shape[0]
+        _want(ckpt_state, "ckpt_state", torch.float32, (nck, H, dk, dv))
+        _want(ckpt_conv, "ckpt_conv", act, (nck, H, C, 3))
+        _want(ckpt_base, "ckpt_base", torch.int32, (N,))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is not None:
+        _want(workspace, "workspace", workspace.dtype)
+    _check(lib().kda_prefill_varlen(ctypes.byref(cfg.c()), N, T, _ptr(cu_seqlens), _ptr(start_pos),
+                                    _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(g), _ptr(beta),
+                                    _ptr(conv_w), _ptr(norm_w), _ptr(state_pool), _ptr(conv_pool), S,
+                                    _ptr(init_slot), _ptr(final_slot), int(ckpt_interval),
+                                    _ptr(ckpt_state), _ptr(ckpt_conv), nck, _ptr(ckpt_base),
+                                    _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def _copy(fn, cfg, src_state, src_conv, src_idx, dst_state, dst_conv, dst_idx, stream):
+    H, dk, dv, C = cfg.num_heads, cfg.head_k, cfg.head_v, cfg.conv_channels
+    act = cfg.torch_act
+    n = src_idx.numel()
+    for nm, t, shape in (("src_state", src_state, (src_state.shape[0], H, dk, dv)),
+                         ("dst_state", dst_state, (dst_state.shape[0], H, dk, dv))):
+        _want(t, nm, torch.float32, shape)
+    _want(src_conv, "src_conv", act, (src_state.shape[0], H, C, 3))
+    _want(dst_conv, "dst_conv", act, (dst_state.shape[0], H, C, 3))
+    _want(src_idx, "src ids", torch.int32, (n,)); _want(dst_idx, "dst ids", torch.int32, (n,))
+    _check(fn(ctypes.byref(cfg.c()), n, _ptr(src_state), _ptr(src_conv), src_state.shape[0],
+              _ptr(src_idx), _ptr(dst_state), _ptr(dst_conv), dst_state.shape[0], _ptr(dst_idx),
+              _stream(stream)))
+
+
+def kda_state_checkpoint(cfg: Config, state_pool, conv_pool, src_slot, ckpt_state, ckpt_conv,
+                         dst_ckpt, stream=None):
+    """ckpt[dst_ckpt[i]] = pool[src_slot[i]] (bitwise copy)."""
+    _copy(lib().kda_state_checkpoint, cfg, state_pool, conv_pool, src_slot, ckpt_state,
+          ckpt_conv, dst_ckpt, stream)
+
+
+def kda_resume(cfg: Config, ckpt_state, ckpt_conv, src_ckpt, state_pool, conv_pool, dst_slot,
+               stream=None):
+    """pool[dst_slot[i]] = ckpt[src_ckpt[i]] (copy-on-write resume)."""
+    _copy(lib().kda_resume, cfg, ckpt_state, ckpt_conv, src_ckpt, state_pool, conv_pool,
+          dst_slot, stream)

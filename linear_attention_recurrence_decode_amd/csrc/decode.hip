@@ -1,0 +1,210 @@
+// decode.hip -- fused single-launch KDA decode step for gfx950.
+//
+// One workgroup per (sequence, head).  The fp32 dk x dv state of the pair is
+// streamed from HBM once into registers with 128-bit loads, updated there and
+// streamed back once; everything else (conv-state shift, causal conv + SiLU,
+// L2 norms, decay, delta update, readout, gated RMSNorm) happens while the
+// state loads are in flight or on registers/LDS, in the same launch.
+// [vLLM blog "A Preview of Production-Scale Kimi K3 Support on vLLM", section
+//  "KDA prefill and decode": decode runs the short convolution, state update,
+//  output gate and normalisation together rather than as separate launches;
+//  agentlenshq "vLLM Kimi K3 Support", section "Fused Kernels and Metadata
+//  Optimization": a single launch avoids intermediate tensors and repeated
+//  state traffic.]
+//
+// Thread layout: the dv columns are split into NCG groups of 4 (one float4
+// per row), the dk rows into RG row groups; thread (rg, cg) owns rows
+// rg, rg+RG, ... and columns 4cg..4cg+3, i.e. RPT float4 registers.  A wave
+// covers 64/NCG consecutive rows per load instruction, so each instruction
+// reads whole 512-byte rows.  The two dk-reductions (S'^T k and S'^T q) go
+// through the thread's rows, then lane shuffles across row groups of a wave,
+// then LDS across waves.
+//
+// The readout uses o = S^T q = S'^T q + u (q . k) (S' the decayed state,
+// u the delta-rule update), so the state is read once and written once.
+
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+template <int DK, int DV, typename ACT, int NT>
+__global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
+    constexpr int NCG = DV / 4;
+    constexpr int RG = NT / NCG;
+    constexpr int RPT = DK / RG;
+    constexpr int NW = NT / 64;
+    constexpr int C = 2 * DK + DV;
+    static_assert(NCG <= 64 && 64 % NCG == 0, "column groups must tile a wave");
+    static_assert(RG * NCG == NT && RPT * RG == DK, "rows must tile the workgroup");
+    using A = Act<ACT>;
+
+    __shared__ float a_s[C];            // SiLU(conv(x)) for q | k | v
+    __shared__ float eg_s[DK];          // exp(g)
+    __shared__ float red_s[NW][2][DV];  // per-wave partial S'^T k and S'^T q
+    __shared__ float nrm_s[NW][3];      // per-wave partial |a_q|^2, |a_k|^2, a_q.a_k
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int cg = tid % NCG, rg = tid / NCG;
+    const int H = p.H;
+    const int b = blockIdx.x / H, h = blockIdx.x % H;
+    const int64_t bh = static_cast<int64_t>(b) * H + h;
+
+    ACT* out = static_cast<ACT*>(p.out) + bh * DV;
+    const int slot = p.slot[b];
+    if (slot < 0 || slot >= p.num_slots) {
+        for (int j = tid; j < DV; j += NT) A::st(out + j, nan_f32());
+        return;
+    }
+    const int64_t sh = static_cast<int64_t>(slot) * H + h;
+    float* S = p.state + sh * DK * DV;
+
+    // 1. issue the state loads first; the rest of the prologue overlaps them
+    float4 s[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; r++)
+        s[r] = *reinterpret_cast<const float4*>(S + (rg + RG * r) * DV + 4 * cg);
+
+    // 2. conv-state shift + causal depthwise conv (width 4) + SiLU
+    const ACT* xq = static_cast<const ACT*>(p.q) + bh * DK;
+    const ACT* xk = static_cast<const ACT*>(p.k) + bh * DK;
+    const ACT* xv = static_cast<const ACT*>(p.v) + bh * DV;
+    ACT* X = static_cast<ACT*>(p.conv) + sh * C * 3;
+    const float* w = p.conv_w + static_cast<int64_t>(h) * C * 4;
+    for (int c = tid; c < C; c += NT) {
+        const float x = c < DK ? A::ld(xq + c) : (c < 2 * DK ? A::ld(xk + c - DK) : A::ld(xv + c - 2 * DK));
+        ACT* xs = X + c * 3;
+        const float x0 = A::ld(xs), x1 = A::ld(xs + 1), x2 = A::ld(xs + 2);
+        const float4 wc = *reinterpret_cast<const float4*>(w + c * 4);
+        float y = wc.x * x0;
+        y = fmaf(wc.y, x1, y);
+        y = fmaf(wc.z, x2, y);
+        y = fmaf(wc.w, x, y);
+        a_s[c] = silu(y);
+        A::st(xs, x1);
+        A::st(xs + 1, x2);
+        A::st(xs + 2, x);
+    }
+    const float* gp = p.g + bh * DK;
+    for (int i = tid; i < DK; i += NT) eg_s[i] = __expf(gp[i]);
+    __syncthreads();
+
+    // 3. L2 norms of q and k, and q.k
+    float pq = 0.f, pk = 0.f, pqk = 0.f;
+    for (int i = tid; i < DK; i += NT) {
+        const float aq = a_s[i], ak = a_s[DK + i];
+        pq = fmaf(aq, aq, pq);
+        pk = fmaf(ak, ak, pk);
+        pqk = fmaf(aq, ak, pqk);
+    }
+    pq = xor_sum_below<64>(pq);
+    pk = xor_sum_below<64>(pk);
+    pqk = xor_sum_below<64>(pqk);
+    if (lane == 0) {
+        nrm_s[wave][0] = pq;
+        nrm_s[wave][1] = pk;
+        nrm_s[wave][2] = pqk;
+    }
+    __syncthreads();
+    float sq = 0.f, sk = 0.f, sqk = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; w2++) {
+        sq += nrm_s[w2][0];
+        sk += nrm_s[w2][1];
+        sqk += nrm_s[w2][2];
+    }
+    const float rq = rsqrtf(sq + p.l2_eps);
+    const float rk = rsqrtf(sk + p.l2_eps);
+    const float qk = sqk * rq * rk;
+
+    // 4. decay, then the two reductions over the decayed rows
+    float kr[RPT];
+    float4 pred = make_float4(0.f, 0.f, 0.f, 0.f), rr = pred;
+#pragma unroll
+    for (int r = 0; r < RPT; r++) {
+        const int i = rg + RG * r;
+        const float e = eg_s[i];
+        const float kh = a_s[DK + i] * rk;
+        const float qh = a_s[i] * rq;
+        kr[r] = kh;
+        s[r].x *= e; s[r].y *= e; s[r].z *= e; s[r].w *= e;
+        pred.x = fmaf(s[r].x, kh, pred.x); pred.y = fmaf(s[r].y, kh, pred.y);
+        pred.z = fmaf(s[r].z, kh, pred.z); pred.w = fmaf(s[r].w, kh, pred.w);
+        rr.x = fmaf(s[r].x, qh, rr.x); rr.y = fmaf(s[r].y, qh, rr.y);
+        rr.z = fmaf(s[r].z, qh, rr.z); rr.w = fmaf(s[r].w, qh, rr.w);
+    }
+    pred.x = xor_sum_from<NCG>(pred.x); pred.y = xor_sum_from<NCG>(pred.y);
+    pred.z = xor_sum_from<NCG>(pred.z); pred.w = xor_sum_from<NCG>(pred.w);
+    rr.x = xor_sum_from<NCG>(rr.x); rr.y = xor_sum_from<NCG>(rr.y);
+    rr.z = xor_sum_from<NCG>(rr.z); rr.w = xor_sum_from<NCG>(rr.w);
+    if (lane < NCG) {
+        *reinterpret_cast<float4*>(&red_s[wave][0][4 * cg]) = pred;
+        *reinterpret_cast<float4*>(&red_s[wave][1][4 * cg]) = rr;
+    }
+    __syncthreads();
+    pred = *reinterpret_cast<const float4*>(&red_s[0][0][4 * cg]);
+    rr = *reinterpret_cast<const float4*>(&red_s[0][1][4 * cg]);
+#pragma unroll
+    for (int w2 = 1; w2 < NW; w2++) {
+        const float4 a = *reinterpret_cast<const float4*>(&red_s[w2][0][4 * cg]);
+        const float4 c = *reinterpret_cast<const float4*>(&red_s[w2][1][4 * cg]);
+        pred.x += a.x; pred.y += a.y; pred.z += a.z; pred.w += a.w;
+        rr.x += c.x; rr.y += c.y; rr.z += c.z; rr.w += c.w;
+    }
+
+    // 5. delta update u = beta (v - S'^T k), readout o = S'^T q + u (q.k)
+    const float bt = p.beta[bh];
+    const float4 vh = *reinterpret_cast<const float4*>(&a_s[2 * DK + 4 * cg]);
+    float4 u, o;
+    u.x = bt * (vh.x - pred.x); u.y = bt * (vh.y - pred.y);
+    u.z = bt * (vh.z - pred.z); u.w = bt * (vh.w - pred.w);
+    o.x = fmaf(u.x, qk, rr.x); o.y = fmaf(u.y, qk, rr.y);
+    o.z = fmaf(u.z, qk, rr.z); o.w = fmaf(u.w, qk, rr.w);
+
+    // 6. S = S' + k u^T, written back once
+#pragma unroll
+    for (int r = 0; r < RPT; r++) {
+        const float kh = kr[r];
+        s[r].x = fmaf(kh, u.x, s[r].x); s[r].y = fmaf(kh, u.y, s[r].y);
+        s[r].z = fmaf(kh, u.z, s[r].z); s[r].w = fmaf(kh, u.w, s[r].w);
+        *reinterpret_cast<float4*>(S + (rg + RG * r) * DV + 4 * cg) = s[r];
+    }
+
+    // 7. gated RMSNorm over dv (every row group holds all of o)
+    float ss = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
+    ss = xor_sum_below<NCG>(ss);
+    if (rg == 0) {
+        const float rinv = rsqrtf(ss * (1.0f / DV) + p.rms_eps);
+        const float4 nw = *reinterpret_cast<const float4*>(p.norm_w + 4 * cg);
+        const float4 zz = A::ld4(static_cast<const ACT*>(p.z) + bh * DV + 4 * cg);
+        float4 y;
+        y.x = o.x * rinv * nw.x * sigmoid(zz.x);
+        y.y = o.y * rinv * nw.y * sigmoid(zz.y);
+        y.z = o.z * rinv * nw.z * sigmoid(zz.z);
+        y.w = o.w * rinv * nw.w * sigmoid(zz.w);
+        A::st4(out + 4 * cg, y);
+    }
+}
+
+template <int DK, int DV, typename ACT, int NT>
+static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
+    const int64_t blocks = static_cast<int64_t>(p.B) * p.H;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_kernel<DK, DV, ACT, NT>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(NT), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(int dk, int dv, int act, const DecodeParams& p, hipStream_t s) {
+    if (dk != dv) return hipErrorInvalidValue;
+    const bool bf = act == 1;
+    switch (dk) {
+        case 32:  return bf ? launch_decode_t<32, 32, bf16_t, 64>(p, s) : launch_decode_t<32, 32, float, 64>(p, s);
+        case 64:  return bf ? launch_decode_t<64, 64, bf16_t, 128>(p, s) : launch_decode_t<64, 64, float, 128>(p, s);
+        case 128: return bf ? launch_decode_t<128, 128, bf16_t, 256>(p, s) : launch_decode_t<128, 128, float, 256>(p, s);
+        default:  return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace kda

@@ -1,0 +1,80 @@
+// kda_device.h -- device helpers shared by the KDA kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Storage type of bf16 activations: the raw 16 bits.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// Activation load/store: element access and 4-wide vector access.
+template <typename ACT> struct Act;
+
+template <> struct Act<float> {
+    static constexpr int kBytes = 4;
+    __device__ __forceinline__ static float ld(const float* p) { return *p; }
+    __device__ __forceinline__ static void st(float* p, float x) { *p = x; }
+    __device__ __forceinline__ static float4 ld4(const float* p) {
+        return *reinterpret_cast<const float4*>(p);
+    }
+    __device__ __forceinline__ static void st4(float* p, float4 x) {
+        *reinterpret_cast<float4*>(p) = x;
+    }
+};
+
+template <> struct Act<bf16_t> {
+    static constexpr int kBytes = 2;
+    __device__ __forceinline__ static float ld(const bf16_t* p) { return bf16_to_f32(p->bits); }
+    __device__ __forceinline__ static void st(bf16_t* p, float x) { p->bits = f32_to_bf16(x); }
+    __device__ __forceinline__ static float4 ld4(const bf16_t* p) {
+        uint2 r = *reinterpret_cast<const uint2*>(p);
+        return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                           __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+    }
+    __device__ __forceinline__ static void st4(bf16_t* p, float4 x) {
+        uint2 r;
+        r.x = static_cast<uint32_t>(f32_to_bf16(x.x)) | (static_cast<uint32_t>(f32_to_bf16(x.y)) << 16);
+        r.y = static_cast<uint32_t>(f32_to_bf16(x.z)) | (static_cast<uint32_t>(f32_to_bf16(x.w)) << 16);
+        *reinterpret_cast<uint2*>(p) = r;
+    }
+};
+
+__device__ __forceinline__ float silu(float y) { return y / (1.0f + __expf(-y)); }
+__device__ __forceinline__ float sigmoid(float y) { return 1.0f / (1.0f + __expf(-y)); }
+
+// Sum over the lanes of a wave64 whose lane ids differ only in the bits of
+// [lo_mask, 64): e.g. lo = 32 sums lane l with lane l ^ 32.
+template <int LO>
+__device__ __forceinline__ float xor_sum_from(float x) {
+#pragma unroll
+    for (int off = LO; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// Sum over the lanes whose ids differ only in bits below HI (HI a power of 2).
+template <int HI>
+__device__ __forceinline__ float xor_sum_below(float x) {
+#pragma unroll
+    for (int off = 1; off < HI; off <<= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+__device__ __forceinline__ float nan_f32() { return __uint_as_float(0x7fc00000u); }
+
+}  // namespace kda

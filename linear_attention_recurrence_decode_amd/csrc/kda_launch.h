@@ -1,0 +1,87 @@
+// kda_launch.h -- internal interface between the C ABI (kda_api.cpp) and the
+// kernel launchers.  Not installed; the public interface is include/kda.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeParams {
+    int32_t B, H, num_slots;
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* z;
+    const float* g;
+    const float* beta;
+    const float* conv_w;
+    const float* norm_w;
+    float* state;
+    void* conv;
+    const int32_t* slot;
+    void* out;
+    float l2_eps, rms_eps;
+};
+
+struct CopyParams {
+    int32_t n, H;
+    int64_t state_floats;  // dk * dv per head
+    int64_t conv_bytes;    // (2dk+dv) * 3 * act bytes per head (multiple of 16)
+    const float* src_state;
+    const void* src_conv;
+    int32_t src_slots;
+    const int32_t* src_idx;
+    float* dst_state;
+    void* dst_conv;
+    int32_t dst_slots;
+    const int32_t* dst_idx;
+};
+
+// Per-sequence work item of the prefill, built on the device from cu_seqlens
+// and start_pos (longest sequences first).
+struct SeqWork {
+    int32_t seq;        // sequence index
+    int32_t tok0;       // first packed token
+    int32_t len;        // tokens
+    int32_t pad;
+    int64_t start;      // absolute position of the first token
+};
+
+struct PrefillParams {
+    int32_t N, H;
+    int64_t T;
+    const int32_t* cu_seqlens;
+    const int64_t* start_pos;
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* z;
+    const float* g;
+    const float* beta;
+    const float* conv_w;
+    const float* norm_w;
+    float* state;
+    void* conv;
+    int32_t num_slots;
+    const int32_t* init_slot;
+    const int32_t* final_slot;
+    int32_t ckpt_interval;
+    float* ckpt_state;
+    void* ckpt_conv;
+    int32_t num_ckpt_slots;
+    const int32_t* ckpt_base;
+    void* out;
+    SeqWork* work;      // [N] in the workspace
+    float l2_eps, rms_eps;
+};
+
+// Each launcher returns hipSuccess or the launch error.
+hipError_t launch_decode(int dk, int dv, int act, const DecodeParams& p, hipStream_t s);
+hipError_t launch_copy(const CopyParams& p, hipStream_t s);
+hipError_t launch_prefill(int dk, int dv, int act, const PrefillParams& p, hipStream_t s);
+bool prefill_supported(int dk, int dv, int act);
+size_t prefill_workspace_bytes(int32_t N, int32_t H, int64_t T, int dk, int dv);
+
+}  // namespace kda

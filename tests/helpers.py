@@ -1,0 +1,53 @@
+"""Small helpers shared by the GPU tests: tensor transfer, error metrics and
+the tolerances the parity tests use.
+
+Tolerances (relative L2 error over a whole tensor, in fp64):
+  fp32 activations:  1e-4 on outputs and final states
+  bf16 activations:  1e-2 on outputs, 5e-3 on final states
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+TOL_F32 = 1e-4
+TOL_BF16_OUT = 1e-2
+TOL_BF16_STATE = 5e-3
+
+
+def say(*a):
+    """Print and flush, so a failing GPU step names its case."""
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a: np.ndarray, dtype=None) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rel_l2(x, ref) -> float:
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = np.linalg.norm((x - ref).ravel())
+    n = np.linalg.norm(ref.ravel())
+    return float(d / n) if n > 0 else float(d)
+
+
+def tols(act: str):
+    if act == "f32":
+        return TOL_F32, TOL_F32
+    return TOL_BF16_OUT, TOL_BF16_STATE
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """Raw bytes of a tensor, for bitwise comparisons."""
+    return t.detach().contiguous().cpu().view(torch.uint8).numpy().copy()

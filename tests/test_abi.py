@@ -1,0 +1,128 @@
+"""C-ABI checks that need no GPU: libkda.so loads, exports every symbol that
+include/kda.h declares, and rejects bad arguments on the host (before any HIP
+call) with the documented status codes.  Fake, aligned, non-NULL addresses
+stand in for device pointers: every call here fails validation or is a no-op,
+so nothing is dereferenced or launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import linear_attention_recurrence_decode_amd as kda
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kda.LIB_PATH), reason="libkda.so not built")
+
+FAKE = 0x10000          # 16-byte aligned stand-in for a device address
+MISALIGNED = 0x10008
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(kda.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(kda.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def cfg(**kw):
+    base = dict(num_heads=4, head_k=128, head_v=128, act_dtype=kda.KDA_BF16)
+    base.update(kw)
+    return kda.Config(**base)
+
+
+def decode_call(c, B=2, num_slots=8, **ptrs):
+    P = {n: FAKE for n in ("q", "k", "v", "z", "g", "beta", "conv_w", "norm_w", "state", "conv",
+                           "slot", "out")}
+    P.update(ptrs)
+    cp = ctypes.byref(c.c()) if c is not None else None
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return kda.lib().kda_decode_step(cp, B, vp(P["q"]), vp(P["k"]), vp(P["v"]), vp(P["z"]),
+                                     vp(P["g"]), vp(P["beta"]), vp(P["conv_w"]), vp(P["norm_w"]),
+                                     vp(P["state"]), vp(P["conv"]), num_slots, vp(P["slot"]),
+                                     vp(P["out"]), None)
+
+
+def test_decode_validation():
+    assert decode_call(None) == kda.KDA_ERR_INVALID_ARG
+    assert "cfg" in kda.last_error()
+    assert decode_call(cfg(head_k=96, head_v=96)) == kda.KDA_ERR_UNSUPPORTED
+    assert decode_call(cfg(head_k=128, head_v=64)) == kda.KDA_ERR_UNSUPPORTED
+    assert decode_call(cfg(conv_width=3)) == kda.KDA_ERR_UNSUPPORTED
+    assert decode_call(cfg(act_dtype=7)) == kda.KDA_ERR_INVALID_ARG
+    assert decode_call(cfg(num_heads=0)) == kda.KDA_ERR_INVALID_ARG
+    assert decode_call(cfg(l2_eps=float("nan"))) == kda.KDA_ERR_INVALID_ARG
+    assert decode_call(cfg(), B=-1) == kda.KDA_ERR_INVALID_ARG
+    assert decode_call(cfg(), num_slots=0) == kda.KDA_ERR_INVALID_ARG
+    for name in ("q", "k", "v", "z", "g", "beta", "conv_w", "norm_w", "state", "conv", "slot", "out"):
+        assert decode_call(cfg(), **{name: None}) == kda.KDA_ERR_INVALID_ARG, name
+    assert decode_call(cfg(), q=MISALIGNED) == kda.KDA_ERR_INVALID_ARG
+    assert "aligned" in kda.last_error()
+    assert decode_call(cfg(), B=1 << 30) == kda.KDA_ERR_INVALID_ARG      # grid overflow
+    # B == 0 is a no-op that touches no pointer
+    assert decode_call(cfg(), B=0, q=None) == kda.KDA_OK
+    assert kda.last_error() == ""
+
+
+def copy_call(fn, c, n=3, src_slots=4, dst_slots=4, **ptrs):
+    P = {n_: FAKE for n_ in ("ss", "sc", "si", "ds", "dc", "di")}
+    P.update(ptrs)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return fn(ctypes.byref(c.c()), n, vp(P["ss"]), vp(P["sc"]), src_slots, vp(P["si"]),
+              vp(P["ds"]), vp(P["dc"]), dst_slots, vp(P["di"]), None)
+
+
+@pytest.mark.parametrize("name", ["kda_state_checkpoint", "kda_resume"])
+def test_copy_validation(name):
+    fn = getattr(kda.lib(), name)
+    assert copy_call(fn, cfg(), n=-1) == kda.KDA_ERR_INVALID_ARG
+    assert copy_call(fn, cfg(), src_slots=0) == kda.KDA_ERR_INVALID_ARG
+    for p in ("ss", "sc", "si", "ds", "dc", "di"):
+        assert copy_call(fn, cfg(), **{p: None}) == kda.KDA_ERR_INVALID_ARG, p
+    assert copy_call(fn, cfg(), ss=MISALIGNED) == kda.KDA_ERR_INVALID_ARG
+    assert copy_call(fn, cfg(head_k=48, head_v=48)) == kda.KDA_ERR_UNSUPPORTED
+    assert copy_call(fn, cfg(), n=0, ss=None) == kda.KDA_OK
+
+
+def prefill_call(c, N=2, T=100, interval=0, ws_bytes=1 << 20, nck=4, **ptrs):
+    names = ("cu", "sp", "q", "k", "v", "z", "g", "beta", "conv_w", "norm_w", "state", "conv",
+             "init", "final", "cks", "ckc", "ckb", "out", "ws")
+    P = {n: FAKE for n in names}
+    P.update(ptrs)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return kda.lib().kda_prefill_varlen(
+        ctypes.byref(c.c()), N, T, vp(P["cu"]), vp(P["sp"]), vp(P["q"]), vp(P["k"]), vp(P["v"]),
+        vp(P["z"]), vp(P["g"]), vp(P["beta"]), vp(P["conv_w"]), vp(P["norm_w"]), vp(P["state"]),
+        vp(P["conv"]), 8, vp(P["init"]), vp(P["final"]), interval, vp(P["cks"]), vp(P["ckc"]),
+        nck, vp(P["ckb"]), vp(P["out"]), vp(P["ws"]), ws_bytes, None)
+
+
+def test_prefill_validation():
+    assert prefill_call(cfg(), N=-1) == kda.KDA_ERR_INVALID_ARG
+    assert prefill_call(cfg(), T=-5) == kda.KDA_ERR_INVALID_ARG
+    assert prefill_call(cfg(), T=1 << 31) == kda.KDA_ERR_INVALID_ARG
+    assert prefill_call(cfg(), interval=100) == kda.KDA_ERR_INVALID_ARG
+    assert prefill_call(cfg(), interval=-64) == kda.KDA_ERR_INVALID_ARG
+    assert prefill_call(cfg(head_k=96, head_v=96)) == kda.KDA_ERR_UNSUPPORTED
+
+
+def test_num_checkpoints_matches_oracle_rule():
+    rng = np.random.default_rng(5)
+    for _ in range(500):
+        start = int(rng.integers(0, 1 << 20))
+        length = int(rng.integers(0, 1 << 16))
+        interval = int(rng.choice([0, 64, 128, 4096, 32768]))
+        assert kda.kda_num_checkpoints(start, length, interval) == oracle.num_checkpoints(start, length, interval)

@@ -13,10 +13,10 @@
 //  state traffic.]
 //
 // Thread layout: the dv columns are split into NCG groups of 4 (one float4
-// per row), the dk rows into RG row groups; thread (rg, cg) owns rows
-// rg, rg+RG, ... and columns 4cg..4cg+3, i.e. RPT float4 registers.  A wave
-// covers 64/NCG consecutive rows per load instruction, so each instruction
-// reads whole 512-byte rows.  The two dk-reductions (S'^T k and S'^T q) go
+// per row), the dk rows into RG blocks of RPT consecutive rows; thread
+// (rg, cg) owns rows rg*RPT .. rg*RPT+RPT-1 and columns 4cg..4cg+3, i.e. RPT
+// float4 registers.  Each load instruction of a wave reads whole rows
+// (NCG lanes x 16 bytes per row).  The two dk-reductions (S'^T k and S'^T q) go
 // through the thread's rows, then lane shuffles across row groups of a wave,
 // then LDS across waves.
 //
@@ -35,8 +35,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
     constexpr int RPT = DK / RG;
     constexpr int NW = NT / 64;
     constexpr int C = 2 * DK + DV;
+    constexpr int CPT = (C + NT - 1) / NT;  // conv channels per thread
     static_assert(NCG <= 64 && 64 % NCG == 0, "column groups must tile a wave");
     static_assert(RG * NCG == NT && RPT * RG == DK, "rows must tile the workgroup");
+    static_assert(DK <= NT, "one thread per key channel for the gate");
     using A = Act<ACT>;
 
     __shared__ float a_s[C];            // SiLU(conv(x)) for q | k | v
@@ -58,39 +60,64 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
         return;
     }
     const int64_t sh = static_cast<int64_t>(slot) * H + h;
-    float* S = p.state + sh * DK * DV;
 
-    // 1. issue the state loads first; the rest of the prologue overlaps them
-    float4 s[RPT];
-#pragma unroll
-    for (int r = 0; r < RPT; r++)
-        s[r] = *reinterpret_cast<const float4*>(S + (rg + RG * r) * DV + 4 * cg);
-
-    // 2. conv-state shift + causal depthwise conv (width 4) + SiLU
+    // 1. small operands first, as raw bits and with unconditional (clamped)
+    // addresses.  Vector-memory waits complete in issue order, so everything
+    // the prologue and epilogue need is requested before the state and
+    // converted only after the state loads are in flight.
     const ACT* xq = static_cast<const ACT*>(p.q) + bh * DK;
     const ACT* xk = static_cast<const ACT*>(p.k) + bh * DK;
     const ACT* xv = static_cast<const ACT*>(p.v) + bh * DV;
     ACT* X = static_cast<ACT*>(p.conv) + sh * C * 3;
     const float* w = p.conv_w + static_cast<int64_t>(h) * C * 4;
-    for (int c = tid; c < C; c += NT) {
-        const float x = c < DK ? A::ld(xq + c) : (c < 2 * DK ? A::ld(xk + c - DK) : A::ld(xv + c - 2 * DK));
-        ACT* xs = X + c * 3;
-        const float x0 = A::ld(xs), x1 = A::ld(xs + 1), x2 = A::ld(xs + 2);
-        const float4 wc = *reinterpret_cast<const float4*>(w + c * 4);
-        float y = wc.x * x0;
-        y = fmaf(wc.y, x1, y);
-        y = fmaf(wc.z, x2, y);
-        y = fmaf(wc.w, x, y);
-        a_s[c] = silu(y);
-        A::st(xs, x1);
-        A::st(xs + 1, x2);
-        A::st(xs + 2, x);
+    typename A::raw xin[CPT], x0[CPT], x1[CPT], x2[CPT];
+    float4 wc[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; j++) {
+        const int c = min(tid + j * NT, C - 1);
+        const ACT* src = c < DK ? xq + c : (c < 2 * DK ? xk + (c - DK) : xv + (c - 2 * DK));
+        xin[j] = A::ld_raw(src);
+        x0[j] = A::ld_raw(X + c * 3);
+        x1[j] = A::ld_raw(X + c * 3 + 1);
+        x2[j] = A::ld_raw(X + c * 3 + 2);
+        wc[j] = *reinterpret_cast<const float4*>(w + c * 4);
     }
-    const float* gp = p.g + bh * DK;
-    for (int i = tid; i < DK; i += NT) eg_s[i] = __expf(gp[i]);
+    const float gv = p.g[bh * DK + min(tid, DK - 1)];
+    const float bt = p.beta[bh];
+    const float4 nw = *reinterpret_cast<const float4*>(p.norm_w + 4 * cg);
+    const typename A::raw4 zraw = A::ld4_raw(static_cast<const ACT*>(p.z) + bh * DV + 4 * cg);
+
+    // 2. the state: RPT consecutive rows x 4 columns per thread, through a
+    // buffer resource covering this (slot, head) only
+    __builtin_amdgcn_sched_barrier(0);
+    const auto rs = make_rsrc(p.state + sh * DK * DV, DK * DV * 4);
+    const uint32_t voff = static_cast<uint32_t>((rg * RPT * DV + 4 * cg) * 4);
+    float4 s[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; r++) s[r] = buf_ld4(rs, voff + (r % 8) * DV * 4, (r / 8) * 8 * DV * 4);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 3. conv-state shift + causal depthwise conv (width 4) + SiLU
+#pragma unroll
+    for (int j = 0; j < CPT; j++) {
+        const int c = tid + j * NT;
+        if (c < C) {
+            const float f0 = A::cvt(x0[j]), f1 = A::cvt(x1[j]), f2 = A::cvt(x2[j]), fx = A::cvt(xin[j]);
+            float y = wc[j].x * f0;
+            y = fmaf(wc[j].y, f1, y);
+            y = fmaf(wc[j].z, f2, y);
+            y = fmaf(wc[j].w, fx, y);
+            a_s[c] = silu(y);
+            ACT* xs = X + c * 3;
+            reinterpret_cast<typename A::raw*>(xs)[0] = x1[j];
+            reinterpret_cast<typename A::raw*>(xs)[1] = x2[j];
+            reinterpret_cast<typename A::raw*>(xs)[2] = xin[j];
+        }
+    }
+    if (tid < DK) eg_s[tid] = __expf(gv);
     __syncthreads();
 
-    // 3. L2 norms of q and k, and q.k
+    // 4. L2 norms of q and k, and q.k
     float pq = 0.f, pk = 0.f, pqk = 0.f;
     for (int i = tid; i < DK; i += NT) {
         const float aq = a_s[i], ak = a_s[DK + i];
@@ -118,16 +145,14 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
     const float rk = rsqrtf(sk + p.l2_eps);
     const float qk = sqk * rq * rk;
 
-    // 4. decay, then the two reductions over the decayed rows
-    float kr[RPT];
+    // 5. decay, then the two reductions over the decayed rows
     float4 pred = make_float4(0.f, 0.f, 0.f, 0.f), rr = pred;
 #pragma unroll
     for (int r = 0; r < RPT; r++) {
-        const int i = rg + RG * r;
+        const int i = rg * RPT + r;
         const float e = eg_s[i];
         const float kh = a_s[DK + i] * rk;
         const float qh = a_s[i] * rq;
-        kr[r] = kh;
         s[r].x *= e; s[r].y *= e; s[r].z *= e; s[r].w *= e;
         pred.x = fmaf(s[r].x, kh, pred.x); pred.y = fmaf(s[r].y, kh, pred.y);
         pred.z = fmaf(s[r].z, kh, pred.z); pred.w = fmaf(s[r].w, kh, pred.w);
@@ -153,8 +178,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
         rr.x += c.x; rr.y += c.y; rr.z += c.z; rr.w += c.w;
     }
 
-    // 5. delta update u = beta (v - S'^T k), readout o = S'^T q + u (q.k)
-    const float bt = p.beta[bh];
+    // 6. delta update u = beta (v - S'^T k), readout o = S'^T q + u (q.k)
     const float4 vh = *reinterpret_cast<const float4*>(&a_s[2 * DK + 4 * cg]);
     float4 u, o;
     u.x = bt * (vh.x - pred.x); u.y = bt * (vh.y - pred.y);
@@ -162,22 +186,21 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
     o.x = fmaf(u.x, qk, rr.x); o.y = fmaf(u.y, qk, rr.y);
     o.z = fmaf(u.z, qk, rr.z); o.w = fmaf(u.w, qk, rr.w);
 
-    // 6. S = S' + k u^T, written back once
+    // 7. S = S' + k u^T, written back once
 #pragma unroll
     for (int r = 0; r < RPT; r++) {
-        const float kh = kr[r];
+        const float kh = a_s[DK + rg * RPT + r] * rk;
         s[r].x = fmaf(kh, u.x, s[r].x); s[r].y = fmaf(kh, u.y, s[r].y);
         s[r].z = fmaf(kh, u.z, s[r].z); s[r].w = fmaf(kh, u.w, s[r].w);
-        *reinterpret_cast<float4*>(S + (rg + RG * r) * DV + 4 * cg) = s[r];
+        buf_st4(rs, voff + (r % 8) * DV * 4, (r / 8) * 8 * DV * 4, s[r]);
     }
 
-    // 7. gated RMSNorm over dv (every row group holds all of o)
+    // 8. gated RMSNorm over dv (every row group holds all of o)
     float ss = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
     ss = xor_sum_below<NCG>(ss);
     if (rg == 0) {
         const float rinv = rsqrtf(ss * (1.0f / DV) + p.rms_eps);
-        const float4 nw = *reinterpret_cast<const float4*>(p.norm_w + 4 * cg);
-        const float4 zz = A::ld4(static_cast<const ACT*>(p.z) + bh * DV + 4 * cg);
+        const float4 zz = A::cvt4(zraw);
         float4 y;
         y.x = o.x * rinv * nw.x * sigmoid(zz.x);
         y.y = o.y * rinv * nw.y * sigmoid(zz.y);

@@ -28,6 +28,12 @@ template <typename ACT> struct Act;
 
 template <> struct Act<float> {
     static constexpr int kBytes = 4;
+    using raw = float;     // as loaded, before conversion
+    __device__ __forceinline__ static raw ld_raw(const float* p) { return *p; }
+    __device__ __forceinline__ static float cvt(raw r) { return r; }
+    using raw4 = float4;
+    __device__ __forceinline__ static raw4 ld4_raw(const float* p) { return *reinterpret_cast<const float4*>(p); }
+    __device__ __forceinline__ static float4 cvt4(raw4 r) { return r; }
     __device__ __forceinline__ static float ld(const float* p) { return *p; }
     __device__ __forceinline__ static void st(float* p, float x) { *p = x; }
     __device__ __forceinline__ static float4 ld4(const float* p) {
@@ -40,6 +46,15 @@ template <> struct Act<float> {
 
 template <> struct Act<bf16_t> {
     static constexpr int kBytes = 2;
+    using raw = uint16_t;
+    __device__ __forceinline__ static raw ld_raw(const bf16_t* p) { return p->bits; }
+    __device__ __forceinline__ static float cvt(raw r) { return bf16_to_f32(r); }
+    using raw4 = uint2;
+    __device__ __forceinline__ static raw4 ld4_raw(const bf16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+    __device__ __forceinline__ static float4 cvt4(raw4 r) {
+        return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                           __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+    }
     __device__ __forceinline__ static float ld(const bf16_t* p) { return bf16_to_f32(p->bits); }
     __device__ __forceinline__ static void st(bf16_t* p, float x) { p->bits = f32_to_bf16(x); }
     __device__ __forceinline__ static float4 ld4(const bf16_t* p) {
@@ -76,5 +91,30 @@ __device__ __forceinline__ float xor_sum_below(float x) {
 }
 
 __device__ __forceinline__ float nan_f32() { return __uint_as_float(0x7fc00000u); }
+
+// Raw buffer access: a 128-bit resource (base, size in bytes) in scalar
+// registers, a per-lane byte offset and a uniform byte offset.  Accesses past
+// `bytes` read zero and drop writes.  The third descriptor word is the gfx9
+// family's raw-buffer format.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ float4 buf_ld4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), 0);
+    return make_float4(__int_as_float(v.x), __int_as_float(v.y), __int_as_float(v.z), __int_as_float(v.w));
+}
+
+__device__ __forceinline__ void buf_st4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float4 x) {
+    i32x4 v;
+    v.x = __float_as_int(x.x);
+    v.y = __float_as_int(x.y);
+    v.z = __float_as_int(x.z);
+    v.w = __float_as_int(x.w);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(voff), static_cast<int>(soff), 0);
+}
 
 }  // namespace kda

@@ -90,6 +90,19 @@ __device__ __forceinline__ float xor_sum_below(float x) {
     return x;
 }
 
+// Sum over aligned groups of G lanes (G = 1, 2, 4, 8 or 16) with DPP lane
+// moves: swap neighbours, swap pairs, mirror within 8, mirror within 16.
+// Every lane of a group ends with the group's sum.
+template <int G>
+__device__ __forceinline__ float dpp_group_sum(float x) {
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "group of 1..16 lanes");
+    if constexpr (G >= 2) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+    if constexpr (G >= 4) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+    if constexpr (G >= 8) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
+    if constexpr (G >= 16) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));
+    return x;
+}
+
 __device__ __forceinline__ float nan_f32() { return __uint_as_float(0x7fc00000u); }
 
 // Raw buffer access: a 128-bit resource (base, size in bytes) in scalar
@@ -106,6 +119,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 __device__ __forceinline__ float4 buf_ld4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), 0);
     return make_float4(__int_as_float(v.x), __int_as_float(v.y), __int_as_float(v.z), __int_as_float(v.w));
+}
+
+__device__ __forceinline__ float buf_ldf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(voff), static_cast<int>(soff), 0));
+}
+
+__device__ __forceinline__ uint16_t buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(voff), static_cast<int>(soff), 0);
+}
+
+__device__ __forceinline__ void buf_stf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(x), r, static_cast<int>(voff), static_cast<int>(soff), 0);
+}
+
+__device__ __forceinline__ void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint16_t x) {
+    __builtin_amdgcn_raw_buffer_store_b16(x, r, static_cast<int>(voff), static_cast<int>(soff), 0);
 }
 
 __device__ __forceinline__ void buf_st4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float4 x) {

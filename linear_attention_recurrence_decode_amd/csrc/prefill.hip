@@ -1,16 +1,766 @@
-// prefill.hip -- chunked KDA prefill (not yet built: every request is
-// reported as unsupported).
+// prefill.hip -- chunked KDA prefill over packed variable-length sequences
+// for gfx950, with recurrent-state checkpoints.
+//
+// [vLLM blog "A Preview of Production-Scale Kimi K3 Support on vLLM",
+//  section "KDA prefill and decode": the prefill gathers each request's
+//  initial recurrent state in one operation and runs a chunked kernel around
+//  the recurrence; section "The Hardest Part: Prefix Caching for KDA": a
+//  resumable state must exist at exact prefix boundaries; agentlenshq "vLLM
+//  Kimi K3 Support", section "Agentic Cache Retention Policies": states are
+//  kept at fixed intervals and at prompt ends.]
+//
+// Chunked form.  For a chunk of n <= 64 tokens entered with state S
+// (dk x dv), Gam the within-chunk cumulative log-decay per key channel, and
+// the gated delta rule S_t = (I - b_t k_t k_t^T) Diag(exp g_t) S_{t-1} +
+// b_t k_t v_t^T unrolled over the chunk:
+//   M[t,s] = sum_i k[t,i] k[s,i] exp(Gam[t,i] - Gam[s,i])   (s <  t)
+//   P[t,s] = sum_i q[t,i] k[s,i] exp(Gam[t,i] - Gam[s,i])   (s <= t)
+//   T      = (I + Diag(b) M)^{-1}                              (unit lower)
+//   U      = T Diag(b) (V - (k * exp(Gam)) S)                  (the chunk's u_t)
+//   O      = (q * exp(Gam)) S + P U                            (readouts)
+//   S'     = Diag(exp Gam_end) S + (k * exp(Gam_end - Gam))^T U
+// The pairwise decays are factored through a reference row r = 31 (the
+// chunk's middle): k*exp(Gam - Gam_r) times k*exp(Gam_r - Gam).  Per-channel
+// factors exp(Gam_r), exp(Gam_end - Gam_r) and exp(Gam_end) then move onto the
+// state side, so the three stored operands K+ = k exp(Gam-Gam_r),
+// K- = k exp(Gam_r-Gam), Q+ = q exp(Gam-Gam_r) serve every product.  This needs
+// |Gam_t - Gam_r| to stay inside the fp32 exponent range for every channel,
+// i.e. the log-decay accumulated over any 32 tokens of a chunk above about
+// -80.
+//
+// Workgroup = one (sequence, head) chain, NW = dv/16 waves, chunks in order.
+// Phase A (state independent): raw rows staged in LDS, causal conv + SiLU,
+// L2 norms, cumulative decay, K+/K-/Q+ as bf16 hi/lo planes, L = Diag(b) M
+// and P on MFMA, and the inverses of the four 16x16 diagonal blocks of I + L
+// by forward substitution in fp32 (eight threads per column).  T itself is
+// never formed: phase B solves (I + L) U = Y block by block,
+// U_a = T_aa (Y_a - sum_{c<a} L_ac U_c).
+// Phase B (state dependent): wave w owns columns [16w, 16w+16) of S in MFMA
+// accumulator layout (lane l: rows 4(l/16)+e of each 16-row tile, column
+// l%16).  Contractions over a 32-index block use the permuted order
+// {4g..4g+3, 16+4g..16+4g+3} for lane group g, which is exactly what two
+// stacked accumulator tiles hold, so S, Y and U feed the MFMA B operand from
+// registers; the LDS operand reads the same permutation.  Every product uses
+// three bf16 MFMAs (hi*hi + hi*lo + lo*hi), i.e. about fp32 accuracy.
+// The gated RMSNorm epilogue, checkpoint writes and the final state write are
+// fused into the same kernel.
+
 #include "kda_device.h"
 #include "kda_launch.h"
 
 namespace kda {
+namespace {
 
-bool prefill_supported(int, int, int) { return false; }
+constexpr int CH = 64;       // chunk length
+constexpr int RREF = 31;     // reference row of the decay factorisation
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+
+struct Frag {
+    bf16x8 hi, lo;
+};
+
+struct Frag4 {
+    bf16x4 hi, lo;
+};
+
+__device__ __forceinline__ f32x4 mfma3_16(const Frag4& a, const Frag4& b, f32x4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b.hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.lo, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.hi, acc, 0, 0, 0);
+    return acc;
+}
+
+__device__ __forceinline__ Frag4 split4(const f32x4& x) {
+    Frag4 f;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        const __bf16 h = static_cast<__bf16>(x[e]);
+        f.hi[e] = h;
+        f.lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(h));
+    }
+    return f;
+}
+
+// Two 4-element halves stacked into one 8-element operand.
+__device__ __forceinline__ Frag cat(const Frag4& a, const Frag4& b) {
+    Frag f;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        f.hi[e] = a.hi[e];
+        f.hi[e + 4] = b.hi[e];
+        f.lo[e] = a.lo[e];
+        f.lo[e + 4] = b.lo[e];
+    }
+    return f;
+}
+
+__device__ __forceinline__ f32x4 mfma3(const Frag& a, const Frag& b, f32x4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+    return acc;
+}
+
+__device__ __forceinline__ Frag split8(const float (&x)[8]) {
+    Frag f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        const __bf16 h = static_cast<__bf16>(x[e]);
+        f.hi[e] = h;
+        f.lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(h));
+    }
+    return f;
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(__bf16 b) { return __builtin_bit_cast(uint16_t, b); }
+
+// Store x as a (hi, lo) bf16 pair into two planes at element index idx.
+__device__ __forceinline__ void st_split(uint16_t* hi, uint16_t* lo, int idx, float x) {
+    const __bf16 h = static_cast<__bf16>(x);
+    hi[idx] = bf16_bits(h);
+    lo[idx] = bf16_bits(static_cast<__bf16>(x - static_cast<float>(h)));
+}
+
+union U128 {
+    uint4 u;
+    bf16x8 v;
+};
+
+// 8 consecutive elements [row][k0, k0+8) of a plane pair.
+__device__ __forceinline__ Frag ld_nat(const uint16_t* hi, const uint16_t* lo, int off) {
+    U128 a, b;
+    a.u = *reinterpret_cast<const uint4*>(hi + off);
+    b.u = *reinterpret_cast<const uint4*>(lo + off);
+    return Frag{a.v, b.v};
+}
+
+// Elements [off, off+4) and [off+16, off+20): the permuted contraction order.
+__device__ __forceinline__ Frag ld_perm(const uint16_t* hi, const uint16_t* lo, int off) {
+    U128 a, b;
+    const uint2 a0 = *reinterpret_cast<const uint2*>(hi + off);
+    const uint2 a1 = *reinterpret_cast<const uint2*>(hi + off + 16);
+    const uint2 b0 = *reinterpret_cast<const uint2*>(lo + off);
+    const uint2 b1 = *reinterpret_cast<const uint2*>(lo + off + 16);
+    a.u = make_uint4(a0.x, a0.y, a1.x, a1.y);
+    b.u = make_uint4(b0.x, b0.y, b1.x, b1.y);
+    return Frag{a.v, b.v};
+}
+
+// 4 consecutive elements of a plane pair.
+__device__ __forceinline__ Frag4 ld4(const uint16_t* hi, const uint16_t* lo, int off) {
+    union {
+        uint2 u;
+        bf16x4 v;
+    } a, b;
+    a.u = *reinterpret_cast<const uint2*>(hi + off);
+    b.u = *reinterpret_cast<const uint2*>(lo + off);
+    return Frag4{a.v, b.v};
+}
+
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+// A copy of x the optimiser cannot see through.  Lane indices are re-derived
+// from such a copy at the start of each phase of the chunk loop, so their
+// address arithmetic stays inside the phase instead of being hoisted out of
+// the loop and kept live (and spilled) across all of it.
+__device__ __forceinline__ int opq(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// An LDS byte offset the optimiser cannot fold into later constants.  LDS
+// instructions take a 16-bit immediate offset; with the region bases opaque,
+// every access inside a region (all < 64 KiB) uses base register + immediate
+// instead of one precomputed address register per access.
+__device__ __forceinline__ char* opaque_lds(char* base, uint32_t off) {
+    uint32_t v = off;
+    asm volatile("" : "+v"(v));
+    return base + v;
+}
+
+// One activation element through a buffer resource (offsets in bytes).
+template <typename ACT>
+__device__ __forceinline__ float buf_ld_act(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    if constexpr (sizeof(ACT) == 2) return bf16_to_f32(buf_ld16(r, voff, soff));
+    else return buf_ldf(r, voff, soff);
+}
+
+template <typename ACT>
+__device__ __forceinline__ void buf_st_act(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float x) {
+    if constexpr (sizeof(ACT) == 2) buf_st16(r, voff, soff, f32_to_bf16(x));
+    else buf_stf(r, voff, soff, x);
+}
+
+// One 32-bit word of raw activations starting at channel c (2 bf16 or 1 fp32).
+template <typename F>
+__device__ __forceinline__ uint32_t pack_word(F&& at, int64_t tok, int c) {
+    using T = decltype(at(tok, c));
+    if constexpr (sizeof(T) == 2) {
+        const T a = at(tok, c), b = at(tok, c + 1);
+        return static_cast<uint32_t>(a.bits) | (static_cast<uint32_t>(b.bits) << 16);
+    } else {
+        return __float_as_uint(at(tok, c));
+    }
+}
+
+// Store the state tiles of one 16-column strip (accumulator layout) into a
+// dk x dv fp32 state at dst.
+template <int IB, int DV>
+__device__ __forceinline__ void store_state_strip(float* dst, const f32x4 (&S)[IB], int g4, int jcol, int dk) {
+    const auto rs = make_rsrc(dst, static_cast<uint32_t>(dk * DV * 4));
+    const uint32_t sv = static_cast<uint32_t>((4 * g4 * DV + jcol) * 4);
+#pragma unroll
+    for (int ib = 0; ib < IB; ib++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) buf_stf(rs, sv, (16 * ib + e) * DV * 4, S[ib][e]);
+}
+
+template <int D, typename ACT>
+struct PrefillShape {
+    static constexpr int DK = D, DV = D;
+    static constexpr int NW = DV / 16;          // waves = 16-column strips of S
+    static constexpr int NT = 64 * NW;
+    static constexpr int C = 2 * DK + DV;       // conv channels
+    static constexpr int KS = DK / 32;          // 32-channel contraction steps
+    static constexpr int IB = DK / 16;          // 16-row tiles of S
+    static constexpr int PS = DK + 8;           // padded row stride of [64][dk] planes
+    static constexpr int QS = CH + 8;           // padded row stride of [*][64] planes
+    static constexpr int VEC = 16 / static_cast<int>(sizeof(ACT));   // elements per 16-byte load
+    // LDS regions (bytes)
+    static constexpr int R0 = cmax(CH * DK * 4, 2 * CH * PS * 2);                // a_k (fp32) / K+ planes
+    static constexpr int R1 = R0;                                                 // a_q (fp32) / Q+ planes
+    static constexpr int R2 = cmax(2 * CH * PS * 2, 2 * DK * QS * 2);           // K- planes / K-^T planes
+    static constexpr int R4 = 2 * CH * QS * 2;                                   // L planes, T_aa on the diagonal
+    static constexpr int R5 = 2 * CH * QS * 2;                                   // P planes
+    static constexpr int RAW = (CH + 3) * C * static_cast<int>(sizeof(ACT));    // raw rows (aliases R2..R5)
+    static constexpr int O0 = 0, O1 = R0, O2 = 2 * R0, O4 = O2 + R2, O5 = O4 + R4;
+    static constexpr int BYTES = O5 + R5;
+    static_assert(RAW <= R2 + R4 + R5, "raw staging must fit in the aliased regions");
+    static_assert(NT / (2 * DK) == 2 && NT / DK == 4, "thread mappings assume nt = 4 * dk");
+};
+
+template <int D, typename ACT>
+__global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
+    using Sh = PrefillShape<D, ACT>;
+    constexpr int DK = Sh::DK, DV = Sh::DV, NW = Sh::NW, NT = Sh::NT, C = Sh::C;
+    constexpr int KS = Sh::KS, IB = Sh::IB, PS = Sh::PS, QS = Sh::QS, VEC = Sh::VEC;
+    using A = Act<ACT>;
+
+    __shared__ __attribute__((aligned(16))) char lds[Sh::BYTES];
+    __shared__ float beta_s[CH], rq_s[CH], rk_s[CH];
+    __shared__ float eGr_s[DK], eGC_s[DK], eGCr_s[DK];
+    __shared__ float gtot_s[4][DK];
+    __shared__ float part_s[NW][CH];
+    __shared__ float ld_s[4][16][16];      // diagonal blocks of L (fp32)
+    __shared__ ACT x0_s[C * 3];
+
+    char* reg0 = opaque_lds(lds, Sh::O0);
+    char* reg1 = opaque_lds(lds, Sh::O1);
+    char* reg2 = opaque_lds(lds, Sh::O2);
+    char* reg4 = opaque_lds(lds, Sh::O4);
+    char* reg5 = opaque_lds(lds, Sh::O5);
+    float* ak_f = reinterpret_cast<float*>(reg0);                // [CH][DK] fp32
+    float* aq_f = reinterpret_cast<float*>(reg1);
+    uint16_t* kp_h = reinterpret_cast<uint16_t*>(reg0);          // K+ planes [CH][PS]
+    uint16_t* kp_l = kp_h + CH * PS;
+    uint16_t* qp_h = reinterpret_cast<uint16_t*>(reg1);          // Q+ planes
+    uint16_t* qp_l = qp_h + CH * PS;
+    uint16_t* km_h = reinterpret_cast<uint16_t*>(reg2);          // K- planes [CH][PS]
+    uint16_t* km_l = km_h + CH * PS;
+    uint16_t* kt_h = reinterpret_cast<uint16_t*>(reg2);          // K-^T planes [DK][QS]
+    uint16_t* kt_l = kt_h + DK * QS;
+    uint16_t* lp_h = reinterpret_cast<uint16_t*>(reg4);          // L planes [CH][QS], T_aa on the diagonal
+    uint16_t* lp_l = lp_h + CH * QS;
+    uint16_t* pp_h = reinterpret_cast<uint16_t*>(reg5);          // P planes [CH][QS]
+    uint16_t* pp_l = pp_h + CH * QS;
+    ACT* raw = reinterpret_cast<ACT*>(reg2);                     // [CH+3][C]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g4 = lane >> 4, l16 = lane & 15;
+    const int H = p.H;
+    const int h = blockIdx.x % H;
+    const SeqWork wk = p.work[blockIdx.x / H];
+    if (wk.len < 0) return;                    // malformed sequence bounds: nothing is touched
+    const int seq = wk.seq;
+    const int64_t tok0 = wk.tok0;
+    const int L = wk.len;
+    const int64_t start = wk.start;
+    const int init = p.init_slot ? p.init_slot[seq] : -1;
+    const int fin = p.final_slot ? p.final_slot[seq] : -1;
+    const int jcol = 16 * wave + l16;          // this lane's state / output column
+
+    // invalid initial slot or position: NaN outputs, no state written
+    if (init < -1 || init >= p.num_slots || start < 0) {
+        for (int64_t e = tid; e < static_cast<int64_t>(L) * DV; e += NT) {
+            const int64_t t = tok0 + e / DV;
+            A::st(static_cast<ACT*>(p.out) + (t * H + h) * DV + e % DV, nan_f32());
+        }
+        return;
+    }
+
+    // ---- chain prologue: initial state (accumulator layout), conv state, weights
+    f32x4 S[IB];
+    {
+        const uint32_t sv = static_cast<uint32_t>((4 * g4 * DV + jcol) * 4);
+        if (init >= 0) {
+            const auto rs = make_rsrc(p.state + (static_cast<int64_t>(init) * H + h) * DK * DV, DK * DV * 4);
+#pragma unroll
+            for (int ib = 0; ib < IB; ib++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) S[ib][e] = buf_ldf(rs, sv, (16 * ib + e) * DV * 4);
+        } else {
+#pragma unroll
+            for (int ib = 0; ib < IB; ib++) S[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        const ACT* x0 = init >= 0 ? static_cast<const ACT*>(p.conv) + (static_cast<int64_t>(init) * H + h) * C * 3
+                                  : nullptr;
+        for (int e = tid; e < C * 3; e += NT) {
+            if (x0) x0_s[e] = x0[e];
+            else A::st(&x0_s[e], 0.f);
+        }
+    }
+    const int cqk = tid % (2 * DK);                              // q/k conv channel of this thread
+    const float4 wqk = *reinterpret_cast<const float4*>(p.conv_w + (static_cast<int64_t>(h) * C + cqk) * 4);
+    const float4 wv = *reinterpret_cast<const float4*>(p.conv_w + (static_cast<int64_t>(h) * C + 2 * DK + jcol) * 4);
+    const float nwj = p.norm_w[jcol];
+    const ACT* qin = static_cast<const ACT*>(p.q);
+    const ACT* kin = static_cast<const ACT*>(p.k);
+    const ACT* vin = static_cast<const ACT*>(p.v);
+    const ACT* zin = static_cast<const ACT*>(p.z);
+    ACT* out = static_cast<ACT*>(p.out);
+    __syncthreads();
+
+    // raw input value of channel c at packed token tok (conv left context)
+    auto raw_at = [&](int64_t tok, int c) -> ACT {
+        if (tok >= tok0) {
+            const ACT* src = c < DK ? qin + (tok * H + h) * DK + c
+                                    : (c < 2 * DK ? kin + (tok * H + h) * DK + (c - DK)
+                                                  : vin + (tok * H + h) * DV + (c - 2 * DK));
+            return *src;
+        }
+        return x0_s[c * 3 + 3 - static_cast<int>(tok0 - tok)];
+    };
+    // conv state after the tokens before packed index tend: the last 3 raw inputs
+    auto write_conv_state = [&](ACT* dst, int64_t tend) {
+        for (int e = tid; e < C * 3; e += NT) {
+            const int c = e / 3, m = e % 3;
+            dst[e] = raw_at(tend - 3 + m, c);
+        }
+    };
+    int64_t pos = start;
+    int done = 0, ck = 0;
+    const int ck_base = (p.ckpt_interval > 0) ? p.ckpt_base[seq] : 0;
+
+    while (done < L) {
+        const int n = min(L - done, CH - static_cast<int>(pos % CH));
+        const int64_t tc0 = tok0 + done;
+        float gq[16];      // log decay of this thread's (channel, quarter), then its prefix sums
+        float vh[4][4];    // SiLU(conv(v)) in accumulator layout
+        float km[16];      // K- column of this thread, kept for the transposed copy
+
+        // ---------------- A1: stage raw rows (3 rows of left context), gates
+        {
+            const int tp = opq(tid);
+            const int cgp = tp % DK, qqp = tp / DK;
+            constexpr int UPR = C / VEC;                 // 16-byte units per row
+            for (int u = tp; u < (CH + 3) * UPR; u += NT) {
+                const int r = u / UPR, c0 = (u % UPR) * VEC;
+                const int64_t tok = tc0 - 3 + r;
+                uint4 val = make_uint4(0, 0, 0, 0);
+                if (r < n + 3) {
+                    if (tok >= tok0) {
+                        const ACT* src = c0 < DK ? qin + (tok * H + h) * DK + c0
+                                                 : (c0 < 2 * DK ? kin + (tok * H + h) * DK + (c0 - DK)
+                                                                : vin + (tok * H + h) * DV + (c0 - 2 * DK));
+                        val = *reinterpret_cast<const uint4*>(src);
+                    } else {
+                        uint32_t wd[4];
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; q4++) wd[q4] = pack_word(raw_at, tok, c0 + q4 * (VEC / 4));
+                        val = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                    }
+                }
+                *reinterpret_cast<uint4*>(raw + r * C + c0) = val;
+            }
+            // per-chunk view: row t of this head at byte offset t * row_bytes.  The
+            // resource ends after row n-1 and the whole offset goes through the
+            // range-checked per-lane offset, so rows past the chunk read as zero.
+            const auto rg = make_rsrc(p.g + (tc0 * H + h) * DK, static_cast<uint32_t>(((n - 1) * H + 1) * DK * 4));
+            const uint32_t gv = static_cast<uint32_t>((16 * qqp * H * DK + cgp) * 4);
+#pragma unroll
+            for (int r = 0; r < 16; r++) gq[r] = buf_ldf(rg, gv + static_cast<uint32_t>(r * H * DK * 4), 0);
+            if (tp < CH) {
+                const auto rb = make_rsrc(p.beta + tc0 * H + h, static_cast<uint32_t>(((n - 1) * H + 1) * 4));
+                beta_s[tp] = buf_ldf(rb, static_cast<uint32_t>(tp * H * 4), 0);
+            }
+        }
+        __syncthreads();
+
+        // ---------------- A2: causal conv + SiLU (q, k channels to LDS; v to registers)
+        {
+            const int tp = opq(tid);
+            const int cqk = tp % (2 * DK), half = tp / (2 * DK);
+            const int r0 = 32 * half;
+            float w0 = A::ld(raw + (r0 + 0) * C + cqk);
+            float w1 = A::ld(raw + (r0 + 1) * C + cqk);
+            float w2 = A::ld(raw + (r0 + 2) * C + cqk);
+            float* dst = cqk < DK ? aq_f + cqk : ak_f + (cqk - DK);
+#pragma unroll 4
+            for (int t = r0; t < r0 + 32; t++) {
+                const float w3 = A::ld(raw + (t + 3) * C + cqk);
+                float y = wqk.x * w0;
+                y = fmaf(wqk.y, w1, y);
+                y = fmaf(wqk.z, w2, y);
+                y = fmaf(wqk.w, w3, y);
+                dst[t * DK] = t < n ? silu(y) : 0.f;
+                w0 = w1;
+                w1 = w2;
+                w2 = w3;
+            }
+            const int ln = tp & 63, jc = 16 * (tp >> 6) + (ln & 15), gg = ln >> 4;
+#pragma unroll
+            for (int tb = 0; tb < 4; tb++) {
+                const int rb = 16 * tb + 4 * gg;
+                float x[7];
+#pragma unroll
+                for (int m = 0; m < 7; m++) x[m] = A::ld(raw + (rb + m) * C + 2 * DK + jc);
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    float y = wv.x * x[e];
+                    y = fmaf(wv.y, x[e + 1], y);
+                    y = fmaf(wv.z, x[e + 2], y);
+                    y = fmaf(wv.w, x[e + 3], y);
+                    vh[tb][e] = (rb + e) < n ? silu(y) : 0.f;
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---------------- A3: L2 norms; decay prefix sums within each quarter
+        {
+            const int tp = opq(tid);
+            constexpr int PPT = NT / (2 * CH);          // threads per (row, tensor)
+            constexpr int SPAN = DK / PPT;
+            const int pair = tp / PPT, part = tp % PPT;
+            const int t = pair % CH;
+            const float* src = (pair < CH ? aq_f : ak_f) + t * DK + part * SPAN;
+            float ssum = 0.f;
+#pragma unroll
+            for (int c = 0; c < SPAN; c += 4) {
+                const float4 a4 = *reinterpret_cast<const float4*>(src + c);
+                ssum = fmaf(a4.x, a4.x, ssum);
+                ssum = fmaf(a4.y, a4.y, ssum);
+                ssum = fmaf(a4.z, a4.z, ssum);
+                ssum = fmaf(a4.w, a4.w, ssum);
+            }
+            ssum = dpp_group_sum<PPT>(ssum);
+            if (part == 0) (pair < CH ? rq_s : rk_s)[t] = rsqrtf(ssum + p.l2_eps);
+#pragma unroll
+            for (int r = 1; r < 16; r++) gq[r] += gq[r - 1];
+            gtot_s[tp / DK][tp % DK] = gq[15];
+        }
+        __syncthreads();
+
+        // ---------------- A4: K+, K-, Q+ (hi/lo planes); per-channel factors
+        {
+            const int tp = opq(tid);
+            const int cgp = tp % DK, qqp = tp / DK;
+            const float t0 = gtot_s[0][cgp], t1 = gtot_s[1][cgp], t2 = gtot_s[2][cgp], t3 = gtot_s[3][cgp];
+            const float gam_r = t0 + t1;                  // Gam at the reference row
+            const float gam_c = gam_r + t2 + t3;          // Gam at the chunk's last row
+            const float off = qqp == 0 ? 0.f : (qqp == 1 ? t0 : (qqp == 2 ? gam_r : gam_r + t2));
+            float kp[16], qp[16];
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int t = 16 * qqp + r;
+                const float d = (gq[r] + off) - gam_r;
+                const float E = __expf(d), Ei = __expf(-d);
+                const float kh = ak_f[t * DK + cgp] * rk_s[t];
+                const float qh = aq_f[t * DK + cgp] * rq_s[t];
+                kp[r] = kh * E;
+                km[r] = kh * Ei;
+                qp[r] = qh * E;
+            }
+            if (qqp == 0) {
+                eGr_s[cgp] = __expf(gam_r);
+                eGCr_s[cgp] = __expf(gam_c - gam_r);
+                eGC_s[cgp] = __expf(gam_c);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int idx = (16 * qqp + r) * PS + cgp;
+                st_split(kp_h, kp_l, idx, kp[r]);
+                st_split(qp_h, qp_l, idx, qp[r]);
+                st_split(km_h, km_l, idx, km[r]);
+            }
+        }
+        __syncthreads();
+
+        // ---------------- A5: L = Diag(b) strictLower(K+ K-^T), P = lower(Q+ K-^T)
+        {
+            const int tp = opq(tid);
+            const int ln = tp & 63, wv5 = tp >> 6, gg = ln >> 4, lc = ln & 15;
+            for (int job = wv5; job < 32; job += NW) {
+                const bool isP = job >= 16;
+                const int a = (job & 15) >> 2, b = job & 3;
+                if (a < b) {
+                    if (isP) {
+#pragma unroll
+                        for (int e = 0; e < 4; e++) {
+                            const int idx = (16 * a + 4 * gg + e) * QS + 16 * b + lc;
+                            pp_h[idx] = 0;
+                            pp_l[idx] = 0;
+                        }
+                    }
+                    continue;
+                }
+                const uint16_t* ah = isP ? qp_h : kp_h;
+                const uint16_t* al = isP ? qp_l : kp_l;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ks++) {
+                    const Frag fa = ld_nat(ah, al, (16 * a + lc) * PS + 32 * ks + 8 * gg);
+                    const Frag fb = ld_nat(km_h, km_l, (16 * b + lc) * PS + 32 * ks + 8 * gg);
+                    acc = mfma3(fa, fb, acc);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int t = 16 * a + 4 * gg + e, s2 = 16 * b + lc;
+                    if (isP) st_split(pp_h, pp_l, t * QS + s2, t >= s2 ? acc[e] : 0.f);
+                    else if (a > b) st_split(lp_h, lp_l, t * QS + s2, beta_s[t] * acc[e]);
+                    else ld_s[a][4 * gg + e][lc] = t > s2 ? beta_s[t] * acc[e] : 0.f;
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---------------- A6: T_aa = (I + L_aa)^{-1} for the 4 diagonal blocks,
+        // forward substitution on one column with PARTS threads splitting each
+        // dot product; then the K-^T planes into the K- region
+        {
+            const int tp = opq(tid);
+            constexpr int PARTS = NT / 64, KPP = 16 / PARTS;
+            const int part = tp % PARTS, col = (tp / PARTS) % 16, blk = tp / (16 * PARTS);
+            float xk[KPP];
+#pragma unroll
+            for (int kk = 0; kk < KPP; kk++) xk[kk] = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                float c2 = 0.f;
+#pragma unroll
+                for (int kk = 0; kk < KPP; kk++) c2 = fmaf(ld_s[blk][r][part * KPP + kk], xk[kk], c2);
+                const float sdot = dpp_group_sum<PARTS>(c2);
+                const float xr = r < col ? 0.f : (r == col ? 1.f : -sdot);
+#pragma unroll
+                for (int kk = 0; kk < KPP; kk++)
+                    if (part * KPP + kk == r) xk[kk] = xr;
+            }
+#pragma unroll
+            for (int kk = 0; kk < KPP; kk++)
+                st_split(lp_h, lp_l, (16 * blk + part * KPP + kk) * QS + 16 * blk + col, xk[kk]);
+            const int cgp = tp % DK, qqp = tp / DK;
+#pragma unroll
+            for (int r = 0; r < 16; r++) st_split(kt_h, kt_l, cgp * QS + 16 * qqp + r, km[r]);
+        }
+        __syncthreads();
+
+        // ---------------- B: state-dependent part; wave = 16-column strip of S
+        f32x4 accr[4];     // readouts O (rows 16tb + 4g + e, this lane's column)
+        {
+            const int tp = opq(tid);
+            const int ln = tp & 63, gg = ln >> 4, lc = ln & 15;
+            f32x4 accx[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; tb++) {
+                accx[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                accr[tb] = accx[tb];
+            }
+            // K_g S and Q_g S: the per-channel exp(Gam_r) goes onto S's rows
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++) {
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    x[e] = eGr_s[32 * ks + 4 * gg + e] * S[2 * ks][e];
+                    x[e + 4] = eGr_s[32 * ks + 16 + 4 * gg + e] * S[2 * ks + 1][e];
+                }
+                const Frag fs = split8(x);
+#pragma unroll
+                for (int tb = 0; tb < 4; tb++) {
+                    const int off = (16 * tb + lc) * PS + 32 * ks + 4 * gg;
+                    accx[tb] = mfma3(ld_perm(kp_h, kp_l, off), fs, accx[tb]);
+                    accr[tb] = mfma3(ld_perm(qp_h, qp_l, off), fs, accr[tb]);
+                }
+            }
+            // Y = Diag(b) (V - K_g S)
+            f32x4 y[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; tb++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) y[tb][e] = beta_s[16 * tb + 4 * gg + e] * (vh[tb][e] - accx[tb][e]);
+            // U: solve (I + L) U = Y block by block, U_a = T_aa (Y_a - sum_{c<a} L_ac U_c)
+            Frag4 fu[4];
+#pragma unroll
+            for (int a = 0; a < 4; a++) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c2 = 0; c2 < a; c2++)
+                    acc = mfma3_16(ld4(lp_h, lp_l, (16 * a + lc) * QS + 16 * c2 + 4 * gg), fu[c2], acc);
+                f32x4 r;
+#pragma unroll
+                for (int e = 0; e < 4; e++) r[e] = y[a][e] - acc[e];
+                const f32x4 ua = mfma3_16(ld4(lp_h, lp_l, (16 * a + lc) * QS + 16 * a + 4 * gg), split4(r),
+                                          f32x4{0.f, 0.f, 0.f, 0.f});
+                fu[a] = split4(ua);
+            }
+            const Frag fu0 = cat(fu[0], fu[1]);
+            const Frag fu1 = cat(fu[2], fu[3]);
+            // O = Q_g S + P U
+#pragma unroll
+            for (int tb = 0; tb < 4; tb++) {
+                const int row = (16 * tb + lc) * QS + 4 * gg;
+                accr[tb] = mfma3(ld_perm(pp_h, pp_l, row), fu0, accr[tb]);
+                if (tb >= 2) accr[tb] = mfma3(ld_perm(pp_h, pp_l, row + 32), fu1, accr[tb]);
+            }
+            // S = Diag(exp Gam_end) S + Diag(exp(Gam_end - Gam_r)) K-^T U
+#pragma unroll
+            for (int ib = 0; ib < IB; ib++) {
+                const int row = (16 * ib + lc) * QS + 4 * gg;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                acc = mfma3(ld_perm(kt_h, kt_l, row), fu0, acc);
+                acc = mfma3(ld_perm(kt_h, kt_l, row + 32), fu1, acc);
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int i = 16 * ib + 4 * gg + e;
+                    S[ib][e] = fmaf(eGC_s[i], S[ib][e], eGCr_s[i] * acc[e]);
+                }
+            }
+            // row sums of O^2 over this wave's 16 columns
+#pragma unroll
+            for (int tb = 0; tb < 4; tb++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const float s2 = dpp_group_sum<16>(accr[tb][e] * accr[tb][e]);
+                    if (lc == 0) part_s[tp >> 6][16 * tb + 4 * gg + e] = s2;
+                }
+        }
+        __syncthreads();
+
+        // ---------------- epilogue: gated RMSNorm over dv, then the outputs
+        {
+            const int tp = opq(tid);
+            const int ln = tp & 63, gg = ln >> 4, jc = 16 * (tp >> 6) + (ln & 15);
+            const uint32_t rowb = static_cast<uint32_t>(H * DV * sizeof(ACT));
+            const uint32_t nb = static_cast<uint32_t>(((n - 1) * H + 1) * DV * sizeof(ACT));
+            // rows past the chunk fall outside the resources (range-checked per-lane
+            // offsets): their z loads read 0, and their stores are also predicated off
+            const auto rz = make_rsrc(zin + (tc0 * H + h) * DV, nb);
+            const auto ro = make_rsrc(out + (tc0 * H + h) * DV, nb);
+            const uint32_t vo = static_cast<uint32_t>(4 * gg * rowb + jc * sizeof(ACT));
+#pragma unroll
+            for (int tb = 0; tb < 4; tb++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int t = 16 * tb + 4 * gg + e;
+                    const uint32_t vrow = vo + static_cast<uint32_t>((16 * tb + e) * rowb);
+                    const float zz = buf_ld_act<ACT>(rz, vrow, 0);
+                    float tot = 0.f;
+#pragma unroll
+                    for (int w2 = 0; w2 < NW; w2++) tot += part_s[w2][t];
+                    const float rinv = rsqrtf(tot * (1.0f / DV) + p.rms_eps);
+                    if (t < n) buf_st_act<ACT>(ro, vrow, 0, accr[tb][e] * rinv * nwj * sigmoid(zz));
+                }
+        }
+
+        done += n;
+        pos += n;
+        // ---------------- checkpoints: interval boundaries inside, and the end
+        if (p.ckpt_interval > 0 && (pos % p.ckpt_interval == 0 || done == L)) {
+            const int slot = ck_base + ck;
+            ck++;
+            if (slot >= 0 && slot < p.num_ckpt_slots) {
+                const int64_t sh = static_cast<int64_t>(slot) * H + h;
+                store_state_strip<IB, DV>(p.ckpt_state + sh * DK * DV, S, g4, jcol, DK);
+                write_conv_state(static_cast<ACT*>(p.ckpt_conv) + sh * C * 3, tok0 + done);
+            }
+        }
+        __syncthreads();
+    }
+
+    if (fin >= 0 && fin < p.num_slots) {
+        const int64_t sh = static_cast<int64_t>(fin) * H + h;
+        store_state_strip<IB, DV>(p.state + sh * DK * DV, S, g4, jcol, DK);
+        write_conv_state(static_cast<ACT*>(p.conv) + sh * C * 3, tok0 + L);
+    }
+}
+
+// One workgroup: per-sequence work items ordered longest first, so the
+// longest chains start first.  Sequences with bounds outside [0, T] get
+// len = -1 and are skipped by the prefill kernel.
+__global__ __launch_bounds__(1024) void prefill_meta_kernel(const int32_t* cu, const int64_t* sp, int32_t N,
+                                                            int64_t T, SeqWork* work) {
+    for (int i = threadIdx.x; i < N; i += 1024) {
+        const int64_t a = cu[i], b = cu[i + 1];
+        const bool ok = a >= 0 && b >= a && b <= T;
+        const int32_t li = ok ? static_cast<int32_t>(b - a) : -1;
+        int rank = i;
+        if (N <= 1024) {
+            rank = 0;
+            for (int j = 0; j < N; j++) {
+                const int64_t aj = cu[j], bj = cu[j + 1];
+                const int32_t lj = (aj >= 0 && bj >= aj && bj <= T) ? static_cast<int32_t>(bj - aj) : -1;
+                rank += (lj > li) || (lj == li && j < i);
+            }
+        }
+        SeqWork w;
+        w.seq = i;
+        w.tok0 = ok ? static_cast<int32_t>(a) : 0;
+        w.len = li;
+        w.pad = 0;
+        w.start = sp ? sp[i] : 0;
+        work[rank] = w;
+    }
+}
+
+template <int D, typename ACT>
+hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
+    hipLaunchKernelGGL(prefill_meta_kernel, dim3(1), dim3(1024), 0, s, p.cu_seqlens, p.start_pos, p.N, p.T, p.work);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t blocks = static_cast<int64_t>(p.N) * p.H;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((prefill_kernel<D, ACT>), dim3(static_cast<unsigned>(blocks)), dim3(4 * D), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefill_supported(int dk, int dv, int act) {
+    if (dk != dv) return false;
+    if (act == 1) return dk == 32 || dk == 64 || dk == 128;
+    return dk == 32 || dk == 64;   // fp32 activations: raw staging of dk=128 exceeds LDS
+}
 
 size_t prefill_workspace_bytes(int32_t N, int32_t, int64_t, int, int) {
     return (static_cast<size_t>(N) * sizeof(SeqWork) + 255) / 256 * 256;
 }
 
-hipError_t launch_prefill(int, int, int, const PrefillParams&, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_prefill(int dk, int dv, int act, const PrefillParams& p, hipStream_t s) {
+    if (!prefill_supported(dk, dv, act)) return hipErrorInvalidValue;
+    if (act == 1) {
+        switch (dk) {
+            case 32: return launch_prefill_t<32, bf16_t>(p, s);
+            case 64: return launch_prefill_t<64, bf16_t>(p, s);
+            default: return launch_prefill_t<128, bf16_t>(p, s);
+        }
+    }
+    return dk == 32 ? launch_prefill_t<32, float>(p, s) : launch_prefill_t<64, float>(p, s);
+}
 
 }  // namespace kda

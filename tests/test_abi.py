@@ -117,6 +117,16 @@ def test_prefill_validation():
     assert prefill_call(cfg(), interval=100) == kda.KDA_ERR_INVALID_ARG
     assert prefill_call(cfg(), interval=-64) == kda.KDA_ERR_INVALID_ARG
     assert prefill_call(cfg(head_k=96, head_v=96)) == kda.KDA_ERR_UNSUPPORTED
+    assert prefill_call(cfg(act_dtype=kda.KDA_F32)) == kda.KDA_ERR_UNSUPPORTED   # fp32 with dk=128
+    assert prefill_call(cfg(), ws_bytes=0) == kda.KDA_ERR_WORKSPACE
+    assert "workspace" in kda.last_error()
+    assert prefill_call(cfg(), cu=None) == kda.KDA_ERR_INVALID_ARG
+    assert prefill_call(cfg(), q=MISALIGNED) == kda.KDA_ERR_INVALID_ARG
+    assert prefill_call(cfg(), interval=64, ckb=None) == kda.KDA_ERR_INVALID_ARG
+    assert prefill_call(cfg(), interval=64, nck=0) == kda.KDA_ERR_INVALID_ARG
+    assert prefill_call(cfg(), N=0, cu=None) == kda.KDA_OK                      # nothing to do
+    ws = kda.kda_prefill_workspace_bytes(cfg(), 16, 1 << 18)
+    assert ws >= 16 * 24 and ws % 256 == 0
 
 
 def test_num_checkpoints_matches_oracle_rule():

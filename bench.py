@@ -11,8 +11,8 @@ step).  The line also carries:
                 (bytes per launch / mean launch duration from HIP events)
                 against the 8 TB/s peak, and the HBM traffic measured by
                 rocprofv3 counters when those were taken on this kernel source
-  prefill       the chunked prefill workload (4 x 8192 tokens) when the
-                prefill kernel is available: tokens/s, HBM and MFMA fractions
+  prefill       the chunked prefill workload (4 x 8192 tokens, one call per
+                pass): tokens/s and the algorithmic HBM and bf16-MFMA fractions
   cpu_baseline  the fp64 oracle timed on this host on a bounded sample of the
                 decode workload
 Only one GPU is supported: --gpus above 1 exits with a message.
@@ -144,6 +144,71 @@ def bench_decode(args):
     return res
 
 
+def prefill_flops_per_token_head(dk, dv, chunk=64):
+    """Algorithmic FLOPs of the chunked form per token and head: the state
+    products (K_g S, Q_g S, K^T U: 2*dk*dv each), the intra-chunk products
+    (M and P: 2*C*dk/2 each on their triangles, W-like and U-like solves:
+    C*(dk+dv)), and the triangular solve (C^2/3); masked triangles are not
+    counted."""
+    return 6 * dk * dv + chunk * (3 * dk + 2 * dv) + chunk * chunk // 3
+
+
+def prefill_bytes_per_token_head(dk, dv, act_bytes=2):
+    """Unavoidable HBM bytes per token and head: q, k, v, z in (activation
+    dtype), g (fp32, per key channel) and beta (fp32) in, out (activation
+    dtype)."""
+    return (2 * dk + 2 * dv) * act_bytes + dk * 4 + 4 + dv * act_bytes
+
+
+def bench_prefill(steps, warmup):
+    import torch
+    import linear_attention_recurrence_decode_amd as kda
+    import workloads as wl
+
+    w = wl.WORKLOADS["prefill_4x8k"]
+    shape, lengths = w["shape"], w["lengths"]
+    H, dk, dv, C = shape.H, shape.dk, shape.dv, shape.C
+    N, T = len(lengths), sum(lengths)
+    cfg = kda.Config(H, dk, dv, kda.KDA_BF16)
+    act = cfg.torch_act
+    log(f"[bench] generating prefill inputs {N} x {lengths[0]} tokens, H={H}")
+    inp = wl.token_inputs(w["seed"], shape, T)
+    q, k, v, z = (torch.from_numpy(a).to(act).cuda() for a in (inp.q, inp.k, inp.v, inp.z))
+    g, beta = torch.from_numpy(inp.g).cuda(), torch.from_numpy(inp.beta).cuda()
+    conv_w, norm_w = torch.from_numpy(inp.conv_w).cuda(), torch.from_numpy(inp.norm_w).cuda()
+    cu = torch.from_numpy(wl.cu_seqlens(lengths).astype(np.int32)).cuda()
+    Sd = torch.zeros((N, H, dk, dv), device="cuda")
+    Xd = torch.zeros((N, H, C, 3), dtype=act, device="cuda")
+    init = torch.full((N,), -1, dtype=torch.int32, device="cuda")
+    final = torch.arange(N, dtype=torch.int32, device="cuda")
+    out = torch.empty((T, H, dv), dtype=act, device="cuda")
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(cfg, N, T), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def one():
+        kda.kda_prefill_varlen(cfg, cu, q, k, v, z, g, beta, conv_w, norm_w, Sd, Xd, init, final, out, ws,
+                               stream=stream)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        one()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / steps
+    th = T * H
+    flops = prefill_flops_per_token_head(dk, dv) * th
+    nbytes = prefill_bytes_per_token_head(dk, dv) * th
+    return {"workload": f"prefill_4x8k: {N} x {lengths[0]} tokens, H={H}, dk=dv={dk}, bf16, chunk 64",
+            "value": T / t, "unit": "tok/s", "ms_per_call": t * 1e3,
+            "mfma_frac": flops / t / BF16_PEAK, "hbm_frac": nbytes / t / HBM_PEAK,
+            "alg_flops": flops, "alg_bytes": nbytes,
+            "attainable_frac": max(flops / BF16_PEAK, nbytes / HBM_PEAK) / t}
+
+
 def cpu_baseline(sample_steps: int):
     """The fp64 oracle on the first `sample_steps` steps of the decode
     workload (all 64 sequences, all 32 heads), timed on this host."""
@@ -173,6 +238,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-sample-steps", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -199,6 +265,8 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": res["roofline"],
     }
+    if not args.no_prefill:
+        line["prefill"] = bench_prefill(max(3, args.steps // 2), max(1, args.warmup))
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_sample_steps} decode steps")
         line["cpu_baseline"] = cpu_baseline(args.cpu_sample_steps)

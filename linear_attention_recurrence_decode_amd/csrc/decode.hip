@@ -192,7 +192,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
         const float kh = a_s[DK + rg * RPT + r] * rk;
         s[r].x = fmaf(kh, u.x, s[r].x); s[r].y = fmaf(kh, u.y, s[r].y);
         s[r].z = fmaf(kh, u.z, s[r].z); s[r].w = fmaf(kh, u.w, s[r].w);
-        buf_st4(rs, voff + (r % 8) * DV * 4, (r / 8) * 8 * DV * 4, s[r]);
+        buf_st4(rs, voff + r * DV * 4, s[r]);
     }
 
     // 8. gated RMSNorm over dv (every row group holds all of o)

@@ -70,8 +70,11 @@ template <> struct Act<bf16_t> {
     }
 };
 
-__device__ __forceinline__ float silu(float y) { return y / (1.0f + __expf(-y)); }
-__device__ __forceinline__ float sigmoid(float y) { return 1.0f / (1.0f + __expf(-y)); }
+// SiLU and the logistic function with the hardware reciprocal (about 1 ulp)
+// instead of an IEEE division sequence.  For y -> -inf, 1 + exp(-y) -> inf and
+// the reciprocal -> 0, so both go to 0 without NaN.
+__device__ __forceinline__ float sigmoid(float y) { return __builtin_amdgcn_rcpf(1.0f + __expf(-y)); }
+__device__ __forceinline__ float silu(float y) { return y * sigmoid(y); }
 
 // Sum over the lanes of a wave64 whose lane ids differ only in the bits of
 // [lo_mask, 64): e.g. lo = 32 sums lane l with lane l ^ 32.
@@ -137,13 +140,19 @@ __device__ __forceinline__ void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t voff
     __builtin_amdgcn_raw_buffer_store_b16(x, r, static_cast<int>(voff), static_cast<int>(soff), 0);
 }
 
-__device__ __forceinline__ void buf_st4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float4 x) {
+// 16-byte buffer store with the whole offset in the per-lane VGPR and a literal
+// zero soffset.  The compiler pads a VALU write to a store-data register that
+// follows a >64-bit buffer store with a wait state only when soffset is not a
+// register; with a register soffset it issued the write right after the store
+// and the store occasionally wrote the new value (seen as corrupted state
+// entries in a few lanes).  So wide buffer stores never take an soffset here.
+__device__ __forceinline__ void buf_st4(__amdgpu_buffer_rsrc_t r, uint32_t voff, float4 x) {
     i32x4 v;
     v.x = __float_as_int(x.x);
     v.y = __float_as_int(x.y);
     v.z = __float_as_int(x.z);
     v.w = __float_as_int(x.w);
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(voff), static_cast<int>(soff), 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(voff), 0, 0);
 }
 
 }  // namespace kda

@@ -105,6 +105,14 @@ __device__ __forceinline__ f32x4 mfma3(const Frag& a, const Frag& b, f32x4 acc) 
     return acc;
 }
 
+// Two-term product hi(a) * (hi(b) + lo(b)): b keeps about fp32 accuracy, a is
+// rounded once to bf16.  Used where a only feeds the outputs.
+__device__ __forceinline__ f32x4 mfma2(const bf16x8& ahi, const Frag& b, f32x4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b.lo, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b.hi, acc, 0, 0, 0);
+    return acc;
+}
+
 __device__ __forceinline__ Frag split8(const float (&x)[8]) {
     Frag f;
 #pragma unroll
@@ -148,6 +156,15 @@ __device__ __forceinline__ Frag ld_perm(const uint16_t* hi, const uint16_t* lo, 
     a.u = make_uint4(a0.x, a0.y, a1.x, a1.y);
     b.u = make_uint4(b0.x, b0.y, b1.x, b1.y);
     return Frag{a.v, b.v};
+}
+
+// The hi plane only of ld_perm.
+__device__ __forceinline__ bf16x8 ld_perm_hi(const uint16_t* hi, int off) {
+    U128 a;
+    const uint2 a0 = *reinterpret_cast<const uint2*>(hi + off);
+    const uint2 a1 = *reinterpret_cast<const uint2*>(hi + off + 16);
+    a.u = make_uint4(a0.x, a0.y, a1.x, a1.y);
+    return a.v;
 }
 
 // 4 consecutive elements of a plane pair.
@@ -249,12 +266,16 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
     constexpr int DK = Sh::DK, DV = Sh::DV, NW = Sh::NW, NT = Sh::NT, C = Sh::C;
     constexpr int KS = Sh::KS, IB = Sh::IB, PS = Sh::PS, QS = Sh::QS, VEC = Sh::VEC;
     using A = Act<ACT>;
+    // With bf16 outputs the output-only products (Q_g S, P U) take the LDS
+    // operand in one bf16 term; fp32 outputs keep three terms everywhere.
+    constexpr bool kOutHi = sizeof(ACT) == 2;
 
     __shared__ __attribute__((aligned(16))) char lds[Sh::BYTES];
     __shared__ float beta_s[CH], rq_s[CH], rk_s[CH];
     __shared__ float eGr_s[DK], eGC_s[DK], eGCr_s[DK];
     __shared__ float gtot_s[4][DK];
     __shared__ float part_s[NW][CH];
+    __shared__ float rinv_s[CH];
     __shared__ float ld_s[4][16][16];      // diagonal blocks of L (fp32)
     __shared__ ACT x0_s[C * 3];
 
@@ -367,25 +388,30 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
         {
             const int tp = opq(tid);
             const int cgp = tp % DK, qqp = tp / DK;
+            // all 16-byte loads of the chunk first (one memory round trip), then
+            // the LDS stores
             constexpr int UPR = C / VEC;                 // 16-byte units per row
-            for (int u = tp; u < (CH + 3) * UPR; u += NT) {
+            constexpr int NU = ((CH + 3) * UPR + NT - 1) / NT;
+            uint4 val[NU];
+#pragma unroll
+            for (int j = 0; j < NU; j++) {
+                const int u = tp + j * NT;
                 const int r = u / UPR, c0 = (u % UPR) * VEC;
                 const int64_t tok = tc0 - 3 + r;
-                uint4 val = make_uint4(0, 0, 0, 0);
-                if (r < n + 3) {
+                val[j] = make_uint4(0, 0, 0, 0);
+                if (u < (CH + 3) * UPR && r < n + 3) {
                     if (tok >= tok0) {
                         const ACT* src = c0 < DK ? qin + (tok * H + h) * DK + c0
                                                  : (c0 < 2 * DK ? kin + (tok * H + h) * DK + (c0 - DK)
                                                                 : vin + (tok * H + h) * DV + (c0 - 2 * DK));
-                        val = *reinterpret_cast<const uint4*>(src);
+                        val[j] = *reinterpret_cast<const uint4*>(src);
                     } else {
                         uint32_t wd[4];
 #pragma unroll
                         for (int q4 = 0; q4 < 4; q4++) wd[q4] = pack_word(raw_at, tok, c0 + q4 * (VEC / 4));
-                        val = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                        val[j] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
                     }
                 }
-                *reinterpret_cast<uint4*>(raw + r * C + c0) = val;
             }
             // per-chunk view: row t of this head at byte offset t * row_bytes.  The
             // resource ends after row n-1 and the whole offset goes through the
@@ -397,6 +423,11 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
             if (tp < CH) {
                 const auto rb = make_rsrc(p.beta + tc0 * H + h, static_cast<uint32_t>(((n - 1) * H + 1) * 4));
                 beta_s[tp] = buf_ldf(rb, static_cast<uint32_t>(tp * H * 4), 0);
+            }
+#pragma unroll
+            for (int j = 0; j < NU; j++) {
+                const int u = tp + j * NT;
+                if (u < (CH + 3) * UPR) *reinterpret_cast<uint4*>(raw + (u / UPR) * C + (u % UPR) * VEC) = val[j];
             }
         }
         __syncthreads();
@@ -572,16 +603,31 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
 
         // ---------------- B: state-dependent part; wave = 16-column strip of S
         f32x4 accr[4];     // readouts O (rows 16tb + 4g + e, this lane's column)
+        float zr[4][4];    // output gate inputs, requested before the MFMA work
+        const uint32_t rowb = static_cast<uint32_t>(H * DV * sizeof(ACT));
+        const uint32_t nb = static_cast<uint32_t>(((n - 1) * H + 1) * DV * sizeof(ACT));
         {
             const int tp = opq(tid);
             const int ln = tp & 63, gg = ln >> 4, lc = ln & 15;
+            {
+                // rows past the chunk fall outside the resource (range-checked
+                // per-lane offsets) and read as zero
+                const auto rz = make_rsrc(zin + (tc0 * H + h) * DV, nb);
+                const uint32_t vo = static_cast<uint32_t>(4 * gg * rowb + (16 * (tp >> 6) + lc) * sizeof(ACT));
+#pragma unroll
+                for (int tb = 0; tb < 4; tb++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        zr[tb][e] = buf_ld_act<ACT>(rz, vo + static_cast<uint32_t>((16 * tb + e) * rowb), 0);
+            }
             f32x4 accx[4];
 #pragma unroll
             for (int tb = 0; tb < 4; tb++) {
                 accx[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
                 accr[tb] = accx[tb];
             }
-            // K_g S and Q_g S: the per-channel exp(Gam_r) goes onto S's rows
+            // K_g S and Q_g S: the per-channel exp(Gam_r) goes onto S's rows.  K+ keeps
+            // about fp32 accuracy; with bf16 outputs Q+ (outputs only) is rounded once
 #pragma unroll
             for (int ks = 0; ks < KS; ks++) {
                 float x[8];
@@ -595,7 +641,8 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
                 for (int tb = 0; tb < 4; tb++) {
                     const int off = (16 * tb + lc) * PS + 32 * ks + 4 * gg;
                     accx[tb] = mfma3(ld_perm(kp_h, kp_l, off), fs, accx[tb]);
-                    accr[tb] = mfma3(ld_perm(qp_h, qp_l, off), fs, accr[tb]);
+                    if constexpr (kOutHi) accr[tb] = mfma2(ld_perm_hi(qp_h, off), fs, accr[tb]);
+                    else accr[tb] = mfma3(ld_perm(qp_h, qp_l, off), fs, accr[tb]);
                 }
             }
             // Y = Diag(b) (V - K_g S)
@@ -621,12 +668,17 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
             }
             const Frag fu0 = cat(fu[0], fu[1]);
             const Frag fu1 = cat(fu[2], fu[3]);
-            // O = Q_g S + P U
+            // O = Q_g S + P U (with bf16 outputs, Q+ and P are rounded once to bf16)
 #pragma unroll
             for (int tb = 0; tb < 4; tb++) {
                 const int row = (16 * tb + lc) * QS + 4 * gg;
-                accr[tb] = mfma3(ld_perm(pp_h, pp_l, row), fu0, accr[tb]);
-                if (tb >= 2) accr[tb] = mfma3(ld_perm(pp_h, pp_l, row + 32), fu1, accr[tb]);
+                if constexpr (kOutHi) {
+                    accr[tb] = mfma2(ld_perm_hi(pp_h, row), fu0, accr[tb]);
+                    if (tb >= 2) accr[tb] = mfma2(ld_perm_hi(pp_h, row + 32), fu1, accr[tb]);
+                } else {
+                    accr[tb] = mfma3(ld_perm(pp_h, pp_l, row), fu0, accr[tb]);
+                    if (tb >= 2) accr[tb] = mfma3(ld_perm(pp_h, pp_l, row + 32), fu1, accr[tb]);
+                }
             }
             // S = Diag(exp Gam_end) S + Diag(exp(Gam_end - Gam_r)) K-^T U
 #pragma unroll
@@ -653,14 +705,16 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
         __syncthreads();
 
         // ---------------- epilogue: gated RMSNorm over dv, then the outputs
+        if (tid < CH) {
+            float tot = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < NW; w2++) tot += part_s[w2][tid];
+            rinv_s[tid] = rsqrtf(tot * (1.0f / DV) + p.rms_eps);
+        }
+        __syncthreads();
         {
             const int tp = opq(tid);
             const int ln = tp & 63, gg = ln >> 4, jc = 16 * (tp >> 6) + (ln & 15);
-            const uint32_t rowb = static_cast<uint32_t>(H * DV * sizeof(ACT));
-            const uint32_t nb = static_cast<uint32_t>(((n - 1) * H + 1) * DV * sizeof(ACT));
-            // rows past the chunk fall outside the resources (range-checked per-lane
-            // offsets): their z loads read 0, and their stores are also predicated off
-            const auto rz = make_rsrc(zin + (tc0 * H + h) * DV, nb);
             const auto ro = make_rsrc(out + (tc0 * H + h) * DV, nb);
             const uint32_t vo = static_cast<uint32_t>(4 * gg * rowb + jc * sizeof(ACT));
 #pragma unroll
@@ -668,13 +722,11 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int t = 16 * tb + 4 * gg + e;
-                    const uint32_t vrow = vo + static_cast<uint32_t>((16 * tb + e) * rowb);
-                    const float zz = buf_ld_act<ACT>(rz, vrow, 0);
-                    float tot = 0.f;
-#pragma unroll
-                    for (int w2 = 0; w2 < NW; w2++) tot += part_s[w2][t];
-                    const float rinv = rsqrtf(tot * (1.0f / DV) + p.rms_eps);
-                    if (t < n) buf_st_act<ACT>(ro, vrow, 0, accr[tb][e] * rinv * nwj * sigmoid(zz));
+                    const float rinv = rinv_s[t];
+                    // rows past the chunk are predicated off (and outside the resource)
+                    if (t < n)
+                        buf_st_act<ACT>(ro, vo + static_cast<uint32_t>((16 * tb + e) * rowb), 0,
+                                        accr[tb][e] * rinv * nwj * sigmoid(zr[tb][e]));
                 }
         }
 

@@ -42,6 +42,24 @@ def rel_l2(x, ref) -> float:
     return float(d / n) if n > 0 else float(d)
 
 
+# Both kernels keep the recurrent state in fp32 and form its products to about
+# fp32 accuracy, so every (sequence, head) state must match the oracle far
+# more tightly than the whole-tensor bf16 tolerance; a per-chain bound catches
+# errors confined to a few chains that a whole-tensor norm would average away.
+TOL_STATE_PER_CHAIN = 1e-4
+
+
+def per_chain_max(x, ref) -> float:
+    """Largest relative L2 error over the leading two axes (sequence, head)."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    a = x.reshape(x.shape[0] * x.shape[1], -1)
+    b = ref.reshape(a.shape)
+    d = np.linalg.norm(a - b, axis=1)
+    n = np.linalg.norm(b, axis=1)
+    return float(np.max(np.where(n > 0, d / np.maximum(n, 1e-300), d))) if len(n) else 0.0
+
+
 def tols(act: str):
     if act == "f32":
         return TOL_F32, TOL_F32

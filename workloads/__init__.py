@@ -27,7 +27,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-BLOCK_TOKENS = 65536
+BLOCK_TOKENS = 4096
 
 # Tensor ids for the seed sequence; fixed forever so stored inputs stay valid.
 TID = {

@@ -239,6 +239,9 @@ def main():
     ap.add_argument("--cpu-sample-steps", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many MiB (a kernel of "
+                         "known traffic, used to scale memory counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -246,6 +249,15 @@ def main():
               "so one GPU's throughput is the figure that matters here)", file=sys.stderr)
         sys.exit(2)
 
+    if args.calibration_copy_mib > 0:
+        import torch
+        n = args.calibration_copy_mib << 18          # float32 elements
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     res = bench_decode(args)
     line = {
         "metric": METRIC,

@@ -227,7 +227,7 @@ def cpu_baseline(sample_steps: int):
                         inp.conv_w, inp.norm_w, S[slots], X[slots])
     dt = time.perf_counter() - t0
     return {"value": B * sample_steps / dt, "unit": "tok/s", "cores": threads, "kind": "oracle",
-            "sample": f"decode workload, first {sample_steps} of 256 steps, 64 sequences x 32 heads, "
+            "sample": f"decode workload, {sample_steps} of 256 steps, 64 sequences x 32 heads, "
                       f"fp64 token-by-token, {dt:.1f} s"}
 
 
@@ -236,7 +236,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-sample-steps", type=int, default=128)
+    ap.add_argument("--cpu-sample-steps", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,

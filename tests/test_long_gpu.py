@@ -1,0 +1,128 @@
+"""Full-size GPU runs of the varlen-with-checkpoints workload and the
+1M-token long-context workload.
+
+Varlen: 16 sequences with lengths floor(exp(U(ln 1K, ln 64K))) (about 248K
+tokens), H=32, dk=dv=128, bf16, checkpoints every 4096 tokens and at sequence
+ends.  Outputs, final states and checkpoints are compared with the oracle on
+sampled heads; every sequence with an interval checkpoint is then resumed from
+a seeded one and finished, and must match the straight run bit for bit.
+
+Long context: one sequence of 1,048,576 tokens, H=8, checkpoints every 32K.
+The oracle checks the first 64K tokens (outputs and the checkpoints there);
+a resume from the checkpoint at 512K must reproduce the second half bit for
+bit; the end state is fanned out to 256 decode slots by copy-on-write resume
+and advanced 512 decode steps, checked on sampled slots against the oracle
+started from the same checkpoint.
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_recurrence_decode_amd as kda
+import oracle
+import workloads as wl
+from tests.helpers import TOL_STATE_PER_CHAIN, bits, dev, host, per_chain_max, rel_l2, say, tols
+from tests.prefill_runner import Run, checkpoint_positions, resume_and_finish
+
+pytestmark = pytest.mark.gpu
+
+
+def test_varlen_checkpoints_and_resume_full_size():
+    w = wl.WORKLOADS["varlen_ckpt"]
+    shape, N, interval = w["shape"], w["n"], w["interval"]
+    lengths = [int(x) for x in wl.loguniform_lengths(w["seed"], N, w["lo"], w["hi"])]
+    say(f"varlen full size: {N} sequences, {sum(lengths)} tokens, lengths {lengths}")
+    inp = wl.token_inputs(w["seed"], shape, sum(lengths))
+    straight = Run(shape, inp, lengths, interval=interval).launch()
+    say(f"  prefill done, {straight.nck} checkpoints")
+    heads = [5, 27]
+    r = oracle.run(inp.q[:, heads], inp.k[:, heads], inp.v[:, heads], inp.z[:, heads], inp.g[:, heads],
+                   inp.beta[:, heads], inp.conv_w[heads], inp.norm_w, straight.cu, ckpt_interval=interval)
+    tol_o, tol_s = tols("bf16")
+    e_out = rel_l2(host(straight.out)[:, heads], r.out)
+    Sf, Xf = straight.final_state()
+    e_s = rel_l2(Sf[:, heads], r.S)
+    e_c = per_chain_max(Sf[:, heads], r.S)
+    ck = host(straight.ckS)[:straight.nck][:, heads]
+    e_ck = rel_l2(ck, r.ckpt_S)
+    e_ckc = per_chain_max(ck, r.ckpt_S)
+    say(f"  sampled heads {heads}: out {e_out:.3e} state {e_s:.3e} (worst chain {e_c:.3e}) "
+        f"checkpoints {e_ck:.3e} (worst {e_ckc:.3e})")
+    assert e_out <= tol_o and e_s <= tol_s and e_c <= TOL_STATE_PER_CHAIN
+    assert e_ck <= tol_s and e_ckc <= TOL_STATE_PER_CHAIN
+    np.testing.assert_array_equal(Xf[:, heads], r.X)
+    np.testing.assert_array_equal(host(straight.ckX)[:straight.nck][:, heads], r.ckpt_X)
+    # resume every sequence that has an interval checkpoint from a seeded one
+    rng = np.random.default_rng([w["seed"], wl.TID["resume"], 0])
+    picks = []
+    for n, L in enumerate(lengths):
+        n_int = len(checkpoint_positions(0, L, interval)) - 1      # interval checkpoints (not the end)
+        picks.append(int(rng.integers(0, n_int)) if n_int > 0 else None)
+    resumed, seqs, res_pos, src_ck, idx = resume_and_finish(straight, picks)
+    say(f"  resumed {len(seqs)} sequences at {res_pos}")
+    assert np.array_equal(bits(resumed.out), bits(straight.out[torch.from_numpy(idx).cuda()]))
+    for j, n in enumerate(seqs):
+        assert np.array_equal(bits(resumed.Sd[int(resumed.final[j])]), bits(straight.Sd[int(straight.final[n])]))
+        assert np.array_equal(bits(resumed.Xd[int(resumed.final[j])]), bits(straight.Xd[int(straight.final[n])]))
+        later = oracle.num_checkpoints(res_pos[j], resumed.lengths[j], interval)
+        assert np.array_equal(bits(resumed.ckS[int(resumed.base[j]):int(resumed.base[j]) + later]),
+                              bits(straight.ckS[src_ck[j] + 1:src_ck[j] + 1 + later]))
+
+
+def test_long_context_1m_full_size():
+    w = wl.WORKLOADS["long_1m"]
+    shape, L, interval = w["shape"], w["lengths"][0], w["interval"]
+    say(f"long context: {L} tokens, H={shape.H}, checkpoints every {interval}")
+    inp = wl.token_inputs(w["seed"], shape, L)
+    straight = Run(shape, inp, [L], interval=interval).launch()
+    say(f"  prefill done, {straight.nck} checkpoints")
+    assert straight.nck == L // interval
+    out = host(straight.out)
+    assert np.isfinite(out).all()
+    # oracle on the first 64K tokens, one sampled head
+    P, hs = 65536, [3]
+    r = oracle.run(inp.q[:P, hs], inp.k[:P, hs], inp.v[:P, hs], inp.z[:P, hs], inp.g[:P, hs], inp.beta[:P, hs],
+                   inp.conv_w[hs], inp.norm_w, [0, P], ckpt_interval=interval)
+    e_out = rel_l2(out[:P, hs], r.out)
+    ck = host(straight.ckS[:2])[:, hs]
+    e_ck = rel_l2(ck, r.ckpt_S[:2])
+    say(f"  first {P} tokens, head {hs}: out {e_out:.3e}, checkpoints at 32K/64K {e_ck:.3e}")
+    assert e_out <= 1e-2 and e_ck <= 5e-3 and per_chain_max(ck, r.ckpt_S[:2]) <= TOL_STATE_PER_CHAIN
+    np.testing.assert_array_equal(host(straight.ckX[:2])[:, hs], r.ckpt_X[:2])
+    # resume from the checkpoint at 512K: the second half is reproduced bit for bit
+    j = L // 2 // interval - 1
+    resumed, _, res_pos, _, idx = resume_and_finish(straight, [j])
+    assert res_pos == [L // 2]
+    assert np.array_equal(bits(resumed.out), bits(straight.out[L // 2:]))
+    assert np.array_equal(bits(resumed.Sd[int(resumed.final[0])]), bits(straight.Sd[int(straight.final[0])]))
+    say("  resume from 512K: bitwise identical")
+    # fan the end state out to 256 decode slots and run 512 decode steps
+    B, steps = w["decode_B"], w["decode_steps"]
+    cfg = straight.cfg
+    Sp = torch.zeros((B, shape.H, shape.dk, shape.dv), device="cuda")
+    Xp = torch.zeros((B, shape.H, shape.C, 3), dtype=cfg.torch_act, device="cuda")
+    last = straight.nck - 1
+    kda.kda_resume(cfg, straight.ckS, straight.ckX, dev(np.full(B, last, np.int32)), Sp, Xp,
+                   dev(np.arange(B, dtype=np.int32)))
+    dinp = wl.token_inputs(w["seed"] + 100, shape, B * steps)
+    rs = lambda a: a.reshape((steps, B) + a.shape[1:])
+    q, k, v, z = (dev(rs(a), cfg.torch_act) for a in (dinp.q, dinp.k, dinp.v, dinp.z))
+    g, beta = dev(rs(dinp.g)), dev(rs(dinp.beta))
+    cw, nw = dev(inp.conv_w), dev(inp.norm_w)
+    slot = dev(np.arange(B, dtype=np.int32))
+    dout = torch.empty((steps, B, shape.H, shape.dv), dtype=cfg.torch_act, device="cuda")
+    for s in range(steps):
+        kda.kda_decode_step(cfg, q[s], k[s], v[s], z[s], g[s], beta[s], cw, nw, Sp, Xp, slot, dout[s])
+    torch.cuda.synchronize()
+    pick = [0, 37, 128, 255]
+    S0 = np.repeat(host(straight.ckS[last:last + 1]), len(pick), axis=0)
+    X0 = np.repeat(host(straight.ckX[last:last + 1]), len(pick), axis=0)
+    sub = lambda a: rs(a)[:, pick]
+    o_ref, S_ref, X_ref = oracle.decode_steps(sub(dinp.q), sub(dinp.k), sub(dinp.v), sub(dinp.z), sub(dinp.g),
+                                              sub(dinp.beta), inp.conv_w, inp.norm_w, S0, X0)
+    e_o = rel_l2(host(dout)[:, pick], o_ref)
+    e_s = rel_l2(host(Sp)[pick], S_ref)
+    e_c = per_chain_max(host(Sp)[pick], S_ref)
+    say(f"  decode fan-out, slots {pick}: out {e_o:.3e} state {e_s:.3e} (worst chain {e_c:.3e})")
+    assert e_o <= 1e-2 and e_s <= 5e-3 and e_c <= TOL_STATE_PER_CHAIN
+    np.testing.assert_array_equal(host(Xp)[pick], X_ref)

@@ -13,100 +13,10 @@ import torch
 import linear_attention_recurrence_decode_amd as kda
 import oracle
 import workloads as wl
-from tests.helpers import TOL_STATE_PER_CHAIN, bits, dev, host, per_chain_max, rel_l2, say, tols
+from tests.helpers import bits, dev, host, rel_l2, say, tols
+from tests.prefill_runner import Run, check_against_oracle, oracle_for, resume_and_finish, states_for
 
 pytestmark = pytest.mark.gpu
-
-
-def cfg_for(shape):
-    return kda.Config(shape.H, shape.dk, shape.dv, kda.KDA_BF16 if shape.act == "bf16" else kda.KDA_F32)
-
-
-class Run:
-    """One prefill call on the GPU with pools, slots and checkpoint buffers."""
-
-    def __init__(self, shape, inp, lengths, *, starts=None, S0=None, X0=None, interval=0,
-                 pool_extra=3, seq_order=None):
-        self.shape, self.inp = shape, inp
-        H, dk, dv, C = shape.H, shape.dk, shape.dv, shape.C
-        N = len(lengths)
-        self.N, self.lengths = N, list(lengths)
-        self.starts = [0] * N if starts is None else list(starts)
-        self.cfg = cfg_for(shape)
-        act = self.cfg.torch_act
-        cu = wl.cu_seqlens(lengths)
-        self.cu = cu
-        nslots = 2 * N + pool_extra
-        S = np.zeros((nslots, H, dk, dv), np.float32)
-        X = np.zeros((nslots, H, C, 3), np.float32)
-        init = np.full(N, -1, np.int32)
-        if S0 is not None:
-            init = np.arange(N, dtype=np.int32)
-            S[:N] = S0
-            X[:N] = X0
-        final = np.arange(N, 2 * N, dtype=np.int32)
-        self.init, self.final = init, final
-        self.Sd, self.Xd = dev(S), dev(X, act)
-        counts = [oracle.num_checkpoints(s, L, interval) for s, L in zip(self.starts, lengths)]
-        base = np.zeros(N, np.int32)
-        if N:
-            base[1:] = np.cumsum(counts)[:-1]
-        self.base, self.nck = base, int(sum(counts))
-        self.interval = interval
-        self.ckS = torch.full((max(self.nck, 1), H, dk, dv), float("nan"), device="cuda")
-        self.ckX = torch.zeros((max(self.nck, 1), H, C, 3), dtype=act, device="cuda")
-        T = int(cu[-1])
-        self.q, self.k, self.v, self.z = (dev(a, act) for a in (inp.q, inp.k, inp.v, inp.z))
-        self.g, self.beta = dev(inp.g), dev(inp.beta)
-        self.conv_w, self.norm_w = dev(inp.conv_w), dev(inp.norm_w)
-        self.out = torch.full((T, H, dv), float("nan"), dtype=act, device="cuda")
-        nbytes = kda.kda_prefill_workspace_bytes(self.cfg, N, T)
-        self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
-
-    def launch(self):
-        kda.kda_prefill_varlen(self.cfg, dev(self.cu.astype(np.int32)), self.q, self.k, self.v, self.z,
-                               self.g, self.beta, self.conv_w, self.norm_w, self.Sd, self.Xd,
-                               dev(self.init), dev(self.final), self.out, self.ws,
-                               start_pos=dev(np.asarray(self.starts, np.int64)),
-                               ckpt_interval=self.interval,
-                               ckpt_state=self.ckS if self.interval else None,
-                               ckpt_conv=self.ckX if self.interval else None,
-                               ckpt_base=dev(self.base) if self.interval else None)
-        torch.cuda.synchronize()
-        return self
-
-    def final_state(self):
-        return host(self.Sd)[self.final], host(self.Xd)[self.final]
-
-
-def oracle_for(run, S0=None, X0=None, heads=None):
-    inp = run.inp
-    sl = (slice(None),) if heads is None else (slice(None), heads)
-    hs = slice(None) if heads is None else heads
-    return oracle.run(inp.q[sl], inp.k[sl], inp.v[sl], inp.z[sl], inp.g[sl], inp.beta[sl],
-                      inp.conv_w[hs], inp.norm_w, run.cu, start_pos=run.starts,
-                      S0=None if S0 is None else S0[:, hs], X0=None if X0 is None else X0[:, hs],
-                      ckpt_interval=run.interval)
-
-
-def states_for(seed, shape, N, scale=0.3):
-    S, X = wl.states(seed + 100, shape, N, state_std=scale, conv_std=1.0)
-    return S, X
-
-
-def check_against_oracle(run, r, heads=None):
-    tol_o, tol_s = tols(run.shape.act)
-    hs = slice(None) if heads is None else heads
-    out = host(run.out)[:, hs]
-    Sf, Xf = run.final_state()
-    e_out = rel_l2(out, r.out)
-    e_s = rel_l2(Sf[:, hs], r.S)
-    e_c = per_chain_max(Sf[:, hs], r.S)
-    say(f"  rel-L2 out {e_out:.3e} (tol {tol_o})  state {e_s:.3e} (tol {tol_s})  worst chain {e_c:.3e}")
-    assert np.isfinite(out).all()
-    assert e_out <= tol_o and e_s <= tol_s and e_c <= TOL_STATE_PER_CHAIN
-    np.testing.assert_array_equal(Xf[:, hs], r.X)
-    return e_out, e_s
 
 
 def test_prefill_tiny_f32_workload():
@@ -180,39 +90,16 @@ def test_resume_is_bitwise_identical(act):
     inp = wl.token_inputs(31, shape, sum(lengths), g_scale=0.05, norm_w="random")
     S0, X0 = states_for(31, shape, N)
     straight = Run(shape, inp, lengths, starts=starts, S0=S0, X0=X0, interval=128).launch()
-    # resume sequence n from its j-th checkpoint (an interval boundary, not the end)
-    picks = [1, 0, 1]
-    cfg = straight.cfg
-    res_pos, src_ck = [], []
-    for n in range(N):
-        ps = [p for p in range(starts[n] + 1, starts[n] + lengths[n] + 1)
-              if p % 128 == 0 or p == starts[n] + lengths[n]]
-        res_pos.append(ps[picks[n]])
-        src_ck.append(int(straight.base[n]) + picks[n])
-    # second batch: the remainders, packed, starting at the resume positions
-    rem = [starts[n] + lengths[n] - res_pos[n] for n in range(N)]
-    offs = [int(straight.cu[n]) + (res_pos[n] - starts[n]) for n in range(N)]
-    idx = np.concatenate([np.arange(o, o + r) for o, r in zip(offs, rem)])
-    sub = wl.Inputs(shape, inp.q[idx], inp.k[idx], inp.v[idx], inp.z[idx], inp.g[idx], inp.beta[idx],
-                    inp.conv_w, inp.norm_w)
-    resumed = Run(shape, sub, rem, starts=res_pos, interval=128)
-    # seed its initial slots from the straight run's checkpoints
-    resumed.init = np.arange(N, dtype=np.int32)
-    kda.kda_resume(cfg, straight.ckS, straight.ckX, dev(np.asarray(src_ck, np.int32)),
-                   resumed.Sd, resumed.Xd, dev(resumed.init))
     ck_before = bits(straight.ckS)
-    resumed.launch()
+    resumed, seqs, res_pos, src_ck, idx = resume_and_finish(straight, [1, 0, 1])
     assert np.array_equal(bits(straight.ckS), ck_before)          # copy-on-write source untouched
-    out_s = bits(straight.out[torch.from_numpy(idx).cuda()])
-    assert np.array_equal(bits(resumed.out), out_s)
-    for n in range(N):
-        assert np.array_equal(bits(resumed.Sd[int(resumed.final[n])]), bits(straight.Sd[int(straight.final[n])]))
-        assert np.array_equal(bits(resumed.Xd[int(resumed.final[n])]), bits(straight.Xd[int(straight.final[n])]))
-        later = oracle.num_checkpoints(res_pos[n], rem[n], 128)
-        for j in range(later):
-            a = resumed.ckS[int(resumed.base[n]) + j]
-            b = straight.ckS[src_ck[n] + 1 + j]
-            assert np.array_equal(bits(a), bits(b))
+    assert np.array_equal(bits(resumed.out), bits(straight.out[torch.from_numpy(idx).cuda()]))
+    for j, n in enumerate(seqs):
+        assert np.array_equal(bits(resumed.Sd[int(resumed.final[j])]), bits(straight.Sd[int(straight.final[n])]))
+        assert np.array_equal(bits(resumed.Xd[int(resumed.final[j])]), bits(straight.Xd[int(straight.final[n])]))
+        later = oracle.num_checkpoints(res_pos[j], resumed.lengths[j], 128)
+        for i in range(later):
+            assert np.array_equal(bits(resumed.ckS[int(resumed.base[j]) + i]), bits(straight.ckS[src_ck[j] + 1 + i]))
 
 
 def test_prefill_deterministic_and_packing_invariant():

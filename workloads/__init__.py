@@ -38,15 +38,21 @@ TID = {
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to the nearest bf16 (ties to even); return float32."""
+    """Round finite float32 values to the nearest bf16 (ties to even); return
+    float32.  Works in place on a float32 array (a copy of anything else)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    b = x.view(np.uint32).astype(np.uint64)
-    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
-    return b.astype(np.uint32).view(np.float32).reshape(x.shape)
+    b = x.view(np.uint32)
+    lsb = (b >> 16) & 1
+    b += np.uint32(0x7FFF)
+    b += lsb
+    b &= np.uint32(0xFFFF0000)
+    return x
 
 
 def _softplus(x: np.ndarray) -> np.ndarray:
-    return np.logaddexp(np.float32(0.0), x).astype(np.float32)
+    """log(1 + exp(x)) in float32, as max(x, 0) + log1p(exp(-|x|))."""
+    x = np.asarray(x, dtype=np.float32)
+    return (np.maximum(x, np.float32(0.0)) + np.log1p(np.exp(-np.abs(x)))).astype(np.float32)
 
 
 def _sigmoid(x: np.ndarray) -> np.ndarray:
@@ -57,9 +63,10 @@ def _threads() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
 
-def draw_tokens(seed: int, tid: int, T: int, inner: tuple, kind: str = "normal",
-                std: float = 1.0) -> np.ndarray:
-    """Draw a [T, *inner] float32 tensor block by block (see module docstring)."""
+def draw_tokens(seed: int, tid: int, T: int, inner: tuple, std: float = 1.0,
+                transform=None) -> np.ndarray:
+    """Draw a [T, *inner] float32 tensor block by block (see module docstring);
+    `transform`, if given, maps each drawn block (in the worker threads)."""
     out = np.empty((T,) + tuple(inner), dtype=np.float32)
     nblk = (T + BLOCK_TOKENS - 1) // BLOCK_TOKENS
 
@@ -69,6 +76,8 @@ def draw_tokens(seed: int, tid: int, T: int, inner: tuple, kind: str = "normal",
         blk = rng.standard_normal((hi - lo,) + tuple(inner), dtype=np.float32)
         if std != 1.0:
             blk *= np.float32(std)
+        if transform is not None:
+            blk = transform(blk)
         out[lo:hi] = blk
 
     if nblk <= 1:
@@ -130,15 +139,16 @@ def token_inputs(seed: int, shape: LayerShape, T: int, *, g_scale: float = 1.0,
     non-unit weight that exposes indexing mistakes).
     """
     H, dk, dv = shape.H, shape.dk, shape.dv
-    rnd = round_bf16 if shape.act == "bf16" else (lambda a: a)
-    q = rnd(draw_tokens(seed, TID["q"], T, (H, dk)))
-    k = rnd(draw_tokens(seed, TID["k"], T, (H, dk)))
-    v = rnd(draw_tokens(seed, TID["v"], T, (H, dv)))
-    z = rnd(draw_tokens(seed, TID["z"], T, (H, dv)))
-    g = -_softplus(draw_tokens(seed, TID["g"], T, (H, dk)))
-    if g_scale != 1.0:
-        g = (g * np.float32(g_scale)).astype(np.float32)
-    beta = _sigmoid(draw_tokens(seed, TID["beta"], T, (H,)))
+    rnd = round_bf16 if shape.act == "bf16" else None
+    q = draw_tokens(seed, TID["q"], T, (H, dk), transform=rnd)
+    k = draw_tokens(seed, TID["k"], T, (H, dk), transform=rnd)
+    v = draw_tokens(seed, TID["v"], T, (H, dv), transform=rnd)
+    z = draw_tokens(seed, TID["z"], T, (H, dv), transform=rnd)
+    gs = np.float32(g_scale)
+    g = draw_tokens(seed, TID["g"], T, (H, dk),
+                    transform=lambda a: (-_softplus(a) * gs).astype(np.float32) if g_scale != 1.0
+                    else -_softplus(a))
+    beta = draw_tokens(seed, TID["beta"], T, (H,), transform=_sigmoid)
     conv_w = draw_plain(seed, TID["conv_w"], (H, shape.C, shape.W), std=conv_w_std)
     if norm_w == "ones":
         nw = np.ones((dv,), np.float32)

@@ -236,6 +236,97 @@ __device__ __forceinline__ void store_state_strip(float* dst, const f32x4 (&S)[I
         for (int e = 0; e < 4; e++) buf_stf(rs, sv, (16 * ib + e) * DV * 4, S[ib][e]);
 }
 
+// Registers holding one chunk's staged inputs between the loads and the LDS
+// stores: raw q|k|v rows (with 3 rows of left context) as 16-byte words, this
+// thread's 16 log-decay values, and (threads 0..63) one beta.
+template <int NU>
+struct Staged {
+    uint4 val[NU];
+    float gq[16];
+    float beta;
+};
+
+// Issue the global loads of the chunk [tc0, tc0+n) of head h (no waits).
+// Left-context rows before the sequence start come from the initial conv
+// state x0 (index 2 = the token just before the start).
+template <typename ACT, int DK, int DV, int NT, int NU>
+__device__ __forceinline__ void stage_issue(Staged<NU>& st, const PrefillParams& p, const ACT* x0,
+                                            int64_t tok0, int64_t tc0, int n, int H, int h, int tp) {
+    constexpr int C = 2 * DK + DV;
+    constexpr int VEC = 16 / static_cast<int>(sizeof(ACT));
+    constexpr int UPR = C / VEC;
+    const ACT* qin = static_cast<const ACT*>(p.q);
+    const ACT* kin = static_cast<const ACT*>(p.k);
+    const ACT* vin = static_cast<const ACT*>(p.v);
+#pragma unroll
+    for (int j = 0; j < NU; j++) {
+        const int u = tp + j * NT;
+        const int r = u / UPR, c0 = (u % UPR) * VEC;
+        const int64_t tok = tc0 - 3 + r;
+        st.val[j] = make_uint4(0, 0, 0, 0);
+        if (u < (CH + 3) * UPR && r < n + 3) {
+            if (tok >= tok0) {
+                const ACT* src = c0 < DK ? qin + (tok * H + h) * DK + c0
+                                         : (c0 < 2 * DK ? kin + (tok * H + h) * DK + (c0 - DK)
+                                                        : vin + (tok * H + h) * DV + (c0 - 2 * DK));
+                st.val[j] = *reinterpret_cast<const uint4*>(src);
+            } else {
+                const int m = 3 - static_cast<int>(tok0 - tok);
+                uint32_t wd[4];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; q4++) {
+                    const int c = c0 + q4 * (VEC / 4);
+                    if constexpr (sizeof(ACT) == 2) {
+                        wd[q4] = static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(x0)[c * 3 + m]) |
+                                 (static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(x0)[(c + 1) * 3 + m]) << 16);
+                    } else {
+                        wd[q4] = __float_as_uint(reinterpret_cast<const float*>(x0)[c * 3 + m]);
+                    }
+                }
+                st.val[j] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+            }
+        }
+    }
+    // row t of this head at byte offset t * row_bytes; the resources end after
+    // row n-1 and the whole offset is in the range-checked per-lane offset, so
+    // rows past the chunk read as zero
+    const int cgp = tp % DK, qqp = tp / DK;
+    const auto rg = make_rsrc(p.g + (tc0 * H + h) * DK, static_cast<uint32_t>(((n - 1) * H + 1) * DK * 4));
+    const uint32_t gv = static_cast<uint32_t>((16 * qqp * H * DK + cgp) * 4);
+#pragma unroll
+    for (int r = 0; r < 16; r++) st.gq[r] = buf_ldf(rg, gv + static_cast<uint32_t>(r * H * DK * 4), 0);
+    st.beta = 0.f;
+    if (tp < CH) {
+        const auto rb = make_rsrc(p.beta + tc0 * H + h, static_cast<uint32_t>(((n - 1) * H + 1) * 4));
+        st.beta = buf_ldf(rb, static_cast<uint32_t>(tp * H * 4), 0);
+    }
+}
+
+// Define every staged register without loading (after the last chunk), so
+// that no value of the previous chunk stays live across the loop.
+template <int NU>
+__device__ __forceinline__ void stage_clear(Staged<NU>& st) {
+#pragma unroll
+    for (int j = 0; j < NU; j++) st.val[j] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; r++) st.gq[r] = 0.f;
+    st.beta = 0.f;
+}
+
+// Store the staged raw rows and beta into LDS.
+template <typename ACT, int DK, int DV, int NT, int NU>
+__device__ __forceinline__ void stage_commit(const Staged<NU>& st, ACT* raw, float* beta_s, int tp) {
+    constexpr int C = 2 * DK + DV;
+    constexpr int VEC = 16 / static_cast<int>(sizeof(ACT));
+    constexpr int UPR = C / VEC;
+#pragma unroll
+    for (int j = 0; j < NU; j++) {
+        const int u = tp + j * NT;
+        if (u < (CH + 3) * UPR) *reinterpret_cast<uint4*>(raw + (u / UPR) * C + (u % UPR) * VEC) = st.val[j];
+    }
+    if (tp < CH) beta_s[tp] = st.beta;
+}
+
 template <int D, typename ACT>
 struct PrefillShape {
     static constexpr int DK = D, DV = D;
@@ -247,6 +338,7 @@ struct PrefillShape {
     static constexpr int PS = DK + 8;           // padded row stride of [64][dk] planes
     static constexpr int QS = CH + 8;           // padded row stride of [*][64] planes
     static constexpr int VEC = 16 / static_cast<int>(sizeof(ACT));   // elements per 16-byte load
+    static constexpr int NU = ((CH + 3) * (C / VEC) + NT - 1) / NT;  // staged 16-byte words per thread
     // LDS regions (bytes)
     static constexpr int R0 = cmax(CH * DK * 4, 2 * CH * PS * 2);                // a_k (fp32) / K+ planes
     static constexpr int R1 = R0;                                                 // a_q (fp32) / Q+ planes
@@ -377,60 +469,22 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
     int done = 0, ck = 0;
     const int ck_base = (p.ckpt_interval > 0) ? p.ckpt_base[seq] : 0;
 
+    // ---------------- A1 of the first chunk (later chunks are staged while the
+    // previous chunk finishes: their loads are issued after its state phase)
+    Staged<Sh::NU> stg;
+    int n = L > 0 ? min(L, CH - static_cast<int>(pos % CH)) : 0;
+    int64_t tc0 = tok0;
+    if (L > 0) {
+        const int tp = opq(tid);
+        stage_issue<ACT, DK, DV, NT>(stg, p, x0_s, tok0, tc0, n, H, h, tp);
+        stage_commit<ACT, DK, DV, NT>(stg, raw, beta_s, tp);
+    }
+    __syncthreads();
+
     while (done < L) {
-        const int n = min(L - done, CH - static_cast<int>(pos % CH));
-        const int64_t tc0 = tok0 + done;
-        float gq[16];      // log decay of this thread's (channel, quarter), then its prefix sums
         float vh[4][4];    // SiLU(conv(v)) in accumulator layout
         float km[16];      // K- column of this thread, kept for the transposed copy
-
-        // ---------------- A1: stage raw rows (3 rows of left context), gates
-        {
-            const int tp = opq(tid);
-            const int cgp = tp % DK, qqp = tp / DK;
-            // all 16-byte loads of the chunk first (one memory round trip), then
-            // the LDS stores
-            constexpr int UPR = C / VEC;                 // 16-byte units per row
-            constexpr int NU = ((CH + 3) * UPR + NT - 1) / NT;
-            uint4 val[NU];
-#pragma unroll
-            for (int j = 0; j < NU; j++) {
-                const int u = tp + j * NT;
-                const int r = u / UPR, c0 = (u % UPR) * VEC;
-                const int64_t tok = tc0 - 3 + r;
-                val[j] = make_uint4(0, 0, 0, 0);
-                if (u < (CH + 3) * UPR && r < n + 3) {
-                    if (tok >= tok0) {
-                        const ACT* src = c0 < DK ? qin + (tok * H + h) * DK + c0
-                                                 : (c0 < 2 * DK ? kin + (tok * H + h) * DK + (c0 - DK)
-                                                                : vin + (tok * H + h) * DV + (c0 - 2 * DK));
-                        val[j] = *reinterpret_cast<const uint4*>(src);
-                    } else {
-                        uint32_t wd[4];
-#pragma unroll
-                        for (int q4 = 0; q4 < 4; q4++) wd[q4] = pack_word(raw_at, tok, c0 + q4 * (VEC / 4));
-                        val[j] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-                    }
-                }
-            }
-            // per-chunk view: row t of this head at byte offset t * row_bytes.  The
-            // resource ends after row n-1 and the whole offset goes through the
-            // range-checked per-lane offset, so rows past the chunk read as zero.
-            const auto rg = make_rsrc(p.g + (tc0 * H + h) * DK, static_cast<uint32_t>(((n - 1) * H + 1) * DK * 4));
-            const uint32_t gv = static_cast<uint32_t>((16 * qqp * H * DK + cgp) * 4);
-#pragma unroll
-            for (int r = 0; r < 16; r++) gq[r] = buf_ldf(rg, gv + static_cast<uint32_t>(r * H * DK * 4), 0);
-            if (tp < CH) {
-                const auto rb = make_rsrc(p.beta + tc0 * H + h, static_cast<uint32_t>(((n - 1) * H + 1) * 4));
-                beta_s[tp] = buf_ldf(rb, static_cast<uint32_t>(tp * H * 4), 0);
-            }
-#pragma unroll
-            for (int j = 0; j < NU; j++) {
-                const int u = tp + j * NT;
-                if (u < (CH + 3) * UPR) *reinterpret_cast<uint4*>(raw + (u / UPR) * C + (u % UPR) * VEC) = val[j];
-            }
-        }
-        __syncthreads();
+        float (&gq)[16] = stg.gq;   // log decay of this thread's (channel, quarter), then its prefix sums
 
         // ---------------- A2: causal conv + SiLU (q, k channels to LDS; v to registers)
         {
@@ -533,39 +587,37 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
         }
         __syncthreads();
 
-        // ---------------- A5: L = Diag(b) strictLower(K+ K-^T), P = lower(Q+ K-^T)
+        // ---------------- A5: L = Diag(b) strictLower(K+ K-^T), P = lower(Q+ K-^T);
+        // one job per 16x16 block pair (a, b) computes both, sharing the K-
+        // fragments.
         {
             const int tp = opq(tid);
             const int ln = tp & 63, wv5 = tp >> 6, gg = ln >> 4, lc = ln & 15;
-            for (int job = wv5; job < 32; job += NW) {
-                const bool isP = job >= 16;
-                const int a = (job & 15) >> 2, b = job & 3;
+            for (int job = wv5; job < 16; job += NW) {
+                const int a = job >> 2, b = job & 3;
                 if (a < b) {
-                    if (isP) {
 #pragma unroll
-                        for (int e = 0; e < 4; e++) {
-                            const int idx = (16 * a + 4 * gg + e) * QS + 16 * b + lc;
-                            pp_h[idx] = 0;
-                            pp_l[idx] = 0;
-                        }
+                    for (int e = 0; e < 4; e++) {
+                        const int idx = (16 * a + 4 * gg + e) * QS + 16 * b + lc;
+                        pp_h[idx] = 0;
+                        pp_l[idx] = 0;
                     }
                     continue;
                 }
-                const uint16_t* ah = isP ? qp_h : kp_h;
-                const uint16_t* al = isP ? qp_l : kp_l;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                f32x4 am = {0.f, 0.f, 0.f, 0.f}, ap = am;
 #pragma unroll
                 for (int ks = 0; ks < KS; ks++) {
-                    const Frag fa = ld_nat(ah, al, (16 * a + lc) * PS + 32 * ks + 8 * gg);
+                    const int offa = (16 * a + lc) * PS + 32 * ks + 8 * gg;
                     const Frag fb = ld_nat(km_h, km_l, (16 * b + lc) * PS + 32 * ks + 8 * gg);
-                    acc = mfma3(fa, fb, acc);
+                    am = mfma3(ld_nat(kp_h, kp_l, offa), fb, am);
+                    ap = mfma3(ld_nat(qp_h, qp_l, offa), fb, ap);
                 }
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int t = 16 * a + 4 * gg + e, s2 = 16 * b + lc;
-                    if (isP) st_split(pp_h, pp_l, t * QS + s2, t >= s2 ? acc[e] : 0.f);
-                    else if (a > b) st_split(lp_h, lp_l, t * QS + s2, beta_s[t] * acc[e]);
-                    else ld_s[a][4 * gg + e][lc] = t > s2 ? beta_s[t] * acc[e] : 0.f;
+                    st_split(pp_h, pp_l, t * QS + s2, t >= s2 ? ap[e] : 0.f);
+                    if (a > b) st_split(lp_h, lp_l, t * QS + s2, beta_s[t] * am[e]);
+                    else ld_s[a][4 * gg + e][lc] = t > s2 ? beta_s[t] * am[e] : 0.f;
                 }
             }
         }
@@ -704,6 +756,13 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
         }
         __syncthreads();
 
+        // ---------------- next chunk's inputs: loads in flight during the epilogue
+        const int done_next = done + n;
+        const int64_t pos_next = pos + n;
+        const int n_next = done_next < L ? min(L - done_next, CH - static_cast<int>(pos_next % CH)) : 0;
+        if (n_next > 0) stage_issue<ACT, DK, DV, NT>(stg, p, x0_s, tok0, tok0 + done_next, n_next, H, h, opq(tid));
+        else stage_clear(stg);
+
         // ---------------- epilogue: gated RMSNorm over dv, then the outputs
         if (tid < CH) {
             float tot = 0.f;
@@ -730,8 +789,10 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
                 }
         }
 
-        done += n;
-        pos += n;
+        // the raw-row region and beta are free: every wave is past its state phase
+        if (n_next > 0) stage_commit<ACT, DK, DV, NT>(stg, raw, beta_s, opq(tid));
+        done = done_next;
+        pos = pos_next;
         // ---------------- checkpoints: interval boundaries inside, and the end
         if (p.ckpt_interval > 0 && (pos % p.ckpt_interval == 0 || done == L)) {
             const int slot = ck_base + ck;
@@ -742,6 +803,8 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
                 write_conv_state(static_cast<ACT*>(p.ckpt_conv) + sh * C * 3, tok0 + done);
             }
         }
+        n = n_next;
+        tc0 = tok0 + done;
         __syncthreads();
     }
 

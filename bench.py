@@ -1,6 +1,7 @@
 """Benchmark of the KDA layer hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --workload varlen_ckpt|long_1m [--steps K] [--warmup W]
 
 A step is one pass of the batched decode workload: 64 sequences advanced by
 256 single-token decode steps (H=32, dk=dv=128, bf16 activations, fp32
@@ -15,6 +16,15 @@ step).  The line also carries:
                 pass): tokens/s and the algorithmic HBM and bf16-MFMA fractions
   cpu_baseline  the fp64 oracle timed on this host on a bounded sample of the
                 decode workload
+With --workload the line instead reports one of the larger prefill
+workloads (inputs resident in HBM, one call per pass):
+  varlen_ckpt   16 sequences of log-uniform length in [1K, 64K] (about 248K
+                tokens), H=32, checkpoints every 4096 tokens and at the ends;
+                then a resume batch (each sequence restarted from a seeded
+                interval checkpoint) timed on its own
+  long_1m       one sequence of 1,048,576 tokens, H=8, checkpoints every 32K,
+                unsplit and split at the checkpoints; then 512 decode steps of
+                256 sequences fanned out from the end state
 Only one GPU is supported: --gpus above 1 exits with a message.
 """
 from __future__ import annotations
@@ -182,7 +192,7 @@ def bench_prefill(steps, warmup):
     init = torch.full((N,), -1, dtype=torch.int32, device="cuda")
     final = torch.arange(N, dtype=torch.int32, device="cuda")
     out = torch.empty((T, H, dv), dtype=act, device="cuda")
-    ws = torch.empty(kda.kda_prefill_workspace_bytes(cfg, N, T), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(cfg, N, T, 0, 0), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def one():
@@ -207,6 +217,160 @@ def bench_prefill(steps, warmup):
             "mfma_frac": flops / t / BF16_PEAK, "hbm_frac": nbytes / t / HBM_PEAK,
             "alg_flops": flops, "alg_bytes": nbytes,
             "attainable_frac": max(flops / BF16_PEAK, nbytes / HBM_PEAK) / t}
+
+
+def _time_calls(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / steps
+
+
+class PrefillSetup:
+    """Device buffers of one packed prefill batch with checkpoints."""
+
+    def __init__(self, kda, wl, shape, inp, lengths, starts, interval, flags_list):
+        import torch
+        H, dk, dv, C = shape.H, shape.dk, shape.dv, shape.C
+        N, T = len(lengths), int(sum(lengths))
+        self.cfg = cfg = kda.Config(H, dk, dv, kda.KDA_BF16)
+        act = cfg.torch_act
+        self.kda, self.N, self.T, self.interval = kda, N, T, interval
+        self.q, self.k, self.v, self.z = (torch.from_numpy(a).to(act).cuda() for a in (inp.q, inp.k, inp.v, inp.z))
+        self.g, self.beta = torch.from_numpy(inp.g).cuda(), torch.from_numpy(inp.beta).cuda()
+        self.conv_w, self.norm_w = torch.from_numpy(inp.conv_w).cuda(), torch.from_numpy(inp.norm_w).cuda()
+        self.cu = torch.from_numpy(wl.cu_seqlens(lengths).astype(np.int32)).cuda()
+        self.sp = torch.tensor(starts, dtype=torch.int64).cuda()
+        self.S = torch.zeros((2 * N, H, dk, dv), device="cuda")
+        self.X = torch.zeros((2 * N, H, C, 3), dtype=act, device="cuda")
+        self.init = torch.full((N,), -1, dtype=torch.int32).cuda()
+        self.final = torch.arange(N, 2 * N, dtype=torch.int32).cuda()
+        counts = [kda.kda_num_checkpoints(s0, L, interval) for s0, L in zip(starts, lengths)]
+        base = np.zeros(N, np.int32)
+        base[1:] = np.cumsum(counts)[:-1]
+        self.base_h, self.nck = base, int(sum(counts))
+        self.base = torch.from_numpy(base).cuda()
+        self.ckS = torch.zeros((max(self.nck, 1), H, dk, dv), device="cuda")
+        self.ckX = torch.zeros((max(self.nck, 1), H, C, 3), dtype=act, device="cuda")
+        self.out = torch.empty((T, H, dv), dtype=act, device="cuda")
+        nbytes = max(kda.kda_prefill_workspace_bytes(cfg, N, T, interval, f) for f in flags_list)
+        self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+
+    def call(self, flags, stream):
+        self.kda.kda_prefill_varlen(self.cfg, self.cu, self.q, self.k, self.v, self.z, self.g, self.beta,
+                                    self.conv_w, self.norm_w, self.S, self.X, self.init, self.final, self.out,
+                                    self.ws, start_pos=self.sp, ckpt_interval=self.interval, ckpt_state=self.ckS,
+                                    ckpt_conv=self.ckX, ckpt_base=self.base, flags=flags, stream=stream)
+
+
+def prefill_rates(T, H, dk, dv, t):
+    th = T * H
+    flops = prefill_flops_per_token_head(dk, dv) * th
+    nbytes = prefill_bytes_per_token_head(dk, dv) * th
+    return {"value": T / t, "unit": "tok/s", "ms_per_call": t * 1e3, "mfma_frac": flops / t / BF16_PEAK,
+            "hbm_frac": nbytes / t / HBM_PEAK, "attainable_frac": max(flops / BF16_PEAK, nbytes / HBM_PEAK) / t}
+
+
+def bench_varlen(steps, warmup):
+    """Varlen prefill with checkpoints, then the resume batch."""
+    import torch
+    import linear_attention_recurrence_decode_amd as kda
+    import workloads as wl
+
+    w = wl.WORKLOADS["varlen_ckpt"]
+    shape, N, interval = w["shape"], w["n"], w["interval"]
+    lengths = [int(x) for x in wl.loguniform_lengths(w["seed"], N, w["lo"], w["hi"])]
+    log(f"[bench] varlen: {N} sequences, {sum(lengths)} tokens")
+    inp = wl.token_inputs(w["seed"], shape, sum(lengths))
+    stream = torch.cuda.current_stream()
+    st = PrefillSetup(kda, wl, shape, inp, lengths, [0] * N, interval, [0])
+    t = _time_calls(lambda: st.call(0, stream), steps, warmup, stream)
+    res = {"workload": f"varlen_ckpt: {N} sequences, {sum(lengths)} tokens (lengths log-uniform in [1K, 64K]), "
+                       f"H={shape.H}, dk=dv={shape.dk}, bf16, checkpoints every {interval} and at ends "
+                       f"({st.nck} checkpoints)",
+           "straight": prefill_rates(st.T, shape.H, shape.dk, shape.dv, t)}
+    # resume batch: each sequence with an interval checkpoint restarts from a seeded one
+    rng = np.random.default_rng([w["seed"], wl.TID["resume"], 0])
+    rem, pos, src, idx = [], [], [], []
+    cu = wl.cu_seqlens(lengths)
+    for n, L in enumerate(lengths):
+        n_int = kda.kda_num_checkpoints(0, L, interval) - 1
+        if n_int <= 0:
+            continue
+        j = int(rng.integers(0, n_int))
+        p = (j + 1) * interval
+        rem.append(L - p)
+        pos.append(p)
+        src.append(int(st.base_h[n]) + j)
+        idx.append(np.arange(cu[n] + p, cu[n] + L))
+    idx = np.concatenate(idx)
+    sub = wl.Inputs(shape, inp.q[idx], inp.k[idx], inp.v[idx], inp.z[idx], inp.g[idx], inp.beta[idx],
+                    inp.conv_w, inp.norm_w)
+    rs = PrefillSetup(kda, wl, shape, sub, rem, pos, interval, [0])
+    n_r = len(rem)
+    rs.init = torch.arange(n_r, dtype=torch.int32).cuda()
+    kda.kda_resume(st.cfg, st.ckS, st.ckX, torch.tensor(src, dtype=torch.int32).cuda(), rs.S, rs.X, rs.init,
+                   stream=stream)
+    # every pass restarts from the resumed slots (the final slots are distinct)
+    t_r = _time_calls(lambda: rs.call(0, stream), steps, warmup, stream)
+    res["resume"] = dict(prefill_rates(rs.T, shape.H, shape.dk, shape.dv, t_r),
+                         sequences=n_r, tokens=int(rs.T))
+    res["value"] = res["straight"]["value"]
+    return res
+
+
+def bench_long(steps, warmup):
+    """The 1M-token sequence, unsplit and split at its checkpoints, then the
+    256-sequence decode fanned out from its end state."""
+    import torch
+    import linear_attention_recurrence_decode_amd as kda
+    import workloads as wl
+
+    w = wl.WORKLOADS["long_1m"]
+    shape, L, interval = w["shape"], w["lengths"][0], w["interval"]
+    log(f"[bench] long context: {L} tokens, H={shape.H}")
+    inp = wl.token_inputs(w["seed"], shape, L)
+    stream = torch.cuda.current_stream()
+    split = kda.KDA_PREFILL_SPLIT
+    st = PrefillSetup(kda, wl, shape, inp, [L], [0], interval, [0, split])
+    res = {"workload": f"long_1m: 1 sequence of {L} tokens, H={shape.H}, dk=dv={shape.dk}, bf16, checkpoints "
+                       f"every {interval}"}
+    t_u = _time_calls(lambda: st.call(0, stream), max(1, steps // 4), min(warmup, 1), stream)
+    res["unsplit"] = prefill_rates(L, shape.H, shape.dk, shape.dv, t_u)
+    t_s = _time_calls(lambda: st.call(split, stream), steps, warmup, stream)
+    res["split"] = prefill_rates(L, shape.H, shape.dk, shape.dv, t_s)
+    res["value"] = res["split"]["value"]
+    # decode fan-out: 256 slots from the end state, 512 steps
+    B, nsteps = w["decode_B"], w["decode_steps"]
+    cfg = st.cfg
+    Sp = torch.zeros((B, shape.H, shape.dk, shape.dv), device="cuda")
+    Xp = torch.zeros((B, shape.H, shape.C, 3), dtype=cfg.torch_act, device="cuda")
+    slot = torch.arange(B, dtype=torch.int32).cuda()
+    kda.kda_resume(cfg, st.ckS, st.ckX, torch.full((B,), st.nck - 1, dtype=torch.int32).cuda(), Sp, Xp, slot,
+                   stream=stream)
+    dinp = wl.token_inputs(w["seed"] + 100, shape, B * nsteps)
+    r = lambda a: torch.from_numpy(a.reshape((nsteps, B) + a.shape[1:]))
+    q, k, v, z = (r(a).to(cfg.torch_act).cuda() for a in (dinp.q, dinp.k, dinp.v, dinp.z))
+    g, beta = r(dinp.g).cuda(), r(dinp.beta).cuda()
+    dout = torch.empty((nsteps, B, shape.H, shape.dv), dtype=cfg.torch_act, device="cuda")
+
+    def decode_pass():
+        for s2 in range(nsteps):
+            kda.kda_decode_step(cfg, q[s2], k[s2], v[s2], z[s2], g[s2], beta[s2], st.conv_w, st.norm_w, Sp, Xp,
+                                slot, dout[s2], stream=stream)
+
+    t_d = _time_calls(decode_pass, max(1, steps // 4), 1, stream)
+    nbytes = decode_bytes_per_launch(B, shape.H, shape.dk, shape.dv)
+    res["decode"] = {"value": B * nsteps / t_d, "unit": "tok/s", "ms_per_pass": t_d * 1e3,
+                     "hbm_frac": nbytes * nsteps / t_d / HBM_PEAK, "B": B, "steps": nsteps}
+    return res
 
 
 def cpu_baseline(sample_steps: int):
@@ -239,6 +403,8 @@ def main():
     ap.add_argument("--cpu-sample-steps", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--workload", choices=["decode_b64", "varlen_ckpt", "long_1m"], default="decode_b64",
+                    help="decode_b64 (default): the headline line; the others report a larger prefill workload")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a kernel of "
                          "known traffic, used to scale memory counters)")
@@ -258,6 +424,16 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.workload != "decode_b64":
+        res = bench_varlen(args.steps, args.warmup) if args.workload == "varlen_ckpt" else \
+            bench_long(args.steps, args.warmup)
+        line = {"metric": "KDA prefill tok/s (" + args.workload + ")", "value": res["value"], "unit": "tok/s",
+                "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+                "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+                "config": {"workload": res.pop("workload"), "parallelism": "single GPU"}}
+        line.update({k: v for k, v in res.items() if k != "value"})
+        print(json.dumps(line), flush=True)
+        return
     res = bench_decode(args)
     line = {
         "metric": METRIC,

@@ -67,6 +67,11 @@ typedef enum {
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 
+/* Flags of kda_prefill_varlen (bitwise or). */
+typedef enum {
+    KDA_PREFILL_SPLIT = 1     /* cut sequences into segments at checkpoint positions */
+} kda_prefill_flags;
+
 typedef struct {
     int32_t num_heads;   /* H: heads handled by this call (one GPU's share) */
     int32_t head_k;      /* dk */
@@ -132,6 +137,24 @@ kda_status kda_decode_step(const kda_config* cfg, int32_t B,
  * out: [total_tokens][H][dv] activation dtype.
  * workspace: device scratch of at least kda_prefill_workspace_bytes(...)
  *   bytes; its contents on entry do not matter.
+ * flags: 0 or KDA_PREFILL_SPLIT (needs ckpt_interval > 0).  Without it each
+ *   (sequence, head) chain runs through its chunks in order in one workgroup,
+ *   so a batch of few long sequences occupies few compute units.  With it,
+ *   every sequence is cut at its interval checkpoint positions into segments
+ *   that run in parallel.  The update is affine in the state (each token
+ *   multiplies it by (I - b k k^T) Diag(exp g) and adds b k v^T), so a
+ *   segment maps its initial state S to F S + G, where F is the state that
+ *   the identity reaches with v = 0 and G the state that zero reaches; the
+ *   segments' F and G are computed in parallel, a scan forms every segment's
+ *   initial state in fp32, and the segments then run again from those states
+ *   to produce their outputs.  The scan results are the interval checkpoints.
+ *   About three times the arithmetic of the unsplit run, for parallelism over
+ *   segments as well as sequences and heads; worth it when sequences x heads
+ *   is well below the number of compute units [vLLM blog, introduction:
+ *   contexts of up to one million tokens].  Results agree with an unsplit run
+ *   to fp32 rounding.  A run resumed from one of its interval checkpoints with
+ *   the same interval and flags reproduces it bit for bit; a continuation
+ *   from a sequence end that is not an interval position agrees to rounding.
  * Precondition on the gate: within any 32 consecutive tokens of a chunk the
  *   accumulated log-decay of every channel stays above -80 (for instance
  *   g >= -2.5 everywhere); the intra-chunk decay factors are formed relative
@@ -145,7 +168,7 @@ kda_status kda_prefill_varlen(const kda_config* cfg, int32_t num_seqs, int64_t t
                               float* state_pool, void* conv_pool, int32_t num_slots,
                               const int32_t* init_slot, const int32_t* final_slot,
                               int32_t ckpt_interval, float* ckpt_state, void* ckpt_conv,
-                              int32_t num_ckpt_slots, const int32_t* ckpt_base,
+                              int32_t num_ckpt_slots, const int32_t* ckpt_base, int32_t flags,
                               void* out, void* workspace, size_t workspace_bytes,
                               void* stream);
 
@@ -178,9 +201,12 @@ kda_status kda_resume(const kda_config* cfg, int32_t n,
                       float* state_pool, void* conv_pool, int32_t num_slots,
                       const int32_t* dst_slot, void* stream);
 
-/* Workspace bytes kda_prefill_varlen needs for these sizes (0 on a config
- * error; kda_last_error() then says why). */
-size_t kda_prefill_workspace_bytes(const kda_config* cfg, int32_t num_seqs, int64_t total_tokens);
+/* Workspace bytes kda_prefill_varlen needs for these sizes, checkpoint
+ * interval and flags (0 on an error; kda_last_error() then says why).  With
+ * KDA_PREFILL_SPLIT it holds, per possible segment (at most 2 num_seqs +
+ * total_tokens / ckpt_interval) and head, three dk x dv fp32 matrices. */
+size_t kda_prefill_workspace_bytes(const kda_config* cfg, int32_t num_seqs, int64_t total_tokens,
+                                   int32_t ckpt_interval, int32_t flags);
 
 /* Number of checkpoints kda_prefill_varlen writes for one sequence: the
  * multiples of interval strictly inside (start, start+len) plus its end; 0

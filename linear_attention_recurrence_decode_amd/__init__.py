@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
 KDA_F32, KDA_BF16 = 0, 1
+KDA_PREFILL_SPLIT = 1
 
 # every symbol include/kda.h declares
 EXPORTS = (
@@ -87,10 +88,10 @@ def lib():
     CP = ctypes.POINTER(_Config)
     L.kda_decode_step.argtypes = [CP, I32] + [P] * 8 + [P, P, I32, P, P, P]
     L.kda_prefill_varlen.argtypes = ([CP, I32, I64, P, P] + [P] * 8 + [P, P, I32, P, P, I32, P, P, I32, P,
-                                     P, P, ctypes.c_size_t, P])
+                                     I32, P, P, ctypes.c_size_t, P])
     L.kda_state_checkpoint.argtypes = [CP, I32, P, P, I32, P, P, P, I32, P, P]
     L.kda_resume.argtypes = [CP, I32, P, P, I32, P, P, P, I32, P, P]
-    L.kda_prefill_workspace_bytes.argtypes = [CP, I32, I64]
+    L.kda_prefill_workspace_bytes.argtypes = [CP, I32, I64, I32, I32]
     L.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
     L.kda_num_checkpoints.argtypes = [I64, I64, I32]
     L.kda_num_checkpoints.restype = I64
@@ -139,8 +140,10 @@ def kda_num_checkpoints(start: int, length: int, interval: int) -> int:
     return int(lib().kda_num_checkpoints(int(start), int(length), int(interval)))
 
 
-def kda_prefill_workspace_bytes(cfg: Config, num_seqs: int, total_tokens: int) -> int:
-    n = int(lib().kda_prefill_workspace_bytes(ctypes.byref(cfg.c()), int(num_seqs), int(total_tokens)))
+def kda_prefill_workspace_bytes(cfg: Config, num_seqs: int, total_tokens: int, ckpt_interval: int = 0,
+                                flags: int = 0) -> int:
+    n = int(lib().kda_prefill_workspace_bytes(ctypes.byref(cfg.c()), int(num_seqs), int(total_tokens),
+                                              int(ckpt_interval), int(flags)))
     if n == 0 and last_error():
         raise KdaError(KDA_ERR_INVALID_ARG, last_error())
     return n
@@ -168,7 +171,7 @@ def kda_decode_step(cfg: Config, q, k, v, z, g, beta, conv_w, norm_w, state_pool
 def kda_prefill_varlen(cfg: Config, cu_seqlens, q, k, v, z, g, beta, conv_w, norm_w,
                        state_pool, conv_pool, init_slot, final_slot, out, workspace,
                        start_pos=None, ckpt_interval: int = 0, ckpt_state=None, ckpt_conv=None,
-                       ckpt_base=None, stream=None):
+                       ckpt_base=None, flags: int = 0, stream=None):
     """Chunked varlen prefill (see include/kda.h)."""
     N = cu_seqlens.numel() - 1
     T = q.shape[0]
@@ -198,7 +201,7 @@ def kda_prefill_varlen(cfg: Config, cu_seqlens, q, k, v, z, g, beta, conv_w, nor
                                     _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(g), _ptr(beta),
                                     _ptr(conv_w), _ptr(norm_w), _ptr(state_pool), _ptr(conv_pool), S,
                                     _ptr(init_slot), _ptr(final_slot), int(ckpt_interval),
-                                    _ptr(ckpt_state), _ptr(ckpt_conv), nck, _ptr(ckpt_base),
+                                    _ptr(ckpt_state), _ptr(ckpt_conv), nck, _ptr(ckpt_base), int(flags),
                                     _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
     return out
 

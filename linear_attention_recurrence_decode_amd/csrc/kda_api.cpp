@@ -171,13 +171,38 @@ kda_status kda_decode_step(const kda_config* cfg, int32_t B, const void* q, cons
                       "decode launch");
 }
 
-size_t kda_prefill_workspace_bytes(const kda_config* cfg, int32_t num_seqs, int64_t total_tokens) {
+namespace {
+
+kda_status check_prefill_mode(int32_t ckpt_interval, int32_t flags) {
+    if (ckpt_interval < 0 || ckpt_interval % 64 != 0)
+        return fail(KDA_ERR_INVALID_ARG, "ckpt_interval must be 0 or a positive multiple of 64 (got %d)",
+                    ckpt_interval);
+    if (flags & ~KDA_PREFILL_SPLIT) return fail(KDA_ERR_INVALID_ARG, "unknown prefill flags 0x%x", flags);
+    if ((flags & KDA_PREFILL_SPLIT) && ckpt_interval == 0)
+        return fail(KDA_ERR_INVALID_ARG, "KDA_PREFILL_SPLIT needs ckpt_interval > 0");
+    return KDA_OK;
+}
+
+kda::PrefillWorkspace workspace_layout(const kda_config* cfg, int32_t num_seqs, int64_t total_tokens,
+                                       int32_t ckpt_interval, int32_t flags) {
+    return kda::prefill_workspace(num_seqs, cfg->num_heads, total_tokens, cfg->head_k, cfg->head_v,
+                                  cfg->act_dtype == KDA_BF16 ? 2 : 4, ckpt_interval,
+                                  (flags & KDA_PREFILL_SPLIT) != 0);
+}
+
+}  // namespace
+
+size_t kda_prefill_workspace_bytes(const kda_config* cfg, int32_t num_seqs, int64_t total_tokens,
+                                   int32_t ckpt_interval, int32_t flags) {
     if (check_cfg(cfg) != KDA_OK) return 0;
     if (num_seqs < 0 || total_tokens < 0) {
         fail(KDA_ERR_INVALID_ARG, "num_seqs and total_tokens must be >= 0");
         return 0;
     }
-    return kda::prefill_workspace_bytes(num_seqs, cfg->num_heads, total_tokens, cfg->head_k, cfg->head_v);
+    if (check_prefill_mode(ckpt_interval, flags) != KDA_OK) return 0;
+    const kda::PrefillWorkspace w = workspace_layout(cfg, num_seqs, total_tokens, ckpt_interval, flags);
+    if (w.bytes == 0 && num_seqs > 0) fail(KDA_ERR_INVALID_ARG, "too many sequences or segments");
+    return w.bytes;
 }
 
 kda_status kda_prefill_varlen(const kda_config* cfg, int32_t num_seqs, int64_t total_tokens,
@@ -186,17 +211,15 @@ kda_status kda_prefill_varlen(const kda_config* cfg, int32_t num_seqs, int64_t t
                               const float* conv_w, const float* norm_w, float* state_pool, void* conv_pool,
                               int32_t num_slots, const int32_t* init_slot, const int32_t* final_slot,
                               int32_t ckpt_interval, float* ckpt_state, void* ckpt_conv,
-                              int32_t num_ckpt_slots, const int32_t* ckpt_base, void* out, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+                              int32_t num_ckpt_slots, const int32_t* ckpt_base, int32_t flags, void* out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
     KDA_TRY(check_cfg(cfg));
     if (num_seqs < 0) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
     if (total_tokens < 0 || total_tokens > 0x7fffffffLL)
         return fail(KDA_ERR_INVALID_ARG, "total_tokens must be in [0, 2^31) (got %lld)",
                     static_cast<long long>(total_tokens));
     if (num_slots < 1) return fail(KDA_ERR_INVALID_ARG, "num_slots must be >= 1 (got %d)", num_slots);
-    if (ckpt_interval < 0 || ckpt_interval % 64 != 0)
-        return fail(KDA_ERR_INVALID_ARG, "ckpt_interval must be 0 or a positive multiple of 64 (got %d)",
-                    ckpt_interval);
+    KDA_TRY(check_prefill_mode(ckpt_interval, flags));
     if (!kda::prefill_supported(cfg->head_k, cfg->head_v, cfg->act_dtype))
         return fail(KDA_ERR_UNSUPPORTED, "prefill does not support dk=%d dv=%d act_dtype=%d", cfg->head_k,
                     cfg->head_v, cfg->act_dtype);
@@ -225,8 +248,12 @@ kda_status kda_prefill_varlen(const kda_config* cfg, int32_t num_seqs, int64_t t
         KDA_TRY(need_vec(ckpt_conv, "ckpt_conv"));
         KDA_TRY(need_idx(ckpt_base, 4, "ckpt_base"));
     }
-    const size_t need = kda::prefill_workspace_bytes(num_seqs, cfg->num_heads, total_tokens, cfg->head_k,
-                                                     cfg->head_v);
+    const kda::PrefillWorkspace wl = workspace_layout(cfg, num_seqs, total_tokens, ckpt_interval, flags);
+    const size_t need = wl.bytes;
+    if (need == 0) return fail(KDA_ERR_INVALID_ARG, "too many sequences or segments");
+    const bool split = (flags & KDA_PREFILL_SPLIT) != 0;
+    if (split && static_cast<int64_t>(wl.max_items) * 2 * cfg->num_heads > 0xffffffffLL)
+        return fail(KDA_ERR_INVALID_ARG, "too many segments x heads for one launch");
     if (workspace_bytes < need)
         return fail(KDA_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
     if (need > 0) KDA_TRY(need_vec(workspace, "workspace"));
@@ -256,9 +283,17 @@ kda_status kda_prefill_varlen(const kda_config* cfg, int32_t num_seqs, int64_t t
     p.num_ckpt_slots = ckpt_interval > 0 ? num_ckpt_slots : 0;
     p.ckpt_base = ckpt_interval > 0 ? ckpt_base : nullptr;
     p.out = out;
-    p.work = static_cast<kda::SeqWork*>(workspace);
+    char* ws = static_cast<char*>(workspace);
+    p.work = reinterpret_cast<kda::SeqWork*>(ws + wl.items);
     p.l2_eps = cfg->l2_eps;
     p.rms_eps = cfg->rms_eps;
+    p.split = split ? 1 : 0;
+    p.max_items = wl.max_items;
+    p.seq_items = split ? reinterpret_cast<int2*>(ws + wl.seq_items) : nullptr;
+    p.seg_F = split ? reinterpret_cast<float*>(ws + wl.seg_F) : nullptr;
+    p.seg_G = split ? reinterpret_cast<float*>(ws + wl.seg_G) : nullptr;
+    p.seg_S = split ? reinterpret_cast<float*>(ws + wl.seg_S) : nullptr;
+    p.seq_x0 = split ? static_cast<void*>(ws + wl.seq_x0) : nullptr;
     return hip_status(kda::launch_prefill(cfg->head_k, cfg->head_v, cfg->act_dtype, p,
                                           static_cast<hipStream_t>(stream)),
                       "prefill launch");

@@ -39,14 +39,17 @@ struct CopyParams {
     const int32_t* dst_idx;
 };
 
-// Per-sequence work item of the prefill, built on the device from cu_seqlens
-// and start_pos (longest sequences first).
+// Work item of the prefill: a whole sequence, or (when sequences are split at
+// checkpoint positions) one segment of it.  Built on the device from
+// cu_seqlens and start_pos.
 struct SeqWork {
     int32_t seq;        // sequence index
-    int32_t tok0;       // first packed token
-    int32_t len;        // tokens
-    int32_t pad;
-    int64_t start;      // absolute position of the first token
+    int32_t tok0;       // first packed token of the item
+    int32_t len;        // tokens (-1: malformed sequence bounds, skipped)
+    int32_t ctx0;       // first packed token of the sequence (conv context before it: initial conv state)
+    int64_t start;      // absolute position of the item's first token
+    int32_t part;       // index of the item within its sequence (0 when not split)
+    int32_t last;       // 1 when the item ends its sequence
 };
 
 struct PrefillParams {
@@ -73,8 +76,17 @@ struct PrefillParams {
     int32_t num_ckpt_slots;
     const int32_t* ckpt_base;
     void* out;
-    SeqWork* work;      // [N] in the workspace
+    SeqWork* work;      // work items, in the workspace
     float l2_eps, rms_eps;
+    // Sequences split at checkpoint positions (segments run in parallel and
+    // are joined by an affine scan of their transitions); all in the workspace.
+    int32_t split;      // 0 or 1
+    int32_t max_items;  // work items allocated
+    int2* seq_items;    // [N] first item and item count per sequence
+    float* seg_F;       // [max_items][H][dk][dk] segment transition matrices
+    float* seg_G;       // [max_items][H][dk][dv] segment end states from a zero state
+    float* seg_S;       // [max_items][H][dk][dv] segment initial states
+    void* seq_x0;       // [N][H][2dk+dv][3] initial conv states (activation dtype)
 };
 
 // Each launcher returns hipSuccess or the launch error.
@@ -82,6 +94,13 @@ hipError_t launch_decode(int dk, int dv, int act, const DecodeParams& p, hipStre
 hipError_t launch_copy(const CopyParams& p, hipStream_t s);
 hipError_t launch_prefill(int dk, int dv, int act, const PrefillParams& p, hipStream_t s);
 bool prefill_supported(int dk, int dv, int act);
-size_t prefill_workspace_bytes(int32_t N, int32_t H, int64_t T, int dk, int dv);
+
+// Workspace layout of the prefill (offsets in bytes; total = bytes).
+struct PrefillWorkspace {
+    int32_t max_items;
+    size_t items, seq_items, seg_F, seg_G, seg_S, seq_x0, bytes;
+};
+PrefillWorkspace prefill_workspace(int32_t N, int32_t H, int64_t T, int dk, int dv, int act_bytes,
+                                   int32_t ckpt_interval, bool split);
 
 }  // namespace kda

@@ -352,7 +352,11 @@ struct PrefillShape {
     static_assert(NT / (2 * DK) == 2 && NT / DK == 4, "thread mappings assume nt = 4 * dk");
 };
 
-template <int D, typename ACT>
+// OUT: outputs, checkpoints and final states of whole sequences or segments.
+// !OUT (segment transitions): blocks [0, items*H) give each segment's end state
+// from a zero state (G), blocks [items*H, 2*items*H) its transition matrix
+// (F: the state propagated from the identity with v = 0).
+template <int D, typename ACT, bool OUT>
 __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
     using Sh = PrefillShape<D, ACT>;
     constexpr int DK = Sh::DK, DV = Sh::DV, NW = Sh::NW, NT = Sh::NT, C = Sh::C;
@@ -397,21 +401,37 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
     const int g4 = lane >> 4, l16 = lane & 15;
     const int H = p.H;
     const int h = blockIdx.x % H;
-    const SeqWork wk = p.work[blockIdx.x / H];
-    if (wk.len < 0) return;                    // malformed sequence bounds: nothing is touched
+    int item = blockIdx.x / H;
+    bool trans = false;
+    if constexpr (!OUT) {
+        trans = item >= p.max_items;
+        if (trans) item -= p.max_items;
+    }
+    const SeqWork wk = p.work[item];
+    if (wk.len < 0) return;                    // malformed sequence bounds or unused item: nothing is touched
+    if constexpr (!OUT) {
+        if (wk.last) return;                   // the last segment of a sequence needs no transition
+    }
     const int seq = wk.seq;
     const int64_t tok0 = wk.tok0;
+    const int64_t ctx0 = wk.ctx0;
     const int L = wk.len;
     const int64_t start = wk.start;
     const int init = p.init_slot ? p.init_slot[seq] : -1;
-    const int fin = p.final_slot ? p.final_slot[seq] : -1;
+    const int fin = (p.final_slot && wk.last) ? p.final_slot[seq] : -1;   // only the last item writes it
     const int jcol = 16 * wave + l16;          // this lane's state / output column
+    // Segments of a split sequence take their initial state and conv state from
+    // the workspace, filled before this launch: a final slot that is also the
+    // initial slot is then only written after every read of it.
+    const bool seg_in = OUT && p.split && !(wk.part == 0 && wk.last);
 
     // invalid initial slot or position: NaN outputs, no state written
     if (init < -1 || init >= p.num_slots || start < 0) {
-        for (int64_t e = tid; e < static_cast<int64_t>(L) * DV; e += NT) {
-            const int64_t t = tok0 + e / DV;
-            A::st(static_cast<ACT*>(p.out) + (t * H + h) * DV + e % DV, nan_f32());
+        if constexpr (OUT) {
+            for (int64_t e = tid; e < static_cast<int64_t>(L) * DV; e += NT) {
+                const int64_t t = tok0 + e / DV;
+                A::st(static_cast<ACT*>(p.out) + (t * H + h) * DV + e % DV, nan_f32());
+            }
         }
         return;
     }
@@ -420,21 +440,34 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
     f32x4 S[IB];
     {
         const uint32_t sv = static_cast<uint32_t>((4 * g4 * DV + jcol) * 4);
-        if (init >= 0) {
-            const auto rs = make_rsrc(p.state + (static_cast<int64_t>(init) * H + h) * DK * DV, DK * DV * 4);
+        const float* s0 = nullptr;
+        if constexpr (OUT) {
+            if (seg_in) s0 = p.seg_S + (static_cast<int64_t>(item) * H + h) * DK * DV;
+            else if (init >= 0) s0 = p.state + (static_cast<int64_t>(init) * H + h) * DK * DV;
+        }
+        if (s0) {
+            const auto rs = make_rsrc(s0, DK * DV * 4);
 #pragma unroll
             for (int ib = 0; ib < IB; ib++)
 #pragma unroll
                 for (int e = 0; e < 4; e++) S[ib][e] = buf_ldf(rs, sv, (16 * ib + e) * DV * 4);
         } else {
 #pragma unroll
-            for (int ib = 0; ib < IB; ib++) S[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int ib = 0; ib < IB; ib++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) S[ib][e] = (trans && 16 * ib + 4 * g4 + e == jcol) ? 1.f : 0.f;
         }
-        const ACT* x0 = init >= 0 ? static_cast<const ACT*>(p.conv) + (static_cast<int64_t>(init) * H + h) * C * 3
-                                  : nullptr;
+        const int64_t hx = (static_cast<int64_t>(seq) * H + h) * C * 3;
+        const ACT* x0 = seg_in ? static_cast<const ACT*>(p.seq_x0) + hx
+                               : (init >= 0 ? static_cast<const ACT*>(p.conv) + (static_cast<int64_t>(init) * H + h) * C * 3
+                                            : nullptr);
+        // the zero-start pass of a sequence's first segment keeps its initial
+        // conv state for the segments' output pass
+        ACT* keep = (!OUT && !trans && wk.part == 0) ? static_cast<ACT*>(p.seq_x0) + hx : nullptr;
         for (int e = tid; e < C * 3; e += NT) {
             if (x0) x0_s[e] = x0[e];
             else A::st(&x0_s[e], 0.f);
+            if (keep) keep[e] = x0_s[e];
         }
     }
     const int cqk = tid % (2 * DK);                              // q/k conv channel of this thread
@@ -450,13 +483,13 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
 
     // raw input value of channel c at packed token tok (conv left context)
     auto raw_at = [&](int64_t tok, int c) -> ACT {
-        if (tok >= tok0) {
+        if (tok >= ctx0) {
             const ACT* src = c < DK ? qin + (tok * H + h) * DK + c
                                     : (c < 2 * DK ? kin + (tok * H + h) * DK + (c - DK)
                                                   : vin + (tok * H + h) * DV + (c - 2 * DK));
             return *src;
         }
-        return x0_s[c * 3 + 3 - static_cast<int>(tok0 - tok)];
+        return x0_s[c * 3 + 3 - static_cast<int>(ctx0 - tok)];
     };
     // conv state after the tokens before packed index tend: the last 3 raw inputs
     auto write_conv_state = [&](ACT* dst, int64_t tend) {
@@ -466,8 +499,26 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
         }
     };
     int64_t pos = start;
-    int done = 0, ck = 0;
-    const int ck_base = (p.ckpt_interval > 0) ? p.ckpt_base[seq] : 0;
+    // checkpoint counter: a segment that ends at a checkpoint position leaves
+    // that checkpoint to the next segment (which starts from the scanned
+    // state), so a segment that is not the last of its sequence writes none
+    int done = 0, ck = wk.last ? wk.part : -(1 << 30);
+    // (clamped so that adding a checkpoint index cannot overflow; no slot lies
+    // outside the clamp range)
+    const int ck_base = (OUT && p.ckpt_interval > 0) ? min(max(p.ckpt_base[seq], -(1 << 30)), 1 << 30) : 0;
+    if constexpr (OUT) {
+        // a segment after the first starts at a checkpoint position: its
+        // initial state (from the scan of the segment transitions) is that
+        // checkpoint
+        if (p.ckpt_interval > 0 && wk.part > 0) {
+            const int slot = ck_base + wk.part - 1;
+            if (slot >= 0 && slot < p.num_ckpt_slots) {
+                const int64_t sh = static_cast<int64_t>(slot) * H + h;
+                store_state_strip<IB, DV>(p.ckpt_state + sh * DK * DV, S, g4, jcol, DK);
+                write_conv_state(static_cast<ACT*>(p.ckpt_conv) + sh * C * 3, tok0);
+            }
+        }
+    }
 
     // ---------------- A1 of the first chunk (later chunks are staged while the
     // previous chunk finishes: their loads are issued after its state phase)
@@ -476,7 +527,7 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
     int64_t tc0 = tok0;
     if (L > 0) {
         const int tp = opq(tid);
-        stage_issue<ACT, DK, DV, NT>(stg, p, x0_s, tok0, tc0, n, H, h, tp);
+        stage_issue<ACT, DK, DV, NT>(stg, p, x0_s, ctx0, tc0, n, H, h, tp);
         stage_commit<ACT, DK, DV, NT>(stg, raw, beta_s, tp);
     }
     __syncthreads();
@@ -521,6 +572,14 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
                     y = fmaf(wv.z, x[e + 2], y);
                     y = fmaf(wv.w, x[e + 3], y);
                     vh[tb][e] = (rb + e) < n ? silu(y) : 0.f;
+                }
+            }
+            if constexpr (!OUT) {
+                if (trans) {
+#pragma unroll
+                    for (int tb = 0; tb < 4; tb++)
+#pragma unroll
+                        for (int e = 0; e < 4; e++) vh[tb][e] = 0.f;
                 }
             }
         }
@@ -581,7 +640,7 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
             for (int r = 0; r < 16; r++) {
                 const int idx = (16 * qqp + r) * PS + cgp;
                 st_split(kp_h, kp_l, idx, kp[r]);
-                st_split(qp_h, qp_l, idx, qp[r]);
+                if constexpr (OUT) st_split(qp_h, qp_l, idx, qp[r]);
                 st_split(km_h, km_l, idx, km[r]);
             }
         }
@@ -596,11 +655,13 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
             for (int job = wv5; job < 16; job += NW) {
                 const int a = job >> 2, b = job & 3;
                 if (a < b) {
+                    if constexpr (OUT) {
 #pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        const int idx = (16 * a + 4 * gg + e) * QS + 16 * b + lc;
-                        pp_h[idx] = 0;
-                        pp_l[idx] = 0;
+                        for (int e = 0; e < 4; e++) {
+                            const int idx = (16 * a + 4 * gg + e) * QS + 16 * b + lc;
+                            pp_h[idx] = 0;
+                            pp_l[idx] = 0;
+                        }
                     }
                     continue;
                 }
@@ -610,12 +671,12 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
                     const int offa = (16 * a + lc) * PS + 32 * ks + 8 * gg;
                     const Frag fb = ld_nat(km_h, km_l, (16 * b + lc) * PS + 32 * ks + 8 * gg);
                     am = mfma3(ld_nat(kp_h, kp_l, offa), fb, am);
-                    ap = mfma3(ld_nat(qp_h, qp_l, offa), fb, ap);
+                    if constexpr (OUT) ap = mfma3(ld_nat(qp_h, qp_l, offa), fb, ap);
                 }
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int t = 16 * a + 4 * gg + e, s2 = 16 * b + lc;
-                    st_split(pp_h, pp_l, t * QS + s2, t >= s2 ? ap[e] : 0.f);
+                    if constexpr (OUT) st_split(pp_h, pp_l, t * QS + s2, t >= s2 ? ap[e] : 0.f);
                     if (a > b) st_split(lp_h, lp_l, t * QS + s2, beta_s[t] * am[e]);
                     else ld_s[a][4 * gg + e][lc] = t > s2 ? beta_s[t] * am[e] : 0.f;
                 }
@@ -661,7 +722,7 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
         {
             const int tp = opq(tid);
             const int ln = tp & 63, gg = ln >> 4, lc = ln & 15;
-            {
+            if constexpr (OUT) {
                 // rows past the chunk fall outside the resource (range-checked
                 // per-lane offsets) and read as zero
                 const auto rz = make_rsrc(zin + (tc0 * H + h) * DV, nb);
@@ -693,6 +754,7 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
                 for (int tb = 0; tb < 4; tb++) {
                     const int off = (16 * tb + lc) * PS + 32 * ks + 4 * gg;
                     accx[tb] = mfma3(ld_perm(kp_h, kp_l, off), fs, accx[tb]);
+                    if constexpr (!OUT) continue;
                     if constexpr (kOutHi) accr[tb] = mfma2(ld_perm_hi(qp_h, off), fs, accr[tb]);
                     else accr[tb] = mfma3(ld_perm(qp_h, qp_l, off), fs, accr[tb]);
                 }
@@ -723,6 +785,7 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
             // O = Q_g S + P U (with bf16 outputs, Q+ and P are rounded once to bf16)
 #pragma unroll
             for (int tb = 0; tb < 4; tb++) {
+                if constexpr (!OUT) break;
                 const int row = (16 * tb + lc) * QS + 4 * gg;
                 if constexpr (kOutHi) {
                     accr[tb] = mfma2(ld_perm_hi(pp_h, row), fu0, accr[tb]);
@@ -746,13 +809,15 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
                 }
             }
             // row sums of O^2 over this wave's 16 columns
+            if constexpr (OUT) {
 #pragma unroll
-            for (int tb = 0; tb < 4; tb++)
+                for (int tb = 0; tb < 4; tb++)
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const float s2 = dpp_group_sum<16>(accr[tb][e] * accr[tb][e]);
-                    if (lc == 0) part_s[tp >> 6][16 * tb + 4 * gg + e] = s2;
-                }
+                    for (int e = 0; e < 4; e++) {
+                        const float s2 = dpp_group_sum<16>(accr[tb][e] * accr[tb][e]);
+                        if (lc == 0) part_s[tp >> 6][16 * tb + 4 * gg + e] = s2;
+                    }
+            }
         }
         __syncthreads();
 
@@ -760,10 +825,11 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
         const int done_next = done + n;
         const int64_t pos_next = pos + n;
         const int n_next = done_next < L ? min(L - done_next, CH - static_cast<int>(pos_next % CH)) : 0;
-        if (n_next > 0) stage_issue<ACT, DK, DV, NT>(stg, p, x0_s, tok0, tok0 + done_next, n_next, H, h, opq(tid));
+        if (n_next > 0) stage_issue<ACT, DK, DV, NT>(stg, p, x0_s, ctx0, tok0 + done_next, n_next, H, h, opq(tid));
         else stage_clear(stg);
 
         // ---------------- epilogue: gated RMSNorm over dv, then the outputs
+        if constexpr (OUT) {
         if (tid < CH) {
             float tot = 0.f;
 #pragma unroll
@@ -788,13 +854,14 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
                                         accr[tb][e] * rinv * nwj * sigmoid(zr[tb][e]));
                 }
         }
+        }
 
         // the raw-row region and beta are free: every wave is past its state phase
         if (n_next > 0) stage_commit<ACT, DK, DV, NT>(stg, raw, beta_s, opq(tid));
         done = done_next;
         pos = pos_next;
         // ---------------- checkpoints: interval boundaries inside, and the end
-        if (p.ckpt_interval > 0 && (pos % p.ckpt_interval == 0 || done == L)) {
+        if (OUT && p.ckpt_interval > 0 && (pos % p.ckpt_interval == 0 || done == L)) {
             const int slot = ck_base + ck;
             ck++;
             if (slot >= 0 && slot < p.num_ckpt_slots) {
@@ -808,10 +875,15 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
         __syncthreads();
     }
 
-    if (fin >= 0 && fin < p.num_slots) {
-        const int64_t sh = static_cast<int64_t>(fin) * H + h;
-        store_state_strip<IB, DV>(p.state + sh * DK * DV, S, g4, jcol, DK);
-        write_conv_state(static_cast<ACT*>(p.conv) + sh * C * 3, tok0 + L);
+    if constexpr (OUT) {
+        if (fin >= 0 && fin < p.num_slots) {
+            const int64_t sh = static_cast<int64_t>(fin) * H + h;
+            store_state_strip<IB, DV>(p.state + sh * DK * DV, S, g4, jcol, DK);
+            write_conv_state(static_cast<ACT*>(p.conv) + sh * C * 3, tok0 + L);
+        }
+    } else {
+        float* dst = (trans ? p.seg_F : p.seg_G) + (static_cast<int64_t>(item) * H + h) * DK * DV;
+        store_state_strip<IB, DV>(dst, S, g4, jcol, DK);
     }
 }
 
@@ -837,20 +909,183 @@ __global__ __launch_bounds__(1024) void prefill_meta_kernel(const int32_t* cu, c
         w.seq = i;
         w.tok0 = ok ? static_cast<int32_t>(a) : 0;
         w.len = li;
-        w.pad = 0;
+        w.ctx0 = w.tok0;
         w.start = sp ? sp[i] : 0;
+        w.part = 0;
+        w.last = 1;
         work[rank] = w;
+    }
+}
+
+// Segments of sequence i when sequences are cut at the checkpoint positions
+// strictly inside (start, start+len); 1 (no cut) for an empty or malformed
+// sequence, a negative start or an invalid initial slot.
+__device__ int32_t split_count(const PrefillParams& p, int i, int64_t* a_out, int64_t* len_out,
+                               int64_t* start_out, int64_t* first_out) {
+    const int64_t a = p.cu_seqlens[i], b = p.cu_seqlens[i + 1];
+    const bool ok = a >= 0 && b >= a && b <= p.T;
+    const int64_t start = p.start_pos ? p.start_pos[i] : 0;
+    const int init = p.init_slot ? p.init_slot[i] : -1;
+    *a_out = a;
+    *len_out = ok ? b - a : -1;
+    *start_out = start;
+    *first_out = 0;
+    if (!ok || b == a || start < 0 || init < -1 || init >= p.num_slots) return 1;
+    const int64_t I = p.ckpt_interval;
+    const int64_t first = (start / I + 1) * I;        // first checkpoint position after start
+    const int64_t endm1 = start + (b - a) - 1;          // cuts at positions <= start+len-1
+    *first_out = first;
+    return endm1 >= first ? static_cast<int32_t>((endm1 - first) / I + 2) : 1;
+}
+
+// One workgroup: items of every sequence in order, segments contiguous.
+// Should the segments not fit the allocated items (only possible when the
+// sequences overlap), no sequence is cut.
+__global__ __launch_bounds__(1024) void prefill_split_meta_kernel(PrefillParams p) {
+    __shared__ int32_t scan_s[1024];
+    __shared__ int64_t total_s;
+    const int tid = threadIdx.x;
+    if (tid == 0) total_s = 0;
+    __syncthreads();
+    for (int base = 0; base < p.N; base += 1024) {
+        const int i = base + tid;
+        int64_t a, len, start, first;
+        const int32_t ns = i < p.N ? split_count(p, i, &a, &len, &start, &first) : 0;
+        scan_s[tid] = ns;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {
+            const int32_t x = tid >= off ? scan_s[tid - off] : 0;
+            __syncthreads();
+            scan_s[tid] += x;
+            __syncthreads();
+        }
+        const int64_t first_item = total_s + scan_s[tid] - ns;
+        if (i < p.N) p.seq_items[i] = make_int2(static_cast<int>(min(first_item, static_cast<int64_t>(INT32_MAX))), ns);
+        __syncthreads();
+        if (tid == 1023) total_s += scan_s[1023];
+        __syncthreads();
+    }
+    const bool fits = total_s <= p.max_items;
+    // each thread reads back only the entries it wrote itself
+    for (int i = tid; i < p.N; i += 1024) {
+        int64_t a, len, start, first;
+        int32_t ns = split_count(p, i, &a, &len, &start, &first);
+        int32_t it0 = p.seq_items[i].x;
+        if (!fits) {
+            ns = 1;
+            it0 = i;
+            p.seq_items[i] = make_int2(i, 1);
+        }
+        for (int m = 0; m < ns; m++) {
+            const int64_t I = p.ckpt_interval;
+            const int64_t p0 = m == 0 ? start : first + (m - 1) * I;
+            const int64_t p1 = m == ns - 1 ? start + len : first + m * I;
+            SeqWork w;
+            w.seq = i;
+            w.tok0 = len >= 0 ? static_cast<int32_t>(a + (p0 - start)) : 0;
+            w.len = len >= 0 ? static_cast<int32_t>(p1 - p0) : -1;
+            w.ctx0 = len >= 0 ? static_cast<int32_t>(a) : 0;
+            w.start = p0;
+            w.part = m;
+            w.last = m == ns - 1;
+            p.work[it0 + m] = w;
+        }
+    }
+    const int64_t used = fits ? total_s : p.N;
+    for (int64_t j = used + tid; j < p.max_items; j += 1024) {
+        SeqWork w;
+        w.seq = 0;
+        w.tok0 = 0;
+        w.len = -1;
+        w.ctx0 = 0;
+        w.start = 0;
+        w.part = 0;
+        w.last = 1;
+        p.work[j] = w;
+    }
+}
+
+// Initial states of the segments of each split sequence, in order:
+// S_0 = the sequence's initial state, S_{m+1} = F_m S_m + G_m, in fp32 with
+// the products summed in channel order.  One workgroup per (sequence, head,
+// 16 state columns); the columns of S evolve independently.
+template <int D>
+__global__ __launch_bounds__(256) void segment_scan_kernel(PrefillParams p) {
+    constexpr int CB = 16, NCB = D / CB, RPT = D / 16, FS = D + 4;
+    __shared__ __attribute__((aligned(16))) float F_s[D * FS];
+    __shared__ float S_s[D * CB];
+    const int H = p.H;
+    const int cb = blockIdx.x % NCB;
+    const int h = (blockIdx.x / NCB) % H;
+    const int seq = blockIdx.x / (NCB * H);
+    const int2 si = p.seq_items[seq];
+    if (si.y <= 1) return;
+    const int tid = threadIdx.x, c = tid % CB, rg = tid / CB;
+    const int col = cb * CB + c;
+    const int init = p.init_slot ? p.init_slot[seq] : -1;   // in range: only such sequences are cut
+    float acc[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; r++)
+        acc[r] = init >= 0 ? p.state[(static_cast<int64_t>(init) * H + h) * D * D + (rg + 16 * r) * D + col] : 0.f;
+    for (int m = 0;; m++) {
+        const int64_t it = static_cast<int64_t>(si.x) + m;
+        float* dst = p.seg_S + (it * H + h) * D * D;
+#pragma unroll
+        for (int r = 0; r < RPT; r++) {
+            dst[(rg + 16 * r) * D + col] = acc[r];
+            S_s[(rg + 16 * r) * CB + c] = acc[r];
+        }
+        if (m == si.y - 1) break;
+        const float4* Fm = reinterpret_cast<const float4*>(p.seg_F + (it * H + h) * D * D);
+        const float* Gm = p.seg_G + (it * H + h) * D * D;
+        for (int e = tid; e < D * D / 4; e += 256) {
+            const int row = (4 * e) / D, k = (4 * e) % D;
+            *reinterpret_cast<float4*>(&F_s[row * FS + k]) = Fm[e];
+        }
+#pragma unroll
+        for (int r = 0; r < RPT; r++) acc[r] = Gm[(rg + 16 * r) * D + col];
+        __syncthreads();
+        for (int k = 0; k < D; k += 4) {
+            const float s0 = S_s[k * CB + c], s1 = S_s[(k + 1) * CB + c];
+            const float s2 = S_s[(k + 2) * CB + c], s3 = S_s[(k + 3) * CB + c];
+#pragma unroll
+            for (int r = 0; r < RPT; r++) {
+                const float4 f = *reinterpret_cast<const float4*>(&F_s[(rg + 16 * r) * FS + k]);
+                acc[r] = fmaf(f.x, s0, acc[r]);
+                acc[r] = fmaf(f.y, s1, acc[r]);
+                acc[r] = fmaf(f.z, s2, acc[r]);
+                acc[r] = fmaf(f.w, s3, acc[r]);
+            }
+        }
+        __syncthreads();
     }
 }
 
 template <int D, typename ACT>
 hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
-    hipLaunchKernelGGL(prefill_meta_kernel, dim3(1), dim3(1024), 0, s, p.cu_seqlens, p.start_pos, p.N, p.T, p.work);
+    if (!p.split) {
+        hipLaunchKernelGGL(prefill_meta_kernel, dim3(1), dim3(1024), 0, s, p.cu_seqlens, p.start_pos, p.N, p.T,
+                           p.work);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t blocks = static_cast<int64_t>(p.N) * p.H;
+        if (blocks == 0) return hipSuccess;
+        hipLaunchKernelGGL((prefill_kernel<D, ACT, true>), dim3(static_cast<unsigned>(blocks)), dim3(4 * D), 0, s,
+                           p);
+        return hipGetLastError();
+    }
+    const int64_t items = static_cast<int64_t>(p.max_items) * p.H;
+    if (p.N == 0 || items == 0) return hipSuccess;
+    hipLaunchKernelGGL(prefill_split_meta_kernel, dim3(1), dim3(1024), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t blocks = static_cast<int64_t>(p.N) * p.H;
-    if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((prefill_kernel<D, ACT>), dim3(static_cast<unsigned>(blocks)), dim3(4 * D), 0, s, p);
+    hipLaunchKernelGGL((prefill_kernel<D, ACT, false>), dim3(static_cast<unsigned>(2 * items)), dim3(4 * D), 0, s,
+                       p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(segment_scan_kernel<D>, dim3(static_cast<unsigned>(static_cast<int64_t>(p.N) * p.H * (D / 16))),
+                       dim3(256), 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((prefill_kernel<D, ACT, true>), dim3(static_cast<unsigned>(items)), dim3(4 * D), 0, s, p);
     return hipGetLastError();
 }
 
@@ -862,8 +1097,31 @@ bool prefill_supported(int dk, int dv, int act) {
     return dk == 32 || dk == 64;   // fp32 activations: raw staging of dk=128 exceeds LDS
 }
 
-size_t prefill_workspace_bytes(int32_t N, int32_t, int64_t, int, int) {
-    return (static_cast<size_t>(N) * sizeof(SeqWork) + 255) / 256 * 256;
+PrefillWorkspace prefill_workspace(int32_t N, int32_t H, int64_t T, int dk, int dv, int act_bytes,
+                                   int32_t ckpt_interval, bool split) {
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    PrefillWorkspace w{};
+    const int64_t items = split && ckpt_interval > 0 ? 2 * static_cast<int64_t>(N) + T / ckpt_interval : N;
+    if (items > INT32_MAX / 4) return w;       // bytes == 0: too many work items
+    w.max_items = static_cast<int32_t>(items);
+    size_t off = 0;
+    w.items = off;
+    off += up(static_cast<size_t>(items) * sizeof(SeqWork));
+    if (split) {
+        const size_t per = static_cast<size_t>(items) * H;
+        w.seq_items = off;
+        off += up(static_cast<size_t>(N) * sizeof(int2));
+        w.seg_F = off;
+        off += up(per * dk * dk * 4);
+        w.seg_G = off;
+        off += up(per * dk * dv * 4);
+        w.seg_S = off;
+        off += up(per * dk * dv * 4);
+        w.seq_x0 = off;
+        off += up(static_cast<size_t>(N) * H * (2 * dk + dv) * 3 * act_bytes);
+    }
+    w.bytes = off;
+    return w;
 }
 
 hipError_t launch_prefill(int dk, int dv, int act, const PrefillParams& p, hipStream_t s) {

@@ -17,7 +17,7 @@ class Run:
     """One prefill call on the GPU with pools, slots and checkpoint buffers."""
 
     def __init__(self, shape, inp, lengths, *, starts=None, S0=None, X0=None, interval=0,
-                 pool_extra=3, seq_order=None):
+                 pool_extra=3, seq_order=None, flags=0):
         self.shape, self.inp = shape, inp
         H, dk, dv, C = shape.H, shape.dk, shape.dv, shape.C
         N = len(lengths)
@@ -51,7 +51,8 @@ class Run:
         self.g, self.beta = dev(inp.g), dev(inp.beta)
         self.conv_w, self.norm_w = dev(inp.conv_w), dev(inp.norm_w)
         self.out = torch.full((T, H, dv), float("nan"), dtype=act, device="cuda")
-        nbytes = kda.kda_prefill_workspace_bytes(self.cfg, N, T)
+        self.flags = flags
+        nbytes = kda.kda_prefill_workspace_bytes(self.cfg, N, T, interval, flags)
         self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
 
     def launch(self):
@@ -62,7 +63,7 @@ class Run:
                                ckpt_interval=self.interval,
                                ckpt_state=self.ckS if self.interval else None,
                                ckpt_conv=self.ckX if self.interval else None,
-                               ckpt_base=dev(self.base) if self.interval else None)
+                               ckpt_base=dev(self.base) if self.interval else None, flags=self.flags)
         torch.cuda.synchronize()
         return self
 
@@ -124,7 +125,7 @@ def resume_and_finish(straight, picks):
     idx = np.concatenate(idx) if idx else np.zeros(0, np.int64)
     sub = wl.Inputs(shape, inp.q[idx], inp.k[idx], inp.v[idx], inp.z[idx], inp.g[idx], inp.beta[idx],
                     inp.conv_w, inp.norm_w)
-    resumed = Run(shape, sub, rem, starts=res_pos, interval=straight.interval)
+    resumed = Run(shape, sub, rem, starts=res_pos, interval=straight.interval, flags=straight.flags)
     resumed.init = np.arange(len(seqs), dtype=np.int32)
     kda.kda_resume(cfg, straight.ckS, straight.ckX, dev(np.asarray(src_ck, np.int32)),
                    resumed.Sd, resumed.Xd, dev(resumed.init))

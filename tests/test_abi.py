@@ -97,7 +97,7 @@ def test_copy_validation(name):
     assert copy_call(fn, cfg(), n=0, ss=None) == kda.KDA_OK
 
 
-def prefill_call(c, N=2, T=100, interval=0, ws_bytes=1 << 20, nck=4, **ptrs):
+def prefill_call(c, N=2, T=100, interval=0, ws_bytes=1 << 20, nck=4, flags=0, **ptrs):
     names = ("cu", "sp", "q", "k", "v", "z", "g", "beta", "conv_w", "norm_w", "state", "conv",
              "init", "final", "cks", "ckc", "ckb", "out", "ws")
     P = {n: FAKE for n in names}
@@ -107,7 +107,7 @@ def prefill_call(c, N=2, T=100, interval=0, ws_bytes=1 << 20, nck=4, **ptrs):
         ctypes.byref(c.c()), N, T, vp(P["cu"]), vp(P["sp"]), vp(P["q"]), vp(P["k"]), vp(P["v"]),
         vp(P["z"]), vp(P["g"]), vp(P["beta"]), vp(P["conv_w"]), vp(P["norm_w"]), vp(P["state"]),
         vp(P["conv"]), 8, vp(P["init"]), vp(P["final"]), interval, vp(P["cks"]), vp(P["ckc"]),
-        nck, vp(P["ckb"]), vp(P["out"]), vp(P["ws"]), ws_bytes, None)
+        nck, vp(P["ckb"]), flags, vp(P["out"]), vp(P["ws"]), ws_bytes, None)
 
 
 def test_prefill_validation():
@@ -125,8 +125,18 @@ def test_prefill_validation():
     assert prefill_call(cfg(), interval=64, ckb=None) == kda.KDA_ERR_INVALID_ARG
     assert prefill_call(cfg(), interval=64, nck=0) == kda.KDA_ERR_INVALID_ARG
     assert prefill_call(cfg(), N=0, cu=None) == kda.KDA_OK                      # nothing to do
+    assert prefill_call(cfg(), flags=2) == kda.KDA_ERR_INVALID_ARG                 # unknown flag
+    assert prefill_call(cfg(), flags=kda.KDA_PREFILL_SPLIT) == kda.KDA_ERR_INVALID_ARG   # split without interval
+    assert "interval" in kda.last_error()
+    assert prefill_call(cfg(), interval=64, flags=kda.KDA_PREFILL_SPLIT, ws_bytes=1 << 20) == kda.KDA_ERR_WORKSPACE
     ws = kda.kda_prefill_workspace_bytes(cfg(), 16, 1 << 18)
-    assert ws >= 16 * 24 and ws % 256 == 0
+    assert ws >= 16 * 32 and ws % 256 == 0
+    # split: room for 2N + T/interval segments, three dk x dv fp32 matrices per segment and head
+    ws_split = kda.kda_prefill_workspace_bytes(cfg(), 16, 1 << 18, 4096, kda.KDA_PREFILL_SPLIT)
+    segs = 2 * 16 + (1 << 18) // 4096
+    assert ws_split >= segs * 4 * 3 * 128 * 128 * 4 and ws_split % 256 == 0
+    with pytest.raises(kda.KdaError):
+        kda.kda_prefill_workspace_bytes(cfg(), 16, 1 << 18, 0, kda.KDA_PREFILL_SPLIT)
 
 
 def test_num_checkpoints_matches_oracle_rule():

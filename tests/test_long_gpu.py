@@ -12,8 +12,12 @@ The oracle checks the first 64K tokens (outputs and the checkpoints there);
 a resume from the checkpoint at 512K must reproduce the second half bit for
 bit; the end state is fanned out to 256 decode slots by copy-on-write resume
 and advanced 512 decode steps, checked on sampled slots against the oracle
-started from the same checkpoint.
+started from the same checkpoint.  The same sequence split at its
+checkpoints (KDA_PREFILL_SPLIT) must agree with the unsplit run to fp32
+rounding, match the oracle on the first 64K tokens and resume bit for bit.
 """
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -69,26 +73,42 @@ def test_varlen_checkpoints_and_resume_full_size():
                               bits(straight.ckS[src_ck[j] + 1:src_ck[j] + 1 + later]))
 
 
+@functools.lru_cache(maxsize=1)
+def long_inputs():
+    w = wl.WORKLOADS["long_1m"]
+    return wl.token_inputs(w["seed"], w["shape"], w["lengths"][0])
+
+
+@functools.lru_cache(maxsize=1)
+def long_unsplit_run():
+    w = wl.WORKLOADS["long_1m"]
+    return Run(w["shape"], long_inputs(), [w["lengths"][0]], interval=w["interval"]).launch()
+
+
+def check_prefix_against_oracle(run, inp, interval):
+    """The oracle on the first 64K tokens of one sampled head: outputs and the
+    checkpoints at 32K and 64K."""
+    P, hs = 65536, [3]
+    r = oracle.run(inp.q[:P, hs], inp.k[:P, hs], inp.v[:P, hs], inp.z[:P, hs], inp.g[:P, hs], inp.beta[:P, hs],
+                   inp.conv_w[hs], inp.norm_w, [0, P], ckpt_interval=interval)
+    e_out = rel_l2(host(run.out[:P])[:, hs], r.out)
+    ck = host(run.ckS[:2])[:, hs]
+    e_ck = rel_l2(ck, r.ckpt_S[:2])
+    say(f"  first {P} tokens, head {hs}: out {e_out:.3e}, checkpoints at 32K/64K {e_ck:.3e}")
+    assert e_out <= 1e-2 and e_ck <= 5e-3 and per_chain_max(ck, r.ckpt_S[:2]) <= TOL_STATE_PER_CHAIN
+    np.testing.assert_array_equal(host(run.ckX[:2])[:, hs], r.ckpt_X[:2])
+
+
 def test_long_context_1m_full_size():
     w = wl.WORKLOADS["long_1m"]
     shape, L, interval = w["shape"], w["lengths"][0], w["interval"]
     say(f"long context: {L} tokens, H={shape.H}, checkpoints every {interval}")
-    inp = wl.token_inputs(w["seed"], shape, L)
-    straight = Run(shape, inp, [L], interval=interval).launch()
+    inp = long_inputs()
+    straight = long_unsplit_run()
     say(f"  prefill done, {straight.nck} checkpoints")
     assert straight.nck == L // interval
-    out = host(straight.out)
-    assert np.isfinite(out).all()
-    # oracle on the first 64K tokens, one sampled head
-    P, hs = 65536, [3]
-    r = oracle.run(inp.q[:P, hs], inp.k[:P, hs], inp.v[:P, hs], inp.z[:P, hs], inp.g[:P, hs], inp.beta[:P, hs],
-                   inp.conv_w[hs], inp.norm_w, [0, P], ckpt_interval=interval)
-    e_out = rel_l2(out[:P, hs], r.out)
-    ck = host(straight.ckS[:2])[:, hs]
-    e_ck = rel_l2(ck, r.ckpt_S[:2])
-    say(f"  first {P} tokens, head {hs}: out {e_out:.3e}, checkpoints at 32K/64K {e_ck:.3e}")
-    assert e_out <= 1e-2 and e_ck <= 5e-3 and per_chain_max(ck, r.ckpt_S[:2]) <= TOL_STATE_PER_CHAIN
-    np.testing.assert_array_equal(host(straight.ckX[:2])[:, hs], r.ckpt_X[:2])
+    assert torch.isfinite(straight.out.float()).all()
+    check_prefix_against_oracle(straight, inp, interval)
     # resume from the checkpoint at 512K: the second half is reproduced bit for bit
     j = L // 2 // interval - 1
     resumed, _, res_pos, _, idx = resume_and_finish(straight, [j])
@@ -126,3 +146,29 @@ def test_long_context_1m_full_size():
     say(f"  decode fan-out, slots {pick}: out {e_o:.3e} state {e_s:.3e} (worst chain {e_c:.3e})")
     assert e_o <= 1e-2 and e_s <= 5e-3 and e_c <= TOL_STATE_PER_CHAIN
     np.testing.assert_array_equal(host(Xp)[pick], X_ref)
+
+
+def test_long_context_1m_split():
+    """The 1M-token sequence cut at its 32 checkpoints (segments in parallel,
+    joined by the scan of their transitions)."""
+    w = wl.WORKLOADS["long_1m"]
+    shape, L, interval = w["shape"], w["lengths"][0], w["interval"]
+    say(f"long context split: {L} tokens, H={shape.H}, segments of {interval}")
+    inp = long_inputs()
+    split = Run(shape, inp, [L], interval=interval, flags=kda.KDA_PREFILL_SPLIT).launch()
+    assert split.nck == L // interval
+    assert torch.isfinite(split.out.float()).all()
+    check_prefix_against_oracle(split, inp, interval)
+    ref = long_unsplit_run()
+    e_o = rel_l2(host(split.out[::97]), host(ref.out[::97]))
+    e_k = per_chain_max(host(split.ckS), host(ref.ckS))
+    say(f"  split vs unsplit: out (every 97th token) {e_o:.3e}, worst checkpoint chain {e_k:.3e}")
+    assert e_o <= 2e-3 and e_k <= 1e-5
+    np.testing.assert_array_equal(bits(split.ckX), bits(ref.ckX))
+    j = L // 2 // interval - 1
+    resumed, _, res_pos, _, idx = resume_and_finish(split, [j])
+    assert res_pos == [L // 2]
+    assert np.array_equal(bits(resumed.out), bits(split.out[L // 2:]))
+    assert np.array_equal(bits(resumed.Sd[int(resumed.final[0])]), bits(split.Sd[int(split.final[0])]))
+    assert np.array_equal(bits(resumed.ckS[:resumed.nck]), bits(split.ckS[j + 1:]))
+    say("  split resume from 512K: bitwise identical")

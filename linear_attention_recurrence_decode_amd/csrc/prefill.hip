@@ -319,10 +319,11 @@ __device__ __forceinline__ void stage_commit(const Staged<NU>& st, ACT* raw, flo
     constexpr int C = 2 * DK + DV;
     constexpr int VEC = 16 / static_cast<int>(sizeof(ACT));
     constexpr int UPR = C / VEC;
+    constexpr int CR = C + VEC;                 // padded row stride (spreads the v reads of the conv over banks)
 #pragma unroll
     for (int j = 0; j < NU; j++) {
         const int u = tp + j * NT;
-        if (u < (CH + 3) * UPR) *reinterpret_cast<uint4*>(raw + (u / UPR) * C + (u % UPR) * VEC) = st.val[j];
+        if (u < (CH + 3) * UPR) *reinterpret_cast<uint4*>(raw + (u / UPR) * CR + (u % UPR) * VEC) = st.val[j];
     }
     if (tp < CH) beta_s[tp] = st.beta;
 }
@@ -338,14 +339,16 @@ struct PrefillShape {
     static constexpr int PS = DK + 8;           // padded row stride of [64][dk] planes
     static constexpr int QS = CH + 8;           // padded row stride of [*][64] planes
     static constexpr int VEC = 16 / static_cast<int>(sizeof(ACT));   // elements per 16-byte load
+    static constexpr int CR = C + VEC;          // padded row stride of the raw rows
+    static constexpr int FP = DK + 4;           // padded row stride of the fp32 q/k planes
     static constexpr int NU = ((CH + 3) * (C / VEC) + NT - 1) / NT;  // staged 16-byte words per thread
     // LDS regions (bytes)
-    static constexpr int R0 = cmax(CH * DK * 4, 2 * CH * PS * 2);                // a_k (fp32) / K+ planes
+    static constexpr int R0 = cmax(CH * FP * 4, 2 * CH * PS * 2);                // a_k (fp32) / K+ planes
     static constexpr int R1 = R0;                                                 // a_q (fp32) / Q+ planes
     static constexpr int R2 = cmax(2 * CH * PS * 2, 2 * DK * QS * 2);           // K- planes / K-^T planes
     static constexpr int R4 = 2 * CH * QS * 2;                                   // L planes, T_aa on the diagonal
     static constexpr int R5 = 2 * CH * QS * 2;                                   // P planes
-    static constexpr int RAW = (CH + 3) * C * static_cast<int>(sizeof(ACT));    // raw rows (aliases R2..R5)
+    static constexpr int RAW = (CH + 3) * CR * static_cast<int>(sizeof(ACT));   // raw rows (aliases R2..R5)
     static constexpr int O0 = 0, O1 = R0, O2 = 2 * R0, O4 = O2 + R2, O5 = O4 + R4;
     static constexpr int BYTES = O5 + R5;
     static_assert(RAW <= R2 + R4 + R5, "raw staging must fit in the aliased regions");
@@ -361,6 +364,7 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
     using Sh = PrefillShape<D, ACT>;
     constexpr int DK = Sh::DK, DV = Sh::DV, NW = Sh::NW, NT = Sh::NT, C = Sh::C;
     constexpr int KS = Sh::KS, IB = Sh::IB, PS = Sh::PS, QS = Sh::QS, VEC = Sh::VEC;
+    constexpr int CR = Sh::CR, FP = Sh::FP;
     using A = Act<ACT>;
     // With bf16 outputs the output-only products (Q_g S, P U) take the LDS
     // operand in one bf16 term; fp32 outputs keep three terms everywhere.
@@ -380,7 +384,7 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
     char* reg2 = opaque_lds(lds, Sh::O2);
     char* reg4 = opaque_lds(lds, Sh::O4);
     char* reg5 = opaque_lds(lds, Sh::O5);
-    float* ak_f = reinterpret_cast<float*>(reg0);                // [CH][DK] fp32
+    float* ak_f = reinterpret_cast<float*>(reg0);                // [CH][FP] fp32
     float* aq_f = reinterpret_cast<float*>(reg1);
     uint16_t* kp_h = reinterpret_cast<uint16_t*>(reg0);          // K+ planes [CH][PS]
     uint16_t* kp_l = kp_h + CH * PS;
@@ -394,7 +398,7 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
     uint16_t* lp_l = lp_h + CH * QS;
     uint16_t* pp_h = reinterpret_cast<uint16_t*>(reg5);          // P planes [CH][QS]
     uint16_t* pp_l = pp_h + CH * QS;
-    ACT* raw = reinterpret_cast<ACT*>(reg2);                     // [CH+3][C]
+    ACT* raw = reinterpret_cast<ACT*>(reg2);                     // [CH+3][CR]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -542,18 +546,18 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
             const int tp = opq(tid);
             const int cqk = tp % (2 * DK), half = tp / (2 * DK);
             const int r0 = 32 * half;
-            float w0 = A::ld(raw + (r0 + 0) * C + cqk);
-            float w1 = A::ld(raw + (r0 + 1) * C + cqk);
-            float w2 = A::ld(raw + (r0 + 2) * C + cqk);
+            float w0 = A::ld(raw + (r0 + 0) * CR + cqk);
+            float w1 = A::ld(raw + (r0 + 1) * CR + cqk);
+            float w2 = A::ld(raw + (r0 + 2) * CR + cqk);
             float* dst = cqk < DK ? aq_f + cqk : ak_f + (cqk - DK);
 #pragma unroll 4
             for (int t = r0; t < r0 + 32; t++) {
-                const float w3 = A::ld(raw + (t + 3) * C + cqk);
+                const float w3 = A::ld(raw + (t + 3) * CR + cqk);
                 float y = wqk.x * w0;
                 y = fmaf(wqk.y, w1, y);
                 y = fmaf(wqk.z, w2, y);
                 y = fmaf(wqk.w, w3, y);
-                dst[t * DK] = t < n ? silu(y) : 0.f;
+                dst[t * FP] = t < n ? silu(y) : 0.f;
                 w0 = w1;
                 w1 = w2;
                 w2 = w3;
@@ -564,7 +568,7 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
                 const int rb = 16 * tb + 4 * gg;
                 float x[7];
 #pragma unroll
-                for (int m = 0; m < 7; m++) x[m] = A::ld(raw + (rb + m) * C + 2 * DK + jc);
+                for (int m = 0; m < 7; m++) x[m] = A::ld(raw + (rb + m) * CR + 2 * DK + jc);
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     float y = wv.x * x[e];
@@ -592,7 +596,7 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
             constexpr int SPAN = DK / PPT;
             const int pair = tp / PPT, part = tp % PPT;
             const int t = pair % CH;
-            const float* src = (pair < CH ? aq_f : ak_f) + t * DK + part * SPAN;
+            const float* src = (pair < CH ? aq_f : ak_f) + t * FP + part * SPAN;
             float ssum = 0.f;
 #pragma unroll
             for (int c = 0; c < SPAN; c += 4) {
@@ -624,8 +628,8 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
                 const int t = 16 * qqp + r;
                 const float d = (gq[r] + off) - gam_r;
                 const float E = __expf(d), Ei = __expf(-d);
-                const float kh = ak_f[t * DK + cgp] * rk_s[t];
-                const float qh = aq_f[t * DK + cgp] * rq_s[t];
+                const float kh = ak_f[t * FP + cgp] * rk_s[t];
+                const float qh = aq_f[t * FP + cgp] * rq_s[t];
                 kp[r] = kh * E;
                 km[r] = kh * Ei;
                 qp[r] = qh * E;
@@ -709,8 +713,23 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
             for (int kk = 0; kk < KPP; kk++)
                 st_split(lp_h, lp_l, (16 * blk + part * KPP + kk) * QS + 16 * blk + col, xk[kk]);
             const int cgp = tp % DK, qqp = tp / DK;
+            // this thread's 16 values are 16 consecutive entries of K-^T row cgp:
+            // two 16-byte stores per plane
+            uint32_t wh[8], wl[8];
 #pragma unroll
-            for (int r = 0; r < 16; r++) st_split(kt_h, kt_l, cgp * QS + 16 * qqp + r, km[r]);
+            for (int r = 0; r < 16; r += 2) {
+                const __bf16 h0 = static_cast<__bf16>(km[r]), h1 = static_cast<__bf16>(km[r + 1]);
+                const __bf16 l0 = static_cast<__bf16>(km[r] - static_cast<float>(h0));
+                const __bf16 l1 = static_cast<__bf16>(km[r + 1] - static_cast<float>(h1));
+                wh[r / 2] = static_cast<uint32_t>(bf16_bits(h0)) | (static_cast<uint32_t>(bf16_bits(h1)) << 16);
+                wl[r / 2] = static_cast<uint32_t>(bf16_bits(l0)) | (static_cast<uint32_t>(bf16_bits(l1)) << 16);
+            }
+            uint4* dh = reinterpret_cast<uint4*>(kt_h + cgp * QS + 16 * qqp);
+            uint4* dl = reinterpret_cast<uint4*>(kt_l + cgp * QS + 16 * qqp);
+            dh[0] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+            dh[1] = make_uint4(wh[4], wh[5], wh[6], wh[7]);
+            dl[0] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+            dl[1] = make_uint4(wl[4], wl[5], wl[6], wl[7]);
         }
         __syncthreads();
 

@@ -208,7 +208,7 @@ __device__ __forceinline__ float buf_ld_act(__amdgpu_buffer_rsrc_t r, uint32_t v
 
 template <typename ACT>
 __device__ __forceinline__ void buf_st_act(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float x) {
-    if constexpr (sizeof(ACT) == 2) buf_st16(r, voff, soff, f32_to_bf16(x));
+    if constexpr (sizeof(ACT) == 2) buf_st16(r, voff, soff, bf16_bits(static_cast<__bf16>(x)));   // RNE
     else buf_stf(r, voff, soff, x);
 }
 
@@ -246,36 +246,81 @@ struct Staged {
     float beta;
 };
 
+// Which 16-byte unit of the raw rows a staging slot covers.  Slots are
+// grouped per wave so that one wave's slot j always reads one tensor (q, k or
+// v): its loads then take a single buffer resource.  A tensor's units are the
+// (CH+3) x (D/VEC) 16-byte pieces of its rows (3 rows of left context first).
+template <typename ACT, int D, int NT>
+struct StageMap {
+    static constexpr int VEC = 16 / static_cast<int>(sizeof(ACT));
+    static constexpr int UPT = D / VEC;                    // units per tensor row
+    static constexpr int UT = (CH + 3) * UPT;              // units per tensor
+    static constexpr int WS = (UT + 63) / 64;              // wave slots per tensor
+    static constexpr int NWV = NT / 64;
+    static constexpr int NU = (3 * WS + NWV - 1) / NWV;    // slots per thread
+    struct Unit {
+        int tensor;   // 0 q, 1 k, 2 v; 3 = unused slot
+        int r, col;   // row (0 = three tokens before the chunk), first channel
+        bool valid;
+    };
+    __device__ static Unit unit(int j, int wv, int lane) {
+        const int w = j * NWV + wv;
+        const int local = (w % WS) * 64 + lane;
+        Unit u;
+        u.tensor = w / WS;
+        u.r = local / UPT;
+        u.col = (local % UPT) * VEC;
+        u.valid = u.tensor < 3 && local < UT;
+        return u;
+    }
+};
+
 // Issue the global loads of the chunk [tc0, tc0+n) of head h (no waits).
-// Left-context rows before the sequence start come from the initial conv
-// state x0 (index 2 = the token just before the start).
+// Left-context rows before the sequence start (first packed token ctx0) come
+// from the initial conv state x0 (index 2 = the token just before the start).
 template <typename ACT, int DK, int DV, int NT, int NU>
 __device__ __forceinline__ void stage_issue(Staged<NU>& st, const PrefillParams& p, const ACT* x0,
-                                            int64_t tok0, int64_t tc0, int n, int H, int h, int tp) {
-    constexpr int C = 2 * DK + DV;
-    constexpr int VEC = 16 / static_cast<int>(sizeof(ACT));
-    constexpr int UPR = C / VEC;
-    const ACT* qin = static_cast<const ACT*>(p.q);
-    const ACT* kin = static_cast<const ACT*>(p.k);
-    const ACT* vin = static_cast<const ACT*>(p.v);
+                                            int64_t ctx0, int64_t tc0, int n, int H, int h, int tp) {
+    static_assert(DK == DV, "one row layout for q, k and v");
+    using M = StageMap<ACT, DK, NT>;
+    static_assert(M::NU == NU, "staging slots");
+    constexpr int D = DK;
+    const int wv = __builtin_amdgcn_readfirstlane(tp >> 6), lane = tp & 63;
+    // resources start at the first row inside the sequence; rows before it
+    // (and rows past the chunk) fall outside and read as zero
+    const int64_t first = max(tc0 - 3, ctx0);
+    const int d0 = static_cast<int>(first - (tc0 - 3));                // 0..3 rows of context from x0
+    const int64_t hoff = (first * H + h) * D;
+    const uint32_t nbytes = static_cast<uint32_t>(((tc0 + n - 1 - first) * H + 1) * D * sizeof(ACT));
+    const uint32_t rowb = static_cast<uint32_t>(H * D * sizeof(ACT));
+    const ACT* tens[3] = {static_cast<const ACT*>(p.q), static_cast<const ACT*>(p.k), static_cast<const ACT*>(p.v)};
 #pragma unroll
     for (int j = 0; j < NU; j++) {
-        const int u = tp + j * NT;
-        const int r = u / UPR, c0 = (u % UPR) * VEC;
-        const int64_t tok = tc0 - 3 + r;
+        const typename M::Unit u = M::unit(j, wv, lane);
         st.val[j] = make_uint4(0, 0, 0, 0);
-        if (u < (CH + 3) * UPR && r < n + 3) {
-            if (tok >= tok0) {
-                const ACT* src = c0 < DK ? qin + (tok * H + h) * DK + c0
-                                         : (c0 < 2 * DK ? kin + (tok * H + h) * DK + (c0 - DK)
-                                                        : vin + (tok * H + h) * DV + (c0 - 2 * DK));
-                st.val[j] = *reinterpret_cast<const uint4*>(src);
-            } else {
-                const int m = 3 - static_cast<int>(tok0 - tok);
+        const int tsel = __builtin_amdgcn_readfirstlane(u.tensor);
+        if (tsel < 3) {
+            const auto rs = make_rsrc(tens[tsel] + hoff, nbytes);
+            const int rel = u.r - d0;
+            const uint32_t vo = (u.valid && rel >= 0) ? static_cast<uint32_t>(rel) * rowb + u.col * sizeof(ACT)
+                                                      : 0x80000000u;
+            const float4 x = buf_ld4(rs, vo, 0);
+            st.val[j] = make_uint4(__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z),
+                                   __float_as_uint(x.w));
+        }
+    }
+    if (d0 > 0) {
+        // context rows before the sequence start: raw values from x0
+#pragma unroll
+        for (int j = 0; j < NU; j++) {
+            const typename M::Unit u = M::unit(j, wv, lane);
+            if (u.valid && u.r < d0) {
+                const int m = 3 - d0 + u.r;                 // x0 index of this token
+                const int c0 = u.tensor * D + u.col;
                 uint32_t wd[4];
 #pragma unroll
                 for (int q4 = 0; q4 < 4; q4++) {
-                    const int c = c0 + q4 * (VEC / 4);
+                    const int c = c0 + q4 * (M::VEC / 4);
                     if constexpr (sizeof(ACT) == 2) {
                         wd[q4] = static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(x0)[c * 3 + m]) |
                                  (static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(x0)[(c + 1) * 3 + m]) << 16);
@@ -313,17 +358,17 @@ __device__ __forceinline__ void stage_clear(Staged<NU>& st) {
     st.beta = 0.f;
 }
 
-// Store the staged raw rows and beta into LDS.
+// Store the staged raw rows and beta into LDS (rows of CR elements: q, k, v).
 template <typename ACT, int DK, int DV, int NT, int NU>
 __device__ __forceinline__ void stage_commit(const Staged<NU>& st, ACT* raw, float* beta_s, int tp) {
+    using M = StageMap<ACT, DK, NT>;
     constexpr int C = 2 * DK + DV;
-    constexpr int VEC = 16 / static_cast<int>(sizeof(ACT));
-    constexpr int UPR = C / VEC;
-    constexpr int CR = C + VEC;                 // padded row stride (spreads the v reads of the conv over banks)
+    constexpr int CR = C + M::VEC;              // padded row stride (spreads the v reads of the conv over banks)
+    const int wv = __builtin_amdgcn_readfirstlane(tp >> 6), lane = tp & 63;
 #pragma unroll
     for (int j = 0; j < NU; j++) {
-        const int u = tp + j * NT;
-        if (u < (CH + 3) * UPR) *reinterpret_cast<uint4*>(raw + (u / UPR) * CR + (u % UPR) * VEC) = st.val[j];
+        const typename M::Unit u = M::unit(j, wv, lane);
+        if (u.valid) *reinterpret_cast<uint4*>(raw + u.r * CR + u.tensor * DK + u.col) = st.val[j];
     }
     if (tp < CH) beta_s[tp] = st.beta;
 }
@@ -341,7 +386,7 @@ struct PrefillShape {
     static constexpr int VEC = 16 / static_cast<int>(sizeof(ACT));   // elements per 16-byte load
     static constexpr int CR = C + VEC;          // padded row stride of the raw rows
     static constexpr int FP = DK + 4;           // padded row stride of the fp32 q/k planes
-    static constexpr int NU = ((CH + 3) * (C / VEC) + NT - 1) / NT;  // staged 16-byte words per thread
+    static constexpr int NU = StageMap<ACT, D, NT>::NU;              // staged 16-byte words per thread
     // LDS regions (bytes)
     static constexpr int R0 = cmax(CH * FP * 4, 2 * CH * PS * 2);                // a_k (fp32) / K+ planes
     static constexpr int R1 = R0;                                                 // a_q (fp32) / Q+ planes
@@ -867,10 +912,10 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
                 for (int e = 0; e < 4; e++) {
                     const int t = 16 * tb + 4 * gg + e;
                     const float rinv = rinv_s[t];
-                    // rows past the chunk are predicated off (and outside the resource)
-                    if (t < n)
-                        buf_st_act<ACT>(ro, vo + static_cast<uint32_t>((16 * tb + e) * rowb), 0,
-                                        accr[tb][e] * rinv * nwj * sigmoid(zr[tb][e]));
+                    // rows past the chunk lie outside the resource (the row offset is
+                    // in the range-checked per-lane offset): those stores are dropped
+                    buf_st_act<ACT>(ro, vo + static_cast<uint32_t>((16 * tb + e) * rowb), 0,
+                                    accr[tb][e] * rinv * nwj * sigmoid(zr[tb][e]));
                 }
         }
         }

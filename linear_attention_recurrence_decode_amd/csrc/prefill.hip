@@ -74,15 +74,28 @@ __device__ __forceinline__ f32x4 mfma3_16(const Frag4& a, const Frag4& b, f32x4 
     return acc;
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Split two floats into packed (hi, lo) bf16 pairs with x = hi + lo to about
+// 16 significant bits: hi = RNE(x) (one packed conversion for both), lo =
+// RNE(x - hi) (x - hi is exact in fp32).
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+    const float ha = __uint_as_float(hi << 16), hb = __uint_as_float(hi & 0xffff0000u);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a - ha, b - hb}, bf16x2));
+}
+
+union U64 {
+    uint2 u;
+    bf16x4 v;
+};
+
 __device__ __forceinline__ Frag4 split4(const f32x4& x) {
-    Frag4 f;
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-        const __bf16 h = static_cast<__bf16>(x[e]);
-        f.hi[e] = h;
-        f.lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(h));
-    }
-    return f;
+    U64 h, l;
+    split2(x[0], x[1], h.u.x, l.u.x);
+    split2(x[2], x[3], h.u.y, l.u.y);
+    return Frag4{h.v, l.v};
 }
 
 // Two 4-element halves stacked into one 8-element operand.
@@ -114,23 +127,27 @@ __device__ __forceinline__ f32x4 mfma2(const bf16x8& ahi, const Frag& b, f32x4 a
 }
 
 __device__ __forceinline__ Frag split8(const float (&x)[8]) {
-    Frag f;
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-        const __bf16 h = static_cast<__bf16>(x[e]);
-        f.hi[e] = h;
-        f.lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(h));
-    }
-    return f;
+    union {
+        uint4 u;
+        bf16x8 v;
+    } h, l;
+    split2(x[0], x[1], h.u.x, l.u.x);
+    split2(x[2], x[3], h.u.y, l.u.y);
+    split2(x[4], x[5], h.u.z, l.u.z);
+    split2(x[6], x[7], h.u.w, l.u.w);
+    return Frag{h.v, l.v};
 }
 
 __device__ __forceinline__ uint16_t bf16_bits(__bf16 b) { return __builtin_bit_cast(uint16_t, b); }
 
-// Store x as a (hi, lo) bf16 pair into two planes at element index idx.
-__device__ __forceinline__ void st_split(uint16_t* hi, uint16_t* lo, int idx, float x) {
-    const __bf16 h = static_cast<__bf16>(x);
-    hi[idx] = bf16_bits(h);
-    lo[idx] = bf16_bits(static_cast<__bf16>(x - static_cast<float>(h)));
+// Store a at element idx and b at idx + stride of two (hi, lo) planes.
+__device__ __forceinline__ void st_split2(uint16_t* hi, uint16_t* lo, int idx, int stride, float a, float b) {
+    uint32_t h, l;
+    split2(a, b, h, l);
+    hi[idx] = static_cast<uint16_t>(h);
+    hi[idx + stride] = static_cast<uint16_t>(h >> 16);
+    lo[idx] = static_cast<uint16_t>(l);
+    lo[idx + stride] = static_cast<uint16_t>(l >> 16);
 }
 
 union U128 {
@@ -686,11 +703,11 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
             }
             __syncthreads();
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
+            for (int r = 0; r < 16; r += 2) {
                 const int idx = (16 * qqp + r) * PS + cgp;
-                st_split(kp_h, kp_l, idx, kp[r]);
-                if constexpr (OUT) st_split(qp_h, qp_l, idx, qp[r]);
-                st_split(km_h, km_l, idx, km[r]);
+                st_split2(kp_h, kp_l, idx, PS, kp[r], kp[r + 1]);
+                if constexpr (OUT) st_split2(qp_h, qp_l, idx, PS, qp[r], qp[r + 1]);
+                st_split2(km_h, km_l, idx, PS, km[r], km[r + 1]);
             }
         }
         __syncthreads();
@@ -723,11 +740,16 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
                     if constexpr (OUT) ap = mfma3(ld_nat(qp_h, qp_l, offa), fb, ap);
                 }
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
+                for (int e = 0; e < 4; e += 2) {
                     const int t = 16 * a + 4 * gg + e, s2 = 16 * b + lc;
-                    if constexpr (OUT) st_split(pp_h, pp_l, t * QS + s2, t >= s2 ? ap[e] : 0.f);
-                    if (a > b) st_split(lp_h, lp_l, t * QS + s2, beta_s[t] * am[e]);
-                    else ld_s[a][4 * gg + e][lc] = t > s2 ? beta_s[t] * am[e] : 0.f;
+                    if constexpr (OUT)
+                        st_split2(pp_h, pp_l, t * QS + s2, QS, t >= s2 ? ap[e] : 0.f, t + 1 >= s2 ? ap[e + 1] : 0.f);
+                    if (a > b) {
+                        st_split2(lp_h, lp_l, t * QS + s2, QS, beta_s[t] * am[e], beta_s[t + 1] * am[e + 1]);
+                    } else {
+                        ld_s[a][4 * gg + e][lc] = t > s2 ? beta_s[t] * am[e] : 0.f;
+                        ld_s[a][4 * gg + e + 1][lc] = t + 1 > s2 ? beta_s[t + 1] * am[e + 1] : 0.f;
+                    }
                 }
             }
         }
@@ -755,20 +777,14 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
                     if (part * KPP + kk == r) xk[kk] = xr;
             }
 #pragma unroll
-            for (int kk = 0; kk < KPP; kk++)
-                st_split(lp_h, lp_l, (16 * blk + part * KPP + kk) * QS + 16 * blk + col, xk[kk]);
+            for (int kk = 0; kk < KPP; kk += 2)
+                st_split2(lp_h, lp_l, (16 * blk + part * KPP + kk) * QS + 16 * blk + col, QS, xk[kk], xk[kk + 1]);
             const int cgp = tp % DK, qqp = tp / DK;
             // this thread's 16 values are 16 consecutive entries of K-^T row cgp:
             // two 16-byte stores per plane
             uint32_t wh[8], wl[8];
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const __bf16 h0 = static_cast<__bf16>(km[r]), h1 = static_cast<__bf16>(km[r + 1]);
-                const __bf16 l0 = static_cast<__bf16>(km[r] - static_cast<float>(h0));
-                const __bf16 l1 = static_cast<__bf16>(km[r + 1] - static_cast<float>(h1));
-                wh[r / 2] = static_cast<uint32_t>(bf16_bits(h0)) | (static_cast<uint32_t>(bf16_bits(h1)) << 16);
-                wl[r / 2] = static_cast<uint32_t>(bf16_bits(l0)) | (static_cast<uint32_t>(bf16_bits(l1)) << 16);
-            }
+            for (int r = 0; r < 16; r += 2) split2(km[r], km[r + 1], wh[r / 2], wl[r / 2]);
             uint4* dh = reinterpret_cast<uint4*>(kt_h + cgp * QS + 16 * qqp);
             uint4* dl = reinterpret_cast<uint4*>(kt_l + cgp * QS + 16 * qqp);
             dh[0] = make_uint4(wh[0], wh[1], wh[2], wh[3]);

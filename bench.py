@@ -19,8 +19,9 @@ step).  The line also carries:
 With --workload the line instead reports one of the larger prefill
 workloads (inputs resident in HBM, one call per pass):
   varlen_ckpt   16 sequences of log-uniform length in [1K, 64K] (about 248K
-                tokens), H=32, checkpoints every 4096 tokens and at the ends;
-                then a resume batch (each sequence restarted from a seeded
+                tokens on average), H=32, checkpoints every 4096 tokens and at
+                the ends, unsplit (the reported value) and split at the
+                checkpoints; then a resume batch (each sequence restarted from a seeded
                 interval checkpoint) timed on its own
   long_1m       one sequence of 1,048,576 tokens, H=8, checkpoints every 32K,
                 unsplit and split at the checkpoints; then 512 decode steps of
@@ -290,12 +291,15 @@ def bench_varlen(steps, warmup):
     log(f"[bench] varlen: {N} sequences, {sum(lengths)} tokens")
     inp = wl.token_inputs(w["seed"], shape, sum(lengths))
     stream = torch.cuda.current_stream()
-    st = PrefillSetup(kda, wl, shape, inp, lengths, [0] * N, interval, [0])
+    split = kda.KDA_PREFILL_SPLIT
+    st = PrefillSetup(kda, wl, shape, inp, lengths, [0] * N, interval, [0, split])
+    t_s = _time_calls(lambda: st.call(split, stream), steps, warmup, stream)
     t = _time_calls(lambda: st.call(0, stream), steps, warmup, stream)
     res = {"workload": f"varlen_ckpt: {N} sequences, {sum(lengths)} tokens (lengths log-uniform in [1K, 64K]), "
                        f"H={shape.H}, dk=dv={shape.dk}, bf16, checkpoints every {interval} and at ends "
                        f"({st.nck} checkpoints)",
-           "straight": prefill_rates(st.T, shape.H, shape.dk, shape.dv, t)}
+           "straight": prefill_rates(st.T, shape.H, shape.dk, shape.dv, t),
+           "straight_split": prefill_rates(st.T, shape.H, shape.dk, shape.dv, t_s)}
     # resume batch: each sequence with an interval checkpoint restarts from a seeded one
     rng = np.random.default_rng([w["seed"], wl.TID["resume"], 0])
     rem, pos, src, idx = [], [], [], []

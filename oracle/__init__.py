@@ -16,6 +16,8 @@ Parity status of the parts (the pins live in tests/test_oracle_pins.py):
   conv + SiLU, tap order, conv-state shift  pinned: unit-tap closed forms
   L2 norm, gated RMSNorm                    pinned: closed forms
   checkpoint positions and contents         pinned: brute-force split runs
+  bf16 state storage (rounding, where)      pinned: library bf16 conversion,
+                                            single rounding at the end, splits
   eps values, unit query scale, logistic output gate, conv tap orientation
   as a convention of the pages               parity unpinned (readings)
 """
@@ -57,12 +59,13 @@ def _load():
             ctypes.c_int, P, P,
             P, P, P, P, P, P, P, P,
             P, P,
-            ctypes.c_int64, P, P, P,
+            ctypes.c_int64, P, P, P, ctypes.c_int,
             P, ctypes.c_int]
         lib.kda_oracle_run.restype = ctypes.c_int
         lib.kda_oracle_num_checkpoints.argtypes = [ctypes.c_int64] * 3
         lib.kda_oracle_num_checkpoints.restype = ctypes.c_int64
         lib.kda_oracle_max_threads.restype = ctypes.c_int
+        lib.kda_oracle_round_bf16.argtypes = [P, P, ctypes.c_int64]
         _lib = lib
     return _lib
 
@@ -73,6 +76,14 @@ def num_checkpoints(start: int, length: int, interval: int) -> int:
 
 def max_threads() -> int:
     return int(_load().kda_oracle_max_threads())
+
+
+def round_bf16(x) -> np.ndarray:
+    """The oracle's rounding of values to the nearest bf16 value (ties to even)."""
+    x = _f64(x)
+    y = np.empty_like(x)
+    _load().kda_oracle_round_bf16(_ptr(x), _ptr(y), x.size)
+    return y
 
 
 @dataclass
@@ -96,13 +107,15 @@ def _ptr(a):
 
 def run(q, k, v, z, g, beta, conv_w, norm_w, cu_seqlens, *, start_pos=None,
         S0=None, X0=None, ckpt_interval: int = 0, l2_eps: float = 1e-6,
-        rms_eps: float = 1e-6, threads: int = 0) -> Result:
+        rms_eps: float = 1e-6, threads: int = 0, state_round: bool = False) -> Result:
     """Run the recurrence over packed sequences.
 
     q, k, g: [T][H][dk]; v, z: [T][H][dv]; beta: [T][H]; conv_w: [H][2dk+dv][W];
     norm_w: [dv]; cu_seqlens: [N+1]; start_pos: [N] absolute position of each
     sequence's first token (default 0); S0: [N][H][dk][dv] and X0:
-    [N][H][2dk+dv][W-1] initial states (default zero).
+    [N][H][2dk+dv][W-1] initial states (default zero).  state_round: bf16 state
+    storage, the state rounded to bf16 wherever it is stored (checkpoints and
+    sequence ends).
     """
     q, k, v, z, g, beta = map(_f64, (q, k, v, z, g, beta))
     conv_w, norm_w = _f64(conv_w), _f64(norm_w)
@@ -132,7 +145,7 @@ def run(q, k, v, z, g, beta, conv_w, norm_w, cu_seqlens, *, start_pos=None,
                                 _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(g), _ptr(beta),
                                 _ptr(conv_w), _ptr(norm_w), _ptr(S), _ptr(X),
                                 int(ckpt_interval), _ptr(base), _ptr(cS), _ptr(cX),
-                                _ptr(out), int(threads))
+                                int(bool(state_round)), _ptr(out), int(threads))
     if rc != 0:
         raise ValueError(f"kda_oracle_run failed with {rc}")
     pos = []
@@ -147,13 +160,15 @@ def run(q, k, v, z, g, beta, conv_w, norm_w, cu_seqlens, *, start_pos=None,
 
 
 def decode_steps(q, k, v, z, g, beta, conv_w, norm_w, S0, X0, *, l2_eps=1e-6,
-                 rms_eps=1e-6, threads: int = 0):
+                 rms_eps=1e-6, threads: int = 0, state_round: bool = False):
     """Run `steps` single-token decode steps for B sequences.
 
     q, k, g: [steps][B][H][dk]; v, z: [steps][B][H][dv]; beta: [steps][B][H];
     S0: [B][H][dk][dv]; X0: [B][H][2dk+dv][W-1].  Returns (out [steps][B][H][dv],
     S [B][H][dk][dv], X).  Each step is one call of the recurrence with every
-    sequence one token long, carrying the state between calls.
+    sequence one token long, carrying the state between calls (with
+    state_round, rounded to bf16 after every step: the state is stored every
+    step).
     """
     steps, B = q.shape[0], q.shape[1]
     S, X = _f64(S0), _f64(X0)
@@ -161,7 +176,7 @@ def decode_steps(q, k, v, z, g, beta, conv_w, norm_w, S0, X0, *, l2_eps=1e-6,
     cu = np.arange(B + 1, dtype=np.int64)
     for s in range(steps):
         r = run(q[s], k[s], v[s], z[s], g[s], beta[s], conv_w, norm_w, cu,
-                S0=S, X0=X, l2_eps=l2_eps, rms_eps=rms_eps, threads=threads)
+                S0=S, X0=X, l2_eps=l2_eps, rms_eps=rms_eps, threads=threads, state_round=state_round)
         S, X = r.S, r.X
         outs.append(r.out)
     return np.stack(outs), S, X

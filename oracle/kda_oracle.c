@@ -38,6 +38,13 @@
  *       prefix boundary; agentlenshq, "Agentic Cache Retention Policies":
  *       interval-based retention checkpoints at fixed intervals and at prompt
  *       boundaries.]
+ *   8. optional bf16 state storage (state_round != 0): wherever the state is
+ *      stored -- every checkpoint and the sequence end -- it is rounded to the
+ *      nearest bf16 value (ties to even) and the run continues from the
+ *      rounded state; the readout of step 5 uses the state before rounding.
+ *      [vLLM recipe "moonshotai/Kimi-K3", section "AMD MI355X: disaggregated
+ *       prefill and decode": the worker command keeps the Mamba-style (KDA)
+ *       state cache in bfloat16.]
  *
  * Steps 3-5 are the gated delta rule with a per-channel decay,
  * S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T and
@@ -76,6 +83,23 @@ int64_t kda_oracle_num_checkpoints(int64_t start, int64_t len, int64_t interval)
     return count + 1;
 }
 
+/* Nearest bf16 value of x (8 significant bits, ties to even; bf16 subnormals
+ * are multiples of 2^-133). */
+static double round_bf16(double x)
+{
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    (void)frexp(x, &e);               /* x = m 2^e with 0.5 <= |m| < 1 */
+    int qe = e - 8;                   /* weight of the last kept bit */
+    if (qe < -133) qe = -133;
+    return ldexp(nearbyint(ldexp(x, -qe)), qe);
+}
+
+static void round_state(double* Sh, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) Sh[i] = round_bf16(Sh[i]);
+}
+
 static double silu(double y) { return y / (1.0 + exp(-y)); }
 static double sigmoid(double y) { return 1.0 / (1.0 + exp(-y)); }
 
@@ -87,7 +111,7 @@ static void run_chain(int n, int h, int H, int dk, int dv, int W,
                       const double* conv_w, const double* norm_w,
                       double* S, double* X,
                       int64_t interval, int64_t ckpt_slot0,
-                      double* ckpt_S, double* ckpt_X, double* out)
+                      double* ckpt_S, double* ckpt_X, int state_round, double* out)
 {
     const int C = 2 * dk + dv;
     const int Wm = W - 1;
@@ -163,17 +187,21 @@ static void run_chain(int n, int h, int H, int dk, int dv, int W,
             const int64_t pos = start + t + 1;
             if (pos % interval == 0 || t == L - 1) {
                 const int64_t slot = ckpt_slot0 + ck++;
+                if (state_round) round_state(Sh, (int64_t)dk * dv);
                 memcpy(ckpt_S + (slot * H + h) * dk * dv, Sh, sizeof(double) * dk * dv);
                 if (Wm > 0)
                     memcpy(ckpt_X + (slot * H + h) * C * Wm, Xh, sizeof(double) * C * Wm);
             }
         }
     }
+    /* 8. the final state is stored too */
+    if (state_round) round_state(Sh, (int64_t)dk * dv);
     free(a); free(u); free(o);
 }
 
 /* Runs the recurrence over num_seqs packed sequences.  Returns 0 on success,
- * a negative value on invalid arguments. */
+ * a negative value on invalid arguments.  state_round != 0 selects bf16 state
+ * storage (step 8). */
 int kda_oracle_run(int H, int dk, int dv, int W, double l2_eps, double rms_eps,
                    int num_seqs, const int64_t* cu_seqlens, const int64_t* start_pos,
                    const double* q, const double* k, const double* v, const double* z,
@@ -181,7 +209,7 @@ int kda_oracle_run(int H, int dk, int dv, int W, double l2_eps, double rms_eps,
                    const double* conv_w, const double* norm_w,
                    double* S, double* X,
                    int64_t ckpt_interval, const int64_t* ckpt_base,
-                   double* ckpt_S, double* ckpt_X,
+                   double* ckpt_S, double* ckpt_X, int state_round,
                    double* out, int num_threads)
 {
     if (H <= 0 || dk <= 0 || dv <= 0 || W <= 0 || num_seqs < 0) return -1;
@@ -199,9 +227,15 @@ int kda_oracle_run(int H, int dk, int dv, int W, double l2_eps, double rms_eps,
         const int64_t start = start_pos ? start_pos[n] : 0;
         run_chain(n, h, H, dk, dv, W, l2_eps, rms_eps, t0, L, start,
                   q, k, v, z, g, beta, conv_w, norm_w, S, X,
-                  ckpt_interval, ckpt_base ? ckpt_base[n] : 0, ckpt_S, ckpt_X, out);
+                  ckpt_interval, ckpt_base ? ckpt_base[n] : 0, ckpt_S, ckpt_X, state_round, out);
     }
     return 0;
+}
+
+/* round_bf16 over an array (exposed for its pin against a library conversion) */
+void kda_oracle_round_bf16(const double* x, double* y, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) y[i] = round_bf16(x[i]);
 }
 
 int kda_oracle_max_threads(void)

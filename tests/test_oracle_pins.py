@@ -386,3 +386,63 @@ def test_golden_hand_worked_example():
     for t, coeffs in enumerate(ex["output_coeffs"]):
         o = np.array(coeffs) @ vh
         np.testing.assert_allclose(r.out[t, 0], o / np.sqrt(np.mean(o * o)), rtol=1e-13)
+
+
+# ---------------------------------------------------------------- bf16 state storage
+
+def test_round_bf16_matches_library_conversion():
+    """The oracle's bf16 rounding equals torch's float32 -> bfloat16 conversion
+    (round to nearest, ties to even) on random values, exact ties, values next
+    to ties, bf16 subnormals and large magnitudes."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(90)
+    x = rng.standard_normal(20000).astype(np.float32) * np.float32(10.0) ** rng.integers(-30, 30, 20000)
+    b = rng.standard_normal(4000).astype(np.float32)
+    bits = b.view(np.uint32) & np.uint32(0xFFFF0000)
+    ties = (bits | np.uint32(0x8000)).view(np.float32)                 # exactly halfway
+    near = np.concatenate([(bits | np.uint32(0x7FFF)).view(np.float32),
+                           (bits | np.uint32(0x8001)).view(np.float32)])
+    sub = (rng.standard_normal(2000) * 2.0 ** -128).astype(np.float32)   # bf16 subnormal range
+    for arr in (x, ties, near, sub):
+        ref = torch.from_numpy(arr).to(torch.bfloat16).double().numpy()
+        np.testing.assert_array_equal(oracle.round_bf16(arr), ref)
+
+
+def test_state_round_only_at_the_end_without_checkpoints():
+    """Without checkpoints the state is stored once, at the end: the outputs are
+    those of the unrounded run and the final state is its rounding."""
+    rng = np.random.default_rng(91)
+    T, H, dk, dv = 70, 2, 8, 8
+    q, k, v, z, g, beta, cw, nw = rand_inputs(rng, T, H, dk, dv, g_scale=0.1)
+    S0 = oracle.round_bf16(rng.standard_normal((1, H, dk, dv)) * 0.3)
+    a = oracle.run(q, k, v, z, g, beta, cw, nw, [0, T], S0=S0)
+    b = oracle.run(q, k, v, z, g, beta, cw, nw, [0, T], S0=S0, state_round=True)
+    np.testing.assert_array_equal(b.out, a.out)
+    np.testing.assert_array_equal(b.S, oracle.round_bf16(a.S))
+    assert not np.array_equal(b.S, a.S)
+
+
+def test_state_round_continues_from_each_checkpoint():
+    """With bf16 storage a run with checkpoints equals, bit for bit, the runs
+    between consecutive checkpoint positions chained through their (rounded)
+    final states; every checkpoint is bf16-representable."""
+    rng = np.random.default_rng(92)
+    T, H, dk, dv, I = 150, 2, 8, 8, 40
+    q, k, v, z, g, beta, cw, nw = rand_inputs(rng, T, H, dk, dv, g_scale=0.1)
+    whole = oracle.run(q, k, v, z, g, beta, cw, nw, [0, T], start_pos=[7], ckpt_interval=I, state_round=True)
+    cuts = [0] + [p - 7 for p in whole.ckpt_pos]                      # 33, 73, 113, 150
+    S, X, outs = None, None, []
+    for j in range(len(cuts) - 1):
+        a, b = cuts[j], cuts[j + 1]
+        r = oracle.run(q[a:b], k[a:b], v[a:b], z[a:b], g[a:b], beta[a:b], cw, nw, [0, b - a],
+                       start_pos=[7 + a], S0=S, X0=X, state_round=True)
+        np.testing.assert_array_equal(whole.ckpt_S[j], r.S[0])
+        S, X = r.S, r.X
+        outs.append(r.out)
+    np.testing.assert_array_equal(np.concatenate(outs), whole.out)
+    np.testing.assert_array_equal(whole.S, S)
+    np.testing.assert_array_equal(whole.ckpt_S, oracle.round_bf16(whole.ckpt_S))
+    # and the unrounded run differs after the first checkpoint
+    plain = oracle.run(q, k, v, z, g, beta, cw, nw, [0, T], start_pos=[7], ckpt_interval=I)
+    np.testing.assert_array_equal(plain.out[:cuts[1]], whole.out[:cuts[1]])
+    assert not np.array_equal(plain.out[cuts[1]:], whole.out[cuts[1]:])

@@ -41,8 +41,8 @@
  *   conv_w    [H][2dk+dv][4] fp32 (per head: q channels, then k, then v;
  *             tap 3 multiplies the current token, tap 0 the token 3 back)
  *   norm_w    [dv] fp32, shared by all heads
- *   state     [S][H][dk][dv] fp32      (pool of recurrent states; also the
- *                                       checkpoint format)
+ *   state     [S][H][dk][dv] state dtype (pool of recurrent states; also
+ *                                       the checkpoint format)
  *   conv      [S][H][2dk+dv][3] activation dtype (raw inputs of the last 3
  *                                       tokens, index 0 = oldest)
  * Supported shapes: dk == dv in {32, 64, 128}; conv width 4; H >= 1.
@@ -77,10 +77,21 @@ typedef struct {
     int32_t head_k;      /* dk */
     int32_t head_v;      /* dv */
     int32_t conv_width;  /* must be 4 */
-    int32_t act_dtype;   /* kda_dtype of q, k, v, z, out and the conv state;
-                            the recurrent state is always fp32 */
+    int32_t act_dtype;   /* kda_dtype of q, k, v, z, out and the conv state */
     float l2_eps;        /* eps inside the q/k L2 norm (1e-6 by convention) */
     float rms_eps;       /* eps inside the output RMSNorm (1e-6 by convention) */
+    int32_t state_dtype; /* kda_dtype of the stored recurrent state (pools and
+                            checkpoints); KDA_F32 (0) by default.  The state
+                            math is fp32 either way.  With KDA_BF16 the state
+                            is rounded to nearest bf16 (ties to even) wherever
+                            it is stored -- after every decode step, at every
+                            prefill checkpoint and at the prefill end -- and
+                            computation continues from the rounded state, so
+                            resuming from a checkpoint stays bit-identical in
+                            the stored dtype.  [vLLM recipe
+                            "moonshotai/Kimi-K3", section "AMD MI355X:
+                            disaggregated prefill and decode": the worker
+                            command keeps this state cache in bfloat16.] */
 } kda_config;
 
 /*
@@ -104,7 +115,7 @@ kda_status kda_decode_step(const kda_config* cfg, int32_t B,
                            const void* q, const void* k, const void* v, const void* z,
                            const float* g, const float* beta,
                            const float* conv_w, const float* norm_w,
-                           float* state_pool, void* conv_pool, int32_t num_slots,
+                           void* state_pool, void* conv_pool, int32_t num_slots,
                            const int32_t* slot, void* out, void* stream);
 
 /*
@@ -165,9 +176,9 @@ kda_status kda_prefill_varlen(const kda_config* cfg, int32_t num_seqs, int64_t t
                               const void* q, const void* k, const void* v, const void* z,
                               const float* g, const float* beta,
                               const float* conv_w, const float* norm_w,
-                              float* state_pool, void* conv_pool, int32_t num_slots,
+                              void* state_pool, void* conv_pool, int32_t num_slots,
                               const int32_t* init_slot, const int32_t* final_slot,
-                              int32_t ckpt_interval, float* ckpt_state, void* ckpt_conv,
+                              int32_t ckpt_interval, void* ckpt_state, void* ckpt_conv,
                               int32_t num_ckpt_slots, const int32_t* ckpt_base, int32_t flags,
                               void* out, void* workspace, size_t workspace_bytes,
                               void* stream);
@@ -180,9 +191,9 @@ kda_status kda_prefill_varlen(const kda_config* cfg, int32_t num_seqs, int64_t t
  * Ids outside their pool are skipped.  Destinations must be distinct.
  */
 kda_status kda_state_checkpoint(const kda_config* cfg, int32_t n,
-                                const float* state_pool, const void* conv_pool, int32_t num_slots,
+                                const void* state_pool, const void* conv_pool, int32_t num_slots,
                                 const int32_t* src_slot,
-                                float* ckpt_state, void* ckpt_conv, int32_t num_ckpt_slots,
+                                void* ckpt_state, void* ckpt_conv, int32_t num_ckpt_slots,
                                 const int32_t* dst_ckpt, void* stream);
 
 /*
@@ -196,9 +207,9 @@ kda_status kda_state_checkpoint(const kda_config* cfg, int32_t n,
  * an event recorded after it).  Ids outside their pool are skipped.
  */
 kda_status kda_resume(const kda_config* cfg, int32_t n,
-                      const float* ckpt_state, const void* ckpt_conv, int32_t num_ckpt_slots,
+                      const void* ckpt_state, const void* ckpt_conv, int32_t num_ckpt_slots,
                       const int32_t* src_ckpt,
-                      float* state_pool, void* conv_pool, int32_t num_slots,
+                      void* state_pool, void* conv_pool, int32_t num_slots,
                       const int32_t* dst_slot, void* stream);
 
 /* Workspace bytes kda_prefill_varlen needs for these sizes, checkpoint

@@ -46,7 +46,7 @@ class _Config(ctypes.Structure):
     _fields_ = [("num_heads", ctypes.c_int32), ("head_k", ctypes.c_int32),
                 ("head_v", ctypes.c_int32), ("conv_width", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("l2_eps", ctypes.c_float),
-                ("rms_eps", ctypes.c_float)]
+                ("rms_eps", ctypes.c_float), ("state_dtype", ctypes.c_int32)]
 
 
 @dataclass
@@ -58,10 +58,15 @@ class Config:
     conv_width: int = 4
     l2_eps: float = 1e-6
     rms_eps: float = 1e-6
+    state_dtype: int = KDA_F32
 
     @property
     def torch_act(self):
         return torch.bfloat16 if self.act_dtype == KDA_BF16 else torch.float32
+
+    @property
+    def torch_state(self):
+        return torch.bfloat16 if self.state_dtype == KDA_BF16 else torch.float32
 
     @property
     def conv_channels(self):
@@ -69,7 +74,7 @@ class Config:
 
     def c(self) -> _Config:
         return _Config(self.num_heads, self.head_k, self.head_v, self.conv_width,
-                       self.act_dtype, self.l2_eps, self.rms_eps)
+                       self.act_dtype, self.l2_eps, self.rms_eps, self.state_dtype)
 
 
 _lib = None
@@ -159,7 +164,7 @@ def kda_decode_step(cfg: Config, q, k, v, z, g, beta, conv_w, norm_w, state_pool
     _want(v, "v", act, (B, H, dv)); _want(z, "z", act, (B, H, dv))
     _want(g, "g", torch.float32, (B, H, dk)); _want(beta, "beta", torch.float32, (B, H))
     _want(conv_w, "conv_w", torch.float32, (H, C, 4)); _want(norm_w, "norm_w", torch.float32, (dv,))
-    _want(state_pool, "state_pool", torch.float32, (S, H, dk, dv))
+    _want(state_pool, "state_pool", cfg.torch_state, (S, H, dk, dv))
     _want(conv_pool, "conv_pool", act, (S, H, C, 3))
     _want(slot, "slot", torch.int32, (B,)); _want(out, "out", act, (B, H, dv))
     _check(lib().kda_decode_step(ctypes.byref(cfg.c()), B, _ptr(q), _ptr(k), _ptr(v), _ptr(z),
@@ -184,14 +189,14 @@ def kda_prefill_varlen(cfg: Config, cu_seqlens, q, k, v, z, g, beta, conv_w, nor
     _want(v, "v", act, (T, H, dv)); _want(z, "z", act, (T, H, dv))
     _want(g, "g", torch.float32, (T, H, dk)); _want(beta, "beta", torch.float32, (T, H))
     _want(conv_w, "conv_w", torch.float32, (H, C, 4)); _want(norm_w, "norm_w", torch.float32, (dv,))
-    _want(state_pool, "state_pool", torch.float32, (S, H, dk, dv))
+    _want(state_pool, "state_pool", cfg.torch_state, (S, H, dk, dv))
     _want(conv_pool, "conv_pool", act, (S, H, C, 3))
     _want(init_slot, "init_slot", torch.int32, (N,)); _want(final_slot, "final_slot", torch.int32, (N,))
     _want(out, "out", act, (T, H, dv))
     nck = 0
     if ckpt_interval:
         nck = ckpt_state.shape[0]
-        _want(ckpt_state, "ckpt_state", torch.float32, (nck, H, dk, dv))
+        _want(ckpt_state, "ckpt_state", cfg.torch_state, (nck, H, dk, dv))
         _want(ckpt_conv, "ckpt_conv", act, (nck, H, C, 3))
         _want(ckpt_base, "ckpt_base", torch.int32, (N,))
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -212,7 +217,7 @@ def _copy(fn, cfg, src_state, src_conv, src_idx, dst_state, dst_conv, dst_idx, s
     n = src_idx.numel()
     for nm, t, shape in (("src_state", src_state, (src_state.shape[0], H, dk, dv)),
                          ("dst_state", dst_state, (dst_state.shape[0], H, dk, dv))):
-        _want(t, nm, torch.float32, shape)
+        _want(t, nm, cfg.torch_state, shape)
     _want(src_conv, "src_conv", act, (src_state.shape[0], H, C, 3))
     _want(dst_conv, "dst_conv", act, (dst_state.shape[0], H, C, 3))
     _want(src_idx, "src ids", torch.int32, (n,)); _want(dst_idx, "dst ids", torch.int32, (n,))

@@ -4,9 +4,9 @@
 //  "The Hardest Part: Prefix Caching for KDA": a cached state is copied into a
 //  private destination before a request extends it.]
 //
-// One workgroup per (pair, head): the head's fp32 state (dk*dv floats) and its
-// conv state (a multiple of 16 bytes) move as 16-byte words.  Ids outside
-// their pool are skipped.
+// One workgroup per (pair, head): the head's state (dk*dv elements of the
+// state dtype) and its conv state (each a multiple of 16 bytes) move as
+// 16-byte words.  Ids outside their pool are skipped.
 
 #include "kda_device.h"
 #include "kda_launch.h"
@@ -21,9 +21,9 @@ __global__ __launch_bounds__(kCopyThreads) void copy_kernel(CopyParams p) {
     if (src < 0 || src >= p.src_slots || dst < 0 || dst >= p.dst_slots) return;
     const int64_t sh = static_cast<int64_t>(src) * p.H + h;
     const int64_t dh = static_cast<int64_t>(dst) * p.H + h;
-    const float4* s4 = reinterpret_cast<const float4*>(p.src_state + sh * p.state_floats);
-    float4* d4 = reinterpret_cast<float4*>(p.dst_state + dh * p.state_floats);
-    const int64_t n4 = p.state_floats / 4;
+    const uint4* s4 = reinterpret_cast<const uint4*>(static_cast<const char*>(p.src_state) + sh * p.state_bytes);
+    uint4* d4 = reinterpret_cast<uint4*>(static_cast<char*>(p.dst_state) + dh * p.state_bytes);
+    const int64_t n4 = p.state_bytes / 16;
     for (int64_t e = threadIdx.x; e < n4; e += kCopyThreads) d4[e] = s4[e];
     const uint4* sc = reinterpret_cast<const uint4*>(static_cast<const char*>(p.src_conv) + sh * p.conv_bytes);
     uint4* dc = reinterpret_cast<uint4*>(static_cast<char*>(p.dst_conv) + dh * p.conv_bytes);

@@ -1,8 +1,8 @@
 // decode.hip -- fused single-launch KDA decode step for gfx950.
 //
-// One workgroup per (sequence, head).  The fp32 dk x dv state of the pair is
-// streamed from HBM once into registers with 128-bit loads, updated there and
-// streamed back once; everything else (conv-state shift, causal conv + SiLU,
+// One workgroup per (sequence, head).  The dk x dv state of the pair is
+// streamed from HBM once into registers (128-bit loads for an fp32 state,
+// 64-bit for a bf16 one), updated there in fp32 and streamed back once; everything else (conv-state shift, causal conv + SiLU,
 // L2 norms, decay, delta update, readout, gated RMSNorm) happens while the
 // state loads are in flight or on registers/LDS, in the same launch.
 // [vLLM blog "A Preview of Production-Scale Kimi K3 Support on vLLM", section
@@ -28,7 +28,9 @@
 
 namespace kda {
 
-template <int DK, int DV, typename ACT, int NT>
+// ST: stored state type (float, or bf16_t: loaded to fp32, rounded to nearest
+// bf16 on the store; the math is fp32 either way).
+template <int DK, int DV, typename ACT, typename ST, int NT>
 __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
     constexpr int NCG = DV / 4;
     constexpr int RG = NT / NCG;
@@ -90,11 +92,15 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
     // 2. the state: RPT consecutive rows x 4 columns per thread, through a
     // buffer resource covering this (slot, head) only
     __builtin_amdgcn_sched_barrier(0);
-    const auto rs = make_rsrc(p.state + sh * DK * DV, DK * DV * 4);
-    const uint32_t voff = static_cast<uint32_t>((rg * RPT * DV + 4 * cg) * 4);
+    constexpr uint32_t SB = sizeof(ST);
+    const auto rs = make_rsrc(static_cast<ST*>(p.state) + sh * DK * DV, DK * DV * SB);
+    const uint32_t voff = static_cast<uint32_t>((rg * RPT * DV + 4 * cg) * SB);
     float4 s[RPT];
 #pragma unroll
-    for (int r = 0; r < RPT; r++) s[r] = buf_ld4(rs, voff + (r % 8) * DV * 4, (r / 8) * 8 * DV * 4);
+    for (int r = 0; r < RPT; r++) {
+        if constexpr (SB == 4) s[r] = buf_ld4(rs, voff + (r % 8) * DV * 4, (r / 8) * 8 * DV * 4);
+        else s[r] = bf16x4_to_f32(buf_ld8(rs, voff + r * DV * 2));
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     // 3. conv-state shift + causal depthwise conv (width 4) + SiLU
@@ -192,7 +198,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
         const float kh = a_s[DK + rg * RPT + r] * rk;
         s[r].x = fmaf(kh, u.x, s[r].x); s[r].y = fmaf(kh, u.y, s[r].y);
         s[r].z = fmaf(kh, u.z, s[r].z); s[r].w = fmaf(kh, u.w, s[r].w);
-        buf_st4(rs, voff + r * DV * 4, s[r]);
+        if constexpr (SB == 4) buf_st4(rs, voff + r * DV * 4, s[r]);
+        else buf_st8(rs, voff + r * DV * 2, f32_to_bf16x4(s[r]));
     }
 
     // 8. gated RMSNorm over dv (every row group holds all of o)
@@ -210,24 +217,29 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
     }
 }
 
-template <int DK, int DV, typename ACT, int NT>
+template <int DK, int DV, typename ACT, typename ST, int NT>
 static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
     const int64_t blocks = static_cast<int64_t>(p.B) * p.H;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_kernel<DK, DV, ACT, NT>), dim3(static_cast<unsigned>(blocks)),
+    hipLaunchKernelGGL((decode_kernel<DK, DV, ACT, ST, NT>), dim3(static_cast<unsigned>(blocks)),
                        dim3(NT), 0, s, p);
     return hipGetLastError();
 }
 
-hipError_t launch_decode(int dk, int dv, int act, const DecodeParams& p, hipStream_t s) {
-    if (dk != dv) return hipErrorInvalidValue;
-    const bool bf = act == 1;
-    switch (dk) {
-        case 32:  return bf ? launch_decode_t<32, 32, bf16_t, 64>(p, s) : launch_decode_t<32, 32, float, 64>(p, s);
-        case 64:  return bf ? launch_decode_t<64, 64, bf16_t, 128>(p, s) : launch_decode_t<64, 64, float, 128>(p, s);
-        case 128: return bf ? launch_decode_t<128, 128, bf16_t, 256>(p, s) : launch_decode_t<128, 128, float, 256>(p, s);
+template <typename ACT, typename ST>
+static hipError_t launch_decode_d(int d, const DecodeParams& p, hipStream_t s) {
+    switch (d) {
+        case 32:  return launch_decode_t<32, 32, ACT, ST, 64>(p, s);
+        case 64:  return launch_decode_t<64, 64, ACT, ST, 128>(p, s);
+        case 128: return launch_decode_t<128, 128, ACT, ST, 256>(p, s);
         default:  return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_decode(int dk, int dv, int act, int state, const DecodeParams& p, hipStream_t s) {
+    if (dk != dv) return hipErrorInvalidValue;
+    if (act == 1) return state == 1 ? launch_decode_d<bf16_t, bf16_t>(dk, p, s) : launch_decode_d<bf16_t, float>(dk, p, s);
+    return state == 1 ? launch_decode_d<float, bf16_t>(dk, p, s) : launch_decode_d<float, float>(dk, p, s);
 }
 
 }  // namespace kda

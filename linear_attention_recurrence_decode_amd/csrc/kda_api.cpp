@@ -59,6 +59,8 @@ kda_status check_cfg(const kda_config* c) {
         return fail(KDA_ERR_INVALID_ARG, "head_k and head_v must be >= 1 (got %d, %d)", c->head_k, c->head_v);
     if (c->act_dtype != KDA_F32 && c->act_dtype != KDA_BF16)
         return fail(KDA_ERR_INVALID_ARG, "act_dtype must be KDA_F32 or KDA_BF16 (got %d)", c->act_dtype);
+    if (c->state_dtype != KDA_F32 && c->state_dtype != KDA_BF16)
+        return fail(KDA_ERR_INVALID_ARG, "state_dtype must be KDA_F32 or KDA_BF16 (got %d)", c->state_dtype);
     if (!(std::isfinite(c->l2_eps) && c->l2_eps >= 0.f && std::isfinite(c->rms_eps) && c->rms_eps >= 0.f))
         return fail(KDA_ERR_INVALID_ARG, "l2_eps and rms_eps must be finite and >= 0");
     if (c->conv_width != 4)
@@ -76,8 +78,8 @@ kda_status hip_status(hipError_t e, const char* what) {
     return ok();
 }
 
-kda_status check_copy_args(const kda_config* cfg, int32_t n, const float* src_state, const void* src_conv,
-                           int32_t src_slots, const int32_t* src_idx, float* dst_state, void* dst_conv,
+kda_status check_copy_args(const kda_config* cfg, int32_t n, const void* src_state, const void* src_conv,
+                           int32_t src_slots, const int32_t* src_idx, void* dst_state, void* dst_conv,
                            int32_t dst_slots, const int32_t* dst_idx) {
     KDA_TRY(check_cfg(cfg));
     if (n < 0) return fail(KDA_ERR_INVALID_ARG, "n must be >= 0 (got %d)", n);
@@ -94,13 +96,13 @@ kda_status check_copy_args(const kda_config* cfg, int32_t n, const float* src_st
     return KDA_OK;
 }
 
-kda::CopyParams copy_params(const kda_config* cfg, int32_t n, const float* src_state, const void* src_conv,
-                            int32_t src_slots, const int32_t* src_idx, float* dst_state, void* dst_conv,
+kda::CopyParams copy_params(const kda_config* cfg, int32_t n, const void* src_state, const void* src_conv,
+                            int32_t src_slots, const int32_t* src_idx, void* dst_state, void* dst_conv,
                             int32_t dst_slots, const int32_t* dst_idx) {
     kda::CopyParams p;
     p.n = n;
     p.H = cfg->num_heads;
-    p.state_floats = static_cast<int64_t>(cfg->head_k) * cfg->head_v;
+    p.state_bytes = static_cast<int64_t>(cfg->head_k) * cfg->head_v * (cfg->state_dtype == KDA_BF16 ? 2 : 4);
     p.conv_bytes = static_cast<int64_t>(2 * cfg->head_k + cfg->head_v) * 3 * act_bytes(cfg);
     p.src_state = src_state;
     p.src_conv = src_conv;
@@ -128,7 +130,7 @@ int64_t kda_num_checkpoints(int64_t start, int64_t len, int32_t interval) {
 
 kda_status kda_decode_step(const kda_config* cfg, int32_t B, const void* q, const void* k, const void* v,
                            const void* z, const float* g, const float* beta, const float* conv_w,
-                           const float* norm_w, float* state_pool, void* conv_pool, int32_t num_slots,
+                           const float* norm_w, void* state_pool, void* conv_pool, int32_t num_slots,
                            const int32_t* slot, void* out, void* stream) {
     KDA_TRY(check_cfg(cfg));
     if (B < 0) return fail(KDA_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
@@ -166,7 +168,7 @@ kda_status kda_decode_step(const kda_config* cfg, int32_t B, const void* q, cons
     p.out = out;
     p.l2_eps = cfg->l2_eps;
     p.rms_eps = cfg->rms_eps;
-    return hip_status(kda::launch_decode(cfg->head_k, cfg->head_v, cfg->act_dtype, p,
+    return hip_status(kda::launch_decode(cfg->head_k, cfg->head_v, cfg->act_dtype, cfg->state_dtype, p,
                                          static_cast<hipStream_t>(stream)),
                       "decode launch");
 }
@@ -208,9 +210,9 @@ size_t kda_prefill_workspace_bytes(const kda_config* cfg, int32_t num_seqs, int6
 kda_status kda_prefill_varlen(const kda_config* cfg, int32_t num_seqs, int64_t total_tokens,
                               const int32_t* cu_seqlens, const int64_t* start_pos, const void* q,
                               const void* k, const void* v, const void* z, const float* g, const float* beta,
-                              const float* conv_w, const float* norm_w, float* state_pool, void* conv_pool,
+                              const float* conv_w, const float* norm_w, void* state_pool, void* conv_pool,
                               int32_t num_slots, const int32_t* init_slot, const int32_t* final_slot,
-                              int32_t ckpt_interval, float* ckpt_state, void* ckpt_conv,
+                              int32_t ckpt_interval, void* ckpt_state, void* ckpt_conv,
                               int32_t num_ckpt_slots, const int32_t* ckpt_base, int32_t flags, void* out,
                               void* workspace, size_t workspace_bytes, void* stream) {
     KDA_TRY(check_cfg(cfg));
@@ -294,13 +296,14 @@ kda_status kda_prefill_varlen(const kda_config* cfg, int32_t num_seqs, int64_t t
     p.seg_G = split ? reinterpret_cast<float*>(ws + wl.seg_G) : nullptr;
     p.seg_S = split ? reinterpret_cast<float*>(ws + wl.seg_S) : nullptr;
     p.seq_x0 = split ? static_cast<void*>(ws + wl.seq_x0) : nullptr;
+    p.state_bf16 = cfg->state_dtype == KDA_BF16 ? 1 : 0;
     return hip_status(kda::launch_prefill(cfg->head_k, cfg->head_v, cfg->act_dtype, p,
                                           static_cast<hipStream_t>(stream)),
                       "prefill launch");
 }
 
-kda_status kda_state_checkpoint(const kda_config* cfg, int32_t n, const float* state_pool, const void* conv_pool,
-                                int32_t num_slots, const int32_t* src_slot, float* ckpt_state, void* ckpt_conv,
+kda_status kda_state_checkpoint(const kda_config* cfg, int32_t n, const void* state_pool, const void* conv_pool,
+                                int32_t num_slots, const int32_t* src_slot, void* ckpt_state, void* ckpt_conv,
                                 int32_t num_ckpt_slots, const int32_t* dst_ckpt, void* stream) {
     KDA_TRY(check_copy_args(cfg, n, state_pool, conv_pool, num_slots, src_slot, ckpt_state, ckpt_conv,
                             num_ckpt_slots, dst_ckpt));
@@ -310,8 +313,8 @@ kda_status kda_state_checkpoint(const kda_config* cfg, int32_t n, const float* s
     return hip_status(kda::launch_copy(p, static_cast<hipStream_t>(stream)), "checkpoint copy launch");
 }
 
-kda_status kda_resume(const kda_config* cfg, int32_t n, const float* ckpt_state, const void* ckpt_conv,
-                      int32_t num_ckpt_slots, const int32_t* src_ckpt, float* state_pool, void* conv_pool,
+kda_status kda_resume(const kda_config* cfg, int32_t n, const void* ckpt_state, const void* ckpt_conv,
+                      int32_t num_ckpt_slots, const int32_t* src_ckpt, void* state_pool, void* conv_pool,
                       int32_t num_slots, const int32_t* dst_slot, void* stream) {
     KDA_TRY(check_copy_args(cfg, n, ckpt_state, ckpt_conv, num_ckpt_slots, src_ckpt, state_pool, conv_pool,
                             num_slots, dst_slot));

@@ -155,4 +155,33 @@ __device__ __forceinline__ void buf_st4(__amdgpu_buffer_rsrc_t r, uint32_t voff,
     __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(voff), 0, 0);
 }
 
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// 8-byte buffer load / store (literal zero soffset, as for the wide stores).
+__device__ __forceinline__ uint2 buf_ld8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    const i32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(voff), 0, 0);
+    return make_uint2(static_cast<uint32_t>(v.x), static_cast<uint32_t>(v.y));
+}
+__device__ __forceinline__ void buf_st8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint2 x) {
+    i32x2 v;
+    v.x = static_cast<int>(x.x);
+    v.y = static_cast<int>(x.y);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, static_cast<int>(voff), 0, 0);
+}
+
+// Four bf16 values (two 32-bit words, lower element in the low half) to fp32.
+__device__ __forceinline__ float4 bf16x4_to_f32(uint2 w) {
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+}
+
+// Four fp32 values to bf16, round to nearest even (packed hardware conversion).
+__device__ __forceinline__ uint2 f32_to_bf16x4(float4 x) {
+    const bf16x2_t a = __builtin_convertvector(f32x2_t{x.x, x.y}, bf16x2_t);
+    const bf16x2_t b = __builtin_convertvector(f32x2_t{x.z, x.w}, bf16x2_t);
+    return make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+}
+
 }  // namespace kda

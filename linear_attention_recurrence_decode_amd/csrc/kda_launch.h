@@ -18,7 +18,7 @@ struct DecodeParams {
     const float* beta;
     const float* conv_w;
     const float* norm_w;
-    float* state;
+    void* state;        // state dtype (fp32 or bf16)
     void* conv;
     const int32_t* slot;
     void* out;
@@ -27,13 +27,13 @@ struct DecodeParams {
 
 struct CopyParams {
     int32_t n, H;
-    int64_t state_floats;  // dk * dv per head
+    int64_t state_bytes;   // dk * dv * state element size per head (multiple of 16)
     int64_t conv_bytes;    // (2dk+dv) * 3 * act bytes per head (multiple of 16)
-    const float* src_state;
+    const void* src_state;
     const void* src_conv;
     int32_t src_slots;
     const int32_t* src_idx;
-    float* dst_state;
+    void* dst_state;
     void* dst_conv;
     int32_t dst_slots;
     const int32_t* dst_idx;
@@ -65,13 +65,13 @@ struct PrefillParams {
     const float* beta;
     const float* conv_w;
     const float* norm_w;
-    float* state;
+    void* state;        // state dtype (fp32 or bf16)
     void* conv;
     int32_t num_slots;
     const int32_t* init_slot;
     const int32_t* final_slot;
     int32_t ckpt_interval;
-    float* ckpt_state;
+    void* ckpt_state;   // state dtype
     void* ckpt_conv;
     int32_t num_ckpt_slots;
     const int32_t* ckpt_base;
@@ -87,10 +87,11 @@ struct PrefillParams {
     float* seg_G;       // [max_items][H][dk][dv] segment end states from a zero state
     float* seg_S;       // [max_items][H][dk][dv] segment initial states
     void* seq_x0;       // [N][H][2dk+dv][3] initial conv states (activation dtype)
+    int32_t state_bf16; // stored state in bf16 (rounded at every store; math in fp32)
 };
 
 // Each launcher returns hipSuccess or the launch error.
-hipError_t launch_decode(int dk, int dv, int act, const DecodeParams& p, hipStream_t s);
+hipError_t launch_decode(int dk, int dv, int act, int state, const DecodeParams& p, hipStream_t s);
 hipError_t launch_copy(const CopyParams& p, hipStream_t s);
 hipError_t launch_prefill(int dk, int dv, int act, const PrefillParams& p, hipStream_t s);
 bool prefill_supported(int dk, int dv, int act);

@@ -253,6 +253,30 @@ __device__ __forceinline__ void store_state_strip(float* dst, const f32x4 (&S)[I
         for (int e = 0; e < 4; e++) buf_stf(rs, sv, (16 * ib + e) * DV * 4, S[ib][e]);
 }
 
+// The strip stored in the state dtype of a pool (fp32, or bf16 rounded to
+// nearest even).  With a bf16 pool the chain continues from the stored
+// value: S is rounded in place.
+template <int IB, int DV>
+__device__ __forceinline__ void store_pool_strip(void* pool, int64_t slot_head, f32x4 (&S)[IB], int g4, int jcol,
+                                                 int dk, bool bf16) {
+    if (!bf16) {
+        store_state_strip<IB, DV>(static_cast<float*>(pool) + slot_head * dk * DV, S, g4, jcol, dk);
+        return;
+    }
+    const auto rs = make_rsrc(static_cast<uint16_t*>(pool) + slot_head * dk * DV, static_cast<uint32_t>(dk * DV * 2));
+    const uint32_t sv = static_cast<uint32_t>((4 * g4 * DV + jcol) * 2);
+#pragma unroll
+    for (int ib = 0; ib < IB; ib++)
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+            const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{S[ib][e], S[ib][e + 1]}, bf16x2));
+            buf_st16(rs, sv, (16 * ib + e) * DV * 2, static_cast<uint16_t>(w));
+            buf_st16(rs, sv, (16 * ib + e + 1) * DV * 2, static_cast<uint16_t>(w >> 16));
+            S[ib][e] = __uint_as_float(w << 16);
+            S[ib][e + 1] = __uint_as_float(w & 0xffff0000u);
+        }
+}
+
 // Registers holding one chunk's staged inputs between the loads and the LDS
 // stores: raw q|k|v rows (with 3 rows of left context) as 16-byte words, this
 // thread's 16 log-decay values, and (threads 0..63) one beta.
@@ -506,10 +530,13 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
     f32x4 S[IB];
     {
         const uint32_t sv = static_cast<uint32_t>((4 * g4 * DV + jcol) * 4);
-        const float* s0 = nullptr;
+        const float* s0 = nullptr;          // fp32 source
+        const uint16_t* s0h = nullptr;      // bf16 source
         if constexpr (OUT) {
+            const int64_t ih = (static_cast<int64_t>(init) * H + h) * DK * DV;
             if (seg_in) s0 = p.seg_S + (static_cast<int64_t>(item) * H + h) * DK * DV;
-            else if (init >= 0) s0 = p.state + (static_cast<int64_t>(init) * H + h) * DK * DV;
+            else if (init >= 0 && p.state_bf16) s0h = static_cast<const uint16_t*>(p.state) + ih;
+            else if (init >= 0) s0 = static_cast<const float*>(p.state) + ih;
         }
         if (s0) {
             const auto rs = make_rsrc(s0, DK * DV * 4);
@@ -517,6 +544,13 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
             for (int ib = 0; ib < IB; ib++)
 #pragma unroll
                 for (int e = 0; e < 4; e++) S[ib][e] = buf_ldf(rs, sv, (16 * ib + e) * DV * 4);
+        } else if (s0h) {
+            const auto rs = make_rsrc(s0h, DK * DV * 2);
+#pragma unroll
+            for (int ib = 0; ib < IB; ib++)
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    S[ib][e] = __uint_as_float(static_cast<uint32_t>(buf_ld16(rs, sv / 2, (16 * ib + e) * DV * 2)) << 16);
         } else {
 #pragma unroll
             for (int ib = 0; ib < IB; ib++)
@@ -580,7 +614,7 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
             const int slot = ck_base + wk.part - 1;
             if (slot >= 0 && slot < p.num_ckpt_slots) {
                 const int64_t sh = static_cast<int64_t>(slot) * H + h;
-                store_state_strip<IB, DV>(p.ckpt_state + sh * DK * DV, S, g4, jcol, DK);
+                store_pool_strip<IB, DV>(p.ckpt_state, sh, S, g4, jcol, DK, p.state_bf16);
                 write_conv_state(static_cast<ACT*>(p.ckpt_conv) + sh * C * 3, tok0);
             }
         }
@@ -946,8 +980,15 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
             ck++;
             if (slot >= 0 && slot < p.num_ckpt_slots) {
                 const int64_t sh = static_cast<int64_t>(slot) * H + h;
-                store_state_strip<IB, DV>(p.ckpt_state + sh * DK * DV, S, g4, jcol, DK);
+                store_pool_strip<IB, DV>(p.ckpt_state, sh, S, g4, jcol, DK, p.state_bf16);
                 write_conv_state(static_cast<ACT*>(p.ckpt_conv) + sh * C * 3, tok0 + done);
+            } else if (p.state_bf16) {
+                // no slot to write, but the stored dtype still applies here
+#pragma unroll
+                for (int ib = 0; ib < IB; ib++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        S[ib][e] = __uint_as_float(static_cast<uint32_t>(bf16_bits(static_cast<__bf16>(S[ib][e]))) << 16);
             }
         }
         n = n_next;
@@ -958,7 +999,7 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
     if constexpr (OUT) {
         if (fin >= 0 && fin < p.num_slots) {
             const int64_t sh = static_cast<int64_t>(fin) * H + h;
-            store_state_strip<IB, DV>(p.state + sh * DK * DV, S, g4, jcol, DK);
+            store_pool_strip<IB, DV>(p.state, sh, S, g4, jcol, DK, p.state_bf16);
             write_conv_state(static_cast<ACT*>(p.conv) + sh * C * 3, tok0 + L);
         }
     } else {
@@ -1103,15 +1144,23 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(PrefillParams p) {
     const int tid = threadIdx.x, c = tid % CB, rg = tid / CB;
     const int col = cb * CB + c;
     const int init = p.init_slot ? p.init_slot[seq] : -1;   // in range: only such sequences are cut
+    const int64_t ih = (static_cast<int64_t>(init) * H + h) * D * D;
     float acc[RPT];
 #pragma unroll
-    for (int r = 0; r < RPT; r++)
-        acc[r] = init >= 0 ? p.state[(static_cast<int64_t>(init) * H + h) * D * D + (rg + 16 * r) * D + col] : 0.f;
+    for (int r = 0; r < RPT; r++) {
+        const int64_t e = ih + (rg + 16 * r) * D + col;
+        acc[r] = init < 0 ? 0.f
+                          : (p.state_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p.state)[e]) << 16)
+                                          : static_cast<const float*>(p.state)[e]);
+    }
     for (int m = 0;; m++) {
         const int64_t it = static_cast<int64_t>(si.x) + m;
         float* dst = p.seg_S + (it * H + h) * D * D;
 #pragma unroll
         for (int r = 0; r < RPT; r++) {
+            // a bf16 state pool stores the boundary states rounded: the chain
+            // continues from the stored value
+            if (p.state_bf16) acc[r] = __uint_as_float(static_cast<uint32_t>(bf16_bits(static_cast<__bf16>(acc[r]))) << 16);
             dst[(rg + 16 * r) * D + col] = acc[r];
             S_s[(rg + 16 * r) * CB + c] = acc[r];
         }

@@ -9,21 +9,22 @@ import workloads as wl
 from tests.helpers import TOL_STATE_PER_CHAIN, dev, host, per_chain_max, rel_l2, say, tols
 
 
-def cfg_for(shape):
-    return kda.Config(shape.H, shape.dk, shape.dv, kda.KDA_BF16 if shape.act == "bf16" else kda.KDA_F32)
+def cfg_for(shape, state_dtype=kda.KDA_F32):
+    return kda.Config(shape.H, shape.dk, shape.dv, kda.KDA_BF16 if shape.act == "bf16" else kda.KDA_F32,
+                      state_dtype=state_dtype)
 
 
 class Run:
     """One prefill call on the GPU with pools, slots and checkpoint buffers."""
 
     def __init__(self, shape, inp, lengths, *, starts=None, S0=None, X0=None, interval=0,
-                 pool_extra=3, seq_order=None, flags=0):
+                 pool_extra=3, seq_order=None, flags=0, state_dtype=kda.KDA_F32):
         self.shape, self.inp = shape, inp
         H, dk, dv, C = shape.H, shape.dk, shape.dv, shape.C
         N = len(lengths)
         self.N, self.lengths = N, list(lengths)
         self.starts = [0] * N if starts is None else list(starts)
-        self.cfg = cfg_for(shape)
+        self.cfg = cfg_for(shape, state_dtype)
         act = self.cfg.torch_act
         cu = wl.cu_seqlens(lengths)
         self.cu = cu
@@ -37,14 +38,14 @@ class Run:
             X[:N] = X0
         final = np.arange(N, 2 * N, dtype=np.int32)
         self.init, self.final = init, final
-        self.Sd, self.Xd = dev(S), dev(X, act)
+        self.Sd, self.Xd = dev(S, self.cfg.torch_state), dev(X, act)
         counts = [oracle.num_checkpoints(s, L, interval) for s, L in zip(self.starts, lengths)]
         base = np.zeros(N, np.int32)
         if N:
             base[1:] = np.cumsum(counts)[:-1]
         self.base, self.nck = base, int(sum(counts))
         self.interval = interval
-        self.ckS = torch.full((max(self.nck, 1), H, dk, dv), float("nan"), device="cuda")
+        self.ckS = torch.full((max(self.nck, 1), H, dk, dv), float("nan"), dtype=self.cfg.torch_state, device="cuda")
         self.ckX = torch.zeros((max(self.nck, 1), H, C, 3), dtype=act, device="cuda")
         T = int(cu[-1])
         self.q, self.k, self.v, self.z = (dev(a, act) for a in (inp.q, inp.k, inp.v, inp.z))
@@ -78,7 +79,7 @@ def oracle_for(run, S0=None, X0=None, heads=None):
     return oracle.run(inp.q[sl], inp.k[sl], inp.v[sl], inp.z[sl], inp.g[sl], inp.beta[sl],
                       inp.conv_w[hs], inp.norm_w, run.cu, start_pos=run.starts,
                       S0=None if S0 is None else S0[:, hs], X0=None if X0 is None else X0[:, hs],
-                      ckpt_interval=run.interval)
+                      ckpt_interval=run.interval, state_round=run.cfg.state_dtype == kda.KDA_BF16)
 
 
 def states_for(seed, shape, N, scale=0.3):
@@ -125,7 +126,8 @@ def resume_and_finish(straight, picks):
     idx = np.concatenate(idx) if idx else np.zeros(0, np.int64)
     sub = wl.Inputs(shape, inp.q[idx], inp.k[idx], inp.v[idx], inp.z[idx], inp.g[idx], inp.beta[idx],
                     inp.conv_w, inp.norm_w)
-    resumed = Run(shape, sub, rem, starts=res_pos, interval=straight.interval, flags=straight.flags)
+    resumed = Run(shape, sub, rem, starts=res_pos, interval=straight.interval, flags=straight.flags,
+                  state_dtype=straight.cfg.state_dtype)
     resumed.init = np.arange(len(seqs), dtype=np.int32)
     kda.kda_resume(cfg, straight.ckS, straight.ckX, dev(np.asarray(src_ck, np.int32)),
                    resumed.Sd, resumed.Xd, dev(resumed.init))

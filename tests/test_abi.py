@@ -64,6 +64,8 @@ def test_decode_validation():
     assert decode_call(cfg(conv_width=3)) == kda.KDA_ERR_UNSUPPORTED
     assert decode_call(cfg(act_dtype=7)) == kda.KDA_ERR_INVALID_ARG
     assert decode_call(cfg(num_heads=0)) == kda.KDA_ERR_INVALID_ARG
+    assert decode_call(cfg(state_dtype=2)) == kda.KDA_ERR_INVALID_ARG
+    assert "state_dtype" in kda.last_error()
     assert decode_call(cfg(l2_eps=float("nan"))) == kda.KDA_ERR_INVALID_ARG
     assert decode_call(cfg(), B=-1) == kda.KDA_ERR_INVALID_ARG
     assert decode_call(cfg(), num_slots=0) == kda.KDA_ERR_INVALID_ARG

@@ -54,12 +54,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def decode_bytes_per_launch(B, H, dk, dv, act_bytes=2):
+def decode_bytes_per_launch(B, H, dk, dv, act_bytes=2, state_bytes=4):
     """Algorithmic HBM bytes of one decode launch: per (sequence, head) the
-    fp32 state read + written, the conv state read + written, q/k/v/z in,
-    g and beta in, out; plus the conv and norm weights and the slot ids."""
+    state read + written (fp32 or bf16), the conv state read + written,
+    q/k/v/z in, g and beta in, out; plus the conv and norm weights and the
+    slot ids."""
     C = 2 * dk + dv
-    per = (2 * dk * dv * 4 + 2 * C * 3 * act_bytes + (2 * dk + 2 * dv) * act_bytes
+    per = (2 * dk * dv * state_bytes + 2 * C * 3 * act_bytes + (2 * dk + 2 * dv) * act_bytes
            + dk * 4 + 4 + dv * act_bytes)
     return B * H * per + H * C * 4 * 4 + dv * 4 + B * 4
 
@@ -93,9 +94,10 @@ def bench_decode(args):
     w = wl.WORKLOADS["decode_b64"]
     shape, B, nsteps, pool = w["shape"], w["B"], w["steps"], w["pool"]
     H, dk, dv = shape.H, shape.dk, shape.dv
-    cfg = kda.Config(H, dk, dv, kda.KDA_BF16)
+    bf16_state = args.state_dtype == "bf16"
+    cfg = kda.Config(H, dk, dv, kda.KDA_BF16, state_dtype=kda.KDA_BF16 if bf16_state else kda.KDA_F32)
     act = cfg.torch_act
-    log(f"[bench] generating decode inputs B={B} steps={nsteps} H={H} d={dk}")
+    log(f"[bench] generating decode inputs B={B} steps={nsteps} H={H} d={dk} state {args.state_dtype}")
     inp = wl.token_inputs(w["seed"], shape, B * nsteps)
     S, X = wl.states(w["seed"], shape, pool, state_std=w["state_std"], conv_std=w["conv_std"])
     slots = wl.slot_permutation(w["seed"], pool, B)
@@ -103,7 +105,7 @@ def bench_decode(args):
     q, k, v, z = (r(a).to(act).cuda() for a in (inp.q, inp.k, inp.v, inp.z))
     g, beta = r(inp.g).cuda(), r(inp.beta).cuda()
     conv_w, norm_w = torch.from_numpy(inp.conv_w).cuda(), torch.from_numpy(inp.norm_w).cuda()
-    Sd = torch.from_numpy(S).cuda()
+    Sd = torch.from_numpy(S).to(cfg.torch_state).cuda()
     Xd = torch.from_numpy(X).to(act).cuda()
     slot_d = torch.from_numpy(slots).cuda()
     out = torch.empty((nsteps, B, H, dv), dtype=act, device="cuda")
@@ -140,16 +142,16 @@ def bench_decode(args):
 
     tokens = B * nsteps * args.steps
     ms_per_step = total_ms / args.steps
-    nbytes = decode_bytes_per_launch(B, H, dk, dv)
+    nbytes = decode_bytes_per_launch(B, H, dk, dv, state_bytes=2 if bf16_state else 4)
     achieved = nbytes / launch_s
-    traffic = measured_traffic()
+    traffic = None if bf16_state else measured_traffic()
     res = {
         "value": tokens / (total_ms * 1e-3),
         "ms_per_step": ms_per_step,
         "wall_s": wall,
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK, "traffic": traffic,
-                     "kernel": "decode_kernel<128,128,bf16,256>",
+                     "kernel": "decode_kernel<128,128,bf16,%s,256>" % ("bf16" if bf16_state else "f32"),
                      "bytes_per_launch": nbytes, "mean_launch_us": launch_s * 1e6},
     }
     return res
@@ -407,6 +409,8 @@ def main():
     ap.add_argument("--cpu-sample-steps", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--state-dtype", choices=["f32", "bf16"], default="f32",
+                    help="stored state dtype of the decode workload (the workload is defined with f32)")
     ap.add_argument("--workload", choices=["decode_b64", "varlen_ckpt", "long_1m"], default="decode_b64",
                     help="decode_b64 (default): the headline line; the others report a larger prefill workload")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -453,8 +457,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "decode_b64: 64 seqs x 256 single-token steps, H=32, dk=dv=128, "
-                               "bf16 activations, fp32 state", "global_batch": 64, "seq_len": 256,
-                   "parallelism": "single GPU"},
+                               "bf16 activations, %s state" % ("bf16-stored" if args.state_dtype == "bf16" else "fp32"),
+                   "global_batch": 64, "seq_len": 256, "parallelism": "single GPU"},
         "roofline": res["roofline"],
     }
     if not args.no_prefill:

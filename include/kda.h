@@ -119,6 +119,34 @@ kda_status kda_decode_step(const kda_config* cfg, int32_t B,
                            const int32_t* slot, void* out, void* stream);
 
 /*
+ * T decode tokens for each of B sequences in ONE launch, for the verify pass
+ * of speculative decoding (K drafted tokens plus one).
+ * [agentlenshq "vLLM Kimi K3 Support", section "Speculative Decoding with
+ *  DSpark": the model is served with a drafting speculator; vLLM recipe
+ *  "moonshotai/Kimi-K3", section "AMD MI355X: disaggregated prefill and
+ *  decode": the decode worker drafts four tokens per step.]
+ *
+ * Inputs as kda_decode_step with a leading token axis: q, k, g [T][B][H][dk],
+ *   v, z, out [T][B][H][dv], beta [T][B][H] (token t of sequence b at [t][b]).
+ * The result equals T successive kda_decode_step calls bit for bit: the pool
+ *   slot ends with the state and conv state after all T tokens.
+ * token_state: NULL or [B][T][H][dk][dv] in the state dtype; token_conv: NULL
+ *   or [B][T][H][2dk+dv][3] in the activation dtype.  When given they receive
+ *   the state / conv state after every token, at slot b*T + t of a pool of
+ *   B*T slots.  Rolling sequence b back to its first a tokens (1 <= a <= T) is
+ *   then kda_resume from source slot b*T + a - 1 of those pools.
+ * A sequence whose slot id is outside the pool gets NaN outputs for all T
+ *   tokens and nothing written.  T >= 1; B == 0 is a no-op.
+ */
+kda_status kda_decode_multi(const kda_config* cfg, int32_t B, int32_t T,
+                            const void* q, const void* k, const void* v, const void* z,
+                            const float* g, const float* beta,
+                            const float* conv_w, const float* norm_w,
+                            void* state_pool, void* conv_pool, int32_t num_slots,
+                            const int32_t* slot, void* out,
+                            void* token_state, void* token_conv, void* stream);
+
+/*
  * Chunked prefill of num_seqs packed sequences (chunk = 64 tokens).
  * [vLLM blog, "KDA prefill and decode": the prefill gathers each request's
  *  initial recurrent state in one operation; "The Hardest Part": a resumable

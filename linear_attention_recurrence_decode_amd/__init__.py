@@ -27,7 +27,7 @@ KDA_PREFILL_SPLIT = 1
 
 # every symbol include/kda.h declares
 EXPORTS = (
-    "kda_decode_step", "kda_prefill_varlen", "kda_state_checkpoint", "kda_resume",
+    "kda_decode_step", "kda_decode_multi", "kda_prefill_varlen", "kda_state_checkpoint", "kda_resume",
     "kda_prefill_workspace_bytes", "kda_num_checkpoints", "kda_last_error",
 )
 
@@ -92,6 +92,7 @@ def lib():
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     CP = ctypes.POINTER(_Config)
     L.kda_decode_step.argtypes = [CP, I32] + [P] * 8 + [P, P, I32, P, P, P]
+    L.kda_decode_multi.argtypes = [CP, I32, I32] + [P] * 8 + [P, P, I32, P, P, P, P, P]
     L.kda_prefill_varlen.argtypes = ([CP, I32, I64, P, P] + [P] * 8 + [P, P, I32, P, P, I32, P, P, I32, P,
                                      I32, P, P, ctypes.c_size_t, P])
     L.kda_state_checkpoint.argtypes = [CP, I32, P, P, I32, P, P, P, I32, P, P]
@@ -101,7 +102,7 @@ def lib():
     L.kda_num_checkpoints.argtypes = [I64, I64, I32]
     L.kda_num_checkpoints.restype = I64
     L.kda_last_error.restype = ctypes.c_char_p
-    for f in ("kda_decode_step", "kda_prefill_varlen", "kda_state_checkpoint", "kda_resume"):
+    for f in ("kda_decode_step", "kda_decode_multi", "kda_prefill_varlen", "kda_state_checkpoint", "kda_resume"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -170,6 +171,31 @@ def kda_decode_step(cfg: Config, q, k, v, z, g, beta, conv_w, norm_w, state_pool
     _check(lib().kda_decode_step(ctypes.byref(cfg.c()), B, _ptr(q), _ptr(k), _ptr(v), _ptr(z),
                                  _ptr(g), _ptr(beta), _ptr(conv_w), _ptr(norm_w), _ptr(state_pool),
                                  _ptr(conv_pool), S, _ptr(slot), _ptr(out), _stream(stream)))
+    return out
+
+
+def kda_decode_multi(cfg: Config, q, k, v, z, g, beta, conv_w, norm_w, state_pool, conv_pool,
+                     slot, out, token_state=None, token_conv=None, stream=None):
+    """T decode tokens per sequence in one launch (see include/kda.h)."""
+    T, B = q.shape[0], slot.numel()
+    H, dk, dv, C = cfg.num_heads, cfg.head_k, cfg.head_v, cfg.conv_channels
+    act = cfg.torch_act
+    S = state_pool.shape[0]
+    _want(q, "q", act, (T, B, H, dk)); _want(k, "k", act, (T, B, H, dk))
+    _want(v, "v", act, (T, B, H, dv)); _want(z, "z", act, (T, B, H, dv))
+    _want(g, "g", torch.float32, (T, B, H, dk)); _want(beta, "beta", torch.float32, (T, B, H))
+    _want(conv_w, "conv_w", torch.float32, (H, C, 4)); _want(norm_w, "norm_w", torch.float32, (dv,))
+    _want(state_pool, "state_pool", cfg.torch_state, (S, H, dk, dv))
+    _want(conv_pool, "conv_pool", act, (S, H, C, 3))
+    _want(slot, "slot", torch.int32, (B,)); _want(out, "out", act, (T, B, H, dv))
+    if token_state is not None:
+        _want(token_state, "token_state", cfg.torch_state, (B, T, H, dk, dv))
+    if token_conv is not None:
+        _want(token_conv, "token_conv", act, (B, T, H, C, 3))
+    _check(lib().kda_decode_multi(ctypes.byref(cfg.c()), B, T, _ptr(q), _ptr(k), _ptr(v), _ptr(z),
+                                  _ptr(g), _ptr(beta), _ptr(conv_w), _ptr(norm_w), _ptr(state_pool),
+                                  _ptr(conv_pool), S, _ptr(slot), _ptr(out), _ptr(token_state),
+                                  _ptr(token_conv), _stream(stream)))
     return out
 
 

@@ -217,6 +217,255 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
     }
 }
 
+// T decode tokens per sequence in one launch (speculative verification: the
+// target model checks K drafted tokens plus one in a single pass).  The state
+// stays in registers across the tokens; token t runs exactly the arithmetic
+// of one decode_kernel step (with a bf16 state, the state is rounded after
+// every token, as a store and reload between steps would), so the results
+// equal T single-token launches bit for bit.  Optionally the state and conv
+// state after every token are written to token_state / token_conv (slot
+// b*T + t), from which a rejected draft is rolled back by a slot copy.
+// [agentlenshq "vLLM Kimi K3 Support", section "Speculative Decoding with
+//  DSpark": vLLM serves the model with a drafting speculator; vLLM recipe
+//  "moonshotai/Kimi-K3", section "AMD MI355X: disaggregated prefill and
+//  decode": the decode worker drafts four tokens per step.]
+template <int DK, int DV, typename ACT, typename ST, int NT>
+__global__ __launch_bounds__(NT) void decode_multi_kernel(DecodeParams p) {
+    constexpr int NCG = DV / 4;
+    constexpr int RG = NT / NCG;
+    constexpr int RPT = DK / RG;
+    constexpr int NW = NT / 64;
+    constexpr int C = 2 * DK + DV;
+    constexpr int CPT = (C + NT - 1) / NT;
+    using A = Act<ACT>;
+    constexpr uint32_t SB = sizeof(ST);
+
+    __shared__ float a_s[C];
+    __shared__ float eg_s[DK];
+    __shared__ float red_s[NW][2][DV];
+    __shared__ float nrm_s[NW][3];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int cg = tid % NCG, rg = tid / NCG;
+    const int H = p.H, B = p.B, T = p.T;
+    const int b = blockIdx.x / H, h = blockIdx.x % H;
+    const int64_t bh = static_cast<int64_t>(b) * H + h;
+    const int64_t step = static_cast<int64_t>(B) * H;     // one token of every (sequence, head)
+
+    ACT* out = static_cast<ACT*>(p.out) + bh * DV;
+    const int slot = p.slot[b];
+    if (slot < 0 || slot >= p.num_slots) {
+        for (int t = 0; t < T; t++)
+            for (int j = tid; j < DV; j += NT) A::st(out + t * step * DV + j, nan_f32());
+        return;
+    }
+    const int64_t sh = static_cast<int64_t>(slot) * H + h;
+
+    // conv window (raw, oldest first), weights, and the first token's operands
+    ACT* X = static_cast<ACT*>(p.conv) + sh * C * 3;
+    const float* w = p.conv_w + static_cast<int64_t>(h) * C * 4;
+    typename A::raw xin[CPT], x0[CPT], x1[CPT], x2[CPT];
+    float4 wc[CPT];
+    auto src_of = [&](int c, int t) -> const ACT* {
+        const int64_t o = t * step;
+        return c < DK ? static_cast<const ACT*>(p.q) + (o + bh) * DK + c
+                      : (c < 2 * DK ? static_cast<const ACT*>(p.k) + (o + bh) * DK + (c - DK)
+                                    : static_cast<const ACT*>(p.v) + (o + bh) * DV + (c - 2 * DK));
+    };
+#pragma unroll
+    for (int j = 0; j < CPT; j++) {
+        const int c = min(tid + j * NT, C - 1);
+        xin[j] = A::ld_raw(src_of(c, 0));
+        x0[j] = A::ld_raw(X + c * 3);
+        x1[j] = A::ld_raw(X + c * 3 + 1);
+        x2[j] = A::ld_raw(X + c * 3 + 2);
+        wc[j] = *reinterpret_cast<const float4*>(w + c * 4);
+    }
+    float gv = p.g[bh * DK + min(tid, DK - 1)];
+    float bt = p.beta[bh];
+    const float4 nw = *reinterpret_cast<const float4*>(p.norm_w + 4 * cg);
+    typename A::raw4 zraw = A::ld4_raw(static_cast<const ACT*>(p.z) + bh * DV + 4 * cg);
+
+    __builtin_amdgcn_sched_barrier(0);
+    const auto rs = make_rsrc(static_cast<ST*>(p.state) + sh * DK * DV, DK * DV * SB);
+    const uint32_t voff = static_cast<uint32_t>((rg * RPT * DV + 4 * cg) * SB);
+    float4 s[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; r++) {
+        if constexpr (SB == 4) s[r] = buf_ld4(rs, voff + (r % 8) * DV * 4, (r / 8) * 8 * DV * 4);
+        else s[r] = bf16x4_to_f32(buf_ld8(rs, voff + r * DV * 2));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    for (int t = 0; t < T; t++) {
+        // the next token's operands are requested now and used next iteration
+        const int tn = min(t + 1, T - 1);
+        typename A::raw xin_n[CPT];
+#pragma unroll
+        for (int j = 0; j < CPT; j++) xin_n[j] = A::ld_raw(src_of(min(tid + j * NT, C - 1), tn));
+        const float gv_n = p.g[(tn * step + bh) * DK + min(tid, DK - 1)];
+        const float bt_n = p.beta[tn * step + bh];
+        const typename A::raw4 zraw_n = A::ld4_raw(static_cast<const ACT*>(p.z) + (tn * step + bh) * DV + 4 * cg);
+
+        // conv + SiLU; the window shifts in registers
+#pragma unroll
+        for (int j = 0; j < CPT; j++) {
+            const int c = tid + j * NT;
+            if (c < C) {
+                const float f0 = A::cvt(x0[j]), f1 = A::cvt(x1[j]), f2 = A::cvt(x2[j]), fx = A::cvt(xin[j]);
+                float y = wc[j].x * f0;
+                y = fmaf(wc[j].y, f1, y);
+                y = fmaf(wc[j].z, f2, y);
+                y = fmaf(wc[j].w, fx, y);
+                a_s[c] = silu(y);
+            }
+            x0[j] = x1[j];
+            x1[j] = x2[j];
+            x2[j] = xin[j];
+        }
+        if (p.token_conv) {
+            ACT* tc = static_cast<ACT*>(p.token_conv) + ((static_cast<int64_t>(b) * T + t) * H + h) * C * 3;
+#pragma unroll
+            for (int j = 0; j < CPT; j++) {
+                const int c = tid + j * NT;
+                if (c < C) {
+                    reinterpret_cast<typename A::raw*>(tc + c * 3)[0] = x0[j];
+                    reinterpret_cast<typename A::raw*>(tc + c * 3)[1] = x1[j];
+                    reinterpret_cast<typename A::raw*>(tc + c * 3)[2] = x2[j];
+                }
+            }
+        }
+        if (tid < DK) eg_s[tid] = __expf(gv);
+        __syncthreads();
+
+        // L2 norms of q and k, and q.k
+        float pq = 0.f, pk = 0.f, pqk = 0.f;
+        for (int i = tid; i < DK; i += NT) {
+            const float aq = a_s[i], ak = a_s[DK + i];
+            pq = fmaf(aq, aq, pq);
+            pk = fmaf(ak, ak, pk);
+            pqk = fmaf(aq, ak, pqk);
+        }
+        pq = xor_sum_below<64>(pq);
+        pk = xor_sum_below<64>(pk);
+        pqk = xor_sum_below<64>(pqk);
+        if (lane == 0) {
+            nrm_s[wave][0] = pq;
+            nrm_s[wave][1] = pk;
+            nrm_s[wave][2] = pqk;
+        }
+        __syncthreads();
+        float sq = 0.f, sk = 0.f, sqk = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; w2++) {
+            sq += nrm_s[w2][0];
+            sk += nrm_s[w2][1];
+            sqk += nrm_s[w2][2];
+        }
+        const float rq = rsqrtf(sq + p.l2_eps);
+        const float rk = rsqrtf(sk + p.l2_eps);
+        const float qk = sqk * rq * rk;
+
+        // decay, then the two reductions over the decayed rows
+        float4 pred = make_float4(0.f, 0.f, 0.f, 0.f), rr = pred;
+#pragma unroll
+        for (int r = 0; r < RPT; r++) {
+            const int i = rg * RPT + r;
+            const float e = eg_s[i];
+            const float kh = a_s[DK + i] * rk;
+            const float qh = a_s[i] * rq;
+            s[r].x *= e; s[r].y *= e; s[r].z *= e; s[r].w *= e;
+            pred.x = fmaf(s[r].x, kh, pred.x); pred.y = fmaf(s[r].y, kh, pred.y);
+            pred.z = fmaf(s[r].z, kh, pred.z); pred.w = fmaf(s[r].w, kh, pred.w);
+            rr.x = fmaf(s[r].x, qh, rr.x); rr.y = fmaf(s[r].y, qh, rr.y);
+            rr.z = fmaf(s[r].z, qh, rr.z); rr.w = fmaf(s[r].w, qh, rr.w);
+        }
+        pred.x = xor_sum_from<NCG>(pred.x); pred.y = xor_sum_from<NCG>(pred.y);
+        pred.z = xor_sum_from<NCG>(pred.z); pred.w = xor_sum_from<NCG>(pred.w);
+        rr.x = xor_sum_from<NCG>(rr.x); rr.y = xor_sum_from<NCG>(rr.y);
+        rr.z = xor_sum_from<NCG>(rr.z); rr.w = xor_sum_from<NCG>(rr.w);
+        if (lane < NCG) {
+            *reinterpret_cast<float4*>(&red_s[wave][0][4 * cg]) = pred;
+            *reinterpret_cast<float4*>(&red_s[wave][1][4 * cg]) = rr;
+        }
+        __syncthreads();
+        pred = *reinterpret_cast<const float4*>(&red_s[0][0][4 * cg]);
+        rr = *reinterpret_cast<const float4*>(&red_s[0][1][4 * cg]);
+#pragma unroll
+        for (int w2 = 1; w2 < NW; w2++) {
+            const float4 a = *reinterpret_cast<const float4*>(&red_s[w2][0][4 * cg]);
+            const float4 c = *reinterpret_cast<const float4*>(&red_s[w2][1][4 * cg]);
+            pred.x += a.x; pred.y += a.y; pred.z += a.z; pred.w += a.w;
+            rr.x += c.x; rr.y += c.y; rr.z += c.z; rr.w += c.w;
+        }
+
+        // delta update and readout
+        const float4 vh = *reinterpret_cast<const float4*>(&a_s[2 * DK + 4 * cg]);
+        float4 u, o;
+        u.x = bt * (vh.x - pred.x); u.y = bt * (vh.y - pred.y);
+        u.z = bt * (vh.z - pred.z); u.w = bt * (vh.w - pred.w);
+        o.x = fmaf(u.x, qk, rr.x); o.y = fmaf(u.y, qk, rr.y);
+        o.z = fmaf(u.z, qk, rr.z); o.w = fmaf(u.w, qk, rr.w);
+
+        // S = S' + k u^T (rounded to the stored dtype: the next token starts
+        // from what a store would hold), optionally kept for rollback
+        const auto rt = make_rsrc(p.token_state ? static_cast<ST*>(p.token_state) +
+                                                      ((static_cast<int64_t>(b) * T + t) * H + h) * DK * DV
+                                                : static_cast<ST*>(p.state),
+                                  p.token_state ? DK * DV * SB : 0u);
+#pragma unroll
+        for (int r = 0; r < RPT; r++) {
+            const float kh = a_s[DK + rg * RPT + r] * rk;
+            s[r].x = fmaf(kh, u.x, s[r].x); s[r].y = fmaf(kh, u.y, s[r].y);
+            s[r].z = fmaf(kh, u.z, s[r].z); s[r].w = fmaf(kh, u.w, s[r].w);
+            if constexpr (SB == 2) {
+                const uint2 hb = f32_to_bf16x4(s[r]);
+                s[r] = bf16x4_to_f32(hb);
+                if (p.token_state) buf_st8(rt, voff + r * DV * 2, hb);
+            } else {
+                if (p.token_state) buf_st4(rt, voff + r * DV * 4, s[r]);
+            }
+        }
+
+        // gated RMSNorm over dv
+        float ss = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
+        ss = xor_sum_below<NCG>(ss);
+        if (rg == 0) {
+            const float rinv = rsqrtf(ss * (1.0f / DV) + p.rms_eps);
+            const float4 zz = A::cvt4(zraw);
+            float4 y;
+            y.x = o.x * rinv * nw.x * sigmoid(zz.x);
+            y.y = o.y * rinv * nw.y * sigmoid(zz.y);
+            y.z = o.z * rinv * nw.z * sigmoid(zz.z);
+            y.w = o.w * rinv * nw.w * sigmoid(zz.w);
+            A::st4(out + t * step * DV + 4 * cg, y);
+        }
+#pragma unroll
+        for (int j = 0; j < CPT; j++) xin[j] = xin_n[j];
+        gv = gv_n;
+        bt = bt_n;
+        zraw = zraw_n;
+        __syncthreads();        // a_s, eg_s and the reduction buffers are reused
+    }
+
+    // final state and conv window to the pool
+#pragma unroll
+    for (int r = 0; r < RPT; r++) {
+        if constexpr (SB == 4) buf_st4(rs, voff + r * DV * 4, s[r]);
+        else buf_st8(rs, voff + r * DV * 2, f32_to_bf16x4(s[r]));
+    }
+#pragma unroll
+    for (int j = 0; j < CPT; j++) {
+        const int c = tid + j * NT;
+        if (c < C) {
+            reinterpret_cast<typename A::raw*>(X + c * 3)[0] = x0[j];
+            reinterpret_cast<typename A::raw*>(X + c * 3)[1] = x1[j];
+            reinterpret_cast<typename A::raw*>(X + c * 3)[2] = x2[j];
+        }
+    }
+}
+
 template <int DK, int DV, typename ACT, typename ST, int NT>
 static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
     const int64_t blocks = static_cast<int64_t>(p.B) * p.H;
@@ -226,12 +475,22 @@ static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int DK, int DV, typename ACT, typename ST, int NT>
+static hipError_t launch_decode_multi_t(const DecodeParams& p, hipStream_t s) {
+    const int64_t blocks = static_cast<int64_t>(p.B) * p.H;
+    if (blocks == 0 || p.T == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_multi_kernel<DK, DV, ACT, ST, NT>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(NT), 0, s, p);
+    return hipGetLastError();
+}
+
 template <typename ACT, typename ST>
 static hipError_t launch_decode_d(int d, const DecodeParams& p, hipStream_t s) {
+    const bool multi = p.T != 1 || p.token_state || p.token_conv;
     switch (d) {
-        case 32:  return launch_decode_t<32, 32, ACT, ST, 64>(p, s);
-        case 64:  return launch_decode_t<64, 64, ACT, ST, 128>(p, s);
-        case 128: return launch_decode_t<128, 128, ACT, ST, 256>(p, s);
+        case 32:  return multi ? launch_decode_multi_t<32, 32, ACT, ST, 64>(p, s) : launch_decode_t<32, 32, ACT, ST, 64>(p, s);
+        case 64:  return multi ? launch_decode_multi_t<64, 64, ACT, ST, 128>(p, s) : launch_decode_t<64, 64, ACT, ST, 128>(p, s);
+        case 128: return multi ? launch_decode_multi_t<128, 128, ACT, ST, 256>(p, s) : launch_decode_t<128, 128, ACT, ST, 256>(p, s);
         default:  return hipErrorInvalidValue;
     }
 }

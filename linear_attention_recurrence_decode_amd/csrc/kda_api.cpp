@@ -128,16 +128,21 @@ int64_t kda_num_checkpoints(int64_t start, int64_t len, int32_t interval) {
     return (end - 1) / interval - start / interval + 1;
 }
 
-kda_status kda_decode_step(const kda_config* cfg, int32_t B, const void* q, const void* k, const void* v,
-                           const void* z, const float* g, const float* beta, const float* conv_w,
-                           const float* norm_w, void* state_pool, void* conv_pool, int32_t num_slots,
-                           const int32_t* slot, void* out, void* stream) {
+namespace {
+
+kda_status decode_common(const kda_config* cfg, int32_t B, int32_t T, const void* q, const void* k, const void* v,
+                         const void* z, const float* g, const float* beta, const float* conv_w,
+                         const float* norm_w, void* state_pool, void* conv_pool, int32_t num_slots,
+                         const int32_t* slot, void* out, void* token_state, void* token_conv, void* stream) {
     KDA_TRY(check_cfg(cfg));
     if (B < 0) return fail(KDA_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
+    if (T < 1) return fail(KDA_ERR_INVALID_ARG, "T must be >= 1 (got %d)", T);
     if (num_slots < 1) return fail(KDA_ERR_INVALID_ARG, "num_slots must be >= 1 (got %d)", num_slots);
     if (B == 0) return ok();
     if (static_cast<int64_t>(B) * cfg->num_heads > 0x7fffffffLL)
         return fail(KDA_ERR_INVALID_ARG, "B * num_heads exceeds the launch grid");
+    if (static_cast<int64_t>(B) * T * cfg->num_heads * cfg->head_v > 0x7fffffffffffLL)
+        return fail(KDA_ERR_INVALID_ARG, "B * T * num_heads * dv is too large");
     KDA_TRY(need_vec(q, "q"));
     KDA_TRY(need_vec(k, "k"));
     KDA_TRY(need_vec(v, "v"));
@@ -150,10 +155,15 @@ kda_status kda_decode_step(const kda_config* cfg, int32_t B, const void* q, cons
     KDA_TRY(need_vec(conv_pool, "conv_pool"));
     KDA_TRY(need_idx(slot, 4, "slot"));
     KDA_TRY(need_vec(out, "out"));
+    if (token_state) KDA_TRY(need_vec(token_state, "token_state"));
+    if (token_conv) KDA_TRY(need_vec(token_conv, "token_conv"));
     kda::DecodeParams p;
     p.B = B;
     p.H = cfg->num_heads;
     p.num_slots = num_slots;
+    p.T = T;
+    p.token_state = token_state;
+    p.token_conv = token_conv;
     p.q = q;
     p.k = k;
     p.v = v;
@@ -171,6 +181,24 @@ kda_status kda_decode_step(const kda_config* cfg, int32_t B, const void* q, cons
     return hip_status(kda::launch_decode(cfg->head_k, cfg->head_v, cfg->act_dtype, cfg->state_dtype, p,
                                          static_cast<hipStream_t>(stream)),
                       "decode launch");
+}
+
+}  // namespace
+
+kda_status kda_decode_step(const kda_config* cfg, int32_t B, const void* q, const void* k, const void* v,
+                           const void* z, const float* g, const float* beta, const float* conv_w,
+                           const float* norm_w, void* state_pool, void* conv_pool, int32_t num_slots,
+                           const int32_t* slot, void* out, void* stream) {
+    return decode_common(cfg, B, 1, q, k, v, z, g, beta, conv_w, norm_w, state_pool, conv_pool, num_slots, slot,
+                         out, nullptr, nullptr, stream);
+}
+
+kda_status kda_decode_multi(const kda_config* cfg, int32_t B, int32_t T, const void* q, const void* k,
+                            const void* v, const void* z, const float* g, const float* beta, const float* conv_w,
+                            const float* norm_w, void* state_pool, void* conv_pool, int32_t num_slots,
+                            const int32_t* slot, void* out, void* token_state, void* token_conv, void* stream) {
+    return decode_common(cfg, B, T, q, k, v, z, g, beta, conv_w, norm_w, state_pool, conv_pool, num_slots, slot,
+                         out, token_state, token_conv, stream);
 }
 
 namespace {

@@ -10,6 +10,9 @@ namespace kda {
 
 struct DecodeParams {
     int32_t B, H, num_slots;
+    int32_t T;          // tokens per sequence in this launch (1: one decode step)
+    void* token_state;  // [B][T][H][dk][dv] state after every token, or null
+    void* token_conv;   // [B][T][H][2dk+dv][3] conv state after every token, or null
     const void* q;
     const void* k;
     const void* v;

@@ -111,7 +111,22 @@ def bench_decode(args):
     out = torch.empty((nsteps, B, H, dv), dtype=act, device="cuda")
     stream = torch.cuda.current_stream()
 
+    T = args.multi_token
+    if T > 1:
+        # speculative verify: nsteps/T launches of T tokens, per-token states kept for rollback
+        assert nsteps % T == 0, "--multi-token must divide the step count"
+        mq, mk, mv, mz = (a.reshape((nsteps // T, T) + a.shape[1:]) for a in (q, k, v, z))
+        mg, mb = g.reshape((nsteps // T, T) + g.shape[1:]), beta.reshape((nsteps // T, T) + beta.shape[1:])
+        mout = out.reshape((nsteps // T, T) + out.shape[1:])
+        tstate = torch.empty((B, T, H, dk, dv), dtype=cfg.torch_state, device="cuda")
+        tconv = torch.empty((B, T, H, 2 * dk + dv, 3), dtype=act, device="cuda")
+
     def one_pass():
+        if T > 1:
+            for s in range(nsteps // T):
+                kda.kda_decode_multi(cfg, mq[s], mk[s], mv[s], mz[s], mg[s], mb[s], conv_w, norm_w, Sd, Xd,
+                                     slot_d, mout[s], token_state=tstate, token_conv=tconv, stream=stream)
+            return
         for s in range(nsteps):
             kda.kda_decode_step(cfg, q[s], k[s], v[s], z[s], g[s], beta[s], conv_w, norm_w, Sd, Xd,
                                 slot_d, out[s], stream=stream)
@@ -138,20 +153,29 @@ def bench_decode(args):
     # mean duration of one decode launch: the timed region's HIP-event time on
     # the launch stream divided by the number of launches (the launches are
     # back to back, so this is the kernel's own duration plus dispatch gaps)
-    launch_s = total_ms * 1e-3 / (args.steps * nsteps)
+    launch_s = total_ms * 1e-3 / (args.steps * nsteps // T)
 
     tokens = B * nsteps * args.steps
     ms_per_step = total_ms / args.steps
-    nbytes = decode_bytes_per_launch(B, H, dk, dv, state_bytes=2 if bf16_state else 4)
+    sb = 2 if bf16_state else 4
+    nbytes = decode_bytes_per_launch(B, H, dk, dv, state_bytes=sb)
+    if T > 1:
+        # per launch: state read once, written to the pool and to T per-token slots,
+        # conv state likewise, and T tokens of inputs and outputs
+        one = decode_bytes_per_launch(B, H, dk, dv, state_bytes=sb)
+        st_b, cv_b = B * H * dk * dv * sb, B * H * (2 * dk + dv) * 3 * 2
+        tok_b = one - 2 * st_b - 2 * cv_b - (H * (2 * dk + dv) * 4 * 4 + dv * 4 + B * 4)
+        nbytes = (2 + T) * st_b + (2 + T) * cv_b + T * tok_b + (H * (2 * dk + dv) * 4 * 4 + dv * 4 + B * 4)
     achieved = nbytes / launch_s
-    traffic = None if bf16_state else measured_traffic()
+    traffic = None if (bf16_state or T > 1) else measured_traffic()
     res = {
         "value": tokens / (total_ms * 1e-3),
         "ms_per_step": ms_per_step,
         "wall_s": wall,
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK, "traffic": traffic,
-                     "kernel": "decode_kernel<128,128,bf16,%s,256>" % ("bf16" if bf16_state else "f32"),
+                     "kernel": ("decode_multi_kernel<128,128,bf16,%s,256>, T=%d" % ("bf16" if bf16_state else "f32", T)
+                                if T > 1 else "decode_kernel<128,128,bf16,%s,256>" % ("bf16" if bf16_state else "f32")),
                      "bytes_per_launch": nbytes, "mean_launch_us": launch_s * 1e6},
     }
     return res
@@ -409,6 +433,8 @@ def main():
     ap.add_argument("--cpu-sample-steps", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--multi-token", type=int, default=1,
+                    help="decode T tokens per launch with per-token states kept (speculative verify); 1 = one step")
     ap.add_argument("--state-dtype", choices=["f32", "bf16"], default="f32",
                     help="stored state dtype of the decode workload (the workload is defined with f32)")
     ap.add_argument("--workload", choices=["decode_b64", "varlen_ckpt", "long_1m"], default="decode_b64",
@@ -457,7 +483,9 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "decode_b64: 64 seqs x 256 single-token steps, H=32, dk=dv=128, "
-                               "bf16 activations, %s state" % ("bf16-stored" if args.state_dtype == "bf16" else "fp32"),
+                               "bf16 activations, %s state%s" % ("bf16-stored" if args.state_dtype == "bf16" else "fp32",
+                                                                   ", %d tokens per launch with per-token states" % args.multi_token
+                                                                   if args.multi_token > 1 else ""),
                    "global_batch": 64, "seq_len": 256, "parallelism": "single GPU"},
         "roofline": res["roofline"],
     }

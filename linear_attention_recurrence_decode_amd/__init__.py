@@ -29,7 +29,13 @@ KDA_PREFILL_SPLIT = 1
 EXPORTS = (
     "kda_decode_step", "kda_decode_multi", "kda_prefill_varlen", "kda_state_checkpoint", "kda_resume",
     "kda_prefill_workspace_bytes", "kda_num_checkpoints", "kda_last_error",
+    # host-side prefix cache (include/kda_prefix_cache.h)
+    "kda_pcache_create", "kda_pcache_destroy", "kda_pcache_lookup", "kda_pcache_release",
+    "kda_pcache_reserve", "kda_pcache_insert", "kda_pcache_insert_many", "kda_pcache_unreserve",
+    "kda_pcache_commit",
+    "kda_pcache_stats", "kda_pcache_last_error",
 )
+KDA_PCACHE_KEEP_ALL, KDA_PCACHE_SECOND_HIT = 0, 1
 
 
 class KdaError(RuntimeError):
@@ -102,6 +108,22 @@ def lib():
     L.kda_num_checkpoints.argtypes = [I64, I64, I32]
     L.kda_num_checkpoints.restype = I64
     L.kda_last_error.restype = ctypes.c_char_p
+    L.kda_pcache_create.argtypes = [I32, I32, I32, I32]
+    L.kda_pcache_create.restype = P
+    L.kda_pcache_destroy.argtypes = [P]
+    L.kda_pcache_lookup.argtypes = [P, P, I64, P]
+    L.kda_pcache_lookup.restype = I64
+    L.kda_pcache_release.argtypes = [P, I32]
+    L.kda_pcache_reserve.argtypes = [P, I32, P]
+    L.kda_pcache_insert.argtypes = [P, P, I64, I32, I64]
+    L.kda_pcache_insert_many.argtypes = [P, P, I32, P, P, I64, P]
+    L.kda_pcache_unreserve.argtypes = [P, I32]
+    L.kda_pcache_commit.argtypes = [P, I64]
+    L.kda_pcache_stats.argtypes = [P, P, I32]
+    L.kda_pcache_last_error.restype = ctypes.c_char_p
+    for f in ("kda_pcache_release", "kda_pcache_reserve", "kda_pcache_insert", "kda_pcache_insert_many",
+              "kda_pcache_unreserve"):
+        getattr(L, f).restype = I32
     for f in ("kda_decode_step", "kda_decode_multi", "kda_prefill_varlen", "kda_state_checkpoint", "kda_resume"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
@@ -264,3 +286,86 @@ def kda_resume(cfg: Config, ckpt_state, ckpt_conv, src_ckpt, state_pool, conv_po
     """pool[dst_slot[i]] = ckpt[src_ckpt[i]] (copy-on-write resume)."""
     _copy(lib().kda_resume, cfg, ckpt_state, ckpt_conv, src_ckpt, state_pool, conv_pool,
           dst_slot, stream)
+
+
+class PrefixCache:
+    """Host-side prefix cache of KDA states over the slots of a state pool
+    (see include/kda_prefix_cache.h).  Token sequences are int32 arrays."""
+
+    STATS = ("entries", "free_slots", "pinned_slots", "hits", "misses", "evictions", "declined", "first_sightings")
+
+    def __init__(self, num_slots: int, unit: int, policy: int = KDA_PCACHE_KEEP_ALL, ghost_capacity: int = 0):
+        self._h = lib().kda_pcache_create(int(num_slots), int(unit), int(policy), int(ghost_capacity))
+        if not self._h:
+            raise KdaError(KDA_ERR_INVALID_ARG, lib().kda_pcache_last_error().decode())
+
+    def close(self):
+        if self._h:
+            lib().kda_pcache_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @staticmethod
+    def _toks(tokens):
+        import numpy as np
+        return np.ascontiguousarray(tokens, dtype=np.int32)
+
+    def _err(self, rc):
+        if rc < 0:
+            raise KdaError(KDA_ERR_INVALID_ARG, lib().kda_pcache_last_error().decode())
+        return rc
+
+    def lookup(self, tokens, max_len=None):
+        """(p, slot) of the longest visible cached prefix of tokens with p <= max_len
+        (default len(tokens)); (0, -1) on a miss.  A hit stays pinned until release()."""
+        t = self._toks(tokens)
+        n = len(t) if max_len is None else min(int(max_len), len(t))
+        slot = ctypes.c_int32(-1)
+        p = self._err(lib().kda_pcache_lookup(self._h, t.ctypes.data_as(ctypes.c_void_p), n, ctypes.byref(slot)))
+        return int(p), int(slot.value)
+
+    def release(self, slot: int):
+        self._err(lib().kda_pcache_release(self._h, int(slot)))
+
+    def reserve(self, n: int):
+        import numpy as np
+        out = np.zeros(max(int(n), 1), np.int32)
+        self._err(lib().kda_pcache_reserve(self._h, int(n), out.ctypes.data_as(ctypes.c_void_p)))
+        return out[:int(n)]
+
+    def unreserve(self, slot: int):
+        self._err(lib().kda_pcache_unreserve(self._h, int(slot)))
+
+    def insert(self, tokens, pos: int, slot: int, step: int) -> bool:
+        t = self._toks(tokens)
+        assert 1 <= pos <= len(t)
+        return bool(self._err(lib().kda_pcache_insert(self._h, t.ctypes.data_as(ctypes.c_void_p), int(pos), int(slot),
+                                                      int(step))))
+
+    def insert_many(self, tokens, positions, slots, step: int):
+        """Register the states after tokens[0:p] for every p in positions (increasing)
+        held in the reserved slots; returns a bool array (kept or declined)."""
+        import numpy as np
+        t = self._toks(tokens)
+        pos = np.ascontiguousarray(positions, dtype=np.int64)
+        sl = np.ascontiguousarray(slots, dtype=np.int32)
+        assert len(pos) == len(sl) and (len(pos) == 0 or pos[-1] <= len(t))
+        kept = np.zeros(max(len(pos), 1), np.int32)
+        self._err(lib().kda_pcache_insert_many(self._h, t.ctypes.data_as(ctypes.c_void_p), len(pos),
+                                               pos.ctypes.data_as(ctypes.c_void_p), sl.ctypes.data_as(ctypes.c_void_p),
+                                               int(step), kept.ctypes.data_as(ctypes.c_void_p)))
+        return kept[:len(pos)].astype(bool)
+
+    def commit(self, step: int):
+        lib().kda_pcache_commit(self._h, int(step))
+
+    def stats(self) -> dict:
+        import numpy as np
+        out = np.zeros(8, np.int64)
+        lib().kda_pcache_stats(self._h, out.ctypes.data_as(ctypes.c_void_p), 8)
+        return dict(zip(self.STATS, (int(x) for x in out)))

@@ -14,7 +14,7 @@ import linear_attention_recurrence_decode_amd as kda
 import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "kda.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("kda.h", "kda_prefix_cache.h")]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(kda.LIB_PATH), reason="libkda.so not built")
 
@@ -23,7 +23,7 @@ MISALIGNED = 0x10008
 
 
 def declared_functions():
-    src = open(HEADER).read()
+    src = "".join(open(h).read() for h in HEADERS)
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src)))
 

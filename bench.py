@@ -403,6 +403,37 @@ def bench_long(steps, warmup):
     return res
 
 
+def bench_project(steps, warmup):
+    """The input projections of the 4 x 8192 prefill: one bf16 GEMM per call."""
+    import torch
+    import linear_attention_recurrence_decode_amd as kda
+    import workloads as wl
+
+    w = wl.WORKLOADS["project_4x8k"]
+    shape, T, Dm = w["shape"], w["T"], w["Dm"]
+    H, dk, dv = shape.H, shape.dk, shape.dv
+    log(f"[bench] projection inputs T={T} Dm={Dm}")
+    x, wt = wl.projection_inputs(w["seed"], shape, T, Dm)
+    cfg = kda.Config(H, dk, dv, kda.KDA_BF16)
+    xd, wd = torch.from_numpy(x).to(torch.bfloat16).cuda(), torch.from_numpy(wt).to(torch.bfloat16).cuda()
+    del x, wt
+    q, k = (torch.empty((T, H, dk), dtype=torch.bfloat16, device="cuda") for _ in range(2))
+    v, z = (torch.empty((T, H, dv), dtype=torch.bfloat16, device="cuda") for _ in range(2))
+    g, beta = torch.empty((T, H, dk), device="cuda"), torch.empty((T, H), device="cuda")
+    stream = torch.cuda.current_stream()
+    t = _time_calls(lambda: kda.kda_project_inputs(cfg, xd, wd, q, k, v, z, g, beta, stream=stream), steps, warmup,
+                    stream)
+    N = kda.projection_rows(cfg)
+    flops = 2.0 * T * Dm * N
+    nbytes = (T * Dm + N * Dm) * 2 + T * H * (2 * dk + 2 * dv) * 2 + T * H * (dk + 1) * 4
+    return {"workload": f"project_4x8k: x [{T}][{Dm}] bf16 times W [{N}][{Dm}] bf16 (q, k, v, z, g, beta of "
+                        f"H={H}, dk=dv={dk})",
+            "value": flops / t / 1e12, "unit": "TFLOP/s", "ms_per_call": t * 1e3,
+            "roofline": {"bound": "mfma", "achieved": flops / t / 1e12, "peak": BF16_PEAK / 1e12, "unit": "TFLOP/s",
+                         "frac": flops / t / BF16_PEAK, "traffic": None, "alg_flops": flops, "alg_bytes": nbytes},
+            "tokens_per_s": T / t}
+
+
 def cpu_baseline(sample_steps: int):
     """The fp64 oracle on the first `sample_steps` steps of the decode
     workload (all 64 sequences, all 32 heads), timed on this host."""
@@ -437,7 +468,8 @@ def main():
                     help="decode T tokens per launch with per-token states kept (speculative verify); 1 = one step")
     ap.add_argument("--state-dtype", choices=["f32", "bf16"], default="f32",
                     help="stored state dtype of the decode workload (the workload is defined with f32)")
-    ap.add_argument("--workload", choices=["decode_b64", "varlen_ckpt", "long_1m"], default="decode_b64",
+    ap.add_argument("--workload", choices=["decode_b64", "varlen_ckpt", "long_1m", "project_4x8k"],
+                    default="decode_b64",
                     help="decode_b64 (default): the headline line; the others report a larger prefill workload")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a kernel of "
@@ -459,11 +491,16 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if args.workload != "decode_b64":
-        res = bench_varlen(args.steps, args.warmup) if args.workload == "varlen_ckpt" else \
-            bench_long(args.steps, args.warmup)
-        line = {"metric": "KDA prefill tok/s (" + args.workload + ")", "value": res["value"], "unit": "tok/s",
+        if args.workload == "project_4x8k":
+            res = bench_project(args.steps, args.warmup)
+        else:
+            res = bench_varlen(args.steps, args.warmup) if args.workload == "varlen_ckpt" else \
+                bench_long(args.steps, args.warmup)
+        metric = ("KDA input projections TFLOP/s (" if args.workload == "project_4x8k" else "KDA prefill tok/s (")
+        line = {"metric": metric + args.workload + ")", "value": res["value"], "unit": res.get("unit", "tok/s"),
                 "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
-                "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+                "scaling": "weak", "vs_baseline": None,
+                "dtype": "bf16" if args.workload == "project_4x8k" else "f32", "data": "synthetic",
                 "config": {"workload": res.pop("workload"), "parallelism": "single GPU"}}
         line.update({k: v for k, v in res.items() if k != "value"})
         print(json.dumps(line), flush=True)

@@ -212,6 +212,26 @@ kda_status kda_prefill_varlen(const kda_config* cfg, int32_t num_seqs, int64_t t
                               void* stream);
 
 /*
+ * Input projections of the layer for T tokens in one bf16 MFMA GEMM:
+ * y = x W^T, routed by rows of W to q, k (H dk each), v, z (H dv each), the
+ * decay gate (H dk: g = -softplus(y)) and beta (H: beta = sigmoid(y)).
+ * [vLLM blog, "KDA prefill and decode": the input projections are fused around
+ *  the recurrence.  The pages give no gate parameterisation; -softplus and the
+ *  logistic function of a linear pre-activation are the readings used here.]
+ *
+ * x: [T][Dm] bf16; w: [N][Dm] bf16 with N = H (3 dk + 2 dv) + H, rows in the
+ *   order q, k, v, z, g, beta (each head's channels consecutive).
+ * q, k: [T][H][dk], v, z: [T][H][dv] bf16 (RNE); g: [T][H][dk] fp32;
+ *   beta: [T][H] fp32 -- exactly the inputs kda_prefill_varlen and
+ *   kda_decode_step take.  Accumulation in fp32.
+ * Requires act_dtype == KDA_BF16 and Dm a positive multiple of 64.
+ */
+kda_status kda_project_inputs(const kda_config* cfg, int32_t T, int32_t Dm,
+                              const void* x, const void* w,
+                              void* q, void* k, void* v, void* z, float* g, float* beta,
+                              void* stream);
+
+/*
  * Copy n (state, conv state) slot pairs from the live pools to checkpoint
  * slots: ckpt[dst_ckpt[i]] = pool[src_slot[i]], bit for bit, all heads.
  * [vLLM blog, "The Hardest Part": the state registered at a boundary is kept

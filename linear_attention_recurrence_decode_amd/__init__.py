@@ -28,7 +28,7 @@ KDA_PREFILL_SPLIT = 1
 # every symbol include/kda.h declares
 EXPORTS = (
     "kda_decode_step", "kda_decode_multi", "kda_prefill_varlen", "kda_state_checkpoint", "kda_resume",
-    "kda_prefill_workspace_bytes", "kda_num_checkpoints", "kda_last_error",
+    "kda_project_inputs", "kda_prefill_workspace_bytes", "kda_num_checkpoints", "kda_last_error",
     # host-side prefix cache (include/kda_prefix_cache.h)
     "kda_pcache_create", "kda_pcache_destroy", "kda_pcache_lookup", "kda_pcache_release",
     "kda_pcache_reserve", "kda_pcache_insert", "kda_pcache_insert_many", "kda_pcache_unreserve",
@@ -99,6 +99,7 @@ def lib():
     CP = ctypes.POINTER(_Config)
     L.kda_decode_step.argtypes = [CP, I32] + [P] * 8 + [P, P, I32, P, P, P]
     L.kda_decode_multi.argtypes = [CP, I32, I32] + [P] * 8 + [P, P, I32, P, P, P, P, P]
+    L.kda_project_inputs.argtypes = [CP, I32, I32] + [P] * 9
     L.kda_prefill_varlen.argtypes = ([CP, I32, I64, P, P] + [P] * 8 + [P, P, I32, P, P, I32, P, P, I32, P,
                                      I32, P, P, ctypes.c_size_t, P])
     L.kda_state_checkpoint.argtypes = [CP, I32, P, P, I32, P, P, P, I32, P, P]
@@ -124,7 +125,8 @@ def lib():
     for f in ("kda_pcache_release", "kda_pcache_reserve", "kda_pcache_insert", "kda_pcache_insert_many",
               "kda_pcache_unreserve"):
         getattr(L, f).restype = I32
-    for f in ("kda_decode_step", "kda_decode_multi", "kda_prefill_varlen", "kda_state_checkpoint", "kda_resume"):
+    for f in ("kda_decode_step", "kda_decode_multi", "kda_prefill_varlen", "kda_state_checkpoint", "kda_resume",
+              "kda_project_inputs"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -219,6 +221,22 @@ def kda_decode_multi(cfg: Config, q, k, v, z, g, beta, conv_w, norm_w, state_poo
                                   _ptr(conv_pool), S, _ptr(slot), _ptr(out), _ptr(token_state),
                                   _ptr(token_conv), _stream(stream)))
     return out
+
+
+def projection_rows(cfg: Config) -> int:
+    return cfg.num_heads * (3 * cfg.head_k + 2 * cfg.head_v) + cfg.num_heads
+
+
+def kda_project_inputs(cfg: Config, x, w, q, k, v, z, g, beta, stream=None):
+    """Input projections y = x W^T routed to q, k, v, z, g, beta (see include/kda.h)."""
+    T, Dm = x.shape
+    H, dk, dv = cfg.num_heads, cfg.head_k, cfg.head_v
+    _want(x, "x", torch.bfloat16, (T, Dm)); _want(w, "w", torch.bfloat16, (projection_rows(cfg), Dm))
+    _want(q, "q", torch.bfloat16, (T, H, dk)); _want(k, "k", torch.bfloat16, (T, H, dk))
+    _want(v, "v", torch.bfloat16, (T, H, dv)); _want(z, "z", torch.bfloat16, (T, H, dv))
+    _want(g, "g", torch.float32, (T, H, dk)); _want(beta, "beta", torch.float32, (T, H))
+    _check(lib().kda_project_inputs(ctypes.byref(cfg.c()), T, Dm, _ptr(x), _ptr(w), _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(z), _ptr(g), _ptr(beta), _stream(stream)))
 
 
 def kda_prefill_varlen(cfg: Config, cu_seqlens, q, k, v, z, g, beta, conv_w, norm_w,

@@ -330,6 +330,43 @@ kda_status kda_prefill_varlen(const kda_config* cfg, int32_t num_seqs, int64_t t
                       "prefill launch");
 }
 
+kda_status kda_project_inputs(const kda_config* cfg, int32_t T, int32_t Dm, const void* x, const void* w, void* q,
+                              void* k, void* v, void* z, float* g, float* beta, void* stream) {
+    KDA_TRY(check_cfg(cfg));
+    if (cfg->act_dtype != KDA_BF16)
+        return fail(KDA_ERR_UNSUPPORTED, "input projections need bf16 activations (act_dtype = KDA_BF16)");
+    if (T < 0) return fail(KDA_ERR_INVALID_ARG, "T must be >= 0 (got %d)", T);
+    if (Dm < 64 || Dm % 64 != 0) return fail(KDA_ERR_INVALID_ARG, "Dm must be a positive multiple of 64 (got %d)", Dm);
+    const int64_t N = static_cast<int64_t>(cfg->num_heads) * (3 * cfg->head_k + 2 * cfg->head_v) + cfg->num_heads;
+    if (N * Dm * 2 >= (1LL << 31) * 2 || static_cast<int64_t>(T) * Dm * 2 >= (1LL << 40))
+        return fail(KDA_ERR_INVALID_ARG, "projection sizes too large");
+    if (T == 0) return ok();
+    KDA_TRY(need_vec(x, "x"));
+    KDA_TRY(need_vec(w, "w"));
+    KDA_TRY(need_vec(q, "q"));
+    KDA_TRY(need_vec(k, "k"));
+    KDA_TRY(need_vec(v, "v"));
+    KDA_TRY(need_vec(z, "z"));
+    KDA_TRY(need_vec(g, "g"));
+    KDA_TRY(need_idx(beta, 4, "beta"));
+    kda::ProjectParams p;
+    p.T = T;
+    p.N = static_cast<int32_t>(N);
+    p.Dm = Dm;
+    p.H = cfg->num_heads;
+    p.dk = cfg->head_k;
+    p.dv = cfg->head_v;
+    p.x = x;
+    p.w = w;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.z = z;
+    p.g = g;
+    p.beta = beta;
+    return hip_status(kda::launch_project(p, static_cast<hipStream_t>(stream)), "projection launch");
+}
+
 kda_status kda_state_checkpoint(const kda_config* cfg, int32_t n, const void* state_pool, const void* conv_pool,
                                 int32_t num_slots, const int32_t* src_slot, void* ckpt_state, void* ckpt_conv,
                                 int32_t num_ckpt_slots, const int32_t* dst_ckpt, void* stream) {

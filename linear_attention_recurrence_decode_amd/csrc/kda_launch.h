@@ -93,9 +93,24 @@ struct PrefillParams {
     int32_t state_bf16; // stored state in bf16 (rounded at every store; math in fp32)
 };
 
+// Input projections: y = x W^T routed to q, k, v, z (activation dtype) and
+// g, beta (fp32).
+struct ProjectParams {
+    int32_t T, N, Dm, H, dk, dv;
+    const void* x;      // [T][Dm] bf16
+    const void* w;      // [N][Dm] bf16
+    void* q;
+    void* k;
+    void* v;
+    void* z;
+    void* g;            // fp32
+    void* beta;         // fp32
+};
+
 // Each launcher returns hipSuccess or the launch error.
 hipError_t launch_decode(int dk, int dv, int act, int state, const DecodeParams& p, hipStream_t s);
 hipError_t launch_copy(const CopyParams& p, hipStream_t s);
+hipError_t launch_project(const ProjectParams& p, hipStream_t s);
 hipError_t launch_prefill(int dk, int dv, int act, const PrefillParams& p, hipStream_t s);
 bool prefill_supported(int dk, int dv, int act);
 

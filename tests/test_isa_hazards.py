@@ -18,7 +18,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "linear_attention_recurrence_decode_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["decode.hip", "prefill.hip", "copy.hip"]
+SOURCES = ["decode.hip", "prefill.hip", "copy.hip", "project.hip"]
 
 pytestmark = pytest.mark.skipif(not (os.path.exists(HIPCC) or shutil.which("hipcc")),
                                 reason="hipcc not available")

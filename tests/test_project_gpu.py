@@ -1,0 +1,93 @@
+"""GPU parity of the fused input projections (kda_project_inputs) against the
+fp64 projection oracle, and the projections composed with the prefill.
+
+Tolerances (relative L2, fp64): q, k, v, z are stored in bf16 (their rounding
+dominates: about 2e-3), bound 1e-2; g and beta are fp32 from an fp32-accumulated
+GEMM, bound 1e-5.  The composed path must match the oracle's projections
+rounded to bf16 and run through the oracle recurrence within the bf16 prefill
+tolerances.
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_recurrence_decode_amd as kda
+import oracle
+import workloads as wl
+from oracle import projection
+from tests.helpers import dev, host, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(shape, x, w):
+    cfg = kda.Config(shape.H, shape.dk, shape.dv, kda.KDA_BF16)
+    T = x.shape[0]
+    H, dk, dv = shape.H, shape.dk, shape.dv
+    xd, wd = dev(x, torch.bfloat16), dev(w, torch.bfloat16)
+    o = dict(q=torch.full((T, H, dk), float("nan"), dtype=torch.bfloat16, device="cuda"),
+             k=torch.full((T, H, dk), float("nan"), dtype=torch.bfloat16, device="cuda"),
+             v=torch.full((T, H, dv), float("nan"), dtype=torch.bfloat16, device="cuda"),
+             z=torch.full((T, H, dv), float("nan"), dtype=torch.bfloat16, device="cuda"),
+             g=torch.full((T, H, dk), float("nan"), device="cuda"),
+             beta=torch.full((T, H), float("nan"), device="cuda"))
+    kda.kda_project_inputs(cfg, xd, wd, o["q"], o["k"], o["v"], o["z"], o["g"], o["beta"])
+    torch.cuda.synchronize()
+    return o
+
+
+def check(o, ref, rows=None):
+    sel = slice(None) if rows is None else rows
+    for name in ("q", "k", "v", "z", "g", "beta"):
+        got = host(o[name])[sel]
+        e = rel_l2(got, ref[name])
+        tol = 1e-2 if name in "qkvz" else 1e-5
+        say(f"  {name}: rel-L2 {e:.3e} (tol {tol})")
+        assert np.isfinite(got).all() and e <= tol, name
+
+
+@pytest.mark.parametrize("H,d,T,Dm", [(2, 64, 300, 256), (4, 128, 1000, 1024), (3, 32, 129, 64)])
+def test_project_matches_oracle(H, d, T, Dm):
+    shape = wl.LayerShape(H, d, d)
+    say(f"projection H={H} d={d} T={T} Dm={Dm}")
+    x, w = wl.projection_inputs(50 + H, shape, T, Dm)
+    o = run_gpu(shape, x, w)
+    check(o, projection.project(x, w, H, d, d))
+
+
+def test_project_full_size_sampled_rows():
+    """The 4 x 8192 token projections (Dm 7168, H=32, d=128), every row on the
+    GPU, 96 sampled rows through the oracle."""
+    wk = wl.WORKLOADS["project_4x8k"]
+    shape, T, Dm = wk["shape"], wk["T"], wk["Dm"]
+    x, w = wl.projection_inputs(wk["seed"], shape, T, Dm)
+    o = run_gpu(shape, x, w)
+    rows = np.sort(np.random.default_rng(wk["seed"]).choice(T, 96, replace=False))
+    check(o, projection.project(x[rows], w, shape.H, shape.dk, shape.dv), rows)
+
+
+def test_projections_feed_the_prefill():
+    shape = wl.LayerShape(2, 64, 64)
+    lengths = [200, 77]
+    T, Dm = sum(lengths), 256
+    x, w = wl.projection_inputs(60, shape, T, Dm)
+    o = run_gpu(shape, x, w)
+    base = wl.token_inputs(60, shape, 1, norm_w="random")          # conv and norm weights
+    cfg = kda.Config(shape.H, shape.dk, shape.dv, kda.KDA_BF16)
+    N = len(lengths)
+    S = torch.zeros((2 * N, shape.H, shape.dk, shape.dv), device="cuda")
+    X = torch.zeros((2 * N, shape.H, shape.C, 3), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((T, shape.H, shape.dv), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(cfg, N, T), dtype=torch.uint8, device="cuda")
+    kda.kda_prefill_varlen(cfg, dev(wl.cu_seqlens(lengths).astype(np.int32)), o["q"], o["k"], o["v"], o["z"], o["g"],
+                           o["beta"], dev(base.conv_w), dev(base.norm_w), S, X, dev(np.full(N, -1, np.int32)),
+                           dev(np.arange(N, 2 * N, dtype=np.int32)), out, ws)
+    torch.cuda.synchronize()
+    p = projection.project(x, w, shape.H, shape.dk, shape.dv)
+    r16 = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    r = oracle.run(r16(p["q"]), r16(p["k"]), r16(p["v"]), r16(p["z"]), p["g"], p["beta"], base.conv_w, base.norm_w,
+                   wl.cu_seqlens(lengths))
+    e_o = rel_l2(host(out), r.out)
+    e_s = rel_l2(host(S)[N:], r.S)
+    say(f"  projections -> prefill: out {e_o:.3e} state {e_s:.3e}")
+    assert e_o <= 1e-2 and e_s <= 5e-3

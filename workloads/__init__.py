@@ -33,7 +33,7 @@ BLOCK_TOKENS = 4096
 TID = {
     "q": 1, "k": 2, "v": 3, "z": 4, "g": 5, "beta": 6,
     "conv_w": 7, "norm_w": 8, "state": 9, "conv_state": 10,
-    "lengths": 11, "slots": 12, "resume": 13,
+    "lengths": 11, "slots": 12, "resume": 13, "hidden": 14, "proj_w": 15,
 }
 
 
@@ -203,4 +203,18 @@ WORKLOADS = {
                         n=16, lo=1024, hi=65536, interval=4096),
     "long_1m": dict(seed=4, shape=LayerShape(H=8, dk=128, dv=128, act="bf16"),
                     lengths=[1 << 20], interval=32768, decode_B=256, decode_steps=512),
+    # input projections of the 4 x 8192 prefill: model width 7168 is a synthetic
+    # choice (the pages give none)
+    "project_4x8k": dict(seed=5, shape=LayerShape(H=32, dk=128, dv=128, act="bf16"), T=32768, Dm=7168),
 }
+
+
+def projection_inputs(seed: int, shape: LayerShape, T: int, Dm: int):
+    """Hidden states x ~ N(0, 1) [T][Dm] and packed projection weights
+    W ~ N(0, 1/Dm) [N][Dm] (so every pre-activation is about N(0, 1), as the
+    token inputs of token_inputs are), both rounded to bf16 and held as
+    float32.  N = H (3 dk + 2 dv) + H."""
+    N = shape.H * (3 * shape.dk + 2 * shape.dv) + shape.H
+    x = draw_tokens(seed, TID["hidden"], T, (Dm,), transform=round_bf16)
+    w = draw_tokens(seed, TID["proj_w"], N, (Dm,), std=float(Dm) ** -0.5, transform=round_bf16)
+    return x, w

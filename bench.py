@@ -48,6 +48,9 @@ BF16_PEAK = 2.5e15           # dense FLOP/s
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "decode_b64_traffic.json")
 DECODE_SOURCES = ["linear_attention_recurrence_decode_amd/csrc/decode.hip",
                   "linear_attention_recurrence_decode_amd/csrc/kda_device.h"]
+PROJECT_TRAFFIC = os.path.join(ROOT, "profiles", "project_4x8k_traffic.json")
+PROJECT_SOURCES = ["linear_attention_recurrence_decode_amd/csrc/project.hip",
+                   "linear_attention_recurrence_decode_amd/csrc/kda_device.h"]
 
 
 def log(*a):
@@ -73,15 +76,15 @@ def source_sha(paths):
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per decode launch from the committed rocprofv3 counter
+def measured_traffic(path=PROFILE_TRAFFIC, sources=DECODE_SOURCES):
+    """HBM bytes per launch of a kernel from its committed rocprofv3 counter
     summary, or None when it is missing or was taken on other kernel code."""
     try:
-        with open(PROFILE_TRAFFIC) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha") != source_sha(DECODE_SOURCES):
+    if rec.get("kernel_source_sha") != source_sha(sources):
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -426,12 +429,19 @@ def bench_project(steps, warmup):
     N = kda.projection_rows(cfg)
     flops = 2.0 * T * Dm * N
     nbytes = (T * Dm + N * Dm) * 2 + T * H * (2 * dk + 2 * dv) * 2 + T * H * (dk + 1) * 4
+    # context only: the library GEMM (torch.matmul) on the same bf16 product, without the routing and gate maps
+    wcol = wd.t().contiguous()
+    t_lib = _time_calls(lambda: torch.matmul(xd, wcol), steps, warmup, stream)
+    del wcol
     return {"workload": f"project_4x8k: x [{T}][{Dm}] bf16 times W [{N}][{Dm}] bf16 (q, k, v, z, g, beta of "
                         f"H={H}, dk=dv={dk})",
             "value": flops / t / 1e12, "unit": "TFLOP/s", "ms_per_call": t * 1e3,
             "roofline": {"bound": "mfma", "achieved": flops / t / 1e12, "peak": BF16_PEAK / 1e12, "unit": "TFLOP/s",
-                         "frac": flops / t / BF16_PEAK, "traffic": None, "alg_flops": flops, "alg_bytes": nbytes},
-            "tokens_per_s": T / t}
+                         "frac": flops / t / BF16_PEAK, "traffic": measured_traffic(PROJECT_TRAFFIC, PROJECT_SOURCES),
+                         "alg_flops": flops, "alg_bytes": nbytes},
+            "tokens_per_s": T / t,
+            "library_matmul": {"TFLOP/s": flops / t_lib / 1e12, "ms_per_call": t_lib * 1e3,
+                               "what": "torch.matmul of the same bf16 x and W^T (plain product, no epilogue)"}}
 
 
 def cpu_baseline(sample_steps: int):

@@ -9,14 +9,16 @@
 // activation dtype, g = -softplus(y) and beta = sigmoid(y) in fp32.  The row
 // blocks of W are q (H dk), k (H dk), v (H dv), z (H dv), g (H dk), beta (H).
 //
-// Tiling: 128 x 128 output tile per workgroup of 4 waves (2 x 2, each wave a
-// 64 x 64 block of four 32x32x16 MFMA tiles), K in steps of 64 staged through
-// two LDS buffers; the next step's tile is loaded into registers while the
-// current one feeds the MFMAs.  Rows of x past T and of W past N read as zero
-// through buffer resources.  Workgroups are mapped so that the tiles of one
-// XCD (workgroups are dealt round-robin over the 8 XCDs) form 8-row groups
-// sweeping N, so the concurrently running tiles of an XCD share panels of x
-// and W in that XCD's L2.
+// Tiling: a 256 x 256 output tile per workgroup of 8 waves (2 x 4, each wave
+// a 128 x 64 block of eight 32x32x16 MFMA tiles, two waves per SIMD), K in
+// steps of 64.  The x and W tiles of a step are copied from global memory
+// straight into LDS (buffer loads with the LDS destination bit, no register
+// staging) into one of two buffers while the other feeds the MFMAs; the LDS
+// rows are unpadded with an XOR swizzle of their 16-byte chunks, so that both
+// the copies (1 KiB contiguous per wave instruction) and the fragment reads
+// are free of bank conflicts.  Workgroups are mapped so that the tiles of one
+// XCD form groups of 4 row tiles sweeping N, sharing panels of x and W in
+// that XCD's L2.  The epilogue stages the fp32 results through LDS.
 
 #include "kda_device.h"
 #include "kda_launch.h"
@@ -27,9 +29,7 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_p;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
-constexpr int BM = 128, BN = 128, BK = 64, LS = BK + 8;   // LDS row stride (bf16), padded
-constexpr int NTH = 256;
-constexpr int XCDS = 8, GROUP_M = 8;
+constexpr int XCDS = 8, GROUP_M = 4;
 
 union V16 {
     uint4 u;
@@ -41,129 +41,255 @@ __device__ __forceinline__ float softplus_f(float y) {
     return fmaxf(y, 0.f) + log1pf(__expf(-fabsf(y)));
 }
 
-__global__ __launch_bounds__(NTH) void project_kernel(ProjectParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LS];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LS];
-
+// Output tile of this workgroup, or false past the last tile.  Workgroups are
+// dealt round-robin over the 8 XCDs, so the ids an XCD receives are made
+// consecutive; within an XCD, groups of GROUP_M row tiles sweep all column
+// tiles so that the concurrently running tiles share panels of x and W in
+// that XCD's L2.
+template <int BM, int BN>
+__device__ __forceinline__ bool tile_origin(const ProjectParams& p, int& m0, int& n0) {
     const int tiles_m = (p.T + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
-    // XCD-aware order: the workgroups an XCD receives get consecutive tile ids
     const int per_xcd = (tiles + XCDS - 1) / XCDS;
     const int b = blockIdx.x;
-    const int tid_lin = (b % XCDS) * per_xcd + b / XCDS;
-    if (tid_lin >= tiles) return;
-    // grouped order: GROUP_M row tiles sweep all column tiles
+    const int t = (b % XCDS) * per_xcd + b / XCDS;
+    if (t >= tiles) return false;
     const int in_group = GROUP_M * tiles_n;
-    const int gidx = tid_lin / in_group;
-    const int first_m = gidx * GROUP_M;
+    const int first_m = (t / in_group) * GROUP_M;
     const int gm = min(tiles_m - first_m, GROUP_M);
-    const int tm = first_m + (tid_lin % in_group) % gm;
-    const int tn = (tid_lin % in_group) / gm;
-    const int m0 = tm * BM, n0 = tn * BN;
+    m0 = (first_m + (t % in_group) % gm) * BM;
+    n0 = ((t % in_group) / gm) * BN;
+    return true;
+}
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+// Epilogue, one 32-row strip of the wave's block at a time: the fp32 tiles go
+// through LDS (element e of a 32x32 tile is at row 8(e/4) + 4(lane/32) + e%4,
+// column lane%32) and come back one row at a time, each lane owning fixed
+// columns, so that a column's routing (tensor, offset, gate map) is worked
+// out once and the gate maps are not unrolled over every element.  The tile
+// buffers must be free (all waves past their last read) on entry.
+template <int BM, int BN, int WM, int WN, int TI = BM / WM / 32, int TJ = BN / WN / 32>
+__device__ __forceinline__ void epilogue(const ProjectParams& p, const f32x16 (&acc)[TI][TJ], float* smem, int m0,
+                                         int n0) {
+    constexpr int RM = BM / WM, RN = BN / WN;
+    constexpr int WC = RN, EP = WC + 4, CT = WC / 64;
+    static_assert(WC % 64 == 0, "wave block width must be a multiple of 64");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lr = lane & 31;
+    const int wm = wave / WN, wn = wave % WN;
+    float* stage = smem + wave * 32 * EP;
+    const int H = p.H, dk = p.dk, dv = p.dv;
+    const int64_t bq = static_cast<int64_t>(H) * dk, bv = static_cast<int64_t>(H) * dv;
+    int kind[CT];
+    int64_t col[CT], width[CT];
+    void* dst[CT];
+#pragma unroll
+    for (int t = 0; t < CT; t++) {
+        const int64_t n = n0 + WC * wn + 64 * t + lane;
+        if (n >= p.N) { kind[t] = -1; col[t] = 0; width[t] = 0; }
+        else if (n < bq) { kind[t] = 0; col[t] = n; width[t] = bq; }
+        else if (n < 2 * bq) { kind[t] = 1; col[t] = n - bq; width[t] = bq; }
+        else if (n < 2 * bq + bv) { kind[t] = 2; col[t] = n - 2 * bq; width[t] = bv; }
+        else if (n < 2 * bq + 2 * bv) { kind[t] = 3; col[t] = n - 2 * bq - bv; width[t] = bv; }
+        else if (n < 3 * bq + 2 * bv) { kind[t] = 4; col[t] = n - 2 * bq - 2 * bv; width[t] = bq; }
+        else { kind[t] = 5; col[t] = n - 3 * bq - 2 * bv; width[t] = H; }
+        const int k = kind[t];
+        dst[t] = k == 0 ? p.q : k == 1 ? p.k : k == 2 ? p.v : k == 3 ? p.z : k == 4 ? p.g : p.beta;
+    }
+#pragma unroll
+    for (int i = 0; i < TI; i++) {
+#pragma unroll
+        for (int j = 0; j < TJ; j++)
+#pragma unroll
+            for (int e = 0; e < 16; e++)
+                stage[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * EP + 32 * j + lr] = acc[i][j][e];
+        __syncthreads();
+        const int mb = m0 + RM * wm + 32 * i;
+#pragma unroll 2
+        for (int r = 0; r < 32; r++) {
+            const int m = mb + r;
+            if (m >= p.T) break;
+#pragma unroll
+            for (int t = 0; t < CT; t++) {
+                const int k = kind[t];
+                if (k < 0) continue;
+                const float y = stage[r * EP + 64 * t + lane];
+                const int64_t o = static_cast<int64_t>(m) * width[t] + col[t];
+                if (k < 4) static_cast<uint16_t*>(dst[t])[o] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(y));
+                else if (k == 4) static_cast<float*>(dst[t])[o] = -softplus_f(y);
+                else static_cast<float*>(dst[t])[o] = sigmoid(y);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Physical 16-byte chunk of logical chunk c in row r of an unpadded LDS tile
+// with CPR chunks per row (XOR is its own inverse, so the same map takes a
+// physical chunk to its logical one).  For every aligned run of 8 rows, and
+// of 16 rows taken with the row's position in a 256-byte bank period, the
+// chunks read by one fragment load land in distinct banks.
+template <int CPR>
+__device__ __forceinline__ int swz(int r, int c) {
+    if constexpr (CPR == 8) return c ^ ((r ^ (r >> 3)) & 7);
+    else return c ^ (((r >> 1) ^ (r >> 3)) & 3);
+}
+
+// One wave copy of 1 KiB into LDS at byte address `lds` (uniform): lane L
+// loads 16 bytes at voff + soff of the buffer and writes them at lds + 16 L.
+// Issued as inline assembly, so that the compiler, which cannot tell which
+// LDS bytes such a copy writes, does not wait for the copies in flight before
+// every LDS read; the kernel waits for its copies itself, at the barriers.
+__device__ __forceinline__ void copy_to_lds(i32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+
+// Wait until this wave's copies have landed and its LDS reads have returned,
+// then a workgroup barrier: one unit that the compiler neither splits nor
+// moves memory accesses across.
+__device__ __forceinline__ void wait_copies_and_barrier() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
+
+__device__ __forceinline__ i32x4 raw_rsrc(const void* p, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    i32x4 r;
+    r[0] = static_cast<int32_t>(a);
+    r[1] = static_cast<int32_t>((a >> 32) & 0xffff);
+    r[2] = static_cast<int32_t>(bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// BM x BN output tile per workgroup of WM x WN waves, each wave a (BM/WM) x
+// (BN/WN) block of TI x TJ tiles of 32x32, K in steps of BK.  The global tiles
+// are copied straight into LDS (buffer_load ... lds, 16 bytes per lane: a wave
+// instruction fills 1 KiB of LDS contiguously), one step ahead, into two
+// buffers; no registers hold them.  Rows past T (or N) read the last valid
+// row instead; they only feed outputs that are never stored.
+template <int BM, int BN, int BK, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void project_kernel(ProjectParams p) {
+    constexpr int NW = WM * WN;
+    constexpr int RM = BM / WM, RN = BN / WN;
+    constexpr int TI = RM / 32, TJ = RN / 32;
+    constexpr int RB = 2 * BK, CPR = BK / 8;      // bytes and 16-byte chunks per row
+    constexpr int RPI = 1024 / RB;                // rows per wave copy instruction
+    constexpr int IA = BM / (RPI * NW), IB = BN / (RPI * NW);
+    static_assert(IA * RPI * NW == BM && IB * RPI * NW == BN, "tile rows must split evenly over the waves");
+    constexpr int SA = BM * RB, SS = (BM + BN) * RB;   // bytes: A part of a buffer, whole buffer
+    constexpr int KK = BK / 16;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * SS];
+
+    int m0, n0;
+    if (!tile_origin<BM, BN>(p, m0, n0)) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / WN, wn = wave % WN;
     const int K = p.Dm;
-
-    // tile loaders: 128 rows x 64 bf16 = 1024 16-byte units per operand, 4 per thread
-    const auto ra = make_rsrc(static_cast<const uint16_t*>(p.x) + static_cast<int64_t>(m0) * K,
-                              static_cast<uint32_t>(min(static_cast<int64_t>(BM), static_cast<int64_t>(p.T - m0)) * K * 2));
-    const auto rb = make_rsrc(static_cast<const uint16_t*>(p.w) + static_cast<int64_t>(n0) * K,
-                              static_cast<uint32_t>(min(static_cast<int64_t>(BN), static_cast<int64_t>(p.N - n0)) * K * 2));
-    uint4 ga[4], gb[4];
-    auto load = [&](int k0) {
+    const int va_rows = min(BM, p.T - m0), vb_rows = min(BN, p.N - n0);
+    const i32x4 ra = raw_rsrc(static_cast<const uint16_t*>(p.x) + static_cast<int64_t>(m0) * K,
+                              static_cast<uint32_t>(va_rows) * K * 2);
+    const i32x4 rb = raw_rsrc(static_cast<const uint16_t*>(p.w) + static_cast<int64_t>(n0) * K,
+                              static_cast<uint32_t>(vb_rows) * K * 2);
+    // per-lane global offsets (the step's k offset goes in soffset)
+    uint32_t oa[IA], ob[IB];
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int u = tid + j * NTH, r = u >> 3, c = (u & 7) * 8;
-            const uint32_t off = static_cast<uint32_t>((r * K + k0 + c) * 2);
-            const float4 fa = buf_ld4(ra, off, 0), fb = buf_ld4(rb, off, 0);
-            ga[j] = make_uint4(__float_as_uint(fa.x), __float_as_uint(fa.y), __float_as_uint(fa.z), __float_as_uint(fa.w));
-            gb[j] = make_uint4(__float_as_uint(fb.x), __float_as_uint(fb.y), __float_as_uint(fb.z), __float_as_uint(fb.w));
-        }
+    for (int j = 0; j < IA; j++) {
+        const int r = (wave * IA + j) * RPI + lane / CPR;
+        oa[j] = static_cast<uint32_t>((min(r, va_rows - 1) * K + 8 * swz<CPR>(r, lane % CPR)) * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < IB; j++) {
+        const int r = (wave * IB + j) * RPI + lane / CPR;
+        ob[j] = static_cast<uint32_t>((min(r, vb_rows - 1) * K + 8 * swz<CPR>(r, lane % CPR)) * 2);
+    }
+    const uint32_t lds0 = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)(smem)));
+    const int nk = K / BK;
+    auto issue = [&](int step) {
+        if (step >= nk) return;
+        const uint32_t st = __builtin_amdgcn_readfirstlane(lds0 + (step & 1) * SS + wave * (IA * 1024));
+        const uint32_t stb = __builtin_amdgcn_readfirstlane(lds0 + (step & 1) * SS + SA + wave * (IB * 1024));
+        const uint32_t soff = __builtin_amdgcn_readfirstlane(step * BK * 2);
+#pragma unroll
+        for (int j = 0; j < IA; j++) copy_to_lds(ra, st + j * 1024, oa[j], soff);
+#pragma unroll
+        for (int j = 0; j < IB; j++) copy_to_lds(rb, stb + j * 1024, ob[j], soff);
     };
-    auto commit = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int u = tid + j * NTH, r = u >> 3, c = (u & 7) * 8;
-            *reinterpret_cast<uint4*>(&As[buf][r * LS + c]) = ga[j];
-            *reinterpret_cast<uint4*>(&Bs[buf][r * LS + c]) = gb[j];
-        }
-    };
 
-    f32x16 acc[2][2];
+    f32x16 acc[TI][TJ];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < TI; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < TJ; j++)
 #pragma unroll
             for (int e = 0; e < 16; e++) acc[i][j][e] = 0.f;
 
-    const int nk = K / BK;
-    load(0);
-    commit(0);
-    __syncthreads();
-    const int lr = lane & 31, lk = 8 * (lane >> 5);
-    for (int ks = 0; ks < nk; ks++) {
-        const int cur = ks & 1;
-        if (ks + 1 < nk) load((ks + 1) * BK);
+    const int lr = lane & 31, hi = lane >> 5;
+    V16 fa[2][TI], fb[2][TJ];
+    auto frags = [&](int slot, const uint8_t* st, int q) {
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 16) {
-            V16 a[2], bb[2];
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-                a[i].u = *reinterpret_cast<const uint4*>(&As[cur][(64 * wm + 32 * i + lr) * LS + kk + lk]);
-#pragma unroll
-            for (int j = 0; j < 2; j++)
-                bb[j].u = *reinterpret_cast<const uint4*>(&Bs[cur][(64 * wn + 32 * j + lr) * LS + kk + lk]);
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-#pragma unroll
-                for (int j = 0; j < 2; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i].v, bb[j].v, acc[i][j], 0, 0, 0);
+        for (int i = 0; i < TI; i++) {
+            const int r = RM * wm + 32 * i + lr;
+            fa[slot][i].u = *reinterpret_cast<const uint4*>(st + r * RB + 16 * swz<CPR>(r, 2 * q + hi));
         }
-        if (ks + 1 < nk) commit(cur ^ 1);
-        __syncthreads();
-    }
+#pragma unroll
+        for (int j = 0; j < TJ; j++) {
+            const int r = RN * wn + 32 * j + lr;
+            fb[slot][j].u = *reinterpret_cast<const uint4*>(st + SA + r * RB + 16 * swz<CPR>(r, 2 * q + hi));
+        }
+    };
+    auto mma = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < TI; i++)
+#pragma unroll
+            for (int j = 0; j < TJ; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i].v, fb[slot][j].v, acc[i][j], 0, 0, 0);
+    };
 
-    // epilogue: column n of y -> its tensor; element e of a 32x32 tile is at
-    // row 8(e/4) + 4(lane/32) + e%4, column lane%32
-    const int H = p.H, dk = p.dk, dv = p.dv;
-    const int64_t bq = static_cast<int64_t>(H) * dk, bv = static_cast<int64_t>(H) * dv;
+    // Two buffers: the copy of step ks + 2 may only start once every wave has
+    // read its last fragments of step ks (same buffer), and step ks + 1 must
+    // have landed before its first fragments are read.  One barrier after the
+    // last fragment read of each step serves both; the MFMAs of that step's
+    // last sub-step, whose operands are already in registers, then cover the
+    // burst of first-fragment reads of step ks + 1 that follows the barrier.
+    issue(0);
+    wait_copies_and_barrier();
+    issue(1);
+    frags(0, smem, 0);
+    for (int ks = 0; ks < nk; ks++) {
+        const uint8_t* st = smem + (ks & 1) * SS;
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-        const int n = n0 + 64 * wn + 32 * j + lr;
-        if (n >= p.N) continue;
-        int kind;
-        int64_t col, width;
-        if (n < bq) { kind = 0; col = n; width = bq; }
-        else if (n < 2 * bq) { kind = 1; col = n - bq; width = bq; }
-        else if (n < 2 * bq + bv) { kind = 2; col = n - 2 * bq; width = bv; }
-        else if (n < 2 * bq + 2 * bv) { kind = 3; col = n - 2 * bq - bv; width = bv; }
-        else if (n < 3 * bq + 2 * bv) { kind = 4; col = n - 2 * bq - 2 * bv; width = bq; }
-        else { kind = 5; col = n - 3 * bq - 2 * bv; width = H; }
-        void* dst = kind == 0 ? p.q : kind == 1 ? p.k : kind == 2 ? p.v : kind == 3 ? p.z : kind == 4 ? p.g : p.beta;
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int e = 0; e < 16; e++) {
-                const int m = m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                if (m >= p.T) continue;
-                const float y = acc[i][j][e];
-                const int64_t o = static_cast<int64_t>(m) * width + col;
-                if (kind < 4) static_cast<uint16_t*>(dst)[o] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(y));
-                else if (kind == 4) static_cast<float*>(dst)[o] = -softplus_f(y);
-                else static_cast<float*>(dst)[o] = sigmoid(y);
-            }
+        for (int q = 0; q + 1 < KK; q++) {
+            frags((q + 1) & 1, st, q + 1);
+            mma(q & 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks + 1 < nk) {
+            wait_copies_and_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            frags(KK & 1, smem + ((ks + 1) & 1) * SS, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(ks + 2);
+        }
+        mma((KK - 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
     }
+    __syncthreads();
+    static_assert(NW * 32 * (RN + 4) * 4 <= sizeof(smem), "epilogue staging exceeds the tile buffers");
+    epilogue<BM, BN, WM, WN>(p, acc, reinterpret_cast<float*>(smem), m0, n0);
 }
 
 }  // namespace
 
 hipError_t launch_project(const ProjectParams& p, hipStream_t s) {
+    constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = 4;
     const int64_t tiles = static_cast<int64_t>((p.T + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     if (tiles == 0) return hipSuccess;
     const int64_t grid = (tiles + XCDS - 1) / XCDS * XCDS;
-    hipLaunchKernelGGL(project_kernel, dim3(static_cast<unsigned>(grid)), dim3(NTH), 0, s, p);
+    hipLaunchKernelGGL((project_kernel<BM, BN, BK, WM, WN>), dim3(static_cast<unsigned>(grid)), dim3(64 * WM * WN), 0,
+                       s, p);
     return hipGetLastError();
 }
 

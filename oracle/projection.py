@@ -15,6 +15,11 @@ pre-activation (H x dk) and beta's pre-activation (H), with
  the logistic function is the plainest reading that yields a log decay <= 0
  and a beta in (0, 1), and matches the workloads' synthetic distributions.]
 
+The output projection maps the layer's gated, normalised output o (H x dv
+per token) back to the model width: y = o W_o^T with W_o [Dm][H dv].  [The
+pages name no output projection; a linear map back to the model width is
+the plainest reading of a layer that sits in the model's residual stream.]
+
 Packed weight layout (one row per output channel, Dm contiguous):
   rows [0, H dk)              q      rows [H dk, 2 H dk)            k
   rows [2 H dk, 2 H dk + H dv) v     then H dv rows of z, H dk rows of the
@@ -56,3 +61,13 @@ def project(x, w, H: int, dk: int, dv: int):
     out["g"] = -softplus(out["g"])
     out["beta"] = sigmoid(y[:, o:o + H])
     return out
+
+
+def output(o, w_o):
+    """o [T][H][dv] (or [T][H dv]), w_o [Dm][H dv] -> y [T][Dm] = o W_o^T in
+    fp64 (the matmul is NumPy's, in fp64)."""
+    o = np.asarray(o, np.float64)
+    o = o.reshape(o.shape[0], -1)
+    w = np.asarray(w_o, np.float64)
+    assert w.shape[1] == o.shape[1]
+    return o @ w.T

@@ -1,5 +1,6 @@
-"""Pins for the input-projection oracle (oracle/projection.py): brute-force
-loops, the packed row order, and the gate activations' closed forms."""
+"""Pins for the projection oracle (oracle/projection.py): brute-force loops,
+the packed row order, the gate activations' closed forms, and the output
+projection's loops and selection weights."""
 import math
 
 import numpy as np
@@ -47,3 +48,25 @@ def test_selection_rows_and_gate_closed_forms():
     # large pre-activations: -softplus(a) -> -a, softplus(-a) -> exp(-a)
     big = projection.softplus(np.array([40.0, -40.0]))
     assert abs(big[0] - 40.0) < 1e-15 and abs(big[1] - math.exp(-40.0)) < 1e-30
+
+
+def test_output_projection_brute_force_and_selection():
+    rng = np.random.default_rng(101)
+    T, H, dv, Dm = 3, 2, 3, 4
+    o = rng.standard_normal((T, H, dv))
+    w = rng.standard_normal((Dm, H * dv))
+    y = projection.output(o, w)
+    assert y.shape == (T, Dm)
+    for t in range(T):
+        for m in range(Dm):
+            want = sum(o[t, h, j] * w[m, h * dv + j] for h in range(H) for j in range(dv))
+            assert abs(y[t, m] - want) <= 1e-12 * (1 + abs(want)), (t, m)
+    # one-hot rows: output m reads head h, channel j (head-major flattening of o)
+    sel = np.zeros((H * dv, H * dv))
+    for h in range(H):
+        for j in range(dv):
+            sel[j * H + h, h * dv + j] = 1.0         # output j*H+h <- (h, j)
+    ys = projection.output(o, sel)
+    for h in range(H):
+        for j in range(dv):
+            np.testing.assert_array_equal(ys[:, j * H + h], o[:, h, j])

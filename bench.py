@@ -407,7 +407,9 @@ def bench_long(steps, warmup):
 
 
 def bench_project(steps, warmup):
-    """The input projections of the 4 x 8192 prefill: one bf16 GEMM per call."""
+    """The input projections of the 4 x 8192 prefill: one bf16 GEMM per call
+    (the line's value); the output projection of the same tokens is timed
+    after it and reported beside it."""
     import torch
     import linear_attention_recurrence_decode_amd as kda
     import workloads as wl
@@ -432,7 +434,14 @@ def bench_project(steps, warmup):
     # context only: the library GEMM (torch.matmul) on the same bf16 product, without the routing and gate maps
     wcol = wd.t().contiguous()
     t_lib = _time_calls(lambda: torch.matmul(xd, wcol), steps, warmup, stream)
-    del wcol
+    del wcol, xd, wd, q, k, v, z, g, beta
+    # the output projection of the same tokens: o [T][H][dv] -> y [T][Dm]
+    o, wo = wl.output_projection_inputs(w["seed"], shape, T, Dm)
+    od, wod = torch.from_numpy(o).to(torch.bfloat16).cuda(), torch.from_numpy(wo).to(torch.bfloat16).cuda()
+    del o, wo
+    y = torch.empty((T, Dm), dtype=torch.bfloat16, device="cuda")
+    t_out = _time_calls(lambda: kda.kda_project_output(cfg, od, wod, y, stream=stream), steps, warmup, stream)
+    flops_out = 2.0 * T * (H * dv) * Dm
     return {"workload": f"project_4x8k: x [{T}][{Dm}] bf16 times W [{N}][{Dm}] bf16 (q, k, v, z, g, beta of "
                         f"H={H}, dk=dv={dk})",
             "value": flops / t / 1e12, "unit": "TFLOP/s", "ms_per_call": t * 1e3,
@@ -441,7 +450,10 @@ def bench_project(steps, warmup):
                          "alg_flops": flops, "alg_bytes": nbytes},
             "tokens_per_s": T / t,
             "library_matmul": {"TFLOP/s": flops / t_lib / 1e12, "ms_per_call": t_lib * 1e3,
-                               "what": "torch.matmul of the same bf16 x and W^T (plain product, no epilogue)"}}
+                               "what": "torch.matmul of the same bf16 x and W^T (plain product, no epilogue)"},
+            "output_projection": {"TFLOP/s": flops_out / t_out / 1e12, "ms_per_call": t_out * 1e3,
+                                  "frac": flops_out / t_out / BF16_PEAK,
+                                  "what": f"kda_project_output: o [{T}][{H * dv}] bf16 times W_o [{Dm}][{H * dv}] bf16"}}
 
 
 def cpu_baseline(sample_steps: int):

@@ -232,6 +232,20 @@ kda_status kda_project_inputs(const kda_config* cfg, int32_t T, int32_t Dm,
                               void* stream);
 
 /*
+ * Output projection of the layer for T tokens in one bf16 MFMA GEMM:
+ * y = o W_o^T, from the layer's gated, normalised output back to the model
+ * width.  [The pages name no output projection; a linear map back to the
+ *  model width is the plain reading of a layer in the residual stream.]
+ *
+ * o: [T][H][dv] bf16 (the `out` of kda_prefill_varlen / kda_decode_step);
+ * w_o: [Dm][H dv] bf16; y: [T][Dm] bf16 (RNE).  Accumulation in fp32.
+ * Requires act_dtype == KDA_BF16 and H dv a multiple of 64; o and w_o
+ * 16-byte aligned, y 2-byte aligned.  Any Dm >= 1.
+ */
+kda_status kda_project_output(const kda_config* cfg, int32_t T, int32_t Dm,
+                              const void* o, const void* w_o, void* y, void* stream);
+
+/*
  * Copy n (state, conv state) slot pairs from the live pools to checkpoint
  * slots: ckpt[dst_ckpt[i]] = pool[src_slot[i]], bit for bit, all heads.
  * [vLLM blog, "The Hardest Part": the state registered at a boundary is kept

@@ -28,7 +28,7 @@ KDA_PREFILL_SPLIT = 1
 # every symbol include/kda.h declares
 EXPORTS = (
     "kda_decode_step", "kda_decode_multi", "kda_prefill_varlen", "kda_state_checkpoint", "kda_resume",
-    "kda_project_inputs", "kda_prefill_workspace_bytes", "kda_num_checkpoints", "kda_last_error",
+    "kda_project_inputs", "kda_project_output", "kda_prefill_workspace_bytes", "kda_num_checkpoints", "kda_last_error",
     # host-side prefix cache (include/kda_prefix_cache.h)
     "kda_pcache_create", "kda_pcache_destroy", "kda_pcache_lookup", "kda_pcache_release",
     "kda_pcache_reserve", "kda_pcache_insert", "kda_pcache_insert_many", "kda_pcache_unreserve",
@@ -100,6 +100,7 @@ def lib():
     L.kda_decode_step.argtypes = [CP, I32] + [P] * 8 + [P, P, I32, P, P, P]
     L.kda_decode_multi.argtypes = [CP, I32, I32] + [P] * 8 + [P, P, I32, P, P, P, P, P]
     L.kda_project_inputs.argtypes = [CP, I32, I32] + [P] * 9
+    L.kda_project_output.argtypes = [CP, I32, I32, P, P, P, P]
     L.kda_prefill_varlen.argtypes = ([CP, I32, I64, P, P] + [P] * 8 + [P, P, I32, P, P, I32, P, P, I32, P,
                                      I32, P, P, ctypes.c_size_t, P])
     L.kda_state_checkpoint.argtypes = [CP, I32, P, P, I32, P, P, P, I32, P, P]
@@ -126,7 +127,7 @@ def lib():
               "kda_pcache_unreserve"):
         getattr(L, f).restype = I32
     for f in ("kda_decode_step", "kda_decode_multi", "kda_prefill_varlen", "kda_state_checkpoint", "kda_resume",
-              "kda_project_inputs"):
+              "kda_project_inputs", "kda_project_output"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -237,6 +238,17 @@ def kda_project_inputs(cfg: Config, x, w, q, k, v, z, g, beta, stream=None):
     _want(g, "g", torch.float32, (T, H, dk)); _want(beta, "beta", torch.float32, (T, H))
     _check(lib().kda_project_inputs(ctypes.byref(cfg.c()), T, Dm, _ptr(x), _ptr(w), _ptr(q), _ptr(k), _ptr(v),
                                     _ptr(z), _ptr(g), _ptr(beta), _stream(stream)))
+
+
+def kda_project_output(cfg: Config, o, w_o, y, stream=None):
+    """Output projection y = o W_o^T (see include/kda.h): o [T][H][dv] bf16,
+    w_o [Dm][H dv] bf16, y [T][Dm] bf16."""
+    T = o.shape[0]
+    H, dv = cfg.num_heads, cfg.head_v
+    Dm = w_o.shape[0]
+    _want(o, "o", torch.bfloat16, (T, H, dv)); _want(w_o, "w_o", torch.bfloat16, (Dm, H * dv))
+    _want(y, "y", torch.bfloat16, (T, Dm))
+    _check(lib().kda_project_output(ctypes.byref(cfg.c()), T, Dm, _ptr(o), _ptr(w_o), _ptr(y), _stream(stream)))
 
 
 def kda_prefill_varlen(cfg: Config, cu_seqlens, q, k, v, z, g, beta, conv_w, norm_w,

@@ -349,10 +349,11 @@ kda_status kda_project_inputs(const kda_config* cfg, int32_t T, int32_t Dm, cons
     KDA_TRY(need_vec(z, "z"));
     KDA_TRY(need_vec(g, "g"));
     KDA_TRY(need_idx(beta, 4, "beta"));
-    kda::ProjectParams p;
+    kda::ProjectParams p{};
     p.T = T;
     p.N = static_cast<int32_t>(N);
     p.Dm = Dm;
+    p.mode = 0;
     p.H = cfg->num_heads;
     p.dk = cfg->head_k;
     p.dv = cfg->head_v;
@@ -365,6 +366,37 @@ kda_status kda_project_inputs(const kda_config* cfg, int32_t T, int32_t Dm, cons
     p.g = g;
     p.beta = beta;
     return hip_status(kda::launch_project(p, static_cast<hipStream_t>(stream)), "projection launch");
+}
+
+kda_status kda_project_output(const kda_config* cfg, int32_t T, int32_t Dm, const void* o, const void* w_o, void* y,
+                              void* stream) {
+    KDA_TRY(check_cfg(cfg));
+    if (cfg->act_dtype != KDA_BF16)
+        return fail(KDA_ERR_UNSUPPORTED, "the output projection needs bf16 activations (act_dtype = KDA_BF16)");
+    if (T < 0) return fail(KDA_ERR_INVALID_ARG, "T must be >= 0 (got %d)", T);
+    if (Dm < 1) return fail(KDA_ERR_INVALID_ARG, "Dm must be >= 1 (got %d)", Dm);
+    const int64_t K = static_cast<int64_t>(cfg->num_heads) * cfg->head_v;
+    if (K % 64 != 0)
+        return fail(KDA_ERR_UNSUPPORTED, "the output projection needs num_heads * head_v to be a multiple of 64 (got %lld)",
+                    static_cast<long long>(K));
+    if (static_cast<int64_t>(Dm) * K * 2 >= (1LL << 32) || static_cast<int64_t>(T) * K * 2 >= (1LL << 40))
+        return fail(KDA_ERR_INVALID_ARG, "projection sizes too large");
+    if (T == 0) return ok();
+    KDA_TRY(need_vec(o, "o"));
+    KDA_TRY(need_vec(w_o, "w_o"));
+    KDA_TRY(need_idx(y, 2, "y"));
+    kda::ProjectParams p{};
+    p.T = T;
+    p.N = Dm;
+    p.Dm = static_cast<int32_t>(K);
+    p.H = cfg->num_heads;
+    p.dk = cfg->head_k;
+    p.dv = cfg->head_v;
+    p.mode = 1;
+    p.x = o;
+    p.w = w_o;
+    p.y = y;
+    return hip_status(kda::launch_project(p, static_cast<hipStream_t>(stream)), "output projection launch");
 }
 
 kda_status kda_state_checkpoint(const kda_config* cfg, int32_t n, const void* state_pool, const void* conv_pool,

@@ -97,6 +97,7 @@ struct PrefillParams {
 // g, beta (fp32).
 struct ProjectParams {
     int32_t T, N, Dm, H, dk, dv;
+    int32_t mode;       // 0: input projections (columns routed to q..beta), 1: plain product into y
     const void* x;      // [T][Dm] bf16
     const void* w;      // [N][Dm] bf16
     void* q;
@@ -105,6 +106,7 @@ struct ProjectParams {
     void* z;
     void* g;            // fp32
     void* beta;         // fp32
+    void* y;            // mode 1: [T][N] bf16
 };
 
 // Each launcher returns hipSuccess or the launch error.

@@ -8,6 +8,8 @@
 // column to its tensor and applies the gate maps: q, k, v, z stored in the
 // activation dtype, g = -softplus(y) and beta = sigmoid(y) in fp32.  The row
 // blocks of W are q (H dk), k (H dk), v (H dv), z (H dv), g (H dk), beta (H).
+// The same kernel in its second mode is the output projection: the layer's
+// output o [T][H dv] times W_o [Dm][H dv]^T, stored as bf16 [T][Dm].
 //
 // Tiling: a 256 x 256 output tile per workgroup of 8 waves (2 x 4, each wave
 // a 128 x 64 block of eight 32x32x16 MFMA tiles, two waves per SIMD), K in
@@ -86,6 +88,7 @@ __device__ __forceinline__ void epilogue(const ProjectParams& p, const f32x16 (&
     for (int t = 0; t < CT; t++) {
         const int64_t n = n0 + WC * wn + 64 * t + lane;
         if (n >= p.N) { kind[t] = -1; col[t] = 0; width[t] = 0; }
+        else if (p.mode == 1) { kind[t] = 0; col[t] = n; width[t] = p.N; }
         else if (n < bq) { kind[t] = 0; col[t] = n; width[t] = bq; }
         else if (n < 2 * bq) { kind[t] = 1; col[t] = n - bq; width[t] = bq; }
         else if (n < 2 * bq + bv) { kind[t] = 2; col[t] = n - 2 * bq; width[t] = bv; }
@@ -93,7 +96,7 @@ __device__ __forceinline__ void epilogue(const ProjectParams& p, const f32x16 (&
         else if (n < 3 * bq + 2 * bv) { kind[t] = 4; col[t] = n - 2 * bq - 2 * bv; width[t] = bq; }
         else { kind[t] = 5; col[t] = n - 3 * bq - 2 * bv; width[t] = H; }
         const int k = kind[t];
-        dst[t] = k == 0 ? p.q : k == 1 ? p.k : k == 2 ? p.v : k == 3 ? p.z : k == 4 ? p.g : p.beta;
+        dst[t] = p.mode == 1 ? p.y : k == 0 ? p.q : k == 1 ? p.k : k == 2 ? p.v : k == 3 ? p.z : k == 4 ? p.g : p.beta;
     }
 #pragma unroll
     for (int i = 0; i < TI; i++) {

@@ -148,3 +148,41 @@ def test_num_checkpoints_matches_oracle_rule():
         length = int(rng.integers(0, 1 << 16))
         interval = int(rng.choice([0, 64, 128, 4096, 32768]))
         assert kda.kda_num_checkpoints(start, length, interval) == oracle.num_checkpoints(start, length, interval)
+
+
+def project_in_call(c, T=4, Dm=256, **ptrs):
+    P = {n: FAKE for n in ("x", "w", "q", "k", "v", "z", "g", "beta")}
+    P.update(ptrs)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return kda.lib().kda_project_inputs(ctypes.byref(c.c()), T, Dm, *(vp(P[n]) for n in
+                                        ("x", "w", "q", "k", "v", "z", "g", "beta")), None)
+
+
+def project_out_call(c, T=4, Dm=7168, **ptrs):
+    P = {n: FAKE for n in ("o", "w_o", "y")}
+    P.update(ptrs)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return kda.lib().kda_project_output(ctypes.byref(c.c()), T, Dm, vp(P["o"]), vp(P["w_o"]), vp(P["y"]), None)
+
+
+def test_projection_validation():
+    assert project_in_call(cfg(act_dtype=kda.KDA_F32)) == kda.KDA_ERR_UNSUPPORTED
+    assert project_in_call(cfg(), Dm=100) == kda.KDA_ERR_INVALID_ARG
+    assert project_in_call(cfg(), Dm=0) == kda.KDA_ERR_INVALID_ARG
+    assert project_in_call(cfg(), T=-1) == kda.KDA_ERR_INVALID_ARG
+    for name in ("x", "w", "q", "k", "v", "z", "g", "beta"):
+        assert project_in_call(cfg(), **{name: None}) == kda.KDA_ERR_INVALID_ARG, name
+    assert project_in_call(cfg(), w=MISALIGNED) == kda.KDA_ERR_INVALID_ARG
+    assert project_in_call(cfg(), T=0, x=None) == kda.KDA_OK
+
+    assert project_out_call(cfg(act_dtype=kda.KDA_F32)) == kda.KDA_ERR_UNSUPPORTED
+    assert project_out_call(cfg(num_heads=1, head_k=32, head_v=32)) == kda.KDA_ERR_UNSUPPORTED   # H dv = 32
+    assert "multiple of 64" in kda.last_error()
+    assert project_out_call(cfg(), Dm=0) == kda.KDA_ERR_INVALID_ARG
+    assert project_out_call(cfg(), T=-1) == kda.KDA_ERR_INVALID_ARG
+    for name in ("o", "w_o", "y"):
+        assert project_out_call(cfg(), **{name: None}) == kda.KDA_ERR_INVALID_ARG, name
+    assert project_out_call(cfg(), o=MISALIGNED) == kda.KDA_ERR_INVALID_ARG
+    assert project_out_call(cfg(), y=FAKE + 1) == kda.KDA_ERR_INVALID_ARG
+    assert project_out_call(cfg(), T=0, o=None) == kda.KDA_OK
+    assert kda.last_error() == ""

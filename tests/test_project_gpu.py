@@ -1,11 +1,12 @@
-"""GPU parity of the fused input projections (kda_project_inputs) against the
-fp64 projection oracle, and the projections composed with the prefill.
+"""GPU parity of the fused input projections (kda_project_inputs) and the
+output projection (kda_project_output) against the fp64 projection oracle,
+and of both composed with the prefill.
 
-Tolerances (relative L2, fp64): q, k, v, z are stored in bf16 (their rounding
-dominates: about 2e-3), bound 1e-2; g and beta are fp32 from an fp32-accumulated
-GEMM, bound 1e-5.  The composed path must match the oracle's projections
-rounded to bf16 and run through the oracle recurrence within the bf16 prefill
-tolerances.
+Tolerances (relative L2, fp64): q, k, v, z and y are stored in bf16 (their
+rounding dominates: about 1e-3 to 2e-3), bound 1e-2; g and beta are fp32 from
+an fp32-accumulated GEMM, bound 1e-5.  The composed path must match the
+oracle's projections rounded to bf16 and run through the oracle recurrence
+within the bf16 prefill tolerances.
 """
 import numpy as np
 import pytest
@@ -34,6 +35,14 @@ def run_gpu(shape, x, w):
     kda.kda_project_inputs(cfg, xd, wd, o["q"], o["k"], o["v"], o["z"], o["g"], o["beta"])
     torch.cuda.synchronize()
     return o
+
+
+def run_output_gpu(shape, o, w):
+    cfg = kda.Config(shape.H, shape.dk, shape.dv, kda.KDA_BF16)
+    y = torch.full((o.shape[0], w.shape[0]), float("nan"), dtype=torch.bfloat16, device="cuda")
+    kda.kda_project_output(cfg, dev(o, torch.bfloat16), dev(w, torch.bfloat16), y)
+    torch.cuda.synchronize()
+    return y
 
 
 def check(o, ref, rows=None):
@@ -66,6 +75,30 @@ def test_project_full_size_sampled_rows():
     check(o, projection.project(x[rows], w, shape.H, shape.dk, shape.dv), rows)
 
 
+@pytest.mark.parametrize("H,dv,T,Dm", [(2, 64, 300, 200), (4, 128, 1000, 1024), (1, 64, 129, 7), (3, 64, 257, 513)])
+def test_output_projection_matches_oracle(H, dv, T, Dm):
+    shape = wl.LayerShape(H, dv, dv)
+    say(f"output projection H={H} dv={dv} T={T} Dm={Dm}")
+    o, w = wl.output_projection_inputs(70 + H, shape, T, Dm)
+    y = host(run_output_gpu(shape, o, w))
+    e = rel_l2(y, projection.output(o, w))
+    say(f"  y: rel-L2 {e:.3e} (tol 1e-2)")
+    assert np.isfinite(y).all() and e <= 1e-2
+
+
+def test_output_projection_full_size_sampled_rows():
+    """The 4 x 8192 token output projection (H=32, dv=128 -> Dm 7168), every
+    row on the GPU, 96 sampled rows through the oracle."""
+    wk = wl.WORKLOADS["project_4x8k"]
+    shape, T, Dm = wk["shape"], wk["T"], wk["Dm"]
+    o, w = wl.output_projection_inputs(wk["seed"], shape, T, Dm)
+    y = host(run_output_gpu(shape, o, w))
+    rows = np.sort(np.random.default_rng(wk["seed"] + 1).choice(T, 96, replace=False))
+    e = rel_l2(y[rows], projection.output(o[rows], w))
+    say(f"  y (96 rows): rel-L2 {e:.3e} (tol 1e-2); all rows finite: {np.isfinite(y).all()}")
+    assert np.isfinite(y).all() and e <= 1e-2
+
+
 def test_projections_feed_the_prefill():
     shape = wl.LayerShape(2, 64, 64)
     lengths = [200, 77]
@@ -89,5 +122,9 @@ def test_projections_feed_the_prefill():
                    wl.cu_seqlens(lengths))
     e_o = rel_l2(host(out), r.out)
     e_s = rel_l2(host(S)[N:], r.S)
-    say(f"  projections -> prefill: out {e_o:.3e} state {e_s:.3e}")
-    assert e_o <= 1e-2 and e_s <= 5e-3
+    # and on to the model width through the output projection
+    _, w_o = wl.output_projection_inputs(61, shape, 1, 192)
+    y = host(run_output_gpu(shape, host(out).astype(np.float32), w_o))
+    e_y = rel_l2(y, projection.output(r.out, w_o))
+    say(f"  projections -> prefill -> output projection: out {e_o:.3e} state {e_s:.3e} y {e_y:.3e}")
+    assert e_o <= 1e-2 and e_s <= 5e-3 and e_y <= 1e-2

@@ -34,6 +34,7 @@ TID = {
     "q": 1, "k": 2, "v": 3, "z": 4, "g": 5, "beta": 6,
     "conv_w": 7, "norm_w": 8, "state": 9, "conv_state": 10,
     "lengths": 11, "slots": 12, "resume": 13, "hidden": 14, "proj_w": 15,
+    "layer_out": 16, "out_proj_w": 17,
 }
 
 
@@ -218,3 +219,13 @@ def projection_inputs(seed: int, shape: LayerShape, T: int, Dm: int):
     x = draw_tokens(seed, TID["hidden"], T, (Dm,), transform=round_bf16)
     w = draw_tokens(seed, TID["proj_w"], N, (Dm,), std=float(Dm) ** -0.5, transform=round_bf16)
     return x, w
+
+
+def output_projection_inputs(seed: int, shape: LayerShape, T: int, Dm: int):
+    """The layer's output o ~ N(0, 1) [T][H][dv] (the scale of a gated RMSNorm
+    output with unit weight) and output-projection weights W_o ~ N(0, 1/(H dv))
+    [Dm][H dv], both rounded to bf16 and held as float32."""
+    K = shape.H * shape.dv
+    o = draw_tokens(seed, TID["layer_out"], T, (shape.H, shape.dv), transform=round_bf16)
+    w = draw_tokens(seed, TID["out_proj_w"], Dm, (K,), std=float(K) ** -0.5, transform=round_bf16)
+    return o, w

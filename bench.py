@@ -171,6 +171,8 @@ def bench_decode(args):
         nbytes = (2 + T) * st_b + (2 + T) * cv_b + T * tok_b + (H * (2 * dk + dv) * 4 * 4 + dv * 4 + B * 4)
     achieved = nbytes / launch_s
     traffic = None if (bf16_state or T > 1) else measured_traffic()
+    variants = decode_variants(kda, cfg, q, k, v, z, g, beta, conv_w, norm_w, Sd, Xd, slot_d, out, nbytes, B, args) \
+        if (args.variants and T == 1) else None
     res = {
         "value": tokens / (total_ms * 1e-3),
         "ms_per_step": ms_per_step,
@@ -181,6 +183,58 @@ def bench_decode(args):
                                 if T > 1 else "decode_kernel<128,128,bf16,%s,256>" % ("bf16" if bf16_state else "f32")),
                      "bytes_per_launch": nbytes, "mean_launch_us": launch_s * 1e6},
     }
+    if variants is not None:
+        res["variants"] = variants
+    return res
+
+
+def decode_variants(kda, cfg, q, k, v, z, g, beta, conv_w, norm_w, Sd, Xd, slot_d, out, nbytes, B, args):
+    """Two more timings of the same decode launches, outside the main timed
+    region: (1) one pass of the launches captured once in a HIP graph and
+    replayed; (2) each launch timed alone with the Infinity Cache flushed
+    first by a 1 GiB read-modify-write sweep (not timed), so the state comes
+    from HBM rather than from the 256 MB memory-side cache."""
+    import torch
+    nsteps = q.shape[0]
+    res = {}
+
+    # (1) HIP graph of one pass
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        st = torch.cuda.current_stream()
+        for s in range(nsteps):
+            kda.kda_decode_step(cfg, q[s], k[s], v[s], z[s], g[s], beta[s], conv_w, norm_w, Sd, Xd,
+                                slot_d, out[s], stream=st)
+    stream = torch.cuda.current_stream()
+    for _ in range(max(1, args.warmup)):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / (args.steps * nsteps)
+    res["hip_graph"] = {"us_per_launch": t * 1e6, "tok_s": B / t, "hbm_frac": nbytes / t / HBM_PEAK,
+                        "what": f"{args.steps} replays of a graph holding one pass ({nsteps} launches)"}
+    del graph
+
+    # (2) Infinity Cache flushed before every launch
+    n = min(nsteps, 64)
+    scratch = torch.zeros(1 << 28, device="cuda")            # 1 GiB
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for s in range(n):
+        scratch.add_(1.0)
+        ev[s][0].record(stream)
+        kda.kda_decode_step(cfg, q[s], k[s], v[s], z[s], g[s], beta[s], conv_w, norm_w, Sd, Xd,
+                            slot_d, out[s], stream=stream)
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    t = sum(a.elapsed_time(b) for a, b in ev) * 1e-3 / n
+    res["mall_flushed"] = {"us_per_launch": t * 1e6, "tok_s": B / t, "hbm_frac": nbytes / t / HBM_PEAK,
+                           "what": f"{n} launches, each after a 1 GiB read-modify-write sweep (untimed)"}
+    del scratch
     return res
 
 
@@ -493,6 +547,9 @@ def main():
     ap.add_argument("--workload", choices=["decode_b64", "varlen_ckpt", "long_1m", "project_4x8k"],
                     default="decode_b64",
                     help="decode_b64 (default): the headline line; the others report a larger prefill workload")
+    ap.add_argument("--variants", action="store_true",
+                    help="decode workload: also time the launches replayed from a HIP graph and with the "
+                         "Infinity Cache flushed before each launch (outside the main timed region)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a kernel of "
                          "known traffic, used to scale memory counters)")
@@ -548,6 +605,8 @@ def main():
                    "global_batch": 64, "seq_len": 256, "parallelism": "single GPU"},
         "roofline": res["roofline"],
     }
+    if "variants" in res:
+        line["variants"] = res["variants"]
     if not args.no_prefill:
         line["prefill"] = bench_prefill(max(3, args.steps // 2), max(1, args.warmup))
     if not args.no_cpu_baseline:

@@ -527,9 +527,29 @@ def cpu_baseline(sample_steps: int):
     oracle.decode_steps(r(inp.q), r(inp.k), r(inp.v), r(inp.z), r(inp.g), r(inp.beta),
                         inp.conv_w, inp.norm_w, S[slots], X[slots])
     dt = time.perf_counter() - t0
+    # the same oracle on one thread, over the first 16 steps
+    n1 = min(16, sample_steps)
+    t1 = time.perf_counter()
+    oracle.decode_steps(r(inp.q)[:n1], r(inp.k)[:n1], r(inp.v)[:n1], r(inp.z)[:n1], r(inp.g)[:n1],
+                        r(inp.beta)[:n1], inp.conv_w, inp.norm_w, S[slots], X[slots], threads=1)
+    dt1 = time.perf_counter() - t1
     return {"value": B * sample_steps / dt, "unit": "tok/s", "cores": threads, "kind": "oracle",
             "sample": f"decode workload, {sample_steps} of 256 steps, 64 sequences x 32 heads, "
-                      f"fp64 token-by-token, {dt:.1f} s"}
+                      f"fp64 token-by-token, {dt:.1f} s",
+            "single_thread": {"value": B * n1 / dt1, "unit": "tok/s",
+                              "sample": f"first {n1} steps of the same workload on one thread, {dt1:.1f} s"},
+            "cpu": cpu_model()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip() + f", {os.cpu_count()} logical CPUs visible"
+    except OSError:
+        pass
+    return None
 
 
 def main():

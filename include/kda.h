@@ -224,7 +224,8 @@ kda_status kda_prefill_varlen(const kda_config* cfg, int32_t num_seqs, int64_t t
  * q, k: [T][H][dk], v, z: [T][H][dv] bf16 (RNE); g: [T][H][dk] fp32;
  *   beta: [T][H] fp32 -- exactly the inputs kda_prefill_varlen and
  *   kda_decode_step take.  Accumulation in fp32.
- * Requires act_dtype == KDA_BF16 and Dm a positive multiple of 64.
+ * Requires act_dtype == KDA_BF16 and Dm a positive multiple of 64, at most
+ * 4194304.
  */
 kda_status kda_project_inputs(const kda_config* cfg, int32_t T, int32_t Dm,
                               const void* x, const void* w,
@@ -239,8 +240,8 @@ kda_status kda_project_inputs(const kda_config* cfg, int32_t T, int32_t Dm,
  *
  * o: [T][H][dv] bf16 (the `out` of kda_prefill_varlen / kda_decode_step);
  * w_o: [Dm][H dv] bf16; y: [T][Dm] bf16 (RNE).  Accumulation in fp32.
- * Requires act_dtype == KDA_BF16 and H dv a multiple of 64; o and w_o
- * 16-byte aligned, y 2-byte aligned.  Any Dm >= 1.
+ * Requires act_dtype == KDA_BF16 and H dv a multiple of 64 (at most
+ * 4194304); o and w_o 16-byte aligned, y 2-byte aligned.  Any Dm >= 1.
  */
 kda_status kda_project_output(const kda_config* cfg, int32_t T, int32_t Dm,
                               const void* o, const void* w_o, void* y, void* stream);

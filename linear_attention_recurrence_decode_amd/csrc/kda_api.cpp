@@ -337,6 +337,7 @@ kda_status kda_project_inputs(const kda_config* cfg, int32_t T, int32_t Dm, cons
         return fail(KDA_ERR_UNSUPPORTED, "input projections need bf16 activations (act_dtype = KDA_BF16)");
     if (T < 0) return fail(KDA_ERR_INVALID_ARG, "T must be >= 0 (got %d)", T);
     if (Dm < 64 || Dm % 64 != 0) return fail(KDA_ERR_INVALID_ARG, "Dm must be a positive multiple of 64 (got %d)", Dm);
+    if (Dm > (1 << 22)) return fail(KDA_ERR_INVALID_ARG, "Dm must be at most 4194304 (got %d)", Dm);
     const int64_t N = static_cast<int64_t>(cfg->num_heads) * (3 * cfg->head_k + 2 * cfg->head_v) + cfg->num_heads;
     if (N * Dm * 2 >= (1LL << 31) * 2 || static_cast<int64_t>(T) * Dm * 2 >= (1LL << 40))
         return fail(KDA_ERR_INVALID_ARG, "projection sizes too large");
@@ -379,6 +380,8 @@ kda_status kda_project_output(const kda_config* cfg, int32_t T, int32_t Dm, cons
     if (K % 64 != 0)
         return fail(KDA_ERR_UNSUPPORTED, "the output projection needs num_heads * head_v to be a multiple of 64 (got %lld)",
                     static_cast<long long>(K));
+    if (K > (1 << 22))
+        return fail(KDA_ERR_INVALID_ARG, "num_heads * head_v must be at most 4194304 (got %lld)", static_cast<long long>(K));
     if (static_cast<int64_t>(Dm) * K * 2 >= (1LL << 32) || static_cast<int64_t>(T) * K * 2 >= (1LL << 40))
         return fail(KDA_ERR_INVALID_ARG, "projection sizes too large");
     if (T == 0) return ok();

@@ -1,4 +1,4 @@
-// project.hip -- fused input projections of the KDA layer on bf16 MFMA.
+// project.hip -- input and output projections of the KDA layer on bf16 MFMA.
 // [vLLM blog "A Preview of Production-Scale Kimi K3 Support on vLLM", section
 //  "KDA prefill and decode": the input projections are fused around the
 //  recurrence.]
@@ -291,6 +291,8 @@ hipError_t launch_project(const ProjectParams& p, hipStream_t s) {
     const int64_t tiles = static_cast<int64_t>((p.T + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     if (tiles == 0) return hipSuccess;
     const int64_t grid = (tiles + XCDS - 1) / XCDS * XCDS;
+    // tile ids and the per-lane byte offsets ((row < BM) x Dm + chunk) x 2 are 32-bit
+    if (grid > INT32_MAX || (static_cast<int64_t>(BM - 1) * p.Dm + BK) * 2 > INT32_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL((project_kernel<BM, BN, BK, WM, WN>), dim3(static_cast<unsigned>(grid)), dim3(64 * WM * WN), 0,
                        s, p);
     return hipGetLastError();

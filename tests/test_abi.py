@@ -169,6 +169,7 @@ def test_projection_validation():
     assert project_in_call(cfg(act_dtype=kda.KDA_F32)) == kda.KDA_ERR_UNSUPPORTED
     assert project_in_call(cfg(), Dm=100) == kda.KDA_ERR_INVALID_ARG
     assert project_in_call(cfg(), Dm=0) == kda.KDA_ERR_INVALID_ARG
+    assert project_in_call(cfg(), Dm=(1 << 22) + 64) == kda.KDA_ERR_INVALID_ARG
     assert project_in_call(cfg(), T=-1) == kda.KDA_ERR_INVALID_ARG
     for name in ("x", "w", "q", "k", "v", "z", "g", "beta"):
         assert project_in_call(cfg(), **{name: None}) == kda.KDA_ERR_INVALID_ARG, name

@@ -55,7 +55,8 @@ def check(o, ref, rows=None):
         assert np.isfinite(got).all() and e <= tol, name
 
 
-@pytest.mark.parametrize("H,d,T,Dm", [(2, 64, 300, 256), (4, 128, 1000, 1024), (3, 32, 129, 64)])
+@pytest.mark.parametrize("H,d,T,Dm", [(2, 64, 300, 256), (4, 128, 1000, 1024), (3, 32, 129, 64), (1, 32, 1, 128),
+                                       (2, 64, 257, 64)])
 def test_project_matches_oracle(H, d, T, Dm):
     shape = wl.LayerShape(H, d, d)
     say(f"projection H={H} d={d} T={T} Dm={Dm}")
@@ -75,7 +76,8 @@ def test_project_full_size_sampled_rows():
     check(o, projection.project(x[rows], w, shape.H, shape.dk, shape.dv), rows)
 
 
-@pytest.mark.parametrize("H,dv,T,Dm", [(2, 64, 300, 200), (4, 128, 1000, 1024), (1, 64, 129, 7), (3, 64, 257, 513)])
+@pytest.mark.parametrize("H,dv,T,Dm", [(2, 64, 300, 200), (4, 128, 1000, 1024), (1, 64, 129, 7), (3, 64, 257, 513),
+                                        (1, 64, 1, 256)])
 def test_output_projection_matches_oracle(H, dv, T, Dm):
     shape = wl.LayerShape(H, dv, dv)
     say(f"output projection H={H} dv={dv} T={T} Dm={Dm}")

@@ -159,6 +159,9 @@ def _want(t, name, dtype, shape=None):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on a GPU device (got {t.device})")
+    if t.device.index != torch.cuda.current_device():
+        # the library launches on the current device's stream
+        raise ValueError(f"{name} is on {t.device}, not on the current device cuda:{torch.cuda.current_device()}")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
     if not t.is_contiguous():

@@ -527,8 +527,8 @@ def cpu_baseline(sample_steps: int):
     oracle.decode_steps(r(inp.q), r(inp.k), r(inp.v), r(inp.z), r(inp.g), r(inp.beta),
                         inp.conv_w, inp.norm_w, S[slots], X[slots])
     dt = time.perf_counter() - t0
-    # the same oracle on one thread, over the first 16 steps
-    n1 = min(16, sample_steps)
+    # the same oracle on one thread, over the first 48 steps
+    n1 = min(48, sample_steps)
     t1 = time.perf_counter()
     oracle.decode_steps(r(inp.q)[:n1], r(inp.k)[:n1], r(inp.v)[:n1], r(inp.z)[:n1], r(inp.g)[:n1],
                         r(inp.beta)[:n1], inp.conv_w, inp.norm_w, S[slots], X[slots], threads=1)

@@ -1,8 +1,11 @@
 /*
  * kda.h -- C ABI of libkda, the MI355X (gfx950) implementation of the Kimi
  * Delta Attention (KDA) layer's inference hot path: a fused single-launch
- * decode step, a chunked varlen prefill that writes recurrent-state
- * checkpoints, and the copy-on-write state copies used to resume from them.
+ * decode step (and its multi-token form for speculative verification), a
+ * chunked varlen prefill that writes recurrent-state checkpoints, the
+ * copy-on-write state copies used to resume from them, and the layer's input
+ * and output projections.  The host-side prefix cache of states has its own
+ * header, kda_prefix_cache.h.
  *
  * The layer, per sequence and head (dk key channels, dv value channels):
  *   a   = SiLU(causal depthwise conv of width 4 over the raw q | k | v channels)
@@ -34,7 +37,8 @@
  *   kda_last_error() describes the problem.  Slot ids are device data and are
  *   checked inside the kernels: an out-of-range id is skipped (its outputs are
  *   filled with NaN where the call has outputs) instead of being dereferenced.
- * Pointers: all device pointers must be 16-byte aligned.
+ * Pointers: device pointers must be 16-byte aligned unless a call states
+ *   otherwise.
  * Layouts (row-major, innermost last; T = tokens of the call, S = slots):
  *   q, k      [T][H][dk]   activation dtype       v, z, out [T][H][dv]  activation dtype
  *   g         [T][H][dk]   fp32 (log decay, <= 0) beta      [T][H]      fp32

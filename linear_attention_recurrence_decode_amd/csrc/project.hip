@@ -66,38 +66,47 @@ __device__ __forceinline__ bool tile_origin(const ProjectParams& p, int& m0, int
 
 // Epilogue, one 32-row strip of the wave's block at a time: the fp32 tiles go
 // through LDS (element e of a 32x32 tile is at row 8(e/4) + 4(lane/32) + e%4,
-// column lane%32) and come back one row at a time, each lane owning fixed
-// columns, so that a column's routing (tensor, offset, gate map) is worked
-// out once and the gate maps are not unrolled over every element.  The tile
-// buffers must be free (all waves past their last read) on entry.
+// column lane%32) and come back as 4 consecutive columns of one row per lane,
+// so that a group's routing (tensor, offset, gate map) is worked out once and
+// its 4 results leave in one 8-byte (bf16) or 16-byte (fp32) store.  The
+// tensor blocks of the input projections start at multiples of 32 columns, so
+// a group never straddles two tensors; a group that runs past N, a row width
+// that is not a multiple of 4 or a destination that is not aligned for the
+// wide store is written element by element.  The tile buffers must be free
+// (all waves past their last read) on entry.
 template <int BM, int BN, int WM, int WN, int TI = BM / WM / 32, int TJ = BN / WN / 32>
 __device__ __forceinline__ void epilogue(const ProjectParams& p, const f32x16 (&acc)[TI][TJ], float* smem, int m0,
                                          int n0) {
     constexpr int RM = BM / WM, RN = BN / WN;
-    constexpr int WC = RN, EP = WC + 4, CT = WC / 64;
-    static_assert(WC % 64 == 0, "wave block width must be a multiple of 64");
+    constexpr int EP = RN + 4;              // staging row stride (floats)
+    constexpr int GPR = RN / 4;             // 4-column groups per row
+    constexpr int RPI = 64 / GPR;           // rows per store instruction
+    static_assert(RN % 4 == 0 && 64 % GPR == 0 && 32 % RPI == 0, "column groups must tile a wave");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lr = lane & 31;
     const int wm = wave / WN, wn = wave % WN;
     float* stage = smem + wave * 32 * EP;
+    const int cg = lane % GPR, rsub = lane / GPR;
+
+    // routing of this lane's 4 columns n .. n+3
     const int H = p.H, dk = p.dk, dv = p.dv;
     const int64_t bq = static_cast<int64_t>(H) * dk, bv = static_cast<int64_t>(H) * dv;
-    int kind[CT];
-    int64_t col[CT], width[CT];
-    void* dst[CT];
-#pragma unroll
-    for (int t = 0; t < CT; t++) {
-        const int64_t n = n0 + WC * wn + 64 * t + lane;
-        if (n >= p.N) { kind[t] = -1; col[t] = 0; width[t] = 0; }
-        else if (p.mode == 1) { kind[t] = 0; col[t] = n; width[t] = p.N; }
-        else if (n < bq) { kind[t] = 0; col[t] = n; width[t] = bq; }
-        else if (n < 2 * bq) { kind[t] = 1; col[t] = n - bq; width[t] = bq; }
-        else if (n < 2 * bq + bv) { kind[t] = 2; col[t] = n - 2 * bq; width[t] = bv; }
-        else if (n < 2 * bq + 2 * bv) { kind[t] = 3; col[t] = n - 2 * bq - bv; width[t] = bv; }
-        else if (n < 3 * bq + 2 * bv) { kind[t] = 4; col[t] = n - 2 * bq - 2 * bv; width[t] = bq; }
-        else { kind[t] = 5; col[t] = n - 3 * bq - 2 * bv; width[t] = H; }
-        const int k = kind[t];
-        dst[t] = p.mode == 1 ? p.y : k == 0 ? p.q : k == 1 ? p.k : k == 2 ? p.v : k == 3 ? p.z : k == 4 ? p.g : p.beta;
-    }
+    const int64_t n = n0 + RN * wn + 4 * cg;
+    const int nv = static_cast<int>(min(static_cast<int64_t>(4), max(static_cast<int64_t>(0), p.N - n)));
+    int kind;
+    int64_t col, width;
+    if (nv == 0) { kind = -1; col = 0; width = 0; }
+    else if (p.mode == 1) { kind = 0; col = n; width = p.N; }
+    else if (n < bq) { kind = 0; col = n; width = bq; }
+    else if (n < 2 * bq) { kind = 1; col = n - bq; width = bq; }
+    else if (n < 2 * bq + bv) { kind = 2; col = n - 2 * bq; width = bv; }
+    else if (n < 2 * bq + 2 * bv) { kind = 3; col = n - 2 * bq - bv; width = bv; }
+    else if (n < 3 * bq + 2 * bv) { kind = 4; col = n - 2 * bq - 2 * bv; width = bq; }
+    else { kind = 5; col = n - 3 * bq - 2 * bv; width = H; }
+    void* dst = p.mode == 1 ? p.y : kind == 0 ? p.q : kind == 1 ? p.k : kind == 2 ? p.v : kind == 3 ? p.z
+                                  : kind == 4 ? p.g : p.beta;
+    const int esz = kind >= 4 ? 4 : 2;
+    const bool wide = nv == 4 && width % 4 == 0 && col % 4 == 0 && reinterpret_cast<uintptr_t>(dst) % (4 * esz) == 0;
+
 #pragma unroll
     for (int i = 0; i < TI; i++) {
 #pragma unroll
@@ -108,18 +117,38 @@ __device__ __forceinline__ void epilogue(const ProjectParams& p, const f32x16 (&
         __syncthreads();
         const int mb = m0 + RM * wm + 32 * i;
 #pragma unroll 2
-        for (int r = 0; r < 32; r++) {
+        for (int it = 0; it < 32 / RPI; it++) {
+            const int r = it * RPI + rsub;
             const int m = mb + r;
-            if (m >= p.T) break;
+            if (kind < 0 || m >= p.T) continue;
+            const float4 y = *reinterpret_cast<const float4*>(&stage[r * EP + 4 * cg]);
+            const int64_t o = static_cast<int64_t>(m) * width + col;
+            float v4[4] = {y.x, y.y, y.z, y.w};
+            if (kind == 4) {
 #pragma unroll
-            for (int t = 0; t < CT; t++) {
-                const int k = kind[t];
-                if (k < 0) continue;
-                const float y = stage[r * EP + 64 * t + lane];
-                const int64_t o = static_cast<int64_t>(m) * width[t] + col[t];
-                if (k < 4) static_cast<uint16_t*>(dst[t])[o] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(y));
-                else if (k == 4) static_cast<float*>(dst[t])[o] = -softplus_f(y);
-                else static_cast<float*>(dst[t])[o] = sigmoid(y);
+                for (int c = 0; c < 4; c++) v4[c] = -softplus_f(v4[c]);
+            } else if (kind == 5) {
+#pragma unroll
+                for (int c = 0; c < 4; c++) v4[c] = sigmoid(v4[c]);
+            }
+            if (wide) {
+                if (kind < 4) {
+                    uint2 w;
+                    w.x = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v4[0]))) |
+                          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v4[1]))) << 16);
+                    w.y = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v4[2]))) |
+                          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v4[3]))) << 16);
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(dst) + o) = w;
+                } else {
+                    *reinterpret_cast<float4*>(static_cast<float*>(dst) + o) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; c++) {
+                    if (c >= nv) break;
+                    if (kind < 4) static_cast<uint16_t*>(dst)[o + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v4[c]));
+                    else static_cast<float*>(dst)[o + c] = v4[c];
+                }
             }
         }
         __syncthreads();

@@ -217,6 +217,21 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
     }
 }
 
+// Non-temporal 16-byte store (cache-policy bit NT): for data written once and
+// not read again by this launch or the next (the fp32 per-token rollback
+// states of a multi-token step).  Without the hint that stream takes the place
+// of the live state in the last-level cache and the next step reads the state
+// from HBM again.  Bit 1 of the intrinsics' cache-policy operand is NT on gfx950.
+constexpr int kCachePolicyNT = 2;
+__device__ __forceinline__ void buf_st4_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, float4 x) {
+    i32x4 v;
+    v.x = __float_as_int(x.x);
+    v.y = __float_as_int(x.y);
+    v.z = __float_as_int(x.z);
+    v.w = __float_as_int(x.w);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(voff), 0, kCachePolicyNT);
+}
+
 // T decode tokens per sequence in one launch (speculative verification: the
 // target model checks K drafted tokens plus one in a single pass).  The state
 // stays in registers across the tokens; token t runs exactly the arithmetic
@@ -424,7 +439,7 @@ __global__ __launch_bounds__(NT) void decode_multi_kernel(DecodeParams p) {
                 s[r] = bf16x4_to_f32(hb);
                 if (p.token_state) buf_st8(rt, voff + r * DV * 2, hb);
             } else {
-                if (p.token_state) buf_st4(rt, voff + r * DV * 4, s[r]);
+                if (p.token_state) buf_st4_nt(rt, voff + r * DV * 4, s[r]);
             }
         }
 

@@ -197,6 +197,11 @@ __device__ __forceinline__ Frag4 ld4(const uint16_t* hi, const uint16_t* lo, int
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
+// Jobs (a, b) = (j >> 2, j & 3) of the intra-chunk block products in the order
+// waves take them, one nibble each from the lowest: 0 4 5 8 9 10 12 13 15 14
+// 1 2 3 6 7 11 (the six jobs with a < b, which only clear P's upper blocks, last).
+constexpr uint64_t kA5Order = 0xB76321EFDCA98540ull;
+
 // A copy of x the optimiser cannot see through.  Lane indices are re-derived
 // from such a copy at the start of each phase of the chunk loop, so their
 // address arithmetic stays inside the phase instead of being hoisted out of
@@ -748,11 +753,15 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
 
         // ---------------- A5: L = Diag(b) strictLower(K+ K-^T), P = lower(Q+ K-^T);
         // one job per 16x16 block pair (a, b) computes both, sharing the K-
-        // fragments.
+        // fragments.  Only the 10 jobs with a >= b multiply; wave w takes jobs
+        // kA5Order[w + i NW], an order that gives the SIMDs 3, 3, 2 and 2 of them
+        // with 8 waves (waves w and w + 4 share a SIMD), 3, 3, 2, 2 with 4 and
+        // 5, 5 with 2.
         {
             const int tp = opq(tid);
-            const int ln = tp & 63, wv5 = tp >> 6, gg = ln >> 4, lc = ln & 15;
-            for (int job = wv5; job < 16; job += NW) {
+            const int ln = tp & 63, wv5 = __builtin_amdgcn_readfirstlane(tp >> 6), gg = ln >> 4, lc = ln & 15;
+            for (int ji = wv5; ji < 16; ji += NW) {
+                const int job = static_cast<int>((kA5Order >> (4 * ji)) & 15);
                 const int a = job >> 2, b = job & 3;
                 if (a < b) {
                     if constexpr (OUT) {

@@ -18,8 +18,8 @@ step).  The line also carries:
                 decode workload
 With --workload the line instead reports one of the larger prefill
 workloads (inputs resident in HBM, one call per pass):
-  varlen_ckpt   16 sequences of log-uniform length in [1K, 64K] (about 248K
-                tokens on average), H=32, checkpoints every 4096 tokens and at
+  varlen_ckpt   16 sequences of log-uniform length in [1K, 64K] (262,990
+                tokens in the seeded draw), H=32, checkpoints every 4096 tokens and at
                 the ends, unsplit (the reported value) and split at the
                 checkpoints; then a resume batch (each sequence restarted from a seeded
                 interval checkpoint) timed on its own

@@ -200,7 +200,10 @@ WORKLOADS = {
                        B=64, steps=256, pool=80, state_std=0.02, conv_std=1.0),
     "prefill_4x8k": dict(seed=2, shape=LayerShape(H=32, dk=128, dv=128, act="bf16"),
                          lengths=[8192] * 4),
-    "varlen_ckpt": dict(seed=3, shape=LayerShape(H=32, dk=128, dv=128, act="bf16"),
+    # seed 6: the first seed from 3 on whose 16 lengths total within 1% of the
+    # workload's 256Ki tokens (262,990 tokens, longest 51,782); seed 3 drew
+    # 165,069 tokens with none above 29,637
+    "varlen_ckpt": dict(seed=6, shape=LayerShape(H=32, dk=128, dv=128, act="bf16"),
                         n=16, lo=1024, hi=65536, interval=4096),
     "long_1m": dict(seed=4, shape=LayerShape(H=8, dk=128, dv=128, act="bf16"),
                     lengths=[1 << 20], interval=32768, decode_B=256, decode_steps=512),

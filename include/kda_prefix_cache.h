@@ -66,7 +66,7 @@ int32_t kda_pcache_release(kda_pcache* c, int32_t slot);
 
 /* Hand out n free slots into slots[0..n): free ones first, then by evicting
  * least recently used unpinned, committed entries.  Returns n, or -1 (nothing
- * handed out) if not enough slots can be freed. */
+ * handed out, nothing evicted) if not enough slots can be freed. */
 int32_t kda_pcache_reserve(kda_pcache* c, int32_t n, int32_t* slots);
 
 /* Register the state after tokens[0:pos] (pos >= 1) held in a reserved slot,

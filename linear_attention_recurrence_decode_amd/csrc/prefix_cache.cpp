@@ -18,6 +18,7 @@
 #include <string>
 #include <unordered_map>
 #include <unordered_set>
+#include <utility>
 #include <vector>
 
 namespace {
@@ -79,7 +80,9 @@ struct kda_pcache {
     size_t ghost_cap;
     int64_t committed = INT64_MIN;
     std::unordered_map<Key, Entry, KeyHash> entries;
-    std::unordered_map<Key, std::vector<int32_t>, KeyHash> tails;   // unit boundary -> offsets of entries after it
+    // unit boundary -> (offset, number of entries at that offset) of the entries
+    // after it: prompts that share the boundary prefix can end at one offset
+    std::unordered_map<Key, std::vector<std::pair<int32_t, int32_t>>, KeyHash> tails;
     std::list<Key> lru;
     std::vector<int32_t> free_slots;
     std::vector<uint8_t> state;            // per slot: 0 free, 1 reserved, 2 owned by an entry
@@ -104,9 +107,11 @@ struct kda_pcache {
                 const int32_t off = static_cast<int32_t>(e.pos % unit);
                 auto& v = t->second;
                 for (size_t i = 0; i < v.size(); i++)
-                    if (v[i] == off) {
-                        v[i] = v.back();
-                        v.pop_back();
+                    if (v[i].first == off) {
+                        if (--v[i].second == 0) {
+                            v[i] = v.back();
+                            v.pop_back();
+                        }
                         break;
                     }
                 if (v.empty()) tails.erase(t);
@@ -116,6 +121,12 @@ struct kda_pcache {
         state[e.slot] = 0;
         free_slots.push_back(e.slot);
         entries.erase(it);
+    }
+
+    int64_t evictable() const {
+        int64_t n = 0;
+        for (const auto& kv : entries) n += kv.second.pins == 0 && kv.second.step <= committed;
+        return n;
     }
 
     bool evict_one() {
@@ -177,7 +188,7 @@ int64_t kda_pcache_lookup(kda_pcache* c, const int32_t* tokens, int64_t max_len,
     {
         auto t = c->tails.find(ch.key(0));
         if (t != c->tails.end())
-            for (int32_t off : t->second) wanted.push_back(off);
+            for (const auto& oc : t->second) wanted.push_back(oc.first);
     }
     auto probe = [&](int64_t p) {
         const Key k = ch.key(p);
@@ -202,7 +213,7 @@ int64_t kda_pcache_lookup(kda_pcache* c, const int32_t* tokens, int64_t max_len,
             wanted.clear();
             auto t = c->tails.find(k);
             if (t != c->tails.end())
-                for (int32_t off : t->second) wanted.push_back(p + off);
+                for (const auto& oc : t->second) wanted.push_back(p + oc.first);
         } else if (listed) {
             probe(p);
         }
@@ -230,9 +241,10 @@ int32_t kda_pcache_release(kda_pcache* c, int32_t slot) {
 
 int32_t kda_pcache_reserve(kda_pcache* c, int32_t n, int32_t* slots) {
     if (!c || n < 0 || (n > 0 && !slots)) return fail("kda_pcache_reserve: bad arguments");
-    while (static_cast<int32_t>(c->free_slots.size()) < n) {
-        if (!c->evict_one()) return fail("kda_pcache_reserve: not enough free or evictable slots");
-    }
+    const int64_t short_by = static_cast<int64_t>(n) - static_cast<int64_t>(c->free_slots.size());
+    // a refused call evicts nothing
+    if (short_by > 0 && c->evictable() < short_by) return fail("kda_pcache_reserve: not enough free or evictable slots");
+    while (static_cast<int32_t>(c->free_slots.size()) < n) c->evict_one();
     for (int32_t i = 0; i < n; i++) {
         const int32_t s = c->free_slots.back();
         c->free_slots.pop_back();
@@ -281,8 +293,12 @@ int32_t insert_key(kda_pcache* c, const Key& k, const Key& boundary, int64_t pos
         auto& offs = c->tails[boundary];
         const int32_t off = static_cast<int32_t>(pos % c->unit);
         bool have = false;
-        for (int32_t o : offs) have |= (o == off);
-        if (!have) offs.push_back(off);
+        for (auto& oc : offs)
+            if (oc.first == off) {
+                oc.second++;
+                have = true;
+            }
+        if (!have) offs.push_back({off, 1});
     }
     return 1;
 }

@@ -187,3 +187,41 @@ def test_insert_many_equals_single_inserts():
         assert p1 == p2 and (p1 == 0 or pos.index(p1) == list(s1).index(q1) == list(s2).index(q2))
     with pytest.raises(kda.KdaError):
         c2.insert_many(a, [5, 4], c2.reserve(2), 1)            # positions must increase
+
+
+def test_shared_prompt_end_offset_survives_eviction():
+    """Two prompts that share the prefix up to a unit boundary and end at the
+    same offset after it are listed under that boundary together; evicting one
+    must leave the other reachable."""
+    rng = np.random.default_rng(10)
+    c = kda.PrefixCache(2, unit=16)
+    base = toks(rng, 32)
+    a = np.concatenate([base, np.array([1, 2], np.int32)])
+    b = np.concatenate([base, np.array([3, 4], np.int32)])
+    sa, sb = put(c, a, 34), put(c, b, 34)
+    c.commit(0)
+    assert c.lookup(b) == (34, sb)
+    c.release(sb)
+    # b was used last, so the next reservation evicts a
+    s = int(c.reserve(1)[0])
+    assert s == sa and c.stats()["evictions"] == 1
+    c.unreserve(s)
+    assert c.lookup(b) == (34, sb)
+    c.release(sb)
+    assert c.lookup(a) == (0, -1)
+
+
+def test_refused_reservation_evicts_nothing():
+    rng = np.random.default_rng(11)
+    c = kda.PrefixCache(2, unit=16)
+    a, b = toks(rng, 32), toks(rng, 32)
+    put(c, a, 32)
+    put(c, b, 32)
+    c.commit(0)
+    p, s = c.lookup(a)              # a pinned: only b can be evicted
+    assert p == 32
+    with pytest.raises(kda.KdaError):
+        c.reserve(2)
+    st = c.stats()
+    assert st["entries"] == 2 and st["evictions"] == 0 and st["free_slots"] == 0
+    assert c.lookup(b)[0] == 32

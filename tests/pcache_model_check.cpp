@@ -6,7 +6,10 @@
 // a plain reference model (an ordered map from prefix to entry); every return
 // value and every counter is compared after each operation.
 //
-//   pcache_model_check <seed> <ops> <unit> <slots>
+//   pcache_model_check <seed> <ops> <unit> <slots> [<policy> <ghost_capacity>]
+//
+// policy 0 keeps every inserted state, 1 only a prefix's second insertion
+// (first sightings are remembered in a FIFO of ghost_capacity keys).
 //
 // Prints "ok <ops>" and exits 0, or prints the first mismatch and exits 1.
 
@@ -17,7 +20,9 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <deque>
 #include <map>
+#include <set>
 #include <random>
 #include <vector>
 
@@ -46,10 +51,12 @@ int g_op = 0;
 }  // namespace
 
 int main(int argc, char** argv) {
-    if (argc != 5) {
-        std::printf("usage: %s seed ops unit slots\n", argv[0]);
+    if (argc != 5 && argc != 7) {
+        std::printf("usage: %s seed ops unit slots [policy ghost_capacity]\n", argv[0]);
         return 2;
     }
+    const int32_t policy = argc == 7 ? std::atoi(argv[5]) : KDA_PCACHE_KEEP_ALL;
+    const int32_t ghost_arg = argc == 7 ? std::atoi(argv[6]) : 0;
     const uint64_t seed = std::strtoull(argv[1], nullptr, 10);
     const int ops = std::atoi(argv[2]);
     const int32_t unit = std::atoi(argv[3]);
@@ -72,7 +79,7 @@ int main(int argc, char** argv) {
         }
     }
 
-    kda_pcache* c = kda_pcache_create(num_slots, unit, KDA_PCACHE_KEEP_ALL, 0);
+    kda_pcache* c = kda_pcache_create(num_slots, unit, policy, ghost_arg);
     CHECK(c != nullptr);
     std::map<Seq, ModelEntry> model;
     std::vector<int> state(num_slots, 0);    // 0 free, 1 reserved, 2 owned by an entry
@@ -80,6 +87,23 @@ int main(int argc, char** argv) {
     std::vector<int32_t> reserved, pinned;
     int64_t committed = INT64_MIN, step = 0, clock = 0;
     int64_t hits = 0, misses = 0, evictions = 0, declined = 0;
+    const size_t ghost_cap = ghost_arg > 0 ? static_cast<size_t>(ghost_arg) : static_cast<size_t>(num_slots) * 4;
+    std::set<Seq> ghosts;          // first sightings remembered by the second-hit policy
+    std::deque<Seq> ghost_order;
+    // expected result of inserting key: 1 kept, 0 declined (updates the ghosts)
+    auto expect_insert = [&](const Seq& key) {
+        if (model.count(key)) return 0;
+        if (policy == KDA_PCACHE_SECOND_HIT && !ghosts.count(key)) {
+            ghosts.insert(key);
+            ghost_order.push_back(key);
+            while (ghost_order.size() > ghost_cap) {
+                ghosts.erase(ghost_order.front());
+                ghost_order.pop_front();
+            }
+            return 0;
+        }
+        return 1;
+    };
 
     auto visible_best = [&](const Seq& s, int64_t max_len) {
         int64_t best = 0;
@@ -143,7 +167,7 @@ int main(int argc, char** argv) {
             const int64_t p = 1 + rnd(static_cast<int64_t>(s.size()));
             const int32_t slot = take_reserved();
             const Seq key(s.begin(), s.begin() + p);
-            const int32_t expect = model.count(key) ? 0 : 1;
+            const int32_t expect = expect_insert(key);
             CHECK(kda_pcache_insert(c, s.data(), p, slot, step) == expect);
             if (expect) {
                 model[key] = ModelEntry{slot, step, 0, ++clock};
@@ -169,7 +193,7 @@ int main(int argc, char** argv) {
             int32_t expect_count = 0;
             std::vector<int32_t> expect(n);
             for (int32_t i = 0; i < n; i++) {
-                expect[i] = model.count(Seq(s.begin(), s.begin() + pos[i])) ? 0 : 1;
+                expect[i] = expect_insert(Seq(s.begin(), s.begin() + pos[i]));
                 expect_count += expect[i];
             }
             CHECK(kda_pcache_insert_many(c, s.data(), n, pos.data(), slots.data(), step, kept.data()) == expect_count);
@@ -210,9 +234,22 @@ int main(int argc, char** argv) {
             CHECK(kda_pcache_release(c, slot) == 0);
             model.at(owner[slot]).pins--;
         } else if (r < 88) {
-            // releasing a slot that holds no pin is refused
+            // refused calls change nothing: releasing a slot without a pin, inserting
+            // into a slot that is not reserved, repeated slots, non-increasing positions
             const int32_t slot = static_cast<int32_t>(rnd(num_slots));
+            const Seq& s = seqs[rnd(static_cast<int64_t>(seqs.size()))];
             if (std::find(pinned.begin(), pinned.end(), slot) == pinned.end()) CHECK(kda_pcache_release(c, slot) == -1);
+            if (state[slot] != 1) CHECK(kda_pcache_insert(c, s.data(), 1, slot, step) == -1);
+            if (!reserved.empty() && s.size() >= 2) {
+                const int32_t two[2] = {reserved[0], reserved[0]};
+                const int64_t pos2[2] = {1, 2};
+                CHECK(kda_pcache_insert_many(c, s.data(), 2, pos2, two, step, nullptr) == -1);
+            }
+            if (reserved.size() >= 2 && s.size() >= 2) {
+                const int32_t two[2] = {reserved[0], reserved[1]};
+                const int64_t pos2[2] = {2, 2};
+                CHECK(kda_pcache_insert_many(c, s.data(), 2, pos2, two, step, nullptr) == -1);
+            }
         } else if (r < 95) {
             kda_pcache_commit(c, step);
             committed = std::max(committed, step);
@@ -236,6 +273,7 @@ int main(int argc, char** argv) {
         CHECK(st[4] == misses);
         CHECK(st[5] == evictions);
         CHECK(st[6] == declined);
+        CHECK(st[7] == static_cast<int64_t>(ghosts.size()));
     }
     kda_pcache_destroy(c);
     std::printf("ok %d\n", ops);

@@ -2,9 +2,10 @@
 
 tests/pcache_model_check.cpp drives csrc/prefix_cache.cpp (host code only,
 built here with g++, no HIP) through random reserve / insert / insert_many /
-lookup / release / commit / unreserve operations against a reference model,
-with pools small enough that reservations evict entries, and compares every
-return value and counter after each operation.
+lookup / release / commit / unreserve operations (and refused calls) against
+a reference model, with pools small enough that reservations evict entries,
+under both retention policies, and compares every return value and counter
+after each operation.
 """
 import os
 import shutil
@@ -31,11 +32,12 @@ def checker(tmp_path_factory):
     return exe
 
 
+@pytest.mark.parametrize("policy", [(0, 0), (1, 0), (1, 5)], ids=["keep_all", "second_hit", "second_hit_ghosts5"])
 @pytest.mark.parametrize("unit", [1, 4, 16, 64])
 @pytest.mark.parametrize("slots", [8, 24, 64])
-def test_model_check_under_sanitizers(checker, unit, slots):
+def test_model_check_under_sanitizers(checker, unit, slots, policy):
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
     for seed in (1, 2, 3):
-        r = subprocess.run([checker, str(seed), "3000", str(unit), str(slots)], capture_output=True, text=True,
-                           timeout=300, env=env)
-        assert r.returncode == 0 and r.stdout.strip() == "ok 3000", (seed, r.stdout[-500:], r.stderr[-2000:])
+        args = [checker, str(seed), "3000", str(unit), str(slots), str(policy[0]), str(policy[1])]
+        r = subprocess.run(args, capture_output=True, text=True, timeout=300, env=env)
+        assert r.returncode == 0 and r.stdout.strip() == "ok 3000", (args, r.stdout[-500:], r.stderr[-2000:])

@@ -185,6 +185,38 @@ def bench_decode(args):
     }
     if variants is not None:
         res["variants"] = variants
+    if T == 1:
+        res["slot_copies"] = slot_copies(kda, cfg, Sd, Xd, slot_d, B, H, dk, dv, sb, args)
+    return res
+
+
+def slot_copies(kda, cfg, Sd, Xd, slot_d, B, H, dk, dv, sb, args):
+    """The checkpoint and resume copies at the decode workload's size: the
+    state and conv state of its 64 live slots (all heads) copied into a
+    64-slot checkpoint pool (kda_state_checkpoint) and back (kda_resume), each
+    timed over `steps` calls after `warmup`.  Algorithmic bytes per call: every
+    copied byte read once and written once."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ckS = torch.empty((B,) + tuple(Sd.shape[1:]), dtype=Sd.dtype, device="cuda")
+    ckX = torch.empty((B,) + tuple(Xd.shape[1:]), dtype=Xd.dtype, device="cuda")
+    ck_ids = torch.arange(B, dtype=torch.int32, device="cuda")
+    nbytes = 2 * B * H * (dk * dv * sb + (2 * dk + dv) * 3 * Xd.element_size())
+    calls = {"checkpoint": lambda: kda.kda_state_checkpoint(cfg, Sd, Xd, slot_d, ckS, ckX, ck_ids, stream=stream),
+             "resume": lambda: kda.kda_resume(cfg, ckS, ckX, ck_ids, Sd, Xd, slot_d, stream=stream)}
+    res = {"what": f"{B} slots x {H} heads per call, live pool <-> checkpoint pool", "bytes_per_call": nbytes}
+    for name in ("checkpoint", "resume"):
+        for _ in range(max(1, args.warmup)):
+            calls[name]()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            calls[name]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / args.steps
+        res[name] = {"us_per_call": t * 1e6, "achieved_GBs": nbytes / t / 1e9, "hbm_frac": nbytes / t / HBM_PEAK}
     return res
 
 
@@ -627,6 +659,8 @@ def main():
     }
     if "variants" in res:
         line["variants"] = res["variants"]
+    if "slot_copies" in res:
+        line["slot_copies"] = res["slot_copies"]
     if not args.no_prefill:
         line["prefill"] = bench_prefill(max(3, args.steps // 2), max(1, args.warmup))
     if not args.no_cpu_baseline:

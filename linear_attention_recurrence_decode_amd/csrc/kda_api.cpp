@@ -85,7 +85,10 @@ kda_status check_copy_args(const kda_config* cfg, int32_t n, const void* src_sta
     if (n < 0) return fail(KDA_ERR_INVALID_ARG, "n must be >= 0 (got %d)", n);
     if (src_slots < 1 || dst_slots < 1) return fail(KDA_ERR_INVALID_ARG, "pool sizes must be >= 1");
     if (n == 0) return KDA_OK;
-    if (static_cast<int64_t>(n) * cfg->num_heads > 0x7fffffffLL)
+    // one workgroup per 4 KiB of each (pair, head)'s state and conv state
+    const int64_t sb = static_cast<int64_t>(cfg->head_k) * cfg->head_v * (cfg->state_dtype == KDA_BF16 ? 2 : 4);
+    const int64_t cb = static_cast<int64_t>(2 * cfg->head_k + cfg->head_v) * 3 * act_bytes(cfg);
+    if (static_cast<int64_t>(n) * cfg->num_heads * ((sb + 4095) / 4096 + (cb + 4095) / 4096) > 0x7fffffffLL)
         return fail(KDA_ERR_INVALID_ARG, "n * num_heads exceeds the launch grid");
     KDA_TRY(need_vec(src_state, "source state"));
     KDA_TRY(need_vec(src_conv, "source conv state"));

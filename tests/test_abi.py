@@ -97,6 +97,12 @@ def test_copy_validation(name):
     assert copy_call(fn, cfg(), ss=MISALIGNED) == kda.KDA_ERR_INVALID_ARG
     assert copy_call(fn, cfg(head_k=48, head_v=48)) == kda.KDA_ERR_UNSUPPORTED
     assert copy_call(fn, cfg(), n=0, ss=None) == kda.KDA_OK
+    # one workgroup per 4 KiB piece of every (pair, head): 17 per head at d=128 with an fp32 state
+    c = cfg()
+    pieces = (c.head_k * c.head_v * 4 + 4095) // 4096 + ((2 * c.head_k + c.head_v) * 3 * 2 + 4095) // 4096
+    n_max = (2 ** 31 - 1) // (c.num_heads * pieces)
+    assert copy_call(fn, c, n=n_max + 1) == kda.KDA_ERR_INVALID_ARG
+    assert "launch grid" in kda.lib().kda_last_error().decode()
 
 
 def prefill_call(c, N=2, T=100, interval=0, ws_bytes=1 << 20, nck=4, flags=0, **ptrs):

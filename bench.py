@@ -12,6 +12,9 @@ step).  The line also carries:
                 (bytes per launch / mean launch duration from HIP events)
                 against the 8 TB/s peak, and the HBM traffic measured by
                 rocprofv3 counters when those were taken on this kernel source
+  slot_copies   the checkpoint and resume copies of the 64 live slots (all
+                heads): microseconds per call and the HBM fraction by the
+                bytes read and written
   prefill       the chunked prefill workload (4 x 8192 tokens, one call per
                 pass): tokens/s and the algorithmic HBM and bf16-MFMA fractions
   cpu_baseline  the fp64 oracle timed on this host on a bounded sample of the

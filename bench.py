@@ -311,31 +311,31 @@ def bench_prefill(steps, warmup):
     init = torch.full((N,), -1, dtype=torch.int32, device="cuda")
     final = torch.arange(N, dtype=torch.int32, device="cuda")
     out = torch.empty((T, H, dv), dtype=act, device="cuda")
-    ws = torch.empty(kda.kda_prefill_workspace_bytes(cfg, N, T, 0, 0), dtype=torch.uint8, device="cuda")
+    paired = kda.KDA_PREFILL_PAIRED
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(cfg, N, T, 0, paired), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def one():
-        kda.kda_prefill_varlen(cfg, cu, q, k, v, z, g, beta, conv_w, norm_w, Sd, Xd, init, final, out, ws,
-                               stream=stream)
+    def timed(flags):
+        def one():
+            kda.kda_prefill_varlen(cfg, cu, q, k, v, z, g, beta, conv_w, norm_w, Sd, Xd, init, final, out, ws,
+                                   flags=flags, stream=stream)
+        return _time_calls(one, steps, warmup, stream)
 
-    for _ in range(warmup):
-        one()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        one()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) * 1e-3 / steps
+    # the paired launch (two workgroups per chain) is the headline: this
+    # workload has 128 chains for 256 compute units
+    t = timed(paired)
+    t1 = timed(0)
     th = T * H
     flops = prefill_flops_per_token_head(dk, dv) * th
     nbytes = prefill_bytes_per_token_head(dk, dv) * th
     return {"workload": f"prefill_4x8k: {N} x {lengths[0]} tokens, H={H}, dk=dv={dk}, bf16, chunk 64",
+            "mode": "paired (KDA_PREFILL_PAIRED)",
             "value": T / t, "unit": "tok/s", "ms_per_call": t * 1e3,
             "mfma_frac": flops / t / BF16_PEAK, "hbm_frac": nbytes / t / HBM_PEAK,
             "alg_flops": flops, "alg_bytes": nbytes,
-            "attainable_frac": max(flops / BF16_PEAK, nbytes / HBM_PEAK) / t}
+            "attainable_frac": max(flops / BF16_PEAK, nbytes / HBM_PEAK) / t,
+            "one_workgroup": {"value": T / t1, "ms_per_call": t1 * 1e3, "mfma_frac": flops / t1 / BF16_PEAK,
+                              "hbm_frac": nbytes / t1 / HBM_PEAK}}
 
 
 def _time_calls(fn, steps, warmup, stream):

@@ -73,7 +73,8 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 
 /* Flags of kda_prefill_varlen (bitwise or). */
 typedef enum {
-    KDA_PREFILL_SPLIT = 1     /* cut sequences into segments at checkpoint positions */
+    KDA_PREFILL_SPLIT = 1,    /* cut sequences into segments at checkpoint positions */
+    KDA_PREFILL_PAIRED = 2    /* two workgroups per chain: state-independent and state phases overlap */
 } kda_prefill_flags;
 
 typedef struct {

@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
 KDA_F32, KDA_BF16 = 0, 1
 KDA_PREFILL_SPLIT = 1
+KDA_PREFILL_PAIRED = 2
 
 # every symbol include/kda.h declares
 EXPORTS = (

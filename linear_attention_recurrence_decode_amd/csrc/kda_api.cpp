@@ -210,9 +210,12 @@ kda_status check_prefill_mode(int32_t ckpt_interval, int32_t flags) {
     if (ckpt_interval < 0 || ckpt_interval % 64 != 0)
         return fail(KDA_ERR_INVALID_ARG, "ckpt_interval must be 0 or a positive multiple of 64 (got %d)",
                     ckpt_interval);
-    if (flags & ~KDA_PREFILL_SPLIT) return fail(KDA_ERR_INVALID_ARG, "unknown prefill flags 0x%x", flags);
+    if (flags & ~(KDA_PREFILL_SPLIT | KDA_PREFILL_PAIRED))
+        return fail(KDA_ERR_INVALID_ARG, "unknown prefill flags 0x%x", flags);
     if ((flags & KDA_PREFILL_SPLIT) && ckpt_interval == 0)
         return fail(KDA_ERR_INVALID_ARG, "KDA_PREFILL_SPLIT needs ckpt_interval > 0");
+    if ((flags & KDA_PREFILL_SPLIT) && (flags & KDA_PREFILL_PAIRED))
+        return fail(KDA_ERR_INVALID_ARG, "KDA_PREFILL_SPLIT and KDA_PREFILL_PAIRED exclude each other");
     return KDA_OK;
 }
 
@@ -220,7 +223,7 @@ kda::PrefillWorkspace workspace_layout(const kda_config* cfg, int32_t num_seqs, 
                                        int32_t ckpt_interval, int32_t flags) {
     return kda::prefill_workspace(num_seqs, cfg->num_heads, total_tokens, cfg->head_k, cfg->head_v,
                                   cfg->act_dtype == KDA_BF16 ? 2 : 4, ckpt_interval,
-                                  (flags & KDA_PREFILL_SPLIT) != 0);
+                                  (flags & KDA_PREFILL_SPLIT) != 0, (flags & KDA_PREFILL_PAIRED) != 0);
 }
 
 }  // namespace
@@ -328,6 +331,16 @@ kda_status kda_prefill_varlen(const kda_config* cfg, int32_t num_seqs, int64_t t
     p.seg_S = split ? reinterpret_cast<float*>(ws + wl.seg_S) : nullptr;
     p.seq_x0 = split ? static_cast<void*>(ws + wl.seq_x0) : nullptr;
     p.state_bf16 = cfg->state_dtype == KDA_BF16 ? 1 : 0;
+    p.ring = nullptr;
+    p.ring_ctr = nullptr;
+    if (wl.ring > 0) {
+        // paired only where every workgroup of the launch is resident at once
+        const int64_t chains = static_cast<int64_t>(num_seqs) * cfg->num_heads;
+        if (kda::pair_grid(chains) <= kda::prefill_pair_capacity(cfg->head_k, cfg->act_dtype)) {
+            p.ring = ws + wl.ring;
+            p.ring_ctr = reinterpret_cast<int32_t*>(ws + wl.ring_ctr);
+        }
+    }
     return hip_status(kda::launch_prefill(cfg->head_k, cfg->head_v, cfg->act_dtype, p,
                                           static_cast<hipStream_t>(stream)),
                       "prefill launch");

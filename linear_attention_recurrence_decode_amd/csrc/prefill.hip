@@ -446,12 +446,109 @@ struct PrefillShape {
     static_assert(NT / (2 * DK) == 2 && NT / DK == 4, "thread mappings assume nt = 4 * dk");
 };
 
+// Shared memory of one chain's workgroup.  sv holds what phase A hands to
+// phase B besides the planes: beta, exp(Gam_r), exp(Gam_end) and
+// exp(Gam_end - Gam_r) per key channel.
+template <int D, typename ACT>
+struct PrefillLds {
+    using Sh = PrefillShape<D, ACT>;
+    __attribute__((aligned(16))) char lds[Sh::BYTES];
+    __attribute__((aligned(16))) float sv[CH + 3 * D];
+    float rq[CH], rk[CH];
+    float gtot[4][D];
+    float part[Sh::NW][CH];
+    float rinv[CH];
+    float ld[4][16][16];       // diagonal blocks of L (fp32)
+    ACT x0[Sh::C * 3];
+    int flag;
+};
+
+// Roles of a chain's workgroup.  FUSED runs both phases of every chunk.  In a
+// paired launch a PRODUCER runs phase A of every chunk of its chain and hands
+// the chunk's planes, sv and SiLU(conv(v)) to its CONSUMER through a ring of
+// RING slots in the workspace; the consumer runs phase B, the epilogue,
+// checkpoints and the final state.  The arithmetic of both phases is the
+// fused code itself, so a paired run gives the fused run's bits.
+constexpr int FUSED = 0, PRODUCER = 1, CONSUMER = 2;
+constexpr int RING = 3;
+// Spin limit of a ring wait (each poll sleeps 128 cycles, several hundred ms
+// in all): far above any legitimate wait (a chunk takes about 20 us), so a
+// wait that reaches it means the partner is gone.
+constexpr int SPIN_LIMIT = 1 << 20;
+
+// Bytes of one ring slot: the LDS planes, sv, then SiLU(conv(v)) (16 floats
+// per thread, 16-byte word e of thread t at word e * NT + t).
+template <int D, typename ACT>
+constexpr int64_t pair_slot_bytes() {
+    using Sh = PrefillShape<D, ACT>;
+    return (static_cast<int64_t>(Sh::BYTES) + (CH + 3 * D) * 4 + Sh::NT * 64 + 255) / 256 * 256;
+}
+
+// Ring words are stored and loaded with the device-coherent cache policy
+// (SC1, the policy of device-scope atomics on gfx950): a store is visible to
+// such loads from every XCD once it has completed, so no L2 write-back or
+// invalidate (a device-scope fence) is needed.  A producer makes every
+// thread wait for its stores to complete, meets at a barrier, and only then
+// moves the chunk counter; a consumer loads only after it has seen the counter.
+constexpr int RING_POL = 16;   // SC1 bit of the buffer cache-policy operand
+constexpr int VMCNT0 = 0x0F70;  // s_waitcnt operand: vector memory count 0, the other counters untouched
+
+__device__ __forceinline__ uint4 ring_ld(__amdgpu_buffer_rsrc_t r, uint32_t word) {
+    const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(word * 16), 0, RING_POL);
+    return make_uint4(static_cast<uint32_t>(v.x), static_cast<uint32_t>(v.y), static_cast<uint32_t>(v.z),
+                      static_cast<uint32_t>(v.w));
+}
+__device__ __forceinline__ void ring_st(__amdgpu_buffer_rsrc_t r, uint32_t word, uint4 x) {
+    i32x4 v;
+    v.x = static_cast<int>(x.x);
+    v.y = static_cast<int>(x.y);
+    v.z = static_cast<int>(x.z);
+    v.w = static_cast<int>(x.w);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(word * 16), 0, RING_POL);
+}
+
+// Copy NW 16-byte words between LDS and a ring slot (from word w0 on), word
+// e by thread e % NT, with six loads in flight before their stores.
+template <int NW, int NT, bool PUT>
+__device__ __forceinline__ void ring_copy(__amdgpu_buffer_rsrc_t r, uint32_t w0, uint4* lds_words, int tp) {
+    constexpr int NB = 6, FULL = NW / NT, REM = NW % NT;
+#pragma unroll
+    for (int b = 0; b < FULL; b += NB) {
+        uint4 w[NB];
+#pragma unroll
+        for (int i = 0; i < NB; i++)
+            if (b + i < FULL) w[i] = PUT ? lds_words[(b + i) * NT + tp] : ring_ld(r, w0 + (b + i) * NT + tp);
+#pragma unroll
+        for (int i = 0; i < NB; i++) {
+            if (b + i >= FULL) continue;
+            if (PUT) ring_st(r, w0 + (b + i) * NT + tp, w[i]);
+            else lds_words[(b + i) * NT + tp] = w[i];
+        }
+    }
+    if (REM > 0 && tp < REM) {
+        if (PUT) ring_st(r, w0 + FULL * NT + tp, lds_words[FULL * NT + tp]);
+        else lds_words[FULL * NT + tp] = ring_ld(r, w0 + FULL * NT + tp);
+    }
+}
+
+// Poll a ring counter until it reaches want (one lane).
+__device__ __forceinline__ bool ring_wait(const int32_t* ctr, int want) {
+    for (int it = 0; it < SPIN_LIMIT; it++) {
+        if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want) return true;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return false;
+}
+
+// One (sequence, head) chain, or one segment of it, in the given role.
 // OUT: outputs, checkpoints and final states of whole sequences or segments.
-// !OUT (segment transitions): blocks [0, items*H) give each segment's end state
-// from a zero state (G), blocks [items*H, 2*items*H) its transition matrix
+// !OUT (segment transitions, FUSED only): trans = false gives the segment's
+// end state from a zero state (G), trans = true its transition matrix
 // (F: the state propagated from the identity with v = 0).
-template <int D, typename ACT, bool OUT>
-__global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
+template <int D, typename ACT, bool OUT, int ROLE>
+__device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds<D, ACT>& sm, int item, const int h,
+                                              bool trans) {
+    static_assert(ROLE == FUSED || OUT, "paired roles produce outputs");
     using Sh = PrefillShape<D, ACT>;
     constexpr int DK = Sh::DK, DV = Sh::DV, NW = Sh::NW, NT = Sh::NT, C = Sh::C;
     constexpr int KS = Sh::KS, IB = Sh::IB, PS = Sh::PS, QS = Sh::QS, VEC = Sh::VEC;
@@ -461,14 +558,18 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
     // operand in one bf16 term; fp32 outputs keep three terms everywhere.
     constexpr bool kOutHi = sizeof(ACT) == 2;
 
-    __shared__ __attribute__((aligned(16))) char lds[Sh::BYTES];
-    __shared__ float beta_s[CH], rq_s[CH], rk_s[CH];
-    __shared__ float eGr_s[DK], eGC_s[DK], eGCr_s[DK];
-    __shared__ float gtot_s[4][DK];
-    __shared__ float part_s[NW][CH];
-    __shared__ float rinv_s[CH];
-    __shared__ float ld_s[4][16][16];      // diagonal blocks of L (fp32)
-    __shared__ ACT x0_s[C * 3];
+    char* const lds = sm.lds;
+    float* const beta_s = sm.sv;
+    float* const eGr_s = sm.sv + CH;
+    float* const eGC_s = sm.sv + CH + DK;
+    float* const eGCr_s = sm.sv + CH + 2 * DK;
+    float (&rq_s)[CH] = sm.rq;
+    float (&rk_s)[CH] = sm.rk;
+    float (&gtot_s)[4][DK] = sm.gtot;
+    float (&part_s)[NW][CH] = sm.part;
+    float (&rinv_s)[CH] = sm.rinv;
+    float (&ld_s)[4][16][16] = sm.ld;
+    ACT (&x0_s)[C * 3] = sm.x0;
 
     char* reg0 = opaque_lds(lds, Sh::O0);
     char* reg1 = opaque_lds(lds, Sh::O1);
@@ -495,13 +596,6 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
     const int lane = tid & 63, wave = tid >> 6;
     const int g4 = lane >> 4, l16 = lane & 15;
     const int H = p.H;
-    const int h = blockIdx.x % H;
-    int item = blockIdx.x / H;
-    bool trans = false;
-    if constexpr (!OUT) {
-        trans = item >= p.max_items;
-        if (trans) item -= p.max_items;
-    }
     const SeqWork wk = p.work[item];
     if (wk.len < 0) return;                    // malformed sequence bounds or unused item: nothing is touched
     if constexpr (!OUT) {
@@ -522,7 +616,7 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
 
     // invalid initial slot or position: NaN outputs, no state written
     if (init < -1 || init >= p.num_slots || start < 0) {
-        if constexpr (OUT) {
+        if constexpr (OUT && ROLE != PRODUCER) {
             for (int64_t e = tid; e < static_cast<int64_t>(L) * DV; e += NT) {
                 const int64_t t = tok0 + e / DV;
                 A::st(static_cast<ACT*>(p.out) + (t * H + h) * DV + e % DV, nan_f32());
@@ -604,6 +698,13 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
         }
     };
     int64_t pos = start;
+    // paired roles: this chain's ring slots and its two counters (chunks
+    // handed over, chunks taken)
+    const int64_t chain = static_cast<int64_t>(item) * H + h;
+    char* const ring = ROLE == FUSED ? nullptr : p.ring + chain * RING * pair_slot_bytes<D, ACT>();
+    int32_t* const ready_ctr = ROLE == FUSED ? nullptr : p.ring_ctr + chain * 32;
+    int32_t* const taken_ctr = ROLE == FUSED ? nullptr : p.ring_ctr + chain * 32 + 16;
+    int chunk = 0;
     // checkpoint counter: a segment that ends at a checkpoint position leaves
     // that checkpoint to the next segment (which starts from the scanned
     // state), so a segment that is not the last of its sequence writes none
@@ -611,7 +712,7 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
     // (clamped so that adding a checkpoint index cannot overflow; no slot lies
     // outside the clamp range)
     const int ck_base = (OUT && p.ckpt_interval > 0) ? min(max(p.ckpt_base[seq], -(1 << 30)), 1 << 30) : 0;
-    if constexpr (OUT) {
+    if constexpr (OUT && ROLE != PRODUCER) {
         // a segment after the first starts at a checkpoint position: its
         // initial state (from the scan of the segment transitions) is that
         // checkpoint
@@ -630,7 +731,7 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
     Staged<Sh::NU> stg;
     int n = L > 0 ? min(L, CH - static_cast<int>(pos % CH)) : 0;
     int64_t tc0 = tok0;
-    if (L > 0) {
+    if (ROLE != CONSUMER && L > 0) {
         const int tp = opq(tid);
         stage_issue<ACT, DK, DV, NT>(stg, p, x0_s, ctx0, tc0, n, H, h, tp);
         stage_commit<ACT, DK, DV, NT>(stg, raw, beta_s, tp);
@@ -641,6 +742,9 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
         float vh[4][4];    // SiLU(conv(v)) in accumulator layout
         float km[16];      // K- column of this thread, kept for the transposed copy
         float (&gq)[16] = stg.gq;   // log decay of this thread's (channel, quarter), then its prefix sums
+        char* const rslot = ROLE == FUSED ? nullptr : ring + (chunk % RING) * pair_slot_bytes<D, ACT>();
+
+        if constexpr (ROLE != CONSUMER) {
 
         // ---------------- A2: causal conv + SiLU (q, k channels to LDS; v to registers)
         {
@@ -835,7 +939,96 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
             dl[0] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
             dl[1] = make_uint4(wl[4], wl[5], wl[6], wl[7]);
         }
+        // producer: the previous chunk's ring stores were issued a whole
+        // phase ago; once every thread has seen its own complete (phase A
+        // issues no other global access), that chunk is published
+        if constexpr (ROLE == PRODUCER) __builtin_amdgcn_s_waitcnt(VMCNT0);
         __syncthreads();
+        if constexpr (ROLE == PRODUCER) {
+            if (tid == 0 && chunk > 0) __hip_atomic_store(ready_ctr, chunk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        }   // phase A
+
+        // 16-byte words of the planes phase B reads: K+ and Q+ (words
+        // [0, NPA)), K-^T, L and P (words [PB0, PB0 + NPB)); with bf16 outputs
+        // phase B reads only the hi planes of Q+ and P
+        constexpr int NPW = Sh::BYTES / 16;
+        constexpr int NPA = (Sh::O1 + (kOutHi ? CH * PS * 2 : Sh::R1)) / 16;
+        constexpr int PB0 = Sh::O2 / 16;
+        constexpr int NPB = (Sh::O5 + (kOutHi ? CH * QS * 2 : Sh::R5)) / 16 - PB0;
+        static_assert(Sh::BYTES % 16 == 0 && Sh::O1 % 16 == 0 && Sh::O2 % 16 == 0 && Sh::O5 % 16 == 0 &&
+                      (CH * PS * 2) % 16 == 0 && (CH * QS * 2) % 16 == 0, "16-byte plane words");
+        constexpr int NSV = (CH + 3 * DK) / 4;               // 16-byte words of sv
+        static_assert(NSV <= NT, "one sv word per thread");
+        const auto rr = make_rsrc(rslot, static_cast<uint32_t>(pair_slot_bytes<D, ACT>()));
+        if constexpr (ROLE == PRODUCER) {
+            // hand the chunk over: wait until the consumer has taken the
+            // chunk that last used this slot, request the next chunk's
+            // inputs, store planes, sv and SiLU(conv(v)) (published at the
+            // end of the next chunk's phase A, or after the last chunk)
+            if (chunk >= RING) {
+                if (tid == 0) sm.flag = ring_wait(taken_ctr, chunk - RING + 1);
+                __syncthreads();
+                if (!sm.flag) return;                         // the consumer is gone
+            }
+            const int done_next = done + n;
+            const int64_t pos_next = pos + n;
+            const int n_next = done_next < L ? min(L - done_next, CH - static_cast<int>(pos_next % CH)) : 0;
+            if (n_next > 0) stage_issue<ACT, DK, DV, NT>(stg, p, x0_s, ctx0, tok0 + done_next, n_next, H, h, opq(tid));
+            else stage_clear(stg);
+            {
+                const int tp = opq(tid);
+                ring_copy<NPA, NT, true>(rr, 0, reinterpret_cast<uint4*>(lds), tp);
+                ring_copy<NPB, NT, true>(rr, PB0, reinterpret_cast<uint4*>(lds) + PB0, tp);
+                if (tp < NSV) ring_st(rr, NPW + tp, reinterpret_cast<const uint4*>(sm.sv)[tp]);
+#pragma unroll
+                for (int tb = 0; tb < 4; tb++)
+                    ring_st(rr, NPW + NSV + tb * NT + tp,
+                            make_uint4(__float_as_uint(vh[tb][0]), __float_as_uint(vh[tb][1]),
+                                       __float_as_uint(vh[tb][2]), __float_as_uint(vh[tb][3])));
+            }
+            // every thread has read its planes, sv and beta out of LDS
+            // (its stores need not be complete) before the next chunk's raw
+            // rows and beta overwrite them
+            __syncthreads();
+            if (n_next > 0) stage_commit<ACT, DK, DV, NT>(stg, raw, beta_s, opq(tid));
+            done = done_next;
+            pos = pos_next;
+            n = n_next;
+            tc0 = tok0 + done;
+            chunk++;
+            __syncthreads();
+            continue;
+        }
+        if constexpr (ROLE == CONSUMER) {
+            // take the chunk over: planes and sv into LDS, SiLU(conv(v)) into
+            // registers
+            if (tid == 0) sm.flag = ring_wait(ready_ctr, chunk + 1);
+            __syncthreads();
+            if (!sm.flag) {
+                // the producer is gone: NaN outputs from here on, no state written
+                for (int64_t e = tid; e < static_cast<int64_t>(L - done) * DV; e += NT) {
+                    const int64_t t = tc0 + e / DV;
+                    A::st(out + (t * H + h) * DV + e % DV, nan_f32());
+                }
+                return;
+            }
+            {
+                const int tp = opq(tid);
+                ring_copy<NPA, NT, false>(rr, 0, reinterpret_cast<uint4*>(lds), tp);
+                ring_copy<NPB, NT, false>(rr, PB0, reinterpret_cast<uint4*>(lds) + PB0, tp);
+                if (tp < NSV) reinterpret_cast<uint4*>(sm.sv)[tp] = ring_ld(rr, NPW + tp);
+#pragma unroll
+                for (int tb = 0; tb < 4; tb++) {
+                    const uint4 x = ring_ld(rr, NPW + NSV + tb * NT + tp);
+                    vh[tb][0] = __uint_as_float(x.x);
+                    vh[tb][1] = __uint_as_float(x.y);
+                    vh[tb][2] = __uint_as_float(x.z);
+                    vh[tb][3] = __uint_as_float(x.w);
+                }
+            }
+            __syncthreads();
+        }
 
         // ---------------- B: state-dependent part; wave = 16-column strip of S
         f32x4 accr[4];     // readouts O (rows 16tb + 4g + e, this lane's column)
@@ -948,8 +1141,14 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
         const int done_next = done + n;
         const int64_t pos_next = pos + n;
         const int n_next = done_next < L ? min(L - done_next, CH - static_cast<int>(pos_next % CH)) : 0;
-        if (n_next > 0) stage_issue<ACT, DK, DV, NT>(stg, p, x0_s, ctx0, tok0 + done_next, n_next, H, h, opq(tid));
-        else stage_clear(stg);
+        if constexpr (ROLE == FUSED) {
+            if (n_next > 0) stage_issue<ACT, DK, DV, NT>(stg, p, x0_s, ctx0, tok0 + done_next, n_next, H, h, opq(tid));
+            else stage_clear(stg);
+        } else {
+            // every read of this slot is complete (its values fed phase B):
+            // the producer may refill it
+            if (tid == 0) __hip_atomic_store(taken_ctr, chunk + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
 
         // ---------------- epilogue: gated RMSNorm over dv, then the outputs
         if constexpr (OUT) {
@@ -980,7 +1179,7 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
         }
 
         // the raw-row region and beta are free: every wave is past its state phase
-        if (n_next > 0) stage_commit<ACT, DK, DV, NT>(stg, raw, beta_s, opq(tid));
+        if (ROLE == FUSED && n_next > 0) stage_commit<ACT, DK, DV, NT>(stg, raw, beta_s, opq(tid));
         done = done_next;
         pos = pos_next;
         // ---------------- checkpoints: interval boundaries inside, and the end
@@ -1002,7 +1201,15 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
         }
         n = n_next;
         tc0 = tok0 + done;
+        chunk++;
         __syncthreads();
+    }
+    if constexpr (ROLE == PRODUCER) {
+        // publish the last chunk
+        __builtin_amdgcn_s_waitcnt(VMCNT0);
+        __syncthreads();
+        if (tid == 0 && chunk > 0) __hip_atomic_store(ready_ctr, chunk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
     }
 
     if constexpr (OUT) {
@@ -1017,11 +1224,47 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
     }
 }
 
+// One workgroup per chain (OUT), or per segment transition (!OUT): blocks
+// [0, items*H) give each segment's end state from a zero state (G), blocks
+// [items*H, 2*items*H) its transition matrix (F).
+template <int D, typename ACT, bool OUT>
+__global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
+    __shared__ PrefillLds<D, ACT> sm;
+    const int h = blockIdx.x % p.H;
+    int item = blockIdx.x / p.H;
+    bool trans = false;
+    if constexpr (!OUT) {
+        trans = item >= p.max_items;
+        if (trans) item -= p.max_items;
+    }
+    prefill_chain<D, ACT, OUT, FUSED>(p, sm, item, h, trans);
+}
+
+// Two workgroups per chain, launched cooperatively so that all of them are
+// resident together (a consumer waits on its producer and the other way
+// round).  Blocks 16m .. 16m+7 produce for chains 8m .. 8m+7 and blocks
+// 16m+8 .. 16m+15 consume them: the two workgroups of a chain have block
+// indices equal mod 8, which places them in the same L2 when workgroups are
+// dealt round-robin over the 8 XCDs.
+template <int D, typename ACT>
+__global__ __launch_bounds__(4 * D) void prefill_pair_kernel(PrefillParams p) {
+    __shared__ PrefillLds<D, ACT> sm;
+    const int b = blockIdx.x;
+    const int chain = 8 * (b / 16) + (b % 8);
+    if (chain >= p.N * p.H) return;
+    const int h = chain % p.H, item = chain / p.H;
+    if ((b % 16) < 8) prefill_chain<D, ACT, true, PRODUCER>(p, sm, item, h, false);
+    else prefill_chain<D, ACT, true, CONSUMER>(p, sm, item, h, false);
+}
+
 // One workgroup: per-sequence work items ordered longest first, so the
 // longest chains start first.  Sequences with bounds outside [0, T] get
 // len = -1 and are skipped by the prefill kernel.
 __global__ __launch_bounds__(1024) void prefill_meta_kernel(const int32_t* cu, const int64_t* sp, int32_t N,
-                                                            int64_t T, SeqWork* work) {
+                                                            int64_t T, SeqWork* work, int32_t* ring_ctr,
+                                                            int32_t n_ctr) {
+    // the ring counters of a paired launch start from zero
+    for (int i = threadIdx.x; i < n_ctr; i += 1024) ring_ctr[i] = 0;
     for (int i = threadIdx.x; i < N; i += 1024) {
         const int64_t a = cu[i], b = cu[i + 1];
         const bool ok = a >= 0 && b >= a && b <= T;
@@ -1202,12 +1445,19 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(PrefillParams p) {
 template <int D, typename ACT>
 hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
     if (!p.split) {
+        const int64_t blocks = static_cast<int64_t>(p.N) * p.H;
         hipLaunchKernelGGL(prefill_meta_kernel, dim3(1), dim3(1024), 0, s, p.cu_seqlens, p.start_pos, p.N, p.T,
-                           p.work);
+                           p.work, p.ring_ctr, p.ring ? static_cast<int32_t>(blocks * 32) : 0);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        const int64_t blocks = static_cast<int64_t>(p.N) * p.H;
         if (blocks == 0) return hipSuccess;
+        if (p.ring) {
+            PrefillParams pc = p;
+            void* args[] = {&pc};
+            return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&prefill_pair_kernel<D, ACT>),
+                                              dim3(static_cast<unsigned>(pair_grid(blocks))), dim3(4 * D), args, 0,
+                                              s);
+        }
         hipLaunchKernelGGL((prefill_kernel<D, ACT, true>), dim3(static_cast<unsigned>(blocks)), dim3(4 * D), 0, s,
                            p);
         return hipGetLastError();
@@ -1229,6 +1479,28 @@ hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
 
 }  // namespace
 
+int64_t pair_grid(int64_t chains) { return 16 * ((chains + 7) / 8); }
+
+int64_t prefill_pair_slot_bytes(int dk, int act) {
+    if (act == 1) return dk == 32 ? pair_slot_bytes<32, bf16_t>() : dk == 64 ? pair_slot_bytes<64, bf16_t>()
+                                                                             : pair_slot_bytes<128, bf16_t>();
+    return dk == 32 ? pair_slot_bytes<32, float>() : pair_slot_bytes<64, float>();
+}
+
+int64_t prefill_pair_capacity(int dk, int act) {
+    const void* f = nullptr;
+    if (act == 1) f = dk == 32 ? reinterpret_cast<const void*>(&prefill_pair_kernel<32, bf16_t>)
+                    : dk == 64 ? reinterpret_cast<const void*>(&prefill_pair_kernel<64, bf16_t>)
+                               : reinterpret_cast<const void*>(&prefill_pair_kernel<128, bf16_t>);
+    else f = dk == 32 ? reinterpret_cast<const void*>(&prefill_pair_kernel<32, float>)
+                      : reinterpret_cast<const void*>(&prefill_pair_kernel<64, float>);
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, 4 * dk, 0) != hipSuccess) return 0;
+    return static_cast<int64_t>(cus) * per_cu;
+}
+
 bool prefill_supported(int dk, int dv, int act) {
     if (dk != dv) return false;
     if (act == 1) return dk == 32 || dk == 64 || dk == 128;
@@ -1236,7 +1508,7 @@ bool prefill_supported(int dk, int dv, int act) {
 }
 
 PrefillWorkspace prefill_workspace(int32_t N, int32_t H, int64_t T, int dk, int dv, int act_bytes,
-                                   int32_t ckpt_interval, bool split) {
+                                   int32_t ckpt_interval, bool split, bool paired) {
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     PrefillWorkspace w{};
     const int64_t items = split && ckpt_interval > 0 ? 2 * static_cast<int64_t>(N) + T / ckpt_interval : N;
@@ -1257,6 +1529,13 @@ PrefillWorkspace prefill_workspace(int32_t N, int32_t H, int64_t T, int dk, int 
         off += up(per * dk * dv * 4);
         w.seq_x0 = off;
         off += up(static_cast<size_t>(N) * H * (2 * dk + dv) * 3 * act_bytes);
+    }
+    const int64_t chains = static_cast<int64_t>(N) * H;
+    if (paired && !split && chains > 0 && chains <= PAIR_MAX_CHAINS) {
+        w.ring_ctr = off;
+        off += up(static_cast<size_t>(chains) * 32 * 4);
+        w.ring = off;
+        off += static_cast<size_t>(chains) * RING * prefill_pair_slot_bytes(dk, act_bytes == 2 ? 1 : 0);
     }
     w.bytes = off;
     return w;

@@ -133,7 +133,10 @@ def test_prefill_validation():
     assert prefill_call(cfg(), interval=64, ckb=None) == kda.KDA_ERR_INVALID_ARG
     assert prefill_call(cfg(), interval=64, nck=0) == kda.KDA_ERR_INVALID_ARG
     assert prefill_call(cfg(), N=0, cu=None) == kda.KDA_OK                      # nothing to do
-    assert prefill_call(cfg(), flags=2) == kda.KDA_ERR_INVALID_ARG                 # unknown flag
+    assert prefill_call(cfg(), flags=4) == kda.KDA_ERR_INVALID_ARG                 # unknown flag
+    both = kda.KDA_PREFILL_SPLIT | kda.KDA_PREFILL_PAIRED
+    assert prefill_call(cfg(), interval=64, flags=both) == kda.KDA_ERR_INVALID_ARG   # exclusive modes
+    assert "exclude" in kda.last_error()
     assert prefill_call(cfg(), flags=kda.KDA_PREFILL_SPLIT) == kda.KDA_ERR_INVALID_ARG   # split without interval
     assert "interval" in kda.last_error()
     assert prefill_call(cfg(), interval=64, flags=kda.KDA_PREFILL_SPLIT, ws_bytes=1 << 20) == kda.KDA_ERR_WORKSPACE
@@ -143,6 +146,13 @@ def test_prefill_validation():
     ws_split = kda.kda_prefill_workspace_bytes(cfg(), 16, 1 << 18, 4096, kda.KDA_PREFILL_SPLIT)
     segs = 2 * 16 + (1 << 18) // 4096
     assert ws_split >= segs * 4 * 3 * 128 * 128 * 4 and ws_split % 256 == 0
+    # paired: two ring slots per (sequence, head) chain, each holding a chunk's planes (at least
+    # K+, Q+ and K-^T as bf16 hi/lo pairs) and SiLU(conv(v)) in fp32; offered up to 1024 chains
+    ws_pair = kda.kda_prefill_workspace_bytes(cfg(), 16, 1 << 18, 0, kda.KDA_PREFILL_PAIRED)
+    slot_min = 3 * 2 * 64 * 128 * 2 + 64 * 128 * 4
+    assert ws_pair >= ws + 16 * 4 * 2 * slot_min and ws_pair % 256 == 0
+    assert kda.kda_prefill_workspace_bytes(cfg(), 512, 1 << 18, 0, kda.KDA_PREFILL_PAIRED) == \
+        kda.kda_prefill_workspace_bytes(cfg(), 512, 1 << 18)
     with pytest.raises(kda.KdaError):
         kda.kda_prefill_workspace_bytes(cfg(), 16, 1 << 18, 0, kda.KDA_PREFILL_SPLIT)
 

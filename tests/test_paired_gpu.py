@@ -1,0 +1,104 @@
+"""GPU tests of the paired prefill (KDA_PREFILL_PAIRED): two workgroups per
+(sequence, head) chain, one for the state-independent phase of every chunk
+and one for the state phase, joined by a ring in the workspace.
+
+Both workgroups run the one-workgroup kernel's own arithmetic, so a paired
+call must reproduce the one-workgroup call bit for bit (outputs, final
+states, conv states, checkpoints), and through it the oracle.  A call with
+more chains than the device can hold as resident pairs runs the
+one-workgroup kernel instead, with the same results.
+"""
+import numpy as np
+import pytest
+
+import linear_attention_recurrence_decode_amd as kda
+import workloads as wl
+from tests.helpers import bits, host, say
+from tests.prefill_runner import Run, check_against_oracle, oracle_for, resume_and_finish, states_for
+from tests.test_prefill_gpu import CASES
+
+pytestmark = pytest.mark.gpu
+
+PAIRED = kda.KDA_PREFILL_PAIRED
+
+
+def assert_same_bits(a, b):
+    assert np.array_equal(bits(a.out), bits(b.out))
+    assert np.array_equal(bits(a.Sd), bits(b.Sd))
+    assert np.array_equal(bits(a.Xd), bits(b.Xd))
+    if a.interval:
+        assert np.array_equal(bits(a.ckS[:a.nck]), bits(b.ckS[:b.nck]))
+        assert np.array_equal(bits(a.ckX[:a.nck]), bits(b.ckX[:b.nck]))
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_paired_matches_oracle_and_one_workgroup_bits(name):
+    seed, shape, lengths, starts, with_state, g_scale, norm_w = CASES[name]
+    say(f"paired case {name}: H={shape.H} d={shape.dk} act={shape.act} lengths={lengths} starts={starts}")
+    inp = wl.token_inputs(seed, shape, sum(lengths), g_scale=g_scale, norm_w=norm_w)
+    S0 = X0 = None
+    if with_state:
+        S0, X0 = states_for(seed, shape, len(lengths))
+    interval = 128
+    paired = Run(shape, inp, lengths, starts=starts, S0=S0, X0=X0, interval=interval, flags=PAIRED).launch()
+    check_against_oracle(paired, oracle_for(paired, S0, X0))
+    single = Run(shape, inp, lengths, starts=starts, S0=S0, X0=X0, interval=interval).launch()
+    assert_same_bits(paired, single)
+
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_paired_resume_is_bitwise_identical(act):
+    """Resume at an interval checkpoint, paired on both sides, reproduces the
+    straight paired run's later outputs and final states bit for bit."""
+    shape = wl.LayerShape(2, 64, 64, act=act)
+    lengths, starts = [700, 300, 129], [0, 64, 3]
+    inp = wl.token_inputs(60, shape, sum(lengths))
+    S0, X0 = states_for(60, shape, len(lengths))
+    straight = Run(shape, inp, lengths, starts=starts, S0=S0, X0=X0, interval=128, flags=PAIRED).launch()
+    resumed, seqs, res_pos, _, idx = resume_and_finish(straight, [2, 1, 0])
+    say(f"  resumed {seqs} at {res_pos}")
+    assert np.array_equal(bits(resumed.out), bits(straight.out[idx]))
+    for j, n in enumerate(seqs):
+        assert np.array_equal(bits(resumed.Sd[int(resumed.final[j])]), bits(straight.Sd[int(straight.final[n])]))
+
+
+def test_paired_4x8192_full_size_equals_one_workgroup():
+    """The 4 x 8192-token workload (128 chains, the shape the paired launch is
+    for): every output, final state and conv state equals the one-workgroup
+    run bit for bit (that run is checked against the oracle and the decode
+    kernel in the prefill tests)."""
+    w = wl.WORKLOADS["prefill_4x8k"]
+    shape, lengths = w["shape"], w["lengths"]
+    inp = wl.token_inputs(w["seed"], shape, sum(lengths))
+    say(f"paired full size: lengths={lengths} H={shape.H}")
+    paired = Run(shape, inp, lengths, flags=PAIRED).launch()
+    single = Run(shape, inp, lengths).launch()
+    assert np.isfinite(host(paired.out)).all()
+    assert_same_bits(paired, single)
+
+
+def test_paired_more_chains_than_pairs_falls_back():
+    """160 chains at dk = dv = 128 need 320 resident workgroups, more than one
+    per compute unit: the call runs the one-workgroup kernel, same bits."""
+    shape = wl.LayerShape(4, 128, 128)
+    rng = np.random.default_rng(61)
+    lengths = [int(x) for x in rng.integers(1, 90, 40)]
+    inp = wl.token_inputs(61, shape, sum(lengths))
+    paired = Run(shape, inp, lengths, interval=64, flags=PAIRED).launch()
+    single = Run(shape, inp, lengths, interval=64).launch()
+    assert_same_bits(paired, single)
+    check_against_oracle(paired, oracle_for(paired, heads=[1]), heads=[1])
+
+
+def test_paired_invalid_slot_gives_nan_and_writes_nothing():
+    shape = wl.LayerShape(2, 64, 64)
+    lengths = [70, 200]
+    inp = wl.token_inputs(62, shape, sum(lengths))
+    run = Run(shape, inp, lengths, flags=PAIRED)
+    run.init = np.array([-1, 999], np.int32)
+    before = bits(run.Sd[int(run.final[1])])
+    run.launch()
+    out = host(run.out)
+    assert np.isfinite(out[:70]).all() and np.isnan(out[70:]).all()
+    assert np.array_equal(bits(run.Sd[int(run.final[1])]), before)
+    assert np.isfinite(host(run.Sd)[int(run.final[0])]).all()

@@ -282,6 +282,14 @@ __device__ __forceinline__ void store_pool_strip(void* pool, int64_t slot_head, 
         }
 }
 
+// One causal conv tap sum over a 4-token window (w.w multiplies the newest).
+__device__ __forceinline__ float conv4(const float4& w, float a, float b, float c, float d) {
+    float y = w.x * a;
+    y = fmaf(w.y, b, y);
+    y = fmaf(w.z, c, y);
+    return fmaf(w.w, d, y);
+}
+
 // Registers holding one chunk's staged inputs between the loads and the LDS
 // stores: raw q|k|v rows (with 3 rows of left context) as 16-byte words, this
 // thread's 16 log-decay values, and (threads 0..63) one beta.
@@ -404,6 +412,56 @@ __device__ __forceinline__ void stage_clear(Staged<NU>& st) {
     st.beta = 0.f;
 }
 
+// The chunk's raw v rows for a consumer: CH + 3 rows of DV values (row 0 is
+// three tokens before the chunk [tc0, tc0 + n)), 16-byte word u of the rows
+// loaded by thread u % NT.  Rows before the sequence start come from the
+// initial conv state; rows past the chunk read as zero (outside the
+// resource) and only feed masked rows.
+template <typename ACT, int DV, int NT>
+struct VWin {
+    static constexpr int VEC = 16 / static_cast<int>(sizeof(ACT));
+    static constexpr int UPR = DV / VEC;                 // words per row
+    static constexpr int UNITS = (CH + 3) * UPR;
+    static constexpr int NI = (UNITS + NT - 1) / NT;
+    uint4 w[NI];    // loaded words of this thread
+    int d0;         // rows taken from the initial conv state
+};
+
+template <typename ACT, int DV, int NT>
+__device__ __forceinline__ void vwin_issue(VWin<ACT, DV, NT>& vw, const PrefillParams& p, int64_t ctx0,
+                                           int64_t tc0, int n, int H, int h, int tp) {
+    using VW = VWin<ACT, DV, NT>;
+    const int64_t first = max(tc0 - 3, ctx0);
+    const int d0 = static_cast<int>(first - (tc0 - 3));
+    vw.d0 = d0;
+    const auto rv = make_rsrc(static_cast<const ACT*>(p.v) + (first * H + h) * DV,
+                              static_cast<uint32_t>(((tc0 + n - 1 - first) * H + 1) * DV * sizeof(ACT)));
+    const uint32_t rowb = static_cast<uint32_t>(H * DV * sizeof(ACT));
+#pragma unroll
+    for (int i = 0; i < VW::NI; i++) {
+        const int u = tp + i * NT, r = u / VW::UPR, col = (u % VW::UPR) * VW::VEC;
+        const uint32_t vo = (u < VW::UNITS && r >= d0) ? static_cast<uint32_t>(r - d0) * rowb + col * sizeof(ACT)
+                                                       : 0x80000000u;
+        const float4 x = buf_ld4(rv, vo, 0);
+        vw.w[i] = make_uint4(__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z), __float_as_uint(x.w));
+    }
+}
+
+template <typename ACT, int DK, int DV, int NT>
+__device__ __forceinline__ void vwin_commit(const VWin<ACT, DV, NT>& vw, ACT* vwin, const ACT* x0, int tp) {
+    using VW = VWin<ACT, DV, NT>;
+    const int d0 = vw.d0;
+#pragma unroll
+    for (int i = 0; i < VW::NI; i++) {
+        const int u = tp + i * NT, r = u / VW::UPR, col = (u % VW::UPR) * VW::VEC;
+        if (u < VW::UNITS && r >= d0) *reinterpret_cast<uint4*>(vwin + r * DV + col) = vw.w[i];
+    }
+    for (int e = tp; e < d0 * DV; e += NT) {
+        const int r = e / DV, c = e % DV;
+        vwin[r * DV + c] = x0[(2 * DK + c) * 3 + 3 - d0 + r];
+    }
+}
+
 // Store the staged raw rows and beta into LDS (rows of CR elements: q, k, v).
 template <typename ACT, int DK, int DV, int NT, int NU>
 __device__ __forceinline__ void stage_commit(const Staged<NU>& st, ACT* raw, float* beta_s, int tp) {
@@ -460,6 +518,7 @@ struct PrefillLds {
     float rinv[CH];
     float ld[4][16][16];       // diagonal blocks of L (fp32)
     ACT x0[Sh::C * 3];
+    ACT vwin[sizeof(ACT) == 2 ? 1 : (CH + 3) * D];   // consumer's raw v rows (fp32 activations)
     int flag;
 };
 
@@ -476,12 +535,11 @@ constexpr int RING = 3;
 // wait that reaches it means the partner is gone.
 constexpr int SPIN_LIMIT = 1 << 20;
 
-// Bytes of one ring slot: the LDS planes, sv, then SiLU(conv(v)) (16 floats
-// per thread, 16-byte word e of thread t at word e * NT + t).
+// Bytes of one ring slot: the LDS planes, then sv.
 template <int D, typename ACT>
 constexpr int64_t pair_slot_bytes() {
     using Sh = PrefillShape<D, ACT>;
-    return (static_cast<int64_t>(Sh::BYTES) + (CH + 3 * D) * 4 + Sh::NT * 64 + 255) / 256 * 256;
+    return (static_cast<int64_t>(Sh::BYTES) + (CH + 3 * D) * 4 + 255) / 256 * 256;
 }
 
 // Ring words are stored and loaded with the device-coherent cache policy
@@ -508,10 +566,10 @@ __device__ __forceinline__ void ring_st(__amdgpu_buffer_rsrc_t r, uint32_t word,
 }
 
 // Copy NW 16-byte words between LDS and a ring slot (from word w0 on), word
-// e by thread e % NT, with six loads in flight before their stores.
-template <int NW, int NT, bool PUT>
+// e by thread e % NT, with NB loads in flight before their stores.
+template <int NW, int NT, bool PUT, int NB>
 __device__ __forceinline__ void ring_copy(__amdgpu_buffer_rsrc_t r, uint32_t w0, uint4* lds_words, int tp) {
-    constexpr int NB = 6, FULL = NW / NT, REM = NW % NT;
+    constexpr int FULL = NW / NT, REM = NW % NT;
 #pragma unroll
     for (int b = 0; b < FULL; b += NB) {
         uint4 w[NB];
@@ -591,6 +649,11 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
     uint16_t* pp_h = reinterpret_cast<uint16_t*>(reg5);          // P planes [CH][QS]
     uint16_t* pp_l = pp_h + CH * QS;
     ACT* raw = reinterpret_cast<ACT*>(reg2);                     // [CH+3][CR]
+    // consumer: raw v rows [CH+3][DV]; with bf16 outputs phase B never reads
+    // the Q+ lo plane, whose region holds them
+    ACT* vwin = kOutHi ? reinterpret_cast<ACT*>(qp_l) : sm.vwin;
+    static_assert(!kOutHi || (CH + 3) * DV * static_cast<int>(sizeof(ACT)) <= Sh::R1 - CH * PS * 2,
+                  "the v rows fit in the Q+ lo plane");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -742,6 +805,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
         float vh[4][4];    // SiLU(conv(v)) in accumulator layout
         float km[16];      // K- column of this thread, kept for the transposed copy
         float (&gq)[16] = stg.gq;   // log decay of this thread's (channel, quarter), then its prefix sums
+        int n_next_p = 0;           // producer: length of the next chunk
         char* const rslot = ROLE == FUSED ? nullptr : ring + (chunk % RING) * pair_slot_bytes<D, ACT>();
 
         if constexpr (ROLE != CONSUMER) {
@@ -770,16 +834,14 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             const int ln = tp & 63, jc = 16 * (tp >> 6) + (ln & 15), gg = ln >> 4;
 #pragma unroll
             for (int tb = 0; tb < 4; tb++) {
+                if constexpr (ROLE == PRODUCER) break;       // the consumer convolves v itself
                 const int rb = 16 * tb + 4 * gg;
                 float x[7];
 #pragma unroll
                 for (int m = 0; m < 7; m++) x[m] = A::ld(raw + (rb + m) * CR + 2 * DK + jc);
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    float y = wv.x * x[e];
-                    y = fmaf(wv.y, x[e + 1], y);
-                    y = fmaf(wv.z, x[e + 2], y);
-                    y = fmaf(wv.w, x[e + 3], y);
+                    const float y = conv4(wv, x[e], x[e + 1], x[e + 2], x[e + 3]);
                     vh[tb][e] = (rb + e) < n ? silu(y) : 0.f;
                 }
             }
@@ -853,7 +915,21 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
                 st_split2(km_h, km_l, idx, PS, km[r], km[r + 1]);
             }
         }
+        // producer: the previous chunk's ring stores were issued a phase
+        // ago; once every thread has seen its own complete (no other global
+        // access is in flight: this chunk's inputs were committed before
+        // phase A), that chunk is published.  Then the next chunk's inputs
+        // are requested (the staging registers are free after A4), so they
+        // arrive during A5, A6 and the ring stores.
+        if constexpr (ROLE == PRODUCER) __builtin_amdgcn_s_waitcnt(VMCNT0);
         __syncthreads();
+        if constexpr (ROLE == PRODUCER) {
+            if (tid == 0 && chunk > 0) __hip_atomic_store(ready_ctr, chunk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int done_next = done + n;
+            n_next_p = done_next < L ? min(L - done_next, CH - static_cast<int>((pos + n) % CH)) : 0;
+            if (n_next_p > 0) stage_issue<ACT, DK, DV, NT>(stg, p, x0_s, ctx0, tok0 + done_next, n_next_p, H, h, opq(tid));
+            else stage_clear(stg);
+        }
 
         // ---------------- A5: L = Diag(b) strictLower(K+ K-^T), P = lower(Q+ K-^T);
         // one job per 16x16 block pair (a, b) computes both, sharing the K-
@@ -939,14 +1015,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             dl[0] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
             dl[1] = make_uint4(wl[4], wl[5], wl[6], wl[7]);
         }
-        // producer: the previous chunk's ring stores were issued a whole
-        // phase ago; once every thread has seen its own complete (phase A
-        // issues no other global access), that chunk is published
-        if constexpr (ROLE == PRODUCER) __builtin_amdgcn_s_waitcnt(VMCNT0);
         __syncthreads();
-        if constexpr (ROLE == PRODUCER) {
-            if (tid == 0 && chunk > 0) __hip_atomic_store(ready_ctr, chunk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
         }   // phase A
 
         // 16-byte words of the planes phase B reads: K+ and Q+ (words
@@ -963,9 +1032,9 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
         const auto rr = make_rsrc(rslot, static_cast<uint32_t>(pair_slot_bytes<D, ACT>()));
         if constexpr (ROLE == PRODUCER) {
             // hand the chunk over: wait until the consumer has taken the
-            // chunk that last used this slot, request the next chunk's
-            // inputs, store planes, sv and SiLU(conv(v)) (published at the
-            // end of the next chunk's phase A, or after the last chunk)
+            // chunk that last used this slot, then store planes and sv
+            // (published in the next chunk's phase A, or after the last
+            // chunk)
             if (chunk >= RING) {
                 if (tid == 0) sm.flag = ring_wait(taken_ctr, chunk - RING + 1);
                 __syncthreads();
@@ -973,19 +1042,12 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             }
             const int done_next = done + n;
             const int64_t pos_next = pos + n;
-            const int n_next = done_next < L ? min(L - done_next, CH - static_cast<int>(pos_next % CH)) : 0;
-            if (n_next > 0) stage_issue<ACT, DK, DV, NT>(stg, p, x0_s, ctx0, tok0 + done_next, n_next, H, h, opq(tid));
-            else stage_clear(stg);
+            const int n_next = n_next_p;
             {
                 const int tp = opq(tid);
-                ring_copy<NPA, NT, true>(rr, 0, reinterpret_cast<uint4*>(lds), tp);
-                ring_copy<NPB, NT, true>(rr, PB0, reinterpret_cast<uint4*>(lds) + PB0, tp);
+                ring_copy<NPA, NT, true, 6>(rr, 0, reinterpret_cast<uint4*>(lds), tp);
+                ring_copy<NPB, NT, true, 6>(rr, PB0, reinterpret_cast<uint4*>(lds) + PB0, tp);
                 if (tp < NSV) ring_st(rr, NPW + tp, reinterpret_cast<const uint4*>(sm.sv)[tp]);
-#pragma unroll
-                for (int tb = 0; tb < 4; tb++)
-                    ring_st(rr, NPW + NSV + tb * NT + tp,
-                            make_uint4(__float_as_uint(vh[tb][0]), __float_as_uint(vh[tb][1]),
-                                       __float_as_uint(vh[tb][2]), __float_as_uint(vh[tb][3])));
             }
             // every thread has read its planes, sv and beta out of LDS
             // (its stores need not be complete) before the next chunk's raw
@@ -1001,8 +1063,11 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             continue;
         }
         if constexpr (ROLE == CONSUMER) {
-            // take the chunk over: planes and sv into LDS, SiLU(conv(v)) into
-            // registers
+            // take the chunk over: request the chunk's raw v rows (with 3
+            // rows of left context), wait for the chunk, then planes and sv
+            // into LDS and the v rows into vwin
+            VWin<ACT, DV, NT> vw;
+            vwin_issue<ACT, DV, NT>(vw, p, ctx0, tc0, n, H, h, opq(tid));
             if (tid == 0) sm.flag = ring_wait(ready_ctr, chunk + 1);
             __syncthreads();
             if (!sm.flag) {
@@ -1015,19 +1080,29 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             }
             {
                 const int tp = opq(tid);
-                ring_copy<NPA, NT, false>(rr, 0, reinterpret_cast<uint4*>(lds), tp);
-                ring_copy<NPB, NT, false>(rr, PB0, reinterpret_cast<uint4*>(lds) + PB0, tp);
+                ring_copy<NPA, NT, false, 9>(rr, 0, reinterpret_cast<uint4*>(lds), tp);
+                ring_copy<NPB, NT, false, 9>(rr, PB0, reinterpret_cast<uint4*>(lds) + PB0, tp);
                 if (tp < NSV) reinterpret_cast<uint4*>(sm.sv)[tp] = ring_ld(rr, NPW + tp);
-#pragma unroll
-                for (int tb = 0; tb < 4; tb++) {
-                    const uint4 x = ring_ld(rr, NPW + NSV + tb * NT + tp);
-                    vh[tb][0] = __uint_as_float(x.x);
-                    vh[tb][1] = __uint_as_float(x.y);
-                    vh[tb][2] = __uint_as_float(x.z);
-                    vh[tb][3] = __uint_as_float(x.w);
-                }
+                vwin_commit<ACT, DK, DV, NT>(vw, vwin, x0_s, tp);
             }
             __syncthreads();
+            {
+                // SiLU(conv(v)) in accumulator layout, as phase A computes it
+                const int tp = opq(tid);
+                const int ln = tp & 63, jc = 16 * (tp >> 6) + (ln & 15), gg = ln >> 4;
+#pragma unroll
+                for (int tb = 0; tb < 4; tb++) {
+                    const int rb = 16 * tb + 4 * gg;
+                    float x[7];
+#pragma unroll
+                    for (int m = 0; m < 7; m++) x[m] = A::ld(vwin + (rb + m) * DV + jc);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const float y = conv4(wv, x[e], x[e + 1], x[e + 2], x[e + 3]);
+                        vh[tb][e] = (rb + e) < n ? silu(y) : 0.f;
+                    }
+                }
+            }
         }
 
         // ---------------- B: state-dependent part; wave = 16-column strip of S

@@ -304,14 +304,14 @@ struct Staged {
 // grouped per wave so that one wave's slot j always reads one tensor (q, k or
 // v): its loads then take a single buffer resource.  A tensor's units are the
 // (CH+3) x (D/VEC) 16-byte pieces of its rows (3 rows of left context first).
-template <typename ACT, int D, int NT>
+template <typename ACT, int D, int NT, int NTEN = 3>
 struct StageMap {
     static constexpr int VEC = 16 / static_cast<int>(sizeof(ACT));
     static constexpr int UPT = D / VEC;                    // units per tensor row
     static constexpr int UT = (CH + 3) * UPT;              // units per tensor
     static constexpr int WS = (UT + 63) / 64;              // wave slots per tensor
     static constexpr int NWV = NT / 64;
-    static constexpr int NU = (3 * WS + NWV - 1) / NWV;    // slots per thread
+    static constexpr int NU = (NTEN * WS + NWV - 1) / NWV; // slots per thread (NTEN tensors: q, k[, v])
     struct Unit {
         int tensor;   // 0 q, 1 k, 2 v; 3 = unused slot
         int r, col;   // row (0 = three tokens before the chunk), first channel
@@ -324,7 +324,7 @@ struct StageMap {
         u.tensor = w / WS;
         u.r = local / UPT;
         u.col = (local % UPT) * VEC;
-        u.valid = u.tensor < 3 && local < UT;
+        u.valid = u.tensor < NTEN && local < UT;
         return u;
     }
 };
@@ -332,11 +332,11 @@ struct StageMap {
 // Issue the global loads of the chunk [tc0, tc0+n) of head h (no waits).
 // Left-context rows before the sequence start (first packed token ctx0) come
 // from the initial conv state x0 (index 2 = the token just before the start).
-template <typename ACT, int DK, int DV, int NT, int NU>
+template <typename ACT, int DK, int DV, int NT, int NTEN, int NU>
 __device__ __forceinline__ void stage_issue(Staged<NU>& st, const PrefillParams& p, const ACT* x0,
                                             int64_t ctx0, int64_t tc0, int n, int H, int h, int tp) {
     static_assert(DK == DV, "one row layout for q, k and v");
-    using M = StageMap<ACT, DK, NT>;
+    using M = StageMap<ACT, DK, NT, NTEN>;
     static_assert(M::NU == NU, "staging slots");
     constexpr int D = DK;
     const int wv = __builtin_amdgcn_readfirstlane(tp >> 6), lane = tp & 63;
@@ -353,7 +353,7 @@ __device__ __forceinline__ void stage_issue(Staged<NU>& st, const PrefillParams&
         const typename M::Unit u = M::unit(j, wv, lane);
         st.val[j] = make_uint4(0, 0, 0, 0);
         const int tsel = __builtin_amdgcn_readfirstlane(u.tensor);
-        if (tsel < 3) {
+        if (tsel < NTEN) {
             const auto rs = make_rsrc(tens[tsel] + hoff, nbytes);
             const int rel = u.r - d0;
             const uint32_t vo = (u.valid && rel >= 0) ? static_cast<uint32_t>(rel) * rowb + u.col * sizeof(ACT)
@@ -463,9 +463,9 @@ __device__ __forceinline__ void vwin_commit(const VWin<ACT, DV, NT>& vw, ACT* vw
 }
 
 // Store the staged raw rows and beta into LDS (rows of CR elements: q, k, v).
-template <typename ACT, int DK, int DV, int NT, int NU>
+template <typename ACT, int DK, int DV, int NT, int NTEN, int NU>
 __device__ __forceinline__ void stage_commit(const Staged<NU>& st, ACT* raw, float* beta_s, int tp) {
-    using M = StageMap<ACT, DK, NT>;
+    using M = StageMap<ACT, DK, NT, NTEN>;
     constexpr int C = 2 * DK + DV;
     constexpr int CR = C + M::VEC;              // padded row stride (spreads the v reads of the conv over banks)
     const int wv = __builtin_amdgcn_readfirstlane(tp >> 6), lane = tp & 63;
@@ -565,34 +565,57 @@ __device__ __forceinline__ void ring_st(__amdgpu_buffer_rsrc_t r, uint32_t word,
     __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(word * 16), 0, RING_POL);
 }
 
-// Copy NW 16-byte words between LDS and a ring slot (from word w0 on), word
-// e by thread e % NT, with NB loads in flight before their stores.
-template <int NW, int NT, bool PUT, int NB>
-__device__ __forceinline__ void ring_copy(__amdgpu_buffer_rsrc_t r, uint32_t w0, uint4* lds_words, int tp) {
+// Store NW 16-byte words of LDS into a ring slot (from word w0 on), word e
+// by thread e % NT, NB LDS reads at a time ahead of their stores.
+template <int NW, int NT, int NB>
+__device__ __forceinline__ void ring_put(__amdgpu_buffer_rsrc_t r, uint32_t w0, const uint4* lds_words, int tp) {
     constexpr int FULL = NW / NT, REM = NW % NT;
 #pragma unroll
     for (int b = 0; b < FULL; b += NB) {
         uint4 w[NB];
 #pragma unroll
         for (int i = 0; i < NB; i++)
-            if (b + i < FULL) w[i] = PUT ? lds_words[(b + i) * NT + tp] : ring_ld(r, w0 + (b + i) * NT + tp);
+            if (b + i < FULL) w[i] = lds_words[(b + i) * NT + tp];
 #pragma unroll
-        for (int i = 0; i < NB; i++) {
-            if (b + i >= FULL) continue;
-            if (PUT) ring_st(r, w0 + (b + i) * NT + tp, w[i]);
-            else lds_words[(b + i) * NT + tp] = w[i];
-        }
+        for (int i = 0; i < NB; i++)
+            if (b + i < FULL) ring_st(r, w0 + (b + i) * NT + tp, w[i]);
     }
-    if (REM > 0 && tp < REM) {
-        if (PUT) ring_st(r, w0 + FULL * NT + tp, lds_words[FULL * NT + tp]);
-        else lds_words[FULL * NT + tp] = ring_ld(r, w0 + FULL * NT + tp);
-    }
+    if (REM > 0 && tp < REM) ring_st(r, w0 + FULL * NT + tp, lds_words[FULL * NT + tp]);
 }
 
-// Poll a ring counter until it reaches want (one lane).
-__device__ __forceinline__ bool ring_wait(const int32_t* ctr, int want) {
+// Load two word ranges of a ring slot, [0, NA) and [B0, B0 + NB), into the
+// same words of LDS: every load is issued before the first LDS store, so the
+// whole copy costs one memory round trip.
+template <int NA, int B0, int NB, int NT>
+__device__ __forceinline__ void ring_get2(__amdgpu_buffer_rsrc_t r, uint4* lds_words, int tp) {
+    constexpr int FA = NA / NT, RA = NA % NT, FB = NB / NT, RB = NB % NT;
+    uint4 wa[FA + 1], wb[FB + 1];
+#pragma unroll
+    for (int i = 0; i < FA; i++) wa[i] = ring_ld(r, i * NT + tp);
+    if (RA > 0 && tp < RA) wa[FA] = ring_ld(r, FA * NT + tp);
+#pragma unroll
+    for (int i = 0; i < FB; i++) wb[i] = ring_ld(r, B0 + i * NT + tp);
+    if (RB > 0 && tp < RB) wb[FB] = ring_ld(r, B0 + FB * NT + tp);
+#pragma unroll
+    for (int i = 0; i < FA; i++) lds_words[i * NT + tp] = wa[i];
+    if (RA > 0 && tp < RA) lds_words[FA * NT + tp] = wa[FA];
+#pragma unroll
+    for (int i = 0; i < FB; i++) lds_words[B0 + i * NT + tp] = wb[i];
+    if (RB > 0 && tp < RB) lds_words[B0 + FB * NT + tp] = wb[FB];
+}
+
+// A ring counter read ahead of need (one lane): the read takes a memory round
+// trip, so it is issued well before the value is needed.
+__device__ __forceinline__ int ring_peek(const int32_t* ctr) {
+    return __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until a ring counter reaches want (one lane), given a value read
+// earlier: only when that value falls short is the counter polled.
+__device__ __forceinline__ bool ring_wait(const int32_t* ctr, int want, int seen) {
+    if (seen >= want) return true;
     for (int it = 0; it < SPIN_LIMIT; it++) {
-        if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want) return true;
+        if (ring_peek(ctr) >= want) return true;
         __builtin_amdgcn_s_sleep(2);
     }
     return false;
@@ -768,6 +791,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
     int32_t* const ready_ctr = ROLE == FUSED ? nullptr : p.ring_ctr + chain * 32;
     int32_t* const taken_ctr = ROLE == FUSED ? nullptr : p.ring_ctr + chain * 32 + 16;
     int chunk = 0;
+    int seen = 0;       // thread 0 of a paired role: the partner's counter as last read
     // checkpoint counter: a segment that ends at a checkpoint position leaves
     // that checkpoint to the next segment (which starts from the scanned
     // state), so a segment that is not the last of its sequence writes none
@@ -791,13 +815,15 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
 
     // ---------------- A1 of the first chunk (later chunks are staged while the
     // previous chunk finishes: their loads are issued after its state phase)
-    Staged<Sh::NU> stg;
+    // the producer stages q and k only: v rows are read by the consumer
+    constexpr int NTEN = ROLE == PRODUCER ? 2 : 3;
+    Staged<StageMap<ACT, D, NT, NTEN>::NU> stg;
     int n = L > 0 ? min(L, CH - static_cast<int>(pos % CH)) : 0;
     int64_t tc0 = tok0;
     if (ROLE != CONSUMER && L > 0) {
         const int tp = opq(tid);
-        stage_issue<ACT, DK, DV, NT>(stg, p, x0_s, ctx0, tc0, n, H, h, tp);
-        stage_commit<ACT, DK, DV, NT>(stg, raw, beta_s, tp);
+        stage_issue<ACT, DK, DV, NT, NTEN>(stg, p, x0_s, ctx0, tc0, n, H, h, tp);
+        stage_commit<ACT, DK, DV, NT, NTEN>(stg, raw, beta_s, tp);
     }
     __syncthreads();
 
@@ -924,10 +950,13 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
         if constexpr (ROLE == PRODUCER) __builtin_amdgcn_s_waitcnt(VMCNT0);
         __syncthreads();
         if constexpr (ROLE == PRODUCER) {
-            if (tid == 0 && chunk > 0) __hip_atomic_store(ready_ctr, chunk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (tid == 0) {
+                if (chunk > 0) __hip_atomic_store(ready_ctr, chunk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                seen = ring_peek(taken_ctr);       // used after A6
+            }
             const int done_next = done + n;
             n_next_p = done_next < L ? min(L - done_next, CH - static_cast<int>((pos + n) % CH)) : 0;
-            if (n_next_p > 0) stage_issue<ACT, DK, DV, NT>(stg, p, x0_s, ctx0, tok0 + done_next, n_next_p, H, h, opq(tid));
+            if (n_next_p > 0) stage_issue<ACT, DK, DV, NT, NTEN>(stg, p, x0_s, ctx0, tok0 + done_next, n_next_p, H, h, opq(tid));
             else stage_clear(stg);
         }
 
@@ -1036,7 +1065,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             // (published in the next chunk's phase A, or after the last
             // chunk)
             if (chunk >= RING) {
-                if (tid == 0) sm.flag = ring_wait(taken_ctr, chunk - RING + 1);
+                if (tid == 0) sm.flag = ring_wait(taken_ctr, chunk - RING + 1, seen);
                 __syncthreads();
                 if (!sm.flag) return;                         // the consumer is gone
             }
@@ -1045,15 +1074,15 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             const int n_next = n_next_p;
             {
                 const int tp = opq(tid);
-                ring_copy<NPA, NT, true, 6>(rr, 0, reinterpret_cast<uint4*>(lds), tp);
-                ring_copy<NPB, NT, true, 6>(rr, PB0, reinterpret_cast<uint4*>(lds) + PB0, tp);
+                ring_put<NPA, NT, 6>(rr, 0, reinterpret_cast<const uint4*>(lds), tp);
+                ring_put<NPB, NT, 6>(rr, PB0, reinterpret_cast<const uint4*>(lds) + PB0, tp);
                 if (tp < NSV) ring_st(rr, NPW + tp, reinterpret_cast<const uint4*>(sm.sv)[tp]);
             }
             // every thread has read its planes, sv and beta out of LDS
             // (its stores need not be complete) before the next chunk's raw
             // rows and beta overwrite them
             __syncthreads();
-            if (n_next > 0) stage_commit<ACT, DK, DV, NT>(stg, raw, beta_s, opq(tid));
+            if (n_next > 0) stage_commit<ACT, DK, DV, NT, NTEN>(stg, raw, beta_s, opq(tid));
             done = done_next;
             pos = pos_next;
             n = n_next;
@@ -1068,7 +1097,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             // into LDS and the v rows into vwin
             VWin<ACT, DV, NT> vw;
             vwin_issue<ACT, DV, NT>(vw, p, ctx0, tc0, n, H, h, opq(tid));
-            if (tid == 0) sm.flag = ring_wait(ready_ctr, chunk + 1);
+            if (tid == 0) sm.flag = ring_wait(ready_ctr, chunk + 1, seen);
             __syncthreads();
             if (!sm.flag) {
                 // the producer is gone: NaN outputs from here on, no state written
@@ -1080,8 +1109,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             }
             {
                 const int tp = opq(tid);
-                ring_copy<NPA, NT, false, 9>(rr, 0, reinterpret_cast<uint4*>(lds), tp);
-                ring_copy<NPB, NT, false, 9>(rr, PB0, reinterpret_cast<uint4*>(lds) + PB0, tp);
+                ring_get2<NPA, PB0, NPB, NT>(rr, reinterpret_cast<uint4*>(lds), tp);
                 if (tp < NSV) reinterpret_cast<uint4*>(sm.sv)[tp] = ring_ld(rr, NPW + tp);
                 vwin_commit<ACT, DK, DV, NT>(vw, vwin, x0_s, tp);
             }
@@ -1217,12 +1245,15 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
         const int64_t pos_next = pos + n;
         const int n_next = done_next < L ? min(L - done_next, CH - static_cast<int>(pos_next % CH)) : 0;
         if constexpr (ROLE == FUSED) {
-            if (n_next > 0) stage_issue<ACT, DK, DV, NT>(stg, p, x0_s, ctx0, tok0 + done_next, n_next, H, h, opq(tid));
+            if (n_next > 0) stage_issue<ACT, DK, DV, NT, NTEN>(stg, p, x0_s, ctx0, tok0 + done_next, n_next, H, h, opq(tid));
             else stage_clear(stg);
         } else {
             // every read of this slot is complete (its values fed phase B):
             // the producer may refill it
-            if (tid == 0) __hip_atomic_store(taken_ctr, chunk + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (tid == 0) {
+                __hip_atomic_store(taken_ctr, chunk + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                seen = ring_peek(ready_ctr);       // used at the next chunk's take-over
+            }
         }
 
         // ---------------- epilogue: gated RMSNorm over dv, then the outputs
@@ -1254,7 +1285,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
         }
 
         // the raw-row region and beta are free: every wave is past its state phase
-        if (ROLE == FUSED && n_next > 0) stage_commit<ACT, DK, DV, NT>(stg, raw, beta_s, opq(tid));
+        if (ROLE == FUSED && n_next > 0) stage_commit<ACT, DK, DV, NT, NTEN>(stg, raw, beta_s, opq(tid));
         done = done_next;
         pos = pos_next;
         // ---------------- checkpoints: interval boundaries inside, and the end

@@ -181,7 +181,8 @@ kda_status kda_decode_multi(const kda_config* cfg, int32_t B, int32_t T,
  * out: [total_tokens][H][dv] activation dtype.
  * workspace: device scratch of at least kda_prefill_workspace_bytes(...)
  *   bytes; its contents on entry do not matter.
- * flags: 0 or KDA_PREFILL_SPLIT (needs ckpt_interval > 0).  Without it each
+ * flags: 0, KDA_PREFILL_SPLIT or KDA_PREFILL_PAIRED (not both).
+ * KDA_PREFILL_SPLIT (needs ckpt_interval > 0).  Without it each
  *   (sequence, head) chain runs through its chunks in order in one workgroup,
  *   so a batch of few long sequences occupies few compute units.  With it,
  *   every sequence is cut at its interval checkpoint positions into segments
@@ -199,6 +200,20 @@ kda_status kda_decode_multi(const kda_config* cfg, int32_t B, int32_t T,
  *   to fp32 rounding.  A run resumed from one of its interval checkpoints with
  *   the same interval and flags reproduces it bit for bit; a continuation
  *   from a sequence end that is not an interval position agrees to rounding.
+ * KDA_PREFILL_PAIRED: two workgroups per (sequence, head) chain.  One
+ *   computes every chunk's state-independent part (conv, norms, decays, the
+ *   intra-chunk products and triangular inverses).  The other applies each
+ *   chunk to the state and writes the outputs, checkpoints and final state.
+ *   The chunks pass between them through a ring in the workspace, so the two
+ *   parts of consecutive chunks overlap.  The launch is cooperative, so both
+ *   workgroups of every chain are resident together.  That is possible only
+ *   when 2 x sequences x heads (rounded up to a multiple of 16) fits on the
+ *   device at once: 128 chains at dk = dv = 128 on a 256-CU GPU.  Larger
+ *   batches run the one-workgroup kernel.  Either way the results are bit
+ *   for bit those of a call without the flag.  The workspace grows by the
+ *   ring (three slots of about 142 KB per chain at dk = dv = 128) when
+ *   sequences x heads <= 1024.  Meant for batches with fewer chains than
+ *   compute units.  Paired calls are not tested under HIP graph capture.
  * Precondition on the gate: within any 32 consecutive tokens of a chunk the
  *   accumulated log-decay of every channel stays above -80 (for instance
  *   g >= -2.5 everywhere); the intra-chunk decay factors are formed relative
@@ -283,7 +298,9 @@ kda_status kda_resume(const kda_config* cfg, int32_t n,
 /* Workspace bytes kda_prefill_varlen needs for these sizes, checkpoint
  * interval and flags (0 on an error; kda_last_error() then says why).  With
  * KDA_PREFILL_SPLIT it holds, per possible segment (at most 2 num_seqs +
- * total_tokens / ckpt_interval) and head, three dk x dv fp32 matrices. */
+ * total_tokens / ckpt_interval) and head, three dk x dv fp32 matrices; with
+ * KDA_PREFILL_PAIRED and num_seqs x heads <= 1024, the ring of the paired
+ * launch and its counters. */
 size_t kda_prefill_workspace_bytes(const kda_config* cfg, int32_t num_seqs, int64_t total_tokens,
                                    int32_t ckpt_interval, int32_t flags);
 

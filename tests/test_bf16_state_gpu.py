@@ -96,7 +96,7 @@ def check_bf16_prefill(run, r):
         np.testing.assert_array_equal(host(run.ckX)[:run.nck], r.ckpt_X)
 
 
-@pytest.mark.parametrize("flags", [0, kda.KDA_PREFILL_SPLIT])
+@pytest.mark.parametrize("flags", [0, kda.KDA_PREFILL_SPLIT, kda.KDA_PREFILL_PAIRED])
 @pytest.mark.parametrize("act", ["bf16", "f32"])
 def test_prefill_bf16_state_matches_oracle(act, flags):
     shape = wl.LayerShape(2, 64, 64, act=act)
@@ -123,7 +123,7 @@ def test_prefill_bf16_state_d128_no_checkpoints():
     check_bf16_prefill(run, oracle_for(run, S0, X0))
 
 
-@pytest.mark.parametrize("flags", [0, kda.KDA_PREFILL_SPLIT])
+@pytest.mark.parametrize("flags", [0, kda.KDA_PREFILL_SPLIT, kda.KDA_PREFILL_PAIRED])
 def test_prefill_bf16_state_resume_is_bitwise(flags):
     shape = wl.LayerShape(2, 64, 64)
     lengths, starts = [700, 450, 300], [0, 128, 64]

@@ -333,12 +333,18 @@ kda_status kda_prefill_varlen(const kda_config* cfg, int32_t num_seqs, int64_t t
     p.state_bf16 = cfg->state_dtype == KDA_BF16 ? 1 : 0;
     p.ring = nullptr;
     p.ring_ctr = nullptr;
+    p.max_pairs = 0;
+    p.sched_grid = 0;
     if (wl.ring > 0) {
-        // paired only where every workgroup of the launch is resident at once
+        // a scheduled launch needs a grid of at least 16 workgroups that the
+        // device holds at once; otherwise the one-workgroup kernel runs
         const int64_t chains = static_cast<int64_t>(num_seqs) * cfg->num_heads;
-        if (kda::pair_grid(chains) <= kda::prefill_pair_capacity(cfg->head_k, cfg->act_dtype)) {
+        const int64_t grid = kda::pair_grid(chains, kda::prefill_pair_capacity(cfg->head_k, cfg->act_dtype));
+        if (grid >= 16) {
             p.ring = ws + wl.ring;
             p.ring_ctr = reinterpret_cast<int32_t*>(ws + wl.ring_ctr);
+            p.max_pairs = wl.max_pairs;
+            p.sched_grid = static_cast<int32_t>(grid);
         }
     }
     return hip_status(kda::launch_prefill(cfg->head_k, cfg->head_v, cfg->act_dtype, p,

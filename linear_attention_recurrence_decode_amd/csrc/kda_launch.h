@@ -91,10 +91,14 @@ struct PrefillParams {
     float* seg_S;       // [max_items][H][dk][dv] segment initial states
     void* seq_x0;       // [N][H][2dk+dv][3] initial conv states (activation dtype)
     int32_t state_bf16; // stored state in bf16 (rounded at every store; math in fp32)
-    // Paired launch (two workgroups per chain, see prefill_pair_kernel); null
-    // for the one-workgroup launch.
-    char* ring;         // [N*H][RING] slots of prefill_pair_slot_bytes each
-    int32_t* ring_ctr;  // [N*H][32]: chunks handed over at 0, chunks taken at 16
+    // Scheduled launch (a resident grid; the longest chains get two
+    // workgroups each, see prefill_pair_kernel); ring null for the
+    // one-workgroup launch.
+    char* ring;         // [max_pairs][RING] slots of prefill_pair_slot_bytes each
+    int32_t* ring_ctr;  // [max_pairs][32]: chunks handed over at 0, chunks taken at 16; then
+                        // [32]: pairs chosen at 0, chain queue at 1
+    int32_t max_pairs;  // pairs the ring holds
+    int32_t sched_grid; // workgroups of the scheduled launch
 };
 
 // Input projections: y = x W^T routed to q, k, v, z (activation dtype) and
@@ -122,18 +126,19 @@ bool prefill_supported(int dk, int dv, int act);
 
 // Workspace layout of the prefill (offsets in bytes; total = bytes).
 struct PrefillWorkspace {
-    int32_t max_items;
+    int32_t max_items, max_pairs;
     size_t items, seq_items, seg_F, seg_G, seg_S, seq_x0, ring_ctr, ring, bytes;
 };
-// Paired launches are offered up to this many chains (sequences x heads);
-// the ring takes RING slots of prefill_pair_slot_bytes per chain.
-constexpr int64_t PAIR_MAX_CHAINS = 1024;
+// A scheduled launch pairs at most this many chains (sequences x heads);
+// the ring takes RING slots of prefill_pair_slot_bytes per pair.
+constexpr int64_t PAIR_MAX_PAIRS = 256;
 PrefillWorkspace prefill_workspace(int32_t N, int32_t H, int64_t T, int dk, int dv, int act_bytes,
                                    int32_t ckpt_interval, bool split, bool paired);
 int64_t prefill_pair_slot_bytes(int dk, int act);
-// Workgroups of a paired launch for this many chains, and how many such
-// workgroups the current device holds at once (0 if it cannot tell).
-int64_t pair_grid(int64_t chains);
+// Workgroups of a scheduled launch for this many chains on a device that
+// holds `capacity` of them at once (a multiple of 16; 0: none), and that
+// capacity for the current device (0 if it cannot tell).
+int64_t pair_grid(int64_t chains, int64_t capacity);
 int64_t prefill_pair_capacity(int dk, int act);
 
 }  // namespace kda

@@ -1346,31 +1346,96 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
     prefill_chain<D, ACT, OUT, FUSED>(p, sm, item, h, trans);
 }
 
-// Two workgroups per chain, launched cooperatively so that all of them are
-// resident together (a consumer waits on its producer and the other way
-// round).  Blocks 16m .. 16m+7 produce for chains 8m .. 8m+7 and blocks
-// 16m+8 .. 16m+15 consume them: the two workgroups of a chain have block
-// indices equal mod 8, which places them in the same L2 when workgroups are
-// dealt round-robin over the 8 XCDs.
+// A resident grid of G workgroups, launched cooperatively so that all of
+// them run at once (a consumer waits on its producer and the other way
+// round).  The first K chains in work order (the longest; K chosen by the
+// metadata kernel) get two workgroups each: blocks 16m .. 16m+7 produce for
+// chains 8m .. 8m+7 and blocks 16m+8 .. 16m+15 consume them, so the two
+// workgroups of a chain have block indices equal mod 8, which places them in
+// the same L2 when workgroups are dealt round-robin over the 8 XCDs.  Every
+// other workgroup, and each pair once its chain is done, takes the remaining
+// chains one at a time from a queue, longest first, and runs each in one
+// workgroup.
 template <int D, typename ACT>
 __global__ __launch_bounds__(4 * D) void prefill_pair_kernel(PrefillParams p) {
     __shared__ PrefillLds<D, ACT> sm;
+    __shared__ int next_s;
+    const int NH = p.N * p.H;
+    const int32_t* sched = p.ring_ctr + static_cast<int64_t>(p.max_pairs) * 32;
+    const int K = sched[0];
     const int b = blockIdx.x;
-    const int chain = 8 * (b / 16) + (b % 8);
-    if (chain >= p.N * p.H) return;
-    const int h = chain % p.H, item = chain / p.H;
-    if ((b % 16) < 8) prefill_chain<D, ACT, true, PRODUCER>(p, sm, item, h, false);
-    else prefill_chain<D, ACT, true, CONSUMER>(p, sm, item, h, false);
+    const int pair = 8 * (b / 16) + (b % 8);
+    if (pair < K) {
+        if ((b % 16) < 8) prefill_chain<D, ACT, true, PRODUCER>(p, sm, pair / p.H, pair % p.H, false);
+        else prefill_chain<D, ACT, true, CONSUMER>(p, sm, pair / p.H, pair % p.H, false);
+        __syncthreads();
+    }
+    for (;;) {
+        if (threadIdx.x == 0) next_s = atomicAdd(const_cast<int32_t*>(sched) + 1, 1);
+        __syncthreads();
+        const int chain = K + next_s;
+        __syncthreads();
+        if (chain >= NH) break;
+        prefill_chain<D, ACT, true, FUSED>(p, sm, chain / p.H, chain % p.H, false);
+        __syncthreads();
+    }
+}
+
+// Chunks of 64 a work item runs (the grid is aligned to absolute positions).
+__device__ __forceinline__ int64_t item_chunks(const SeqWork& w) {
+    if (w.len <= 0) return 0;
+    const int64_t s0 = w.start < 0 ? 0 : w.start % CH;
+    return (s0 + w.len + CH - 1) / CH;
+}
+
+// Scheduled launch (one workgroup of 1024 threads, after the work items are
+// written): zero the ring counters and the chain queue, and choose K, the
+// number of leading chains that get a producer/consumer pair.  Cost model in
+// chunk steps of one workgroup: a paired chain costs 0.72 per chunk (its two
+// halves overlap), a single one 1; the G - 2K unpaired workgroups share the
+// other chains.  K minimises the larger of the longest paired chain, the
+// longest single chain and the single chains' total over those workgroups.
+__device__ void schedule_pairs(const SeqWork* work, int32_t N, int32_t H, int32_t* ring_ctr, int32_t max_pairs,
+                               int32_t grid) {
+    __shared__ double part_s[1024];
+    for (int64_t i = threadIdx.x; i < static_cast<int64_t>(max_pairs) * 32 + 32; i += 1024) ring_ctr[i] = 0;
+    double tot = 0.0;
+    for (int i = threadIdx.x; i < N; i += 1024) tot += static_cast<double>(item_chunks(work[i]));
+    part_s[threadIdx.x] = tot;
+    __syncthreads();
+    for (int off = 512; off > 0; off >>= 1) {
+        if (static_cast<int>(threadIdx.x) < off) part_s[threadIdx.x] += part_s[threadIdx.x + off];
+        __syncthreads();
+    }
+    if (threadIdx.x != 0) return;
+    const int64_t NH = static_cast<int64_t>(N) * H;
+    const double W = part_s[0] * H;                  // chunk steps of all chains
+    const int64_t kmax = min(min(static_cast<int64_t>(max_pairs), static_cast<int64_t>(grid / 2)), NH);
+    const double l0 = NH > 0 ? static_cast<double>(item_chunks(work[0])) : 0.0;
+    double best = 1e300, paired = 0.0;
+    int bestk = 0;
+    for (int64_t k = 0; k <= kmax; k++) {
+        const double lu = k < NH ? static_cast<double>(item_chunks(work[k / H])) : 0.0;
+        const int64_t workers = grid - 2 * k;
+        if (k == NH || workers > 0) {
+            const double rest = W - paired;
+            const double mk = fmax(fmax(k > 0 ? 0.72 * l0 : 0.0, lu), workers > 0 ? rest / workers : 0.0);
+            if (mk < best * (1.0 - 1e-9)) {
+                best = mk;
+                bestk = static_cast<int>(k);
+            }
+        }
+        if (k < NH) paired += lu;
+    }
+    ring_ctr[static_cast<int64_t>(max_pairs) * 32] = bestk;
 }
 
 // One workgroup: per-sequence work items ordered longest first, so the
 // longest chains start first.  Sequences with bounds outside [0, T] get
 // len = -1 and are skipped by the prefill kernel.
 __global__ __launch_bounds__(1024) void prefill_meta_kernel(const int32_t* cu, const int64_t* sp, int32_t N,
-                                                            int64_t T, SeqWork* work, int32_t* ring_ctr,
-                                                            int32_t n_ctr) {
-    // the ring counters of a paired launch start from zero
-    for (int i = threadIdx.x; i < n_ctr; i += 1024) ring_ctr[i] = 0;
+                                                            int64_t T, SeqWork* work, int32_t H, int32_t* ring_ctr,
+                                                            int32_t max_pairs, int32_t grid) {
     for (int i = threadIdx.x; i < N; i += 1024) {
         const int64_t a = cu[i], b = cu[i + 1];
         const bool ok = a >= 0 && b >= a && b <= T;
@@ -1394,6 +1459,7 @@ __global__ __launch_bounds__(1024) void prefill_meta_kernel(const int32_t* cu, c
         w.last = 1;
         work[rank] = w;
     }
+    if (ring_ctr) schedule_pairs(work, N, H, ring_ctr, max_pairs, grid);
 }
 
 // Segments of sequence i when sequences are cut at the checkpoint positions
@@ -1553,7 +1619,7 @@ hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
     if (!p.split) {
         const int64_t blocks = static_cast<int64_t>(p.N) * p.H;
         hipLaunchKernelGGL(prefill_meta_kernel, dim3(1), dim3(1024), 0, s, p.cu_seqlens, p.start_pos, p.N, p.T,
-                           p.work, p.ring_ctr, p.ring ? static_cast<int32_t>(blocks * 32) : 0);
+                           p.work, p.H, p.ring ? p.ring_ctr : nullptr, p.max_pairs, p.sched_grid);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (blocks == 0) return hipSuccess;
@@ -1561,8 +1627,7 @@ hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
             PrefillParams pc = p;
             void* args[] = {&pc};
             return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&prefill_pair_kernel<D, ACT>),
-                                              dim3(static_cast<unsigned>(pair_grid(blocks))), dim3(4 * D), args, 0,
-                                              s);
+                                              dim3(static_cast<unsigned>(p.sched_grid)), dim3(4 * D), args, 0, s);
         }
         hipLaunchKernelGGL((prefill_kernel<D, ACT, true>), dim3(static_cast<unsigned>(blocks)), dim3(4 * D), 0, s,
                            p);
@@ -1585,7 +1650,9 @@ hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
 
 }  // namespace
 
-int64_t pair_grid(int64_t chains) { return 16 * ((chains + 7) / 8); }
+int64_t pair_grid(int64_t chains, int64_t capacity) {
+    return min(capacity / 16 * 16, 16 * ((chains + 7) / 8));
+}
 
 int64_t prefill_pair_slot_bytes(int dk, int act) {
     if (act == 1) return dk == 32 ? pair_slot_bytes<32, bf16_t>() : dk == 64 ? pair_slot_bytes<64, bf16_t>()
@@ -1637,11 +1704,13 @@ PrefillWorkspace prefill_workspace(int32_t N, int32_t H, int64_t T, int dk, int 
         off += up(static_cast<size_t>(N) * H * (2 * dk + dv) * 3 * act_bytes);
     }
     const int64_t chains = static_cast<int64_t>(N) * H;
-    if (paired && !split && chains > 0 && chains <= PAIR_MAX_CHAINS) {
+    w.max_pairs = 0;
+    if (paired && !split && chains > 0) {
+        w.max_pairs = static_cast<int32_t>(min(chains, PAIR_MAX_PAIRS));
         w.ring_ctr = off;
-        off += up(static_cast<size_t>(chains) * 32 * 4);
+        off += up((static_cast<size_t>(w.max_pairs) * 32 + 32) * 4);
         w.ring = off;
-        off += static_cast<size_t>(chains) * RING * prefill_pair_slot_bytes(dk, act_bytes == 2 ? 1 : 0);
+        off += static_cast<size_t>(w.max_pairs) * RING * prefill_pair_slot_bytes(dk, act_bytes == 2 ? 1 : 0);
     }
     w.bytes = off;
     return w;

@@ -146,13 +146,14 @@ def test_prefill_validation():
     ws_split = kda.kda_prefill_workspace_bytes(cfg(), 16, 1 << 18, 4096, kda.KDA_PREFILL_SPLIT)
     segs = 2 * 16 + (1 << 18) // 4096
     assert ws_split >= segs * 4 * 3 * 128 * 128 * 4 and ws_split % 256 == 0
-    # paired: two ring slots per (sequence, head) chain, each holding a chunk's planes (at least
-    # K+, Q+ and K-^T as bf16 hi/lo pairs) and SiLU(conv(v)) in fp32; offered up to 1024 chains
+    # paired: a ring of three slots per pair of workgroups, each slot holding a chunk's planes (at
+    # least K+ and K-^T as bf16 hi/lo pairs and Q+ hi); up to min(chains, 256) pairs
     ws_pair = kda.kda_prefill_workspace_bytes(cfg(), 16, 1 << 18, 0, kda.KDA_PREFILL_PAIRED)
-    slot_min = 3 * 2 * 64 * 128 * 2 + 64 * 128 * 4
-    assert ws_pair >= ws + 16 * 4 * 2 * slot_min and ws_pair % 256 == 0
-    assert kda.kda_prefill_workspace_bytes(cfg(), 512, 1 << 18, 0, kda.KDA_PREFILL_PAIRED) == \
-        kda.kda_prefill_workspace_bytes(cfg(), 512, 1 << 18)
+    slot_min = 2 * 2 * 64 * 128 * 2 + 64 * 128 * 2
+    assert ws_pair >= ws + 16 * 4 * 3 * slot_min and ws_pair % 256 == 0
+    ws_big = kda.kda_prefill_workspace_bytes(cfg(), 512, 1 << 18)
+    ws_big_pair = kda.kda_prefill_workspace_bytes(cfg(), 512, 1 << 18, 0, kda.KDA_PREFILL_PAIRED)
+    assert ws_big + 256 * 3 * slot_min <= ws_big_pair < ws_big + 257 * 3 * 2 * slot_min
     with pytest.raises(kda.KdaError):
         kda.kda_prefill_workspace_bytes(cfg(), 16, 1 << 18, 0, kda.KDA_PREFILL_SPLIT)
 

@@ -4,9 +4,10 @@ and one for the state phase, joined by a ring in the workspace.
 
 Both workgroups run the one-workgroup kernel's own arithmetic, so a paired
 call must reproduce the one-workgroup call bit for bit (outputs, final
-states, conv states, checkpoints), and through it the oracle.  A call with
-more chains than the device can hold as resident pairs runs the
-one-workgroup kernel instead, with the same results.
+states, conv states, checkpoints), and through it the oracle.  In a batch
+with more chains than the device holds as resident pairs, the launch pairs
+the longest chains and runs the others one workgroup each from a queue, with
+the same results.
 """
 import numpy as np
 import pytest
@@ -77,13 +78,20 @@ def test_paired_4x8192_full_size_equals_one_workgroup():
     assert_same_bits(paired, single)
 
 
-def test_paired_more_chains_than_pairs_falls_back():
-    """160 chains at dk = dv = 128 need 320 resident workgroups, more than one
-    per compute unit: the call runs the one-workgroup kernel, same bits."""
+@pytest.mark.parametrize("case", ["uniform_160_chains", "skewed_lengths"])
+def test_paired_schedule_mixes_pairs_and_singles(case):
+    """More chains than pairs fit: the scheduled launch pairs the longest
+    chains and runs the rest one workgroup each from a queue.  Same bits as
+    the one-workgroup kernel, and the oracle on one head."""
     shape = wl.LayerShape(4, 128, 128)
     rng = np.random.default_rng(61)
-    lengths = [int(x) for x in rng.integers(1, 90, 40)]
+    if case == "uniform_160_chains":
+        lengths = [int(x) for x in rng.integers(1, 90, 40)]
+    else:
+        # a few long sequences among many short ones (the shape of a varlen batch)
+        lengths = [1500, 900] + [int(x) for x in rng.integers(1, 200, 70)] + [0, 3]
     inp = wl.token_inputs(61, shape, sum(lengths))
+    say(f"paired schedule {case}: {len(lengths)} sequences x {shape.H} heads, {sum(lengths)} tokens")
     paired = Run(shape, inp, lengths, interval=64, flags=PAIRED).launch()
     single = Run(shape, inp, lengths, interval=64).launch()
     assert_same_bits(paired, single)

@@ -200,20 +200,22 @@ kda_status kda_decode_multi(const kda_config* cfg, int32_t B, int32_t T,
  *   to fp32 rounding.  A run resumed from one of its interval checkpoints with
  *   the same interval and flags reproduces it bit for bit; a continuation
  *   from a sequence end that is not an interval position agrees to rounding.
- * KDA_PREFILL_PAIRED: two workgroups per (sequence, head) chain.  One
- *   computes every chunk's state-independent part (conv, norms, decays, the
- *   intra-chunk products and triangular inverses).  The other applies each
- *   chunk to the state and writes the outputs, checkpoints and final state.
- *   The chunks pass between them through a ring in the workspace, so the two
- *   parts of consecutive chunks overlap.  The launch is cooperative, so both
- *   workgroups of every chain are resident together.  That is possible only
- *   when 2 x sequences x heads (rounded up to a multiple of 16) fits on the
- *   device at once: 128 chains at dk = dv = 128 on a 256-CU GPU.  Larger
- *   batches run the one-workgroup kernel.  Either way the results are bit
- *   for bit those of a call without the flag.  The workspace grows by the
- *   ring (three slots of about 142 KB per chain at dk = dv = 128) when
- *   sequences x heads <= 1024.  Meant for batches with fewer chains than
- *   compute units.  Paired calls are not tested under HIP graph capture.
+ * KDA_PREFILL_PAIRED: a grid of workgroups that are all resident at once
+ *   (cooperative launch) schedules the (sequence, head) chains.  The longest
+ *   chains get two workgroups each.  One computes every chunk's
+ *   state-independent part (conv, norms, decays, the intra-chunk products
+ *   and triangular inverses).  The other applies each chunk to the state and
+ *   writes the outputs, checkpoints and final state; the chunks pass between
+ *   them through a ring in the workspace, so the two parts of consecutive
+ *   chunks overlap.  The other workgroups, and each pair once its chain is
+ *   done, take the remaining chains one at a time from a queue, longest
+ *   first.  How many chains to pair is decided on the device from the
+ *   sequence lengths.  The results are bit for bit those of a call without
+ *   the flag.  The workspace grows by the ring: three slots of about 142 KB
+ *   per pair at dk = dv = 128, for up to min(sequences x heads, 256) pairs.
+ *   On a device that cannot hold 16 such workgroups at once, the call runs
+ *   as without the flag.  Paired calls are not tested under HIP graph
+ *   capture.
  * Precondition on the gate: within any 32 consecutive tokens of a chunk the
  *   accumulated log-decay of every channel stays above -80 (for instance
  *   g >= -2.5 everywhere); the intra-chunk decay factors are formed relative

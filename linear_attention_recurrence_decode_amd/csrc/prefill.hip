@@ -1398,9 +1398,14 @@ __device__ __forceinline__ int64_t item_chunks(const SeqWork& w) {
 __device__ void schedule_pairs(const SeqWork* work, int32_t N, int32_t H, int32_t* ring_ctr, int32_t max_pairs,
                                int32_t grid) {
     __shared__ double part_s[1024];
+    __shared__ float lead_s[PAIR_MAX_PAIRS + 1];      // chunks of the leading items
     for (int64_t i = threadIdx.x; i < static_cast<int64_t>(max_pairs) * 32 + 32; i += 1024) ring_ctr[i] = 0;
     double tot = 0.0;
-    for (int i = threadIdx.x; i < N; i += 1024) tot += static_cast<double>(item_chunks(work[i]));
+    for (int i = threadIdx.x; i < N; i += 1024) {
+        const int64_t c = item_chunks(work[i]);
+        tot += static_cast<double>(c);
+        if (i <= PAIR_MAX_PAIRS) lead_s[i] = static_cast<float>(c);
+    }
     part_s[threadIdx.x] = tot;
     __syncthreads();
     for (int off = 512; off > 0; off >>= 1) {
@@ -1411,11 +1416,11 @@ __device__ void schedule_pairs(const SeqWork* work, int32_t N, int32_t H, int32_
     const int64_t NH = static_cast<int64_t>(N) * H;
     const double W = part_s[0] * H;                  // chunk steps of all chains
     const int64_t kmax = min(min(static_cast<int64_t>(max_pairs), static_cast<int64_t>(grid / 2)), NH);
-    const double l0 = NH > 0 ? static_cast<double>(item_chunks(work[0])) : 0.0;
+    const double l0 = NH > 0 ? lead_s[0] : 0.0;
     double best = 1e300, paired = 0.0;
     int bestk = 0;
     for (int64_t k = 0; k <= kmax; k++) {
-        const double lu = k < NH ? static_cast<double>(item_chunks(work[k / H])) : 0.0;
+        const double lu = k < NH ? lead_s[k / H] : 0.0;   // k / H <= kmax <= PAIR_MAX_PAIRS
         const int64_t workers = grid - 2 * k;
         if (k == NH || workers > 0) {
             const double rest = W - paired;

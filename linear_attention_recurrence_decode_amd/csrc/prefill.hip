@@ -490,7 +490,6 @@ struct PrefillShape {
     static constexpr int VEC = 16 / static_cast<int>(sizeof(ACT));   // elements per 16-byte load
     static constexpr int CR = C + VEC;          // padded row stride of the raw rows
     static constexpr int FP = DK + 4;           // padded row stride of the fp32 q/k planes
-    static constexpr int NU = StageMap<ACT, D, NT>::NU;              // staged 16-byte words per thread
     // LDS regions (bytes)
     static constexpr int R0 = cmax(CH * FP * 4, 2 * CH * PS * 2);                // a_k (fp32) / K+ planes
     static constexpr int R1 = R0;                                                 // a_q (fp32) / Q+ planes
@@ -523,11 +522,11 @@ struct PrefillLds {
 };
 
 // Roles of a chain's workgroup.  FUSED runs both phases of every chunk.  In a
-// paired launch a PRODUCER runs phase A of every chunk of its chain and hands
-// the chunk's planes, sv and SiLU(conv(v)) to its CONSUMER through a ring of
-// RING slots in the workspace; the consumer runs phase B, the epilogue,
-// checkpoints and the final state.  The arithmetic of both phases is the
-// fused code itself, so a paired run gives the fused run's bits.
+// pair, a PRODUCER runs phase A of every chunk of its chain (without v's
+// conv) and hands the chunk's planes and sv to its CONSUMER through a ring of
+// RING slots in the workspace; the consumer convolves v, runs phase B, the
+// epilogue, checkpoints and the final state.  The arithmetic is the fused
+// code itself, so a paired chain gives the fused run's bits.
 constexpr int FUSED = 0, PRODUCER = 1, CONSUMER = 2;
 constexpr int RING = 3;
 // Spin limit of a ring wait (each poll sleeps 128 cycles, several hundred ms

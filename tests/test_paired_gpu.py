@@ -110,3 +110,52 @@ def test_paired_invalid_slot_gives_nan_and_writes_nothing():
     assert np.isfinite(out[:70]).all() and np.isnan(out[70:]).all()
     assert np.array_equal(bits(run.Sd[int(run.final[1])]), before)
     assert np.isfinite(host(run.Sd)[int(run.final[0])]).all()
+
+
+def schedule_pairs_model(lengths, starts, H, G, max_pairs):
+    """Host statement of the launch's choice of K (pairs for the leading
+    chains, longest first): chunk steps of one workgroup, a paired chain at
+    0.72 per chunk, the unpaired chains spread over the G - 2K other
+    workgroups; K minimises the largest of the three times."""
+    order = sorted(range(len(lengths)), key=lambda i: (-lengths[i], i))
+    chunks = [0 if lengths[i] <= 0 else (starts[i] % 64 + lengths[i] + 63) // 64 for i in order]
+    NH = len(lengths) * H
+    W = float(sum(chunks) * H)
+    kmax = min(max_pairs, G // 2, NH)
+    best, bestk, paired = float("inf"), 0, 0.0
+    for k in range(kmax + 1):
+        lu = float(chunks[k // H]) if k < NH else 0.0
+        workers = G - 2 * k
+        if k == NH or workers > 0:
+            mk = max(0.72 * chunks[0] if k > 0 else 0.0, lu, (W - paired) / workers if workers > 0 else 0.0)
+            if mk < best * (1.0 - 1e-9):
+                best, bestk = mk, k
+        if k < NH:
+            paired += lu
+    return bestk
+
+
+@pytest.mark.parametrize("case", ["equal", "one_long", "skewed"])
+def test_paired_schedule_choice_matches_model(case):
+    """The number of paired chains the metadata kernel writes into the
+    workspace equals the host statement of the cost model."""
+    import torch
+    shape = wl.LayerShape(4, 128, 128)
+    rng = np.random.default_rng(63)
+    lengths = {"equal": [256] * 8,
+               "one_long": [2000] + [int(x) for x in rng.integers(1, 60, 90)],
+               "skewed": [1500, 900] + [int(x) for x in rng.integers(1, 200, 70)] + [0, 3]}[case]
+    inp = wl.token_inputs(63, shape, sum(lengths))
+    run = Run(shape, inp, lengths, flags=PAIRED).launch()
+    NH = len(lengths) * shape.H
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    G = min(cus // 16 * 16, 16 * ((NH + 7) // 8))          # one 512-thread workgroup per CU at d = 128
+    max_pairs = min(NH, 256)
+    ctr_off = (len(lengths) * 32 + 255) // 256 * 256        # after the work items (32 bytes each)
+    ws = run.ws.cpu().numpy()
+    k_dev = int(ws[ctr_off + max_pairs * 128: ctr_off + max_pairs * 128 + 4].view(np.int32)[0])
+    k_host = schedule_pairs_model(lengths, [0] * len(lengths), shape.H, G, max_pairs)
+    say(f"  {case}: {NH} chains, grid {G}: pairs {k_dev} (model {k_host})")
+    assert k_dev == k_host
+    if case == "equal":
+        assert k_dev == NH                                    # every chain paired

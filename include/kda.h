@@ -215,8 +215,11 @@ kda_status kda_decode_multi(const kda_config* cfg, int32_t B, int32_t T,
  *   per pair at dk = dv = 128, for up to min(sequences x heads, 256) pairs.
  *   On a device that cannot hold 16 such workgroups at once, the call runs
  *   as without the flag.  The launch needs its whole grid resident, so
- *   work running on the device at the same time can delay its start.
- *   Paired calls are not tested under HIP graph capture.
+ *   work running on the device at the same time can delay its start.  A
+ *   paired call captured in a HIP graph replays bit for bit in the tests;
+ *   every wait between the two workgroups of a chain is bounded, so a launch
+ *   whose grid is not all resident cannot hang: a chain whose partner never
+ *   starts gets NaN outputs and no state.
  * Precondition on the gate: within any 32 consecutive tokens of a chunk the
  *   accumulated log-decay of every channel stays above -80 (for instance
  *   g >= -2.5 everywhere); the intra-chunk decay factors are formed relative

@@ -56,7 +56,8 @@ def test_decode_steps_in_a_graph():
         assert torch.equal(outg, oute) and torch.equal(Sg, Se) and torch.equal(Xg, Xe), rep
 
 
-def test_prefill_call_in_a_graph():
+@pytest.mark.parametrize("flags", [0, kda.KDA_PREFILL_PAIRED])
+def test_prefill_call_in_a_graph(flags):
     shape = wl.LayerShape(H=2, dk=64, dv=64, act="bf16")
     cfg = kda.Config(2, 64, 64, kda.KDA_BF16)
     lengths = [300, 77, 129]
@@ -74,11 +75,11 @@ def test_prefill_call_in_a_graph():
     ck_S = torch.empty((nck, 2, 64, 64), device="cuda")
     ck_X = torch.empty((nck, 2, 2 * 64 + 64, 3), dtype=torch.bfloat16, device="cuda")
     based = dev(np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int32))
-    ws = torch.empty(kda.kda_prefill_workspace_bytes(cfg, N, T, 64), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(cfg, N, T, 64, flags), dtype=torch.uint8, device="cuda")
 
     def run(S, X, out, cS, cX, stream):
         kda.kda_prefill_varlen(cfg, cu, q, k, v, z, g, beta, cw, nw, S, X, init, fin, out, ws, ckpt_interval=64,
-                               ckpt_state=cS, ckpt_conv=cX, ckpt_base=based, stream=stream)
+                               ckpt_state=cS, ckpt_conv=cX, ckpt_base=based, flags=flags, stream=stream)
 
     Se, Xe, oute = S0d.clone(), X0d.clone(), torch.empty((T, 2, 64), dtype=torch.bfloat16, device="cuda")
     cSe, cXe = torch.full_like(ck_S, float("nan")), torch.zeros_like(ck_X)

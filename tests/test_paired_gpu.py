@@ -159,3 +159,17 @@ def test_paired_schedule_choice_matches_model(case):
     assert k_dev == k_host
     if case == "equal":
         assert k_dev == NH                                    # every chain paired
+
+
+def test_paired_many_short_sequences():
+    """More than 1024 sequences (work items then keep their input order):
+    the scheduled launch still equals the one-workgroup kernel bit for bit."""
+    shape = wl.LayerShape(1, 32, 32, act="f32")
+    rng = np.random.default_rng(64)
+    lengths = [int(x) for x in rng.integers(0, 70, 1100)]
+    lengths[500] = 400                                        # one long sequence in the middle
+    inp = wl.token_inputs(64, shape, sum(lengths))
+    say(f"paired many short: {len(lengths)} sequences, {sum(lengths)} tokens")
+    paired = Run(shape, inp, lengths, interval=64, flags=PAIRED).launch()
+    single = Run(shape, inp, lengths, interval=64).launch()
+    assert_same_bits(paired, single)

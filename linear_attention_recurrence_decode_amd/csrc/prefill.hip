@@ -1355,7 +1355,10 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
 // other workgroup, and each pair once its chain is done, takes the remaining
 // chains one at a time from a queue, longest first, and runs each in one
 // workgroup.
-template <int D, typename ACT>
+// QUEUE = false: every chain is paired (the grid holds them all), and the
+// one-workgroup code is left out of the kernel, which keeps the two roles'
+// register allocation free of it.
+template <int D, typename ACT, bool QUEUE>
 __global__ __launch_bounds__(4 * D) void prefill_pair_kernel(PrefillParams p) {
     __shared__ PrefillLds<D, ACT> sm;
     __shared__ int next_s;
@@ -1369,6 +1372,7 @@ __global__ __launch_bounds__(4 * D) void prefill_pair_kernel(PrefillParams p) {
         else prefill_chain<D, ACT, true, CONSUMER>(p, sm, pair / p.H, pair % p.H, false);
         __syncthreads();
     }
+    if constexpr (!QUEUE) return;
     for (;;) {
         if (threadIdx.x == 0) next_s = atomicAdd(const_cast<int32_t*>(sched) + 1, 1);
         __syncthreads();
@@ -1413,6 +1417,11 @@ __device__ void schedule_pairs(const SeqWork* work, int32_t N, int32_t H, int32_
     }
     if (threadIdx.x != 0) return;
     const int64_t NH = static_cast<int64_t>(N) * H;
+    if (2 * NH <= grid && NH <= max_pairs) {
+        // the grid holds a pair for every chain: pair them all
+        ring_ctr[static_cast<int64_t>(max_pairs) * 32] = static_cast<int32_t>(NH);
+        return;
+    }
     const double W = part_s[0] * H;                  // chunk steps of all chains
     const int64_t kmax = min(min(static_cast<int64_t>(max_pairs), static_cast<int64_t>(grid / 2)), NH);
     const double l0 = NH > 0 ? lead_s[0] : 0.0;
@@ -1630,8 +1639,10 @@ hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
         if (p.ring) {
             PrefillParams pc = p;
             void* args[] = {&pc};
-            return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&prefill_pair_kernel<D, ACT>),
-                                              dim3(static_cast<unsigned>(p.sched_grid)), dim3(4 * D), args, 0, s);
+            const bool all_paired = 2 * blocks <= p.sched_grid && blocks <= p.max_pairs;
+            const void* f = all_paired ? reinterpret_cast<const void*>(&prefill_pair_kernel<D, ACT, false>)
+                                       : reinterpret_cast<const void*>(&prefill_pair_kernel<D, ACT, true>);
+            return hipLaunchCooperativeKernel(f, dim3(static_cast<unsigned>(p.sched_grid)), dim3(4 * D), args, 0, s);
         }
         hipLaunchKernelGGL((prefill_kernel<D, ACT, true>), dim3(static_cast<unsigned>(blocks)), dim3(4 * D), 0, s,
                            p);
@@ -1666,11 +1677,11 @@ int64_t prefill_pair_slot_bytes(int dk, int act) {
 
 int64_t prefill_pair_capacity(int dk, int act) {
     const void* f = nullptr;
-    if (act == 1) f = dk == 32 ? reinterpret_cast<const void*>(&prefill_pair_kernel<32, bf16_t>)
-                    : dk == 64 ? reinterpret_cast<const void*>(&prefill_pair_kernel<64, bf16_t>)
-                               : reinterpret_cast<const void*>(&prefill_pair_kernel<128, bf16_t>);
-    else f = dk == 32 ? reinterpret_cast<const void*>(&prefill_pair_kernel<32, float>)
-                      : reinterpret_cast<const void*>(&prefill_pair_kernel<64, float>);
+    if (act == 1) f = dk == 32 ? reinterpret_cast<const void*>(&prefill_pair_kernel<32, bf16_t, true>)
+                    : dk == 64 ? reinterpret_cast<const void*>(&prefill_pair_kernel<64, bf16_t, true>)
+                               : reinterpret_cast<const void*>(&prefill_pair_kernel<128, bf16_t, true>);
+    else f = dk == 32 ? reinterpret_cast<const void*>(&prefill_pair_kernel<32, float, true>)
+                      : reinterpret_cast<const void*>(&prefill_pair_kernel<64, float, true>);
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;

@@ -114,12 +114,15 @@ def test_paired_invalid_slot_gives_nan_and_writes_nothing():
 
 def schedule_pairs_model(lengths, starts, H, G, max_pairs):
     """Host statement of the launch's choice of K (pairs for the leading
-    chains, longest first): chunk steps of one workgroup, a paired chain at
-    0.72 per chunk, the unpaired chains spread over the G - 2K other
-    workgroups; K minimises the largest of the three times."""
+    chains, longest first): every chain when the grid holds a pair for each;
+    otherwise, in chunk steps of one workgroup, a paired chain at 0.72 per
+    chunk, the unpaired chains spread over the G - 2K other workgroups, and K
+    minimises the largest of the three times."""
     order = sorted(range(len(lengths)), key=lambda i: (-lengths[i], i))
     chunks = [0 if lengths[i] <= 0 else (starts[i] % 64 + lengths[i] + 63) // 64 for i in order]
     NH = len(lengths) * H
+    if 2 * NH <= G and NH <= max_pairs:
+        return NH                                             # a pair for every chain fits: all paired
     W = float(sum(chunks) * H)
     kmax = min(max_pairs, G // 2, NH)
     best, bestk, paired = float("inf"), 0, 0.0

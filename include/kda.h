@@ -305,8 +305,8 @@ kda_status kda_resume(const kda_config* cfg, int32_t n,
  * interval and flags (0 on an error; kda_last_error() then says why).  With
  * KDA_PREFILL_SPLIT it holds, per possible segment (at most 2 num_seqs +
  * total_tokens / ckpt_interval) and head, three dk x dv fp32 matrices; with
- * KDA_PREFILL_PAIRED and num_seqs x heads <= 1024, the ring of the paired
- * launch and its counters. */
+ * KDA_PREFILL_PAIRED, the ring of the scheduled launch (three slots per
+ * pair, for min(num_seqs x heads, 256) pairs), its counters and its queue. */
 size_t kda_prefill_workspace_bytes(const kda_config* cfg, int32_t num_seqs, int64_t total_tokens,
                                    int32_t ckpt_interval, int32_t flags);
 

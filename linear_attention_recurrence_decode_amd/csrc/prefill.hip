@@ -1682,8 +1682,9 @@ int64_t prefill_pair_capacity(int dk, int act) {
                                : reinterpret_cast<const void*>(&prefill_pair_kernel<128, bf16_t, true>);
     else f = dk == 32 ? reinterpret_cast<const void*>(&prefill_pair_kernel<32, float, true>)
                       : reinterpret_cast<const void*>(&prefill_pair_kernel<64, float, true>);
-    int dev = 0, cus = 0, per_cu = 0;
+    int dev = 0, cus = 0, per_cu = 0, coop = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, 4 * dk, 0) != hipSuccess) return 0;
     return static_cast<int64_t>(cus) * per_cu;

@@ -465,12 +465,15 @@ def bench_long(steps, warmup):
     log(f"[bench] long context: {L} tokens, H={shape.H}")
     inp = wl.token_inputs(w["seed"], shape, L)
     stream = torch.cuda.current_stream()
-    split = kda.KDA_PREFILL_SPLIT
-    st = PrefillSetup(kda, wl, shape, inp, [L], [0], interval, [0, split])
+    split, paired = kda.KDA_PREFILL_SPLIT, kda.KDA_PREFILL_PAIRED
+    st = PrefillSetup(kda, wl, shape, inp, [L], [0], interval, [0, split, paired])
     res = {"workload": f"long_1m: 1 sequence of {L} tokens, H={shape.H}, dk=dv={shape.dk}, bf16, checkpoints "
                        f"every {interval}"}
     t_u = _time_calls(lambda: st.call(0, stream), max(1, steps // 4), min(warmup, 1), stream)
     res["unsplit"] = prefill_rates(L, shape.H, shape.dk, shape.dv, t_u)
+    # the 8 chains paired (producer and consumer workgroups), not split
+    t_p = _time_calls(lambda: st.call(paired, stream), max(1, steps // 4), min(warmup, 1), stream)
+    res["unsplit_paired"] = prefill_rates(L, shape.H, shape.dk, shape.dv, t_p)
     t_s = _time_calls(lambda: st.call(split, stream), steps, warmup, stream)
     res["split"] = prefill_rates(L, shape.H, shape.dk, shape.dv, t_s)
     res["value"] = res["split"]["value"]

@@ -977,7 +977,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
                         for (int e = 0; e < 4; e++) {
                             const int idx = (16 * a + 4 * gg + e) * QS + 16 * b + lc;
                             pp_h[idx] = 0;
-                            pp_l[idx] = 0;
+                            if constexpr (!kOutHi) pp_l[idx] = 0;   // with bf16 outputs only P's hi plane is read
                         }
                     }
                     continue;
@@ -993,8 +993,16 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
 #pragma unroll
                 for (int e = 0; e < 4; e += 2) {
                     const int t = 16 * a + 4 * gg + e, s2 = 16 * b + lc;
-                    if constexpr (OUT)
+                    if constexpr (OUT && kOutHi) {
+                        // hi plane only (the same rounding as split2's hi)
+                        const uint32_t hw = __builtin_bit_cast(
+                            uint32_t, __builtin_convertvector(f32x2{t >= s2 ? ap[e] : 0.f, t + 1 >= s2 ? ap[e + 1] : 0.f},
+                                                              bf16x2));
+                        pp_h[t * QS + s2] = static_cast<uint16_t>(hw);
+                        pp_h[(t + 1) * QS + s2] = static_cast<uint16_t>(hw >> 16);
+                    } else if constexpr (OUT) {
                         st_split2(pp_h, pp_l, t * QS + s2, QS, t >= s2 ? ap[e] : 0.f, t + 1 >= s2 ? ap[e + 1] : 0.f);
+                    }
                     if (a > b) {
                         st_split2(lp_h, lp_l, t * QS + s2, QS, beta_s[t] * am[e], beta_s[t + 1] * am[e + 1]);
                     } else {

@@ -49,7 +49,12 @@
  *                                       the checkpoint format)
  *   conv      [S][H][2dk+dv][3] activation dtype (raw inputs of the last 3
  *                                       tokens, index 0 = oldest)
- * Supported shapes: dk == dv in {32, 64, 128}; conv width 4; H >= 1.
+ * Supported shapes: dk == dv in {32, 64, 128}; conv width 4; H >= 1.  One
+ *   exception: kda_prefill_varlen with fp32 activations takes dk == dv in
+ *   {32, 64} only (its LDS staging of 64 fp32 token rows at 128 does not fit
+ *   a workgroup's 160 KB) and returns KDA_ERR_UNSUPPORTED for 128.
+ * Gates: every call accepts any log-decay g <= 0, including -inf (that
+ *   channel of the state is forgotten).  A NaN gate gives NaN results.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -74,7 +79,9 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 /* Flags of kda_prefill_varlen (bitwise or). */
 typedef enum {
     KDA_PREFILL_SPLIT = 1,    /* cut sequences into segments at checkpoint positions */
-    KDA_PREFILL_PAIRED = 2    /* two workgroups per chain: state-independent and state phases overlap */
+    KDA_PREFILL_PAIRED = 2,   /* two workgroups per chain: state-independent and state phases overlap */
+    KDA_PREFILL_PAIRED_POLL_ONCE = 4  /* with KDA_PREFILL_PAIRED, for tests only: every wait between
+                                         the two workgroups of a chain polls once before it gives up */
 } kda_prefill_flags;
 
 typedef struct {
@@ -180,8 +187,14 @@ kda_status kda_decode_multi(const kda_config* cfg, int32_t B, int32_t T,
  *   A checkpoint at p holds the state after the tokens before position p.
  * out: [total_tokens][H][dv] activation dtype.
  * workspace: device scratch of at least kda_prefill_workspace_bytes(...)
- *   bytes; its contents on entry do not matter.
- * flags: 0, KDA_PREFILL_SPLIT or KDA_PREFILL_PAIRED (not both).
+ *   bytes; its contents on entry do not matter.  Its first 4 bytes are the
+ *   call's status word (int32): once the call has completed on its stream it
+ *   holds the number of waits between paired workgroups that gave up (see
+ *   KDA_PREFILL_PAIRED), 0 when every chain ran to its end.  It is always 0
+ *   after a call without KDA_PREFILL_PAIRED; a call with num_seqs == 0
+ *   launches nothing and leaves it untouched.
+ * flags: 0, KDA_PREFILL_SPLIT or KDA_PREFILL_PAIRED (not both), and
+ *   KDA_PREFILL_PAIRED_POLL_ONCE only together with KDA_PREFILL_PAIRED.
  * KDA_PREFILL_SPLIT (needs ckpt_interval > 0).  Without it each
  *   (sequence, head) chain runs through its chunks in order in one workgroup,
  *   so a batch of few long sequences occupies few compute units.  With it,
@@ -218,12 +231,21 @@ kda_status kda_decode_multi(const kda_config* cfg, int32_t B, int32_t T,
  *   work running on the device at the same time can delay its start.  A
  *   paired call captured in a HIP graph replays bit for bit in the tests;
  *   every wait between the two workgroups of a chain is bounded, so a launch
- *   whose grid is not all resident cannot hang: a chain whose partner never
- *   starts gets NaN outputs and no state.
- * Precondition on the gate: within any 32 consecutive tokens of a chunk the
- *   accumulated log-decay of every channel stays above -80 (for instance
- *   g >= -2.5 everywhere); the intra-chunk decay factors are formed relative
- *   to the middle of the chunk and would leave the fp32 range otherwise.
+ *   whose grid is not all resident cannot hang.  A wait that gives up counts
+ *   in the status word; when it is the state-phase workgroup's, its chain's
+ *   outputs from that chunk on, its final slot's state and the states of its
+ *   checkpoints still due (this head's) are written as NaN, so none of them
+ *   passes for a valid state.  KDA_PREFILL_PAIRED_POLL_ONCE makes every such
+ *   wait poll only once, so tests can drive this path without a stalled
+ *   partner.
+ * Gates: any g <= 0, including -inf.  Within a chunk the pairwise decays
+ *   exp(Gam_t - Gam_s) (Gam the running sum of g) are formed through the
+ *   chunk's middle row while every channel's decay over each half of the
+ *   chunk stays above -80, and from sums over 16-token blocks otherwise (a
+ *   slower path, exact pairs within a block); log-decays below -30 then count
+ *   as -30 (exp(-30) = 9.4e-14: what they let through is below the fp32
+ *   resolution of the state).  Which path a chunk takes depends only on its
+ *   own gates, so resumes stay bit-identical.
  */
 kda_status kda_prefill_varlen(const kda_config* cfg, int32_t num_seqs, int64_t total_tokens,
                               const int32_t* cu_seqlens, const int64_t* start_pos,

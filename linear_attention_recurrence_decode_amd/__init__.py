@@ -25,6 +25,7 @@ KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP
 KDA_F32, KDA_BF16 = 0, 1
 KDA_PREFILL_SPLIT = 1
 KDA_PREFILL_PAIRED = 2
+KDA_PREFILL_PAIRED_POLL_ONCE = 4
 
 # every symbol include/kda.h declares
 EXPORTS = (
@@ -291,6 +292,13 @@ def kda_prefill_varlen(cfg: Config, cu_seqlens, q, k, v, z, g, beta, conv_w, nor
                                     _ptr(ckpt_state), _ptr(ckpt_conv), nck, _ptr(ckpt_base), int(flags),
                                     _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
     return out
+
+
+def prefill_status(workspace) -> int:
+    """The status word of the last kda_prefill_varlen call on this workspace
+    (bytes 0..3, int32): waits between paired workgroups that gave up.  Read
+    after the call has completed on its stream (this synchronises)."""
+    return int(workspace[:4].view(torch.int32).item())
 
 
 def _copy(fn, cfg, src_state, src_conv, src_idx, dst_state, dst_conv, dst_idx, stream):

@@ -210,8 +210,10 @@ kda_status check_prefill_mode(int32_t ckpt_interval, int32_t flags) {
     if (ckpt_interval < 0 || ckpt_interval % 64 != 0)
         return fail(KDA_ERR_INVALID_ARG, "ckpt_interval must be 0 or a positive multiple of 64 (got %d)",
                     ckpt_interval);
-    if (flags & ~(KDA_PREFILL_SPLIT | KDA_PREFILL_PAIRED))
+    if (flags & ~(KDA_PREFILL_SPLIT | KDA_PREFILL_PAIRED | KDA_PREFILL_PAIRED_POLL_ONCE))
         return fail(KDA_ERR_INVALID_ARG, "unknown prefill flags 0x%x", flags);
+    if ((flags & KDA_PREFILL_PAIRED_POLL_ONCE) && !(flags & KDA_PREFILL_PAIRED))
+        return fail(KDA_ERR_INVALID_ARG, "KDA_PREFILL_PAIRED_POLL_ONCE needs KDA_PREFILL_PAIRED");
     if ((flags & KDA_PREFILL_SPLIT) && ckpt_interval == 0)
         return fail(KDA_ERR_INVALID_ARG, "KDA_PREFILL_SPLIT needs ckpt_interval > 0");
     if ((flags & KDA_PREFILL_SPLIT) && (flags & KDA_PREFILL_PAIRED))
@@ -335,6 +337,8 @@ kda_status kda_prefill_varlen(const kda_config* cfg, int32_t num_seqs, int64_t t
     p.ring_ctr = nullptr;
     p.max_pairs = 0;
     p.sched_grid = 0;
+    p.spin_limit = (flags & KDA_PREFILL_PAIRED_POLL_ONCE) ? 1 : kda::PAIR_SPIN_LIMIT;
+    p.status = reinterpret_cast<int32_t*>(ws + wl.status);
     if (wl.ring > 0) {
         // a scheduled launch needs a grid of at least 16 workgroups that the
         // device holds at once; otherwise the one-workgroup kernel runs

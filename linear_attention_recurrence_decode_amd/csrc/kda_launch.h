@@ -99,6 +99,8 @@ struct PrefillParams {
                         // [32]: pairs chosen at 0, chain queue at 1
     int32_t max_pairs;  // pairs the ring holds
     int32_t sched_grid; // workgroups of the scheduled launch
+    int32_t spin_limit; // polls before a wait between paired workgroups gives up
+    int32_t* status;    // workspace word: waits that gave up in this call (zeroed by the metadata kernel)
 };
 
 // Input projections: y = x W^T routed to q, k, v, z (activation dtype) and
@@ -127,8 +129,12 @@ bool prefill_supported(int dk, int dv, int act);
 // Workspace layout of the prefill (offsets in bytes; total = bytes).
 struct PrefillWorkspace {
     int32_t max_items, max_pairs;
-    size_t items, seq_items, seg_F, seg_G, seg_S, seq_x0, ring_ctr, ring, bytes;
+    size_t status, items, seq_items, seg_F, seg_G, seg_S, seq_x0, ring_ctr, ring, bytes;
 };
+// Polls (of 128 cycles each) before a wait between the two workgroups of a
+// paired chain gives up: several hundred milliseconds, far above any
+// legitimate wait (a chunk takes about 20 us).
+constexpr int32_t PAIR_SPIN_LIMIT = 1 << 20;
 // A scheduled launch pairs at most this many chains (sequences x heads);
 // the ring takes RING slots of prefill_pair_slot_bytes per pair.
 constexpr int64_t PAIR_MAX_PAIRS = 256;

@@ -24,9 +24,10 @@
 // factors exp(Gam_r), exp(Gam_end - Gam_r) and exp(Gam_end) then move onto the
 // state side, so the three stored operands K+ = k exp(Gam-Gam_r),
 // K- = k exp(Gam_r-Gam), Q+ = q exp(Gam-Gam_r) serve every product.  This needs
-// |Gam_t - Gam_r| to stay inside the fp32 exponent range for every channel,
-// i.e. the log-decay accumulated over any 32 tokens of a chunk above about
-// -80.
+// |Gam_t - Gam_r| inside the fp32 exponent range for every channel; a chunk
+// with a channel whose decay over one of its 16-row blocks reaches -40 (or a
+// gate of -inf) takes a block-local form instead, with every factor <= 1
+// (local_planes, local_products, local_rescale), so any g <= 0 is handled.
 //
 // Workgroup = one (sequence, head) chain, NW = dv/16 waves, chunks in order.
 // Phase A (state independent): raw rows staged in LDS, causal conv + SiLU,
@@ -53,6 +54,18 @@ namespace {
 
 constexpr int CH = 64;       // chunk length
 constexpr int RREF = 31;     // reference row of the decay factorisation
+// The factorisation through row RREF needs, for every key channel, Gam_RREF
+// and Gam_end - Gam_RREF above -FAST_BOUND: every factor then lies in
+// [exp(-80), exp(80)], inside the fp32 range.  A chunk uses it when every
+// channel's decay over each of its four 16-row blocks stays above
+// -FAST_BOUND / 2 (which implies the bound on both halves); other chunks take
+// the block-local path (local_planes in prefill_chain).
+constexpr float FAST_BOUND = 80.f;
+// The block-local path floors each log-decay at -G_FLOOR: exp(-30) = 9.4e-14,
+// so what a floored token lets through is below the fp32 resolution of the
+// state it multiplies, and the local sums stay finite (a gate of -inf would
+// otherwise give -inf - (-inf) in a difference of prefix sums).
+constexpr float G_FLOOR = 30.f;
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
@@ -138,6 +151,14 @@ __device__ __forceinline__ Frag split8(const float (&x)[8]) {
     return Frag{h.v, l.v};
 }
 
+// A fragment scaled element by element by d and split again into hi/lo.
+__device__ __forceinline__ Frag scale_frag(const Frag& f, const float (&d)[8]) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) x[e] = (static_cast<float>(f.hi[e]) + static_cast<float>(f.lo[e])) * d[e];
+    return split8(x);
+}
+
 __device__ __forceinline__ uint16_t bf16_bits(__bf16 b) { return __builtin_bit_cast(uint16_t, b); }
 
 // Store a at element idx and b at idx + stride of two (hi, lo) planes.
@@ -148,6 +169,19 @@ __device__ __forceinline__ void st_split2(uint16_t* hi, uint16_t* lo, int idx, i
     hi[idx + stride] = static_cast<uint16_t>(h >> 16);
     lo[idx] = static_cast<uint16_t>(l);
     lo[idx + stride] = static_cast<uint16_t>(l >> 16);
+}
+
+// One element of a plane pair (the lo plane skipped when lo is null).
+__device__ __forceinline__ void st_split1(uint16_t* hi, uint16_t* lo, int idx, float a) {
+    uint32_t h, l;
+    split2(a, 0.f, h, l);
+    hi[idx] = static_cast<uint16_t>(h);
+    if (lo) lo[idx] = static_cast<uint16_t>(l);
+}
+
+// The value hi + lo of one element of a plane pair (exact in fp32).
+__device__ __forceinline__ float ld_pair(const uint16_t* hi, const uint16_t* lo, int idx) {
+    return __uint_as_float(static_cast<uint32_t>(hi[idx]) << 16) + __uint_as_float(static_cast<uint32_t>(lo[idx]) << 16);
 }
 
 union U128 {
@@ -519,7 +553,23 @@ struct PrefillLds {
     ACT x0[Sh::C * 3];
     ACT vwin[sizeof(ACT) == 2 ? 1 : (CH + 3) * D];   // consumer's raw v rows (fp32 activations)
     int flag;
+    int local;                 // the chunk takes the block-local decay path
 };
+
+// A thread's 16 consecutive entries of K-^T row c (chunk rows 16 qq ..
+// 16 qq + 15) into the hi/lo planes: two 16-byte stores per plane.
+template <int QS>
+__device__ __forceinline__ void st_kt(uint16_t* kt_h, uint16_t* kt_l, int c, int qq, const float (&km)[16]) {
+    uint32_t wh[8], wl[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) split2(km[r], km[r + 1], wh[r / 2], wl[r / 2]);
+    uint4* dh = reinterpret_cast<uint4*>(kt_h + c * QS + 16 * qq);
+    uint4* dl = reinterpret_cast<uint4*>(kt_l + c * QS + 16 * qq);
+    dh[0] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+    dh[1] = make_uint4(wh[4], wh[5], wh[6], wh[7]);
+    dl[0] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+    dl[1] = make_uint4(wl[4], wl[5], wl[6], wl[7]);
+}
 
 // Roles of a chain's workgroup.  FUSED runs both phases of every chunk.  In a
 // pair, a PRODUCER runs phase A of every chunk of its chain (without v's
@@ -529,10 +579,6 @@ struct PrefillLds {
 // code itself, so a paired chain gives the fused run's bits.
 constexpr int FUSED = 0, PRODUCER = 1, CONSUMER = 2;
 constexpr int RING = 3;
-// Spin limit of a ring wait (each poll sleeps 128 cycles, several hundred ms
-// in all): far above any legitimate wait (a chunk takes about 20 us), so a
-// wait that reaches it means the partner is gone.
-constexpr int SPIN_LIMIT = 1 << 20;
 
 // Bytes of one ring slot: the LDS planes, then sv.
 template <int D, typename ACT>
@@ -610,13 +656,16 @@ __device__ __forceinline__ int ring_peek(const int32_t* ctr) {
 }
 
 // Wait until a ring counter reaches want (one lane), given a value read
-// earlier: only when that value falls short is the counter polled.
-__device__ __forceinline__ bool ring_wait(const int32_t* ctr, int want, int seen) {
+// earlier: only when that value falls short is the counter polled, at most
+// `limit` times (each poll sleeps 128 cycles).  A wait that runs out means
+// the partner is gone; it is counted in the call's status word.
+__device__ __forceinline__ bool ring_wait(const int32_t* ctr, int want, int seen, int limit, int32_t* status) {
     if (seen >= want) return true;
-    for (int it = 0; it < SPIN_LIMIT; it++) {
+    for (int it = 0; it < limit; it++) {
         if (ring_peek(ctr) >= want) return true;
         __builtin_amdgcn_s_sleep(2);
     }
+    __hip_atomic_fetch_add(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return false;
 }
 
@@ -824,7 +873,202 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
         stage_issue<ACT, DK, DV, NT, NTEN>(stg, p, x0_s, ctx0, tc0, n, H, h, tp);
         stage_commit<ACT, DK, DV, NT, NTEN>(stg, raw, beta_s, tp);
     }
+    if (tid == 0) sm.local = 0;
     __syncthreads();
+
+    // ---- block-local decay path, for chunks whose decay leaves the range of
+    // the factorisation through row RREF.  Every pairwise factor
+    // exp(Gam_t - Gam_s) (s <= t) is formed from sums over 16-row blocks:
+    //   same block:    exp(pi_t - pi_s), pi the prefix sum from the block start,
+    //                  summed over the channels on the VALU (exact pairs);
+    //   t in block a, s in block b < a:
+    //                  exp(pi_t) * exp(sum of the blocks between) * exp(tau_b - pi_s),
+    //                  tau_b the block total, so both MFMA operands carry
+    //                  factors <= 1 and the middle one scales one operand.
+    // Log-decays are floored at -G_FLOOR so that the sums stay finite.  The
+    // state phase is unchanged: K+ and Q+ carry exp(Gam_t), K-^T carries
+    // exp(Gam_end - Gam_s), and the per-channel factors on the state side are
+    // exp(Gam_end) and 1.
+    //
+    // LP1: floored log-decays reloaded (16 rows of one channel per thread),
+    // block prefix sums to gq (registers), to the fp32 plane pi in the K-
+    // region (free: the raw rows are consumed) and block totals to gtot;
+    // LP2: diagonal blocks of Diag(b) M (fp32, to ld) and of P (planes);
+    // LP3: block-relative K+, Q+ and K- planes, the full K- column in km.
+    auto local_planes = [&](float (&gq)[16], float (&km)[16]) {
+        float* const pi_f = reinterpret_cast<float*>(reg2);     // [CH][FP]
+        {
+            const int tp = opq(tid);
+            const int cgp = tp % DK, qqp = tp / DK;
+            const auto rg = make_rsrc(p.g + (tc0 * H + h) * DK, static_cast<uint32_t>(((n - 1) * H + 1) * DK * 4));
+            const uint32_t gv = static_cast<uint32_t>((16 * qqp * H * DK + cgp) * 4);
+            float acc = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                float gr = buf_ldf(rg, gv + static_cast<uint32_t>(r * H * DK * 4), 0);
+                gr = gr < -G_FLOOR ? -G_FLOOR : gr;        // NaN stays NaN
+                acc += gr;
+                gq[r] = acc;
+                pi_f[(16 * qqp + r) * FP + cgp] = acc;
+            }
+            gtot_s[qqp][cgp] = acc;
+        }
+        __syncthreads();
+        {
+            // lanes: P2 per (block a, row pair pr), 8 channels each; a lane
+            // takes rows pr and 15 - pr of block a (17 pairs (t, s) in all)
+            const int tp = opq(tid);
+            constexpr int P2 = DK / 8;
+            const int part = tp % P2, pr = (tp / P2) % 8, a = tp / (8 * P2);
+            const int c0 = 8 * part;
+            uint16_t* const plo = kOutHi ? nullptr : pp_l;
+            for (int half = 0; half < 2; half++) {
+                const int rl = half == 0 ? pr : 15 - pr;
+                const int R = 16 * a + rl;
+                float kr[8], qr[8], pr8[8];
+#pragma unroll
+                for (int e = 0; e < 8; e += 4) {
+                    *reinterpret_cast<float4*>(kr + e) = *reinterpret_cast<const float4*>(ak_f + R * FP + c0 + e);
+                    *reinterpret_cast<float4*>(qr + e) = *reinterpret_cast<const float4*>(aq_f + R * FP + c0 + e);
+                    *reinterpret_cast<float4*>(pr8 + e) = *reinterpret_cast<const float4*>(pi_f + R * FP + c0 + e);
+                }
+                const float sk = rk_s[R], sq = rq_s[R], bt = beta_s[R];
+                for (int sl = 0; sl <= rl; sl++) {
+                    const int S2 = 16 * a + sl;
+                    float ks[8], ps[8];
+#pragma unroll
+                    for (int e = 0; e < 8; e += 4) {
+                        *reinterpret_cast<float4*>(ks + e) = *reinterpret_cast<const float4*>(ak_f + S2 * FP + c0 + e);
+                        *reinterpret_cast<float4*>(ps + e) = *reinterpret_cast<const float4*>(pi_f + S2 * FP + c0 + e);
+                    }
+                    float m = 0.f, pp = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; e++) {
+                        const float w = ks[e] * __expf(pr8[e] - ps[e]);
+                        m = fmaf(kr[e], w, m);
+                        pp = fmaf(qr[e], w, pp);
+                    }
+                    m = dpp_group_sum<P2>(m);
+                    if constexpr (OUT) pp = dpp_group_sum<P2>(pp);
+                    if (part == 0) {
+                        const float kn = rk_s[S2];
+                        ld_s[a][rl][sl] = sl < rl ? bt * (m * sk * kn) : 0.f;
+                        if constexpr (OUT) st_split1(pp_h, plo, R * QS + S2, pp * sq * kn);
+                    }
+                }
+            }
+            // entries above the diagonal of the diagonal blocks: 15 per row pair
+            for (int e = part; e < 15; e += P2) {
+                const bool first = e < 15 - pr;
+                const int rl = first ? pr : 15 - pr;
+                const int sl = first ? pr + 1 + e : 1 + e;
+                ld_s[a][rl][sl] = 0.f;
+                if constexpr (OUT) st_split1(pp_h, plo, (16 * a + rl) * QS + 16 * a + sl, 0.f);
+            }
+        }
+        __syncthreads();
+        {
+            const int tp = opq(tid);
+            const int cgp = tp % DK, qqp = tp / DK;
+            const float tau = gq[15];
+            float suf = 0.f;                               // blocks after this one
+            for (int q2 = qqp + 1; q2 < 4; q2++) suf += gtot_s[q2][cgp];
+            float kp[16], qp[16], kb[16];
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int t = 16 * qqp + r;
+                const float kh = ak_f[t * FP + cgp] * rk_s[t];
+                const float qh = aq_f[t * FP + cgp] * rq_s[t];
+                const float E = __expf(gq[r]);
+                const float sl = tau - gq[r];
+                kp[r] = kh * E;
+                qp[r] = qh * E;
+                kb[r] = kh * __expf(sl);
+                km[r] = kh * __expf(sl + suf);
+            }
+            if (qqp == 0) {
+                eGr_s[cgp] = 1.f;
+                eGCr_s[cgp] = 1.f;
+                eGC_s[cgp] = __expf(((gtot_s[0][cgp] + gtot_s[1][cgp]) + gtot_s[2][cgp]) + gtot_s[3][cgp]);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const int idx = (16 * qqp + r) * PS + cgp;
+                st_split2(kp_h, kp_l, idx, PS, kp[r], kp[r + 1]);
+                if constexpr (OUT) st_split2(qp_h, qp_l, idx, PS, qp[r], qp[r + 1]);
+                st_split2(km_h, km_l, idx, PS, kb[r], kb[r + 1]);
+            }
+        }
+    };
+    // LP4 (in place of A5): the off-diagonal blocks (a > b) of L and P from the
+    // block-relative planes, blocks two or three apart with the decay of the
+    // blocks between them applied to the K- operand; P's upper blocks zeroed.
+    auto local_products = [&]() {
+        const int tp = opq(tid);
+        const int ln = tp & 63, wv5 = __builtin_amdgcn_readfirstlane(tp >> 6), gg = ln >> 4, lc = ln & 15;
+        for (int ji = wv5; ji < 16; ji += NW) {
+            const int job = static_cast<int>((kA5Order >> (4 * ji)) & 15);
+            const int a = job >> 2, b = job & 3;
+            if (a == b) continue;
+            if (a < b) {
+                if constexpr (OUT) {
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const int idx = (16 * a + 4 * gg + e) * QS + 16 * b + lc;
+                        pp_h[idx] = 0;
+                        if constexpr (!kOutHi) pp_l[idx] = 0;
+                    }
+                }
+                continue;
+            }
+            f32x4 am = {0.f, 0.f, 0.f, 0.f}, ap = am;
+            for (int ks = 0; ks < KS; ks++) {
+                const int offa = (16 * a + lc) * PS + 32 * ks + 8 * gg;
+                Frag fb = ld_nat(km_h, km_l, (16 * b + lc) * PS + 32 * ks + 8 * gg);
+                if (a >= b + 2) {
+                    float d[8];
+#pragma unroll
+                    for (int e = 0; e < 8; e++) {
+                        const int c = 32 * ks + 8 * gg + e;
+                        float s2 = gtot_s[b + 1][c];
+                        if (a == b + 3) s2 += gtot_s[b + 2][c];
+                        d[e] = __expf(s2);
+                    }
+                    fb = scale_frag(fb, d);
+                }
+                am = mfma3(ld_nat(kp_h, kp_l, offa), fb, am);
+                if constexpr (OUT) ap = mfma3(ld_nat(qp_h, qp_l, offa), fb, ap);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; e += 2) {
+                const int t = 16 * a + 4 * gg + e, s2 = 16 * b + lc;
+                if constexpr (OUT && kOutHi) {
+                    const uint32_t hw = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{ap[e], ap[e + 1]}, bf16x2));
+                    pp_h[t * QS + s2] = static_cast<uint16_t>(hw);
+                    pp_h[(t + 1) * QS + s2] = static_cast<uint16_t>(hw >> 16);
+                } else if constexpr (OUT) {
+                    st_split2(pp_h, pp_l, t * QS + s2, QS, ap[e], ap[e + 1]);
+                }
+                st_split2(lp_h, lp_l, t * QS + s2, QS, beta_s[t] * am[e], beta_s[t + 1] * am[e + 1]);
+            }
+        }
+    };
+    // LP5 (beside A6): K+ and Q+ planes from block-relative to chunk factors,
+    // exp(pi_t) * exp(sum of the earlier blocks) = exp(Gam_t).
+    auto local_rescale = [&]() {
+        const int tp = opq(tid);
+        const int cgp = tp % DK, qqp = tp / DK;
+        float pre = 0.f;
+        for (int q2 = 0; q2 < qqp; q2++) pre += gtot_s[q2][cgp];
+        const float E = __expf(pre);
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            const int idx = (16 * qqp + r) * PS + cgp;
+            st_split1(kp_h, kp_l, idx, ld_pair(kp_h, kp_l, idx) * E);
+            if constexpr (OUT) st_split1(qp_h, qp_l, idx, ld_pair(qp_h, qp_l, idx) * E);
+        }
+    };
 
     while (done < L) {
         float vh[4][4];    // SiLU(conv(v)) in accumulator layout
@@ -903,8 +1147,39 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
 #pragma unroll
             for (int r = 1; r < 16; r++) gq[r] += gq[r - 1];
             gtot_s[tp / DK][tp % DK] = gq[15];
+            // a 16-row block total at or below -FAST_BOUND / 2 (or NaN) sends
+            // the chunk to the block-local path
+            if (!(gq[15] > -0.5f * FAST_BOUND)) sm.local = 1;
         }
         __syncthreads();
+        const int local = __builtin_amdgcn_readfirstlane(sm.local);
+        // producer, after the planes are stored: the previous chunk's ring
+        // stores were issued a phase ago; once every thread has seen its own
+        // complete (no other global access is in flight: this chunk's inputs
+        // were committed before phase A), that chunk is published.  Then the
+        // next chunk's inputs are requested (the staging registers are free
+        // here), so they arrive during A5, A6 and the ring stores.
+        auto after_planes = [&]() {
+            if constexpr (ROLE == PRODUCER) __builtin_amdgcn_s_waitcnt(VMCNT0);
+            __syncthreads();
+            if constexpr (ROLE == PRODUCER) {
+                if (tid == 0) {
+                    if (chunk > 0) __hip_atomic_store(ready_ctr, chunk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    seen = ring_peek(taken_ctr);       // used after A6
+                }
+                const int done_next = done + n;
+                n_next_p = done_next < L ? min(L - done_next, CH - static_cast<int>((pos + n) % CH)) : 0;
+                if (n_next_p > 0) stage_issue<ACT, DK, DV, NT, NTEN>(stg, p, x0_s, ctx0, tok0 + done_next, n_next_p, H, h, opq(tid));
+                else stage_clear(stg);
+            }
+        };
+        if (__builtin_expect(local, 0)) {
+            local_planes(gq, km);
+            after_planes();
+            local_products();
+            __syncthreads();
+            local_rescale();
+        } else {
 
         // ---------------- A4: K+, K-, Q+ (hi/lo planes); per-channel factors
         {
@@ -940,24 +1215,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
                 st_split2(km_h, km_l, idx, PS, km[r], km[r + 1]);
             }
         }
-        // producer: the previous chunk's ring stores were issued a phase
-        // ago; once every thread has seen its own complete (no other global
-        // access is in flight: this chunk's inputs were committed before
-        // phase A), that chunk is published.  Then the next chunk's inputs
-        // are requested (the staging registers are free after A4), so they
-        // arrive during A5, A6 and the ring stores.
-        if constexpr (ROLE == PRODUCER) __builtin_amdgcn_s_waitcnt(VMCNT0);
-        __syncthreads();
-        if constexpr (ROLE == PRODUCER) {
-            if (tid == 0) {
-                if (chunk > 0) __hip_atomic_store(ready_ctr, chunk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                seen = ring_peek(taken_ctr);       // used after A6
-            }
-            const int done_next = done + n;
-            n_next_p = done_next < L ? min(L - done_next, CH - static_cast<int>((pos + n) % CH)) : 0;
-            if (n_next_p > 0) stage_issue<ACT, DK, DV, NT, NTEN>(stg, p, x0_s, ctx0, tok0 + done_next, n_next_p, H, h, opq(tid));
-            else stage_clear(stg);
-        }
+        after_planes();
 
         // ---------------- A5: L = Diag(b) strictLower(K+ K-^T), P = lower(Q+ K-^T);
         // one job per 16x16 block pair (a, b) computes both, sharing the K-
@@ -1013,12 +1271,14 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             }
         }
         __syncthreads();
+        }   // fast path of A4 and A5
 
         // ---------------- A6: T_aa = (I + L_aa)^{-1} for the 4 diagonal blocks,
         // forward substitution on one column with PARTS threads splitting each
         // dot product; then the K-^T planes into the K- region
         {
             const int tp = opq(tid);
+            if (tp == 0) sm.local = 0;                   // read after A3: free for the next chunk
             constexpr int PARTS = NT / 64, KPP = 16 / PARTS;
             const int part = tp % PARTS, col = (tp / PARTS) % 16, blk = tp / (16 * PARTS);
             float xk[KPP];
@@ -1039,17 +1299,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             for (int kk = 0; kk < KPP; kk += 2)
                 st_split2(lp_h, lp_l, (16 * blk + part * KPP + kk) * QS + 16 * blk + col, QS, xk[kk], xk[kk + 1]);
             const int cgp = tp % DK, qqp = tp / DK;
-            // this thread's 16 values are 16 consecutive entries of K-^T row cgp:
-            // two 16-byte stores per plane
-            uint32_t wh[8], wl[8];
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) split2(km[r], km[r + 1], wh[r / 2], wl[r / 2]);
-            uint4* dh = reinterpret_cast<uint4*>(kt_h + cgp * QS + 16 * qqp);
-            uint4* dl = reinterpret_cast<uint4*>(kt_l + cgp * QS + 16 * qqp);
-            dh[0] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
-            dh[1] = make_uint4(wh[4], wh[5], wh[6], wh[7]);
-            dl[0] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
-            dl[1] = make_uint4(wl[4], wl[5], wl[6], wl[7]);
+            st_kt<QS>(kt_h, kt_l, cgp, qqp, km);
         }
         __syncthreads();
         }   // phase A
@@ -1072,7 +1322,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             // (published in the next chunk's phase A, or after the last
             // chunk)
             if (chunk >= RING) {
-                if (tid == 0) sm.flag = ring_wait(taken_ctr, chunk - RING + 1, seen);
+                if (tid == 0) sm.flag = ring_wait(taken_ctr, chunk - RING + 1, seen, p.spin_limit, p.status);
                 __syncthreads();
                 if (!sm.flag) return;                         // the consumer is gone
             }
@@ -1104,14 +1354,32 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             // into LDS and the v rows into vwin
             VWin<ACT, DV, NT> vw;
             vwin_issue<ACT, DV, NT>(vw, p, ctx0, tc0, n, H, h, opq(tid));
-            if (tid == 0) sm.flag = ring_wait(ready_ctr, chunk + 1, seen);
+            if (tid == 0) sm.flag = ring_wait(ready_ctr, chunk + 1, seen, p.spin_limit, p.status);
             __syncthreads();
             if (!sm.flag) {
-                // the producer is gone: NaN outputs from here on, no state written
+                // the producer is gone: NaN outputs from here on, and NaN in
+                // this head's state of every checkpoint still due and of the
+                // final slot, so that none of them passes for a valid state
                 for (int64_t e = tid; e < static_cast<int64_t>(L - done) * DV; e += NT) {
                     const int64_t t = tc0 + e / DV;
                     A::st(out + (t * H + h) * DV + e % DV, nan_f32());
                 }
+                auto nan_state = [&](void* pool, int64_t slot) {
+                    const int64_t sh = (slot * H + h) * DK * DV;
+                    for (int e = tid; e < DK * DV; e += NT) {
+                        if (p.state_bf16) static_cast<uint16_t*>(pool)[sh + e] = 0x7fc0u;
+                        else static_cast<float*>(pool)[sh + e] = nan_f32();
+                    }
+                };
+                if (p.ckpt_interval > 0) {
+                    const int64_t I = p.ckpt_interval;
+                    const int64_t total = (start + L - 1) / I - start / I + 1;   // checkpoints of the sequence
+                    for (int64_t j = ck; j < total; j++) {
+                        const int64_t slot = ck_base + j;
+                        if (slot >= 0 && slot < p.num_ckpt_slots) nan_state(p.ckpt_state, slot);
+                    }
+                }
+                if (fin >= 0 && fin < p.num_slots) nan_state(p.state, fin);
                 return;
             }
             {
@@ -1456,7 +1724,8 @@ __device__ void schedule_pairs(const SeqWork* work, int32_t N, int32_t H, int32_
 // len = -1 and are skipped by the prefill kernel.
 __global__ __launch_bounds__(1024) void prefill_meta_kernel(const int32_t* cu, const int64_t* sp, int32_t N,
                                                             int64_t T, SeqWork* work, int32_t H, int32_t* ring_ctr,
-                                                            int32_t max_pairs, int32_t grid) {
+                                                            int32_t max_pairs, int32_t grid, int32_t* status) {
+    if (threadIdx.x == 0) *status = 0;
     for (int i = threadIdx.x; i < N; i += 1024) {
         const int64_t a = cu[i], b = cu[i + 1];
         const bool ok = a >= 0 && b >= a && b <= T;
@@ -1480,6 +1749,9 @@ __global__ __launch_bounds__(1024) void prefill_meta_kernel(const int32_t* cu, c
         w.last = 1;
         work[rank] = w;
     }
+    // work[i] was written by the thread that ranked sequence i, not by
+    // thread i: every write must be complete before the schedule reads them
+    __syncthreads();
     if (ring_ctr) schedule_pairs(work, N, H, ring_ctr, max_pairs, grid);
 }
 
@@ -1511,7 +1783,10 @@ __global__ __launch_bounds__(1024) void prefill_split_meta_kernel(PrefillParams 
     __shared__ int32_t scan_s[1024];
     __shared__ int64_t total_s;
     const int tid = threadIdx.x;
-    if (tid == 0) total_s = 0;
+    if (tid == 0) {
+        total_s = 0;
+        *p.status = 0;
+    }
     __syncthreads();
     for (int base = 0; base < p.N; base += 1024) {
         const int i = base + tid;
@@ -1640,7 +1915,7 @@ hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
     if (!p.split) {
         const int64_t blocks = static_cast<int64_t>(p.N) * p.H;
         hipLaunchKernelGGL(prefill_meta_kernel, dim3(1), dim3(1024), 0, s, p.cu_seqlens, p.start_pos, p.N, p.T,
-                           p.work, p.H, p.ring ? p.ring_ctr : nullptr, p.max_pairs, p.sched_grid);
+                           p.work, p.H, p.ring ? p.ring_ctr : nullptr, p.max_pairs, p.sched_grid, p.status);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (blocks == 0) return hipSuccess;
@@ -1712,6 +1987,8 @@ PrefillWorkspace prefill_workspace(int32_t N, int32_t H, int64_t T, int dk, int 
     if (items > INT32_MAX / 4) return w;       // bytes == 0: too many work items
     w.max_items = static_cast<int32_t>(items);
     size_t off = 0;
+    w.status = off;                            // int32 status word at byte 0
+    off += 256;
     w.items = off;
     off += up(static_cast<size_t>(items) * sizeof(SeqWork));
     if (split) {

@@ -60,6 +60,33 @@ def per_chain_max(x, ref) -> float:
     return float(np.max(np.where(n > 0, d / np.maximum(n, 1e-300), d))) if len(n) else 0.0
 
 
+# Worst (token, head) output row: the whole-tensor norm can hide one wrong
+# row among a million; every row must stay within these relative errors
+# (bf16 outputs are rounded to 8 significant bits, about 4e-3 per element).
+TOL_ROW_F32 = 1e-3
+TOL_ROW_BF16 = 5e-2
+
+
+def per_row_max(x, ref, row_axes: int = 2) -> float:
+    """Largest relative L2 error over rows of the last axis grouped by the
+    leading `row_axes` axes (for outputs [T][H][dv]: one row per token and
+    head).  A row whose reference is zero counts its absolute error."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    n_rows = int(np.prod(x.shape[:row_axes])) if x.ndim else 0
+    if n_rows == 0:
+        return 0.0
+    a = x.reshape(n_rows, -1)
+    b = ref.reshape(a.shape)
+    d = np.linalg.norm(a - b, axis=1)
+    n = np.linalg.norm(b, axis=1)
+    return float(np.max(np.where(n > 0, d / np.maximum(n, 1e-300), d)))
+
+
+def tol_row(act: str) -> float:
+    return TOL_ROW_F32 if act == "f32" else TOL_ROW_BF16
+
+
 def tols(act: str):
     if act == "f32":
         return TOL_F32, TOL_F32

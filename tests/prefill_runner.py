@@ -6,7 +6,7 @@ import torch
 import linear_attention_recurrence_decode_amd as kda
 import oracle
 import workloads as wl
-from tests.helpers import TOL_STATE_PER_CHAIN, dev, host, per_chain_max, rel_l2, say, tols
+from tests.helpers import TOL_STATE_PER_CHAIN, dev, host, per_chain_max, per_row_max, rel_l2, say, tol_row, tols
 
 
 def cfg_for(shape, state_dtype=kda.KDA_F32):
@@ -95,9 +95,12 @@ def check_against_oracle(run, r, heads=None):
     e_out = rel_l2(out, r.out)
     e_s = rel_l2(Sf[:, hs], r.S)
     e_c = per_chain_max(Sf[:, hs], r.S)
-    say(f"  rel-L2 out {e_out:.3e} (tol {tol_o})  state {e_s:.3e} (tol {tol_s})  worst chain {e_c:.3e}")
-    assert np.isfinite(out).all()
+    e_r = per_row_max(out, r.out)
+    say(f"  rel-L2 out {e_out:.3e} (tol {tol_o})  state {e_s:.3e} (tol {tol_s})  worst chain {e_c:.3e}"
+        f"  worst row {e_r:.3e} (tol {tol_row(run.shape.act)})")
+    assert np.isfinite(out).all() and np.isfinite(Sf[:, hs]).all()
     assert e_out <= tol_o and e_s <= tol_s and e_c <= TOL_STATE_PER_CHAIN
+    assert e_r <= tol_row(run.shape.act)
     np.testing.assert_array_equal(Xf[:, hs], r.X)
     return e_out, e_s
 

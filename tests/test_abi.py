@@ -133,7 +133,10 @@ def test_prefill_validation():
     assert prefill_call(cfg(), interval=64, ckb=None) == kda.KDA_ERR_INVALID_ARG
     assert prefill_call(cfg(), interval=64, nck=0) == kda.KDA_ERR_INVALID_ARG
     assert prefill_call(cfg(), N=0, cu=None) == kda.KDA_OK                      # nothing to do
-    assert prefill_call(cfg(), flags=4) == kda.KDA_ERR_INVALID_ARG                 # unknown flag
+    assert prefill_call(cfg(), flags=8) == kda.KDA_ERR_INVALID_ARG                 # unknown flag
+    assert "unknown" in kda.last_error()
+    assert prefill_call(cfg(), flags=kda.KDA_PREFILL_PAIRED_POLL_ONCE) == kda.KDA_ERR_INVALID_ARG
+    assert "needs KDA_PREFILL_PAIRED" in kda.last_error()
     both = kda.KDA_PREFILL_SPLIT | kda.KDA_PREFILL_PAIRED
     assert prefill_call(cfg(), interval=64, flags=both) == kda.KDA_ERR_INVALID_ARG   # exclusive modes
     assert "exclude" in kda.last_error()
@@ -141,7 +144,8 @@ def test_prefill_validation():
     assert "interval" in kda.last_error()
     assert prefill_call(cfg(), interval=64, flags=kda.KDA_PREFILL_SPLIT, ws_bytes=1 << 20) == kda.KDA_ERR_WORKSPACE
     ws = kda.kda_prefill_workspace_bytes(cfg(), 16, 1 << 18)
-    assert ws >= 16 * 32 and ws % 256 == 0
+    assert ws >= 256 + 16 * 32 and ws % 256 == 0          # status word block, then the work items
+    assert kda.kda_prefill_workspace_bytes(cfg(), 0, 0) == 256
     # split: room for 2N + T/interval segments, three dk x dv fp32 matrices per segment and head
     ws_split = kda.kda_prefill_workspace_bytes(cfg(), 16, 1 << 18, 4096, kda.KDA_PREFILL_SPLIT)
     segs = 2 * 16 + (1 << 18) // 4096

@@ -154,7 +154,7 @@ def test_paired_schedule_choice_matches_model(case):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     G = min(cus // 16 * 16, 16 * ((NH + 7) // 8))          # one 512-thread workgroup per CU at d = 128
     max_pairs = min(NH, 256)
-    ctr_off = (len(lengths) * 32 + 255) // 256 * 256        # after the work items (32 bytes each)
+    ctr_off = 256 + (len(lengths) * 32 + 255) // 256 * 256  # after the status block and the work items (32 B each)
     ws = run.ws.cpu().numpy()
     k_dev = int(ws[ctr_off + max_pairs * 128: ctr_off + max_pairs * 128 + 4].view(np.int32)[0])
     k_host = schedule_pairs_model(lengths, [0] * len(lengths), shape.H, G, max_pairs)
@@ -176,3 +176,45 @@ def test_paired_many_short_sequences():
     paired = Run(shape, inp, lengths, interval=64, flags=PAIRED).launch()
     single = Run(shape, inp, lengths, interval=64).launch()
     assert_same_bits(paired, single)
+
+
+def test_paired_wait_gives_up_with_status_and_nan():
+    """Every wait between paired workgroups limited to one poll (the test-only
+    flag), so waits give up although both workgroups run and every kernel
+    exits normally.  The workspace status word counts the waits that gave up;
+    a chain whose state-phase workgroup gave up has NaN outputs from a chunk
+    boundary on, a NaN final state and NaN in its later checkpoints, and its
+    rows before that chunk, like every chain that completed, equal the
+    one-workgroup run bit for bit."""
+    shape = wl.LayerShape(4, 128, 128)
+    lengths, starts = [640, 513, 300, 64], [0, 64, 7, 0]
+    inp = wl.token_inputs(61, shape, sum(lengths))
+    ref = Run(shape, inp, lengths, starts=starts, interval=128).launch()
+    assert kda.prefill_status(ref.ws) == 0
+    run = Run(shape, inp, lengths, starts=starts, interval=128,
+              flags=PAIRED | kda.KDA_PREFILL_PAIRED_POLL_ONCE).launch()
+    status = kda.prefill_status(run.ws)
+    out, ro = host(run.out), host(ref.out)
+    Sf, Sr = host(run.Sd), host(ref.Sd)
+    ck = host(run.ckS)
+    failed = 0
+    for n, L in enumerate(lengths):
+        a = int(ref.cu[n])
+        fin = int(run.final[n])
+        for h in range(shape.H):
+            rows, rrows = out[a:a + L, h], ro[a:a + L, h]
+            nan_rows = np.isnan(rows).any(axis=1)
+            if not nan_rows.any():
+                assert np.array_equal(rows, rrows)
+                assert np.array_equal(Sf[fin, h], Sr[fin, h])
+                continue
+            failed += 1
+            first = int(np.argmax(nan_rows))
+            assert np.isnan(rows[first:]).all() and not np.isnan(rows[:first]).any()
+            assert first == 0 or (starts[n] + first) % 64 == 0
+            assert np.array_equal(rows[:first], rrows[:first])
+            assert np.isnan(Sf[fin, h]).all()
+            last = int(run.base[n]) + kda.kda_num_checkpoints(starts[n], L, 128) - 1
+            assert np.isnan(ck[last, h]).all()
+    say(f"  status word {status}, chains with NaN tails {failed} of {len(lengths) * shape.H}")
+    assert status > 0 and status >= failed

@@ -28,7 +28,9 @@
  * --------------------------------
  * Ownership: the caller owns every buffer.  The library allocates nothing,
  *   keeps no pointer after a call returns, and holds no global mutable state
- *   apart from a thread-local error message.
+ *   apart from a thread-local error message and, for
+ *   kda_prefill_varlen_static, one static device buffer per device and its
+ *   address.
  * Execution: every call enqueues its kernels on `stream` (a hipStream_t; NULL
  *   means the null stream) and returns without synchronising.  A fault inside
  *   a kernel surfaces at the caller's next synchronisation.
@@ -258,6 +260,42 @@ kda_status kda_prefill_varlen(const kda_config* cfg, int32_t num_seqs, int64_t t
                               int32_t num_ckpt_slots, const int32_t* ckpt_base, int32_t flags,
                               void* out, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/*
+ * For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation:
+ * kda_prefill_varlen with the same arguments and results, its workspace taken
+ * from a static device buffer of KDA_STATIC_WORKSPACE_BYTES instead of an
+ * argument.  The library holds one such buffer on every device it runs on
+ * until the process ends, and this call allocates nothing.
+ *
+ * Limit: the call must fit the buffer, i.e. kda_prefill_workspace_bytes(cfg,
+ *   num_seqs, total_tokens, ckpt_interval, flags) <= KDA_STATIC_WORKSPACE_BYTES;
+ *   otherwise it returns KDA_ERR_WORKSPACE and launches nothing.  That holds
+ *   for the one-workgroup launch of up to about two million sequences, for
+ *   KDA_PREFILL_PAIRED with up to 153 (sequence, head) chains at dk = dv = 128
+ *   (its ring takes 436 KB per chain), and for KDA_PREFILL_SPLIT with up to
+ *   about 340 (possible segment, head) pairs at dk = dv = 128 (192 KB each;
+ *   a call has 2 num_seqs + total_tokens / ckpt_interval possible segments).
+ * Sharing: every call on a device uses that device's one buffer, and the
+ *   buffer keeps the last call's contents (each call initialises what it
+ *   reads).  Calls whose kernels overlap in time on one device -- on
+ *   different streams, or from different host threads -- race on it and give
+ *   undefined results; serialise them (one stream, or events).
+ * The status word of the workspace (see kda_prefill_varlen) is not visible to
+ *   the caller; a chain whose paired wait gave up still shows NaN outputs.
+ */
+#define KDA_STATIC_WORKSPACE_BYTES (64LL << 20)
+kda_status kda_prefill_varlen_static(const kda_config* cfg, int32_t num_seqs, int64_t total_tokens,
+                                     const int32_t* cu_seqlens, const int64_t* start_pos,
+                                     const void* q, const void* k, const void* v, const void* z,
+                                     const float* g, const float* beta,
+                                     const float* conv_w, const float* norm_w,
+                                     void* state_pool, void* conv_pool, int32_t num_slots,
+                                     const int32_t* init_slot, const int32_t* final_slot,
+                                     int32_t ckpt_interval, void* ckpt_state, void* ckpt_conv,
+                                     int32_t num_ckpt_slots, const int32_t* ckpt_base, int32_t flags,
+                                     void* out, void* stream);
 
 /*
  * Input projections of the layer for T tokens in one bf16 MFMA GEMM:

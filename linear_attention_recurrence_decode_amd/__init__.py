@@ -29,7 +29,8 @@ KDA_PREFILL_PAIRED_POLL_ONCE = 4
 
 # every symbol include/kda.h declares
 EXPORTS = (
-    "kda_decode_step", "kda_decode_multi", "kda_prefill_varlen", "kda_state_checkpoint", "kda_resume",
+    "kda_decode_step", "kda_decode_multi", "kda_prefill_varlen", "kda_prefill_varlen_static",
+    "kda_state_checkpoint", "kda_resume",
     "kda_project_inputs", "kda_project_output", "kda_prefill_workspace_bytes", "kda_num_checkpoints", "kda_last_error",
     # host-side prefix cache (include/kda_prefix_cache.h)
     "kda_pcache_create", "kda_pcache_destroy", "kda_pcache_lookup", "kda_pcache_release",
@@ -105,6 +106,8 @@ def lib():
     L.kda_project_output.argtypes = [CP, I32, I32, P, P, P, P]
     L.kda_prefill_varlen.argtypes = ([CP, I32, I64, P, P] + [P] * 8 + [P, P, I32, P, P, I32, P, P, I32, P,
                                      I32, P, P, ctypes.c_size_t, P])
+    L.kda_prefill_varlen_static.argtypes = ([CP, I32, I64, P, P] + [P] * 8 + [P, P, I32, P, P, I32, P, P, I32, P,
+                                            I32, P, P])
     L.kda_state_checkpoint.argtypes = [CP, I32, P, P, I32, P, P, P, I32, P, P]
     L.kda_resume.argtypes = [CP, I32, P, P, I32, P, P, P, I32, P, P]
     L.kda_prefill_workspace_bytes.argtypes = [CP, I32, I64, I32, I32]
@@ -128,8 +131,8 @@ def lib():
     for f in ("kda_pcache_release", "kda_pcache_reserve", "kda_pcache_insert", "kda_pcache_insert_many",
               "kda_pcache_unreserve"):
         getattr(L, f).restype = I32
-    for f in ("kda_decode_step", "kda_decode_multi", "kda_prefill_varlen", "kda_state_checkpoint", "kda_resume",
-              "kda_project_inputs", "kda_project_output"):
+    for f in ("kda_decode_step", "kda_decode_multi", "kda_prefill_varlen", "kda_prefill_varlen_static",
+              "kda_state_checkpoint", "kda_resume", "kda_project_inputs", "kda_project_output"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -256,11 +259,39 @@ def kda_project_output(cfg: Config, o, w_o, y, stream=None):
     _check(lib().kda_project_output(ctypes.byref(cfg.c()), T, Dm, _ptr(o), _ptr(w_o), _ptr(y), _stream(stream)))
 
 
+STATIC_WORKSPACE_BYTES = 64 << 20      # KDA_STATIC_WORKSPACE_BYTES
+
+
 def kda_prefill_varlen(cfg: Config, cu_seqlens, q, k, v, z, g, beta, conv_w, norm_w,
                        state_pool, conv_pool, init_slot, final_slot, out, workspace,
                        start_pos=None, ckpt_interval: int = 0, ckpt_state=None, ckpt_conv=None,
                        ckpt_base=None, flags: int = 0, stream=None):
     """Chunked varlen prefill (see include/kda.h)."""
+    a = _prefill_args(cfg, cu_seqlens, q, k, v, z, g, beta, conv_w, norm_w, state_pool, conv_pool,
+                      init_slot, final_slot, out, start_pos, ckpt_interval, ckpt_state, ckpt_conv, ckpt_base)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is not None:
+        _want(workspace, "workspace", workspace.dtype)
+    _check(lib().kda_prefill_varlen(*a, int(flags), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def kda_prefill_varlen_static(cfg: Config, cu_seqlens, q, k, v, z, g, beta, conv_w, norm_w,
+                              state_pool, conv_pool, init_slot, final_slot, out,
+                              start_pos=None, ckpt_interval: int = 0, ckpt_state=None, ckpt_conv=None,
+                              ckpt_base=None, flags: int = 0, stream=None):
+    """kda_prefill_varlen with the library's static device workspace: allocates
+    nothing (see include/kda.h)."""
+    a = _prefill_args(cfg, cu_seqlens, q, k, v, z, g, beta, conv_w, norm_w, state_pool, conv_pool,
+                      init_slot, final_slot, out, start_pos, ckpt_interval, ckpt_state, ckpt_conv, ckpt_base)
+    _check(lib().kda_prefill_varlen_static(*a, int(flags), _ptr(out), _stream(stream)))
+    return out
+
+
+def _prefill_args(cfg, cu_seqlens, q, k, v, z, g, beta, conv_w, norm_w, state_pool, conv_pool,
+                  init_slot, final_slot, out, start_pos, ckpt_interval, ckpt_state, ckpt_conv, ckpt_base):
+    """Checked leading arguments shared by the two prefill entry points, up to
+    ckpt_base."""
     N = cu_seqlens.numel() - 1
     T = q.shape[0]
     H, dk, dv, C = cfg.num_heads, cfg.head_k, cfg.head_v, cfg.conv_channels
@@ -282,16 +313,11 @@ def kda_prefill_varlen(cfg: Config, cu_seqlens, q, k, v, z, g, beta, conv_w, nor
         _want(ckpt_state, "ckpt_state", cfg.torch_state, (nck, H, dk, dv))
         _want(ckpt_conv, "ckpt_conv", act, (nck, H, C, 3))
         _want(ckpt_base, "ckpt_base", torch.int32, (N,))
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if workspace is not None:
-        _want(workspace, "workspace", workspace.dtype)
-    _check(lib().kda_prefill_varlen(ctypes.byref(cfg.c()), N, T, _ptr(cu_seqlens), _ptr(start_pos),
-                                    _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(g), _ptr(beta),
-                                    _ptr(conv_w), _ptr(norm_w), _ptr(state_pool), _ptr(conv_pool), S,
-                                    _ptr(init_slot), _ptr(final_slot), int(ckpt_interval),
-                                    _ptr(ckpt_state), _ptr(ckpt_conv), nck, _ptr(ckpt_base), int(flags),
-                                    _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
-    return out
+    return (ctypes.byref(cfg.c()), N, T, _ptr(cu_seqlens), _ptr(start_pos),
+            _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(g), _ptr(beta),
+            _ptr(conv_w), _ptr(norm_w), _ptr(state_pool), _ptr(conv_pool), S,
+            _ptr(init_slot), _ptr(final_slot), int(ckpt_interval),
+            _ptr(ckpt_state), _ptr(ckpt_conv), nck, _ptr(ckpt_base))
 
 
 def prefill_status(workspace) -> int:

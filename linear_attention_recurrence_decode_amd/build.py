@@ -28,7 +28,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-SOURCES = ["kda_api.cpp", "prefix_cache.cpp", "decode.hip", "copy.hip", "prefill.hip", "project.hip"]
+SOURCES = ["kda_api.cpp", "prefix_cache.cpp", "decode.hip", "copy.hip", "prefill.hip", "prefill_static.hip",
+           "project.hip"]
 
 
 def _compile(src: str) -> str:

@@ -120,6 +120,14 @@ kda::CopyParams copy_params(const kda_config* cfg, int32_t n, const void* src_st
 
 }  // namespace
 
+int kda::set_error(int st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
 extern "C" {
 
 const char* kda_last_error(void) { return g_err; }

@@ -147,4 +147,8 @@ int64_t prefill_pair_slot_bytes(int dk, int act);
 int64_t pair_grid(int64_t chains, int64_t capacity);
 int64_t prefill_pair_capacity(int dk, int act);
 
+// Record an error message for kda_last_error() on this thread (printf-style)
+// and return st; for entry points defined outside kda_api.cpp.
+int set_error(int st, const char* fmt, ...);
+
 }  // namespace kda

@@ -56,15 +56,20 @@ class Run:
         nbytes = kda.kda_prefill_workspace_bytes(self.cfg, N, T, interval, flags)
         self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
 
-    def launch(self):
-        kda.kda_prefill_varlen(self.cfg, dev(self.cu.astype(np.int32)), self.q, self.k, self.v, self.z,
-                               self.g, self.beta, self.conv_w, self.norm_w, self.Sd, self.Xd,
-                               dev(self.init), dev(self.final), self.out, self.ws,
-                               start_pos=dev(np.asarray(self.starts, np.int64)),
-                               ckpt_interval=self.interval,
-                               ckpt_state=self.ckS if self.interval else None,
-                               ckpt_conv=self.ckX if self.interval else None,
-                               ckpt_base=dev(self.base) if self.interval else None, flags=self.flags)
+    def launch(self, static: bool = False):
+        """Run the call; static=True goes through kda_prefill_varlen_static
+        (the library's static workspace) instead of the allocated one."""
+        args = (self.cfg, dev(self.cu.astype(np.int32)), self.q, self.k, self.v, self.z,
+                self.g, self.beta, self.conv_w, self.norm_w, self.Sd, self.Xd,
+                dev(self.init), dev(self.final), self.out)
+        kw = dict(start_pos=dev(np.asarray(self.starts, np.int64)), ckpt_interval=self.interval,
+                  ckpt_state=self.ckS if self.interval else None,
+                  ckpt_conv=self.ckX if self.interval else None,
+                  ckpt_base=dev(self.base) if self.interval else None, flags=self.flags)
+        if static:
+            kda.kda_prefill_varlen_static(*args, **kw)
+        else:
+            kda.kda_prefill_varlen(*args, self.ws, **kw)
         torch.cuda.synchronize()
         return self
 

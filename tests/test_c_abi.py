@@ -50,6 +50,17 @@ int main(void) {
     CHECK(kda_project_output(&cfg, 0, 7168, NULL, NULL, NULL, NULL) == KDA_OK);
     CHECK(kda_project_inputs(&cfg, 4, 100, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == KDA_ERR_INVALID_ARG);
 
+    /* the static-workspace prefill refuses, before any device call, a call its
+       buffer cannot hold (a paired ring for 256 chains) and invalid arguments */
+    CHECK(kda_prefill_varlen_static(&cfg, 512, 100000, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
+                                    NULL, NULL, 8, NULL, NULL, 0, NULL, NULL, 0, NULL, KDA_PREFILL_PAIRED, NULL,
+                                    NULL) == KDA_ERR_WORKSPACE);
+    CHECK(strstr(kda_last_error(), "static workspace") != NULL);
+    CHECK(kda_prefill_workspace_bytes(&cfg, 512, 100000, 0, KDA_PREFILL_PAIRED) > (size_t)KDA_STATIC_WORKSPACE_BYTES);
+    CHECK(kda_prefill_varlen_static(&cfg, -1, 100, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
+                                    NULL, NULL, 8, NULL, NULL, 0, NULL, NULL, 0, NULL, 0, NULL, NULL)
+          == KDA_ERR_INVALID_ARG);
+
     /* the host prefix cache */
     for (i = 0; i < 300; i++) tokens[i] = (i * 7919) % 1000;
     c = kda_pcache_create(4, 64, KDA_PCACHE_KEEP_ALL, 0);

@@ -12,7 +12,7 @@ import torch
 import linear_attention_recurrence_decode_amd as kda
 import oracle
 import workloads as wl
-from tests.helpers import TOL_STATE_PER_CHAIN, bits, dev, host, per_chain_max, rel_l2, say, tols
+from tests.helpers import TOL_STATE_PER_CHAIN, bits, dev, host, per_chain_max, per_row_max, rel_l2, say, tol_row, tols
 
 pytestmark = pytest.mark.gpu
 
@@ -74,6 +74,7 @@ CASES = {
     "bf16_d32": (7, wl.LayerShape(4, 32, 32), 6, 30, 8, {}),
     "bf16_d64_nodecay": (8, wl.LayerShape(2, 64, 64), 4, 30, 6, dict(g_scale=0.0, norm_w="random")),
     "bf16_d128_weakdecay": (9, wl.LayerShape(4, 128, 128), 8, 48, 12, dict(g_scale=0.01, norm_w="random")),
+    "bf16_d128_strongdecay": (10, wl.LayerShape(4, 128, 128), 8, 48, 12, dict(g_scale=4.0, norm_w="random")),
 }
 
 
@@ -88,8 +89,9 @@ def test_decode_matches_oracle(name):
     e_out = rel_l2(host(out), o_ref)
     e_s = rel_l2(host(Sd)[slots], S_ref)
     e_c = per_chain_max(host(Sd)[slots], S_ref)
-    say(f"  rel-L2 out {e_out:.3e}  state {e_s:.3e}  worst chain {e_c:.3e}")
-    assert e_out <= tol_o and e_s <= tol_s and e_c <= TOL_STATE_PER_CHAIN
+    e_r = per_row_max(host(out), o_ref, 3)
+    say(f"  rel-L2 out {e_out:.3e}  state {e_s:.3e}  worst chain {e_c:.3e}  worst row {e_r:.3e}")
+    assert e_out <= tol_o and e_s <= tol_s and e_c <= TOL_STATE_PER_CHAIN and e_r <= tol_row(shape.act)
     # the conv state holds raw inputs: exact
     np.testing.assert_array_equal(host(Xd)[slots], X_ref)
 
@@ -108,8 +110,9 @@ def test_decode_batched_b64_full_size():
     e_out = rel_l2(host(out), o_ref)
     e_s = rel_l2(host(Sd)[slots], S_ref)
     e_c = per_chain_max(host(Sd)[slots], S_ref)
-    say(f"  rel-L2 out {e_out:.3e}  state {e_s:.3e}  worst chain {e_c:.3e}")
-    assert e_out <= 1e-2 and e_s <= 5e-3 and e_c <= TOL_STATE_PER_CHAIN
+    e_r = per_row_max(host(out), o_ref, 3)
+    say(f"  rel-L2 out {e_out:.3e}  state {e_s:.3e}  worst chain {e_c:.3e}  worst row {e_r:.3e}")
+    assert e_out <= 1e-2 and e_s <= 5e-3 and e_c <= TOL_STATE_PER_CHAIN and e_r <= tol_row("bf16")
     np.testing.assert_array_equal(host(Xd)[slots], X_ref)
 
 

@@ -12,8 +12,9 @@ import pytest
 import torch
 
 import linear_attention_recurrence_decode_amd as kda
+import oracle
 import workloads as wl
-from tests.helpers import TOL_STATE_PER_CHAIN, bits, dev, host, per_chain_max, rel_l2, say
+from tests.helpers import TOL_STATE_PER_CHAIN, bits, dev, host, per_chain_max, per_row_max, rel_l2, say, tol_row
 
 pytestmark = pytest.mark.gpu
 
@@ -47,6 +48,24 @@ class Layer:
                                start_pos=dev(np.array([start], np.int64)), ckpt_interval=iv, ckpt_state=ckS,
                                ckpt_conv=ckX, ckpt_base=dev(np.array([ckbase], np.int32)) if iv else None)
         return out
+
+
+def check_hit_against_oracle(layer, ids, p, out_hit, S_hit, X_hit):
+    """The fp64 oracle over the whole request ids from a zero state: the
+    outputs the hit prefilled (tokens p..) and the final state and conv
+    state, within the bf16 tolerances (outputs 1e-2 whole and 5e-2 per row,
+    states 5e-3 whole and 1e-4 per head)."""
+    t = layer.table
+    idx = np.asarray(ids, np.int64)
+    r = oracle.run(t.q[idx], t.k[idx], t.v[idx], t.z[idx], t.g[idx], t.beta[idx], t.conv_w, t.norm_w,
+                   [0, len(ids)])
+    o = host(out_hit)
+    e_o, e_r = rel_l2(o, r.out[p:]), per_row_max(o, r.out[p:])
+    S = host(S_hit)[None]
+    e_s, e_c = rel_l2(S, r.S), per_chain_max(S, r.S)
+    say(f"  hit at {p} vs oracle: out {e_o:.3e} (worst row {e_r:.3e}), state {e_s:.3e} (worst head {e_c:.3e})")
+    assert e_o <= 1e-2 and e_r <= tol_row("bf16") and e_s <= 5e-3 and e_c <= TOL_STATE_PER_CHAIN
+    np.testing.assert_array_equal(host(X_hit)[None], r.X)
 
 
 def pools(n):
@@ -88,6 +107,7 @@ def test_prefix_hit_resumes_and_matches_straight_runs():
     assert np.array_equal(bits(out_hit), bits(out_ref[p:]))
     assert np.array_equal(bits(live_S[1]), bits(live_S[2])) and np.array_equal(bits(live_X[1]), bits(live_X[2]))
     say(f"  hit at {p}: {len(B) - p} of {len(B)} tokens prefilled, bitwise equal to the straight run")
+    check_hit_against_oracle(layer, B, p, out_hit, live_S[1], live_X[1])
 
     # request C extends the whole prompt A: hit at the prompt end 700
     Cq = np.concatenate([A, rng.integers(0, VOCAB, 100)])
@@ -102,6 +122,7 @@ def test_prefix_hit_resumes_and_matches_straight_runs():
     e_s = per_chain_max(host(live_S[3:4]), host(live_S[4:5]))
     say(f"  hit at prompt end {p}: outputs {e_o:.3e}, state {e_s:.3e} from the straight run")
     assert e_o <= 1e-2 and e_s <= TOL_STATE_PER_CHAIN
+    check_hit_against_oracle(layer, Cq, p, out_hit, live_S[3], live_X[3])
     # the cached states were never written by the requests that extended them
     assert np.array_equal(bits(cache_S[torch.from_numpy(slots.astype(np.int64)).cuda()]),
                           bits(stage_S[:len(positions)]))

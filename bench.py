@@ -15,10 +15,20 @@ step).  The line also carries:
   slot_copies   the checkpoint and resume copies of the 64 live slots (all
                 heads): microseconds per call and the HBM fraction by the
                 bytes read and written
+  cold_state    the same decode step cycled over 4 distinct state pools (640
+                MiB, standing in for consecutive layers, so each launch reads
+                its state from HBM, not from the 256 MB Infinity Cache), and a
+                2 GiB read+write copy for the streaming rate this box attains
   prefill       the chunked prefill workload (4 x 8192 tokens, one call per
                 pass): tokens/s and the algorithmic HBM and bf16-MFMA fractions
+  varlen_ckpt   the varlen prefill with checkpoints (16 sequences, 262,990
+                tokens), one workgroup per chain and scheduled
+  long_1m       the 1M-token prefill split at its checkpoints, and with its 8
+                chains paired
   cpu_baseline  the fp64 oracle timed on this host on a bounded sample of the
-                decode workload
+                decode workload, and (prefill_workloads) on samples of the
+                three prefill workloads
+--no-paired leaves out every KDA_PREFILL_PAIRED (cooperative) launch.
 With --workload the line instead reports one of the larger prefill
 workloads (inputs resident in HBM, one call per pass):
   varlen_ckpt   16 sequences of log-uniform length in [1K, 64K] (262,990
@@ -190,7 +200,45 @@ def bench_decode(args):
         res["variants"] = variants
     if T == 1:
         res["slot_copies"] = slot_copies(kda, cfg, Sd, Xd, slot_d, B, H, dk, dv, sb, args)
+        res["cold_state"] = cold_state_decode(kda, cfg, q, k, v, z, g, beta, conv_w, norm_w, S, X, slot_d,
+                                              nbytes, B, args)
     return res
+
+
+def cold_state_decode(kda, cfg, q, k, v, z, g, beta, conv_w, norm_w, S, X, slot_d, nbytes, B, args, layers=4):
+    """The decode step with its state coming from HBM: `layers` distinct state
+    pools (standing in for consecutive KDA layers of a model, 160 MiB each
+    with fp32 states, 640 MiB in all, beyond the 256 MB Infinity Cache) are
+    stepped in turn, launch after launch, so each launch finds its pool last
+    touched three launches (480 MiB of other states) ago.  Beside it, a
+    plain 1 GiB device-to-device copy (2 GiB read and written) gives the
+    streaming rate this box attains."""
+    import torch
+    stream = torch.cuda.current_stream()
+    pools = [(torch.from_numpy(S).to(cfg.torch_state).cuda(), torch.from_numpy(X).to(cfg.torch_act).cuda())
+             for _ in range(layers)]
+    out = torch.empty((B,) + tuple(q.shape[2:]), dtype=cfg.torch_act, device="cuda")
+    nsteps = min(q.shape[0], 64)
+
+    def one_pass():
+        for s in range(nsteps):
+            for Sl, Xl in pools:
+                kda.kda_decode_step(cfg, q[s], k[s], v[s], z[s], g[s], beta[s], conv_w, norm_w, Sl, Xl,
+                                    slot_d, out, stream=stream)
+
+    t = _time_calls(one_pass, max(1, args.steps // 4), 1, stream) / (nsteps * layers)
+    src = torch.ones(1 << 28, device="cuda")
+    dst = torch.empty_like(src)
+    t_copy = _time_calls(lambda: dst.copy_(src), max(3, args.steps // 2), 2, stream)
+    copy_bytes = 2 * src.numel() * 4
+    del pools, src, dst
+    return {"what": f"{layers} state pools of {S.nbytes >> 20} MiB stepped in turn ({nsteps} steps x {layers} "
+                    f"launches); each launch's state last touched {layers - 1} launches earlier",
+            "us_per_launch": t * 1e6, "tok_s_per_layer": B / t, "achieved_GBs": nbytes / t / 1e9,
+            "hbm_frac": nbytes / t / HBM_PEAK,
+            "streaming_copy": {"what": "torch copy_ of 1 GiB fp32 (2 GiB read and written)",
+                               "achieved_GBs": copy_bytes / t_copy / 1e9, "hbm_frac": copy_bytes / t_copy / HBM_PEAK},
+            "frac_of_streaming": (nbytes / t) / (copy_bytes / t_copy)}
 
 
 def slot_copies(kda, cfg, Sd, Xd, slot_d, B, H, dk, dv, sb, args):
@@ -289,7 +337,7 @@ def prefill_bytes_per_token_head(dk, dv, act_bytes=2):
     return (2 * dk + 2 * dv) * act_bytes + dk * 4 + 4 + dv * act_bytes
 
 
-def bench_prefill(steps, warmup):
+def bench_prefill(steps, warmup, paired_leg=True):
     import torch
     import linear_attention_recurrence_decode_amd as kda
     import workloads as wl
@@ -323,13 +371,13 @@ def bench_prefill(steps, warmup):
 
     # the paired launch (two workgroups per chain) is the headline: this
     # workload has 128 chains for 256 compute units
-    t = timed(paired)
     t1 = timed(0)
+    t = timed(paired) if paired_leg else t1
     th = T * H
     flops = prefill_flops_per_token_head(dk, dv) * th
     nbytes = prefill_bytes_per_token_head(dk, dv) * th
     return {"workload": f"prefill_4x8k: {N} x {lengths[0]} tokens, H={H}, dk=dv={dk}, bf16, chunk 64",
-            "mode": "paired (KDA_PREFILL_PAIRED)",
+            "mode": "paired (KDA_PREFILL_PAIRED)" if paired_leg else "one workgroup per chain",
             "value": T / t, "unit": "tok/s", "ms_per_call": t * 1e3,
             "mfma_frac": flops / t / BF16_PEAK, "hbm_frac": nbytes / t / HBM_PEAK,
             "alg_flops": flops, "alg_bytes": nbytes,
@@ -397,8 +445,10 @@ def prefill_rates(T, H, dk, dv, t):
             "hbm_frac": nbytes / t / HBM_PEAK, "attainable_frac": max(flops / BF16_PEAK, nbytes / HBM_PEAK) / t}
 
 
-def bench_varlen(steps, warmup):
-    """Varlen prefill with checkpoints, then the resume batch."""
+def bench_varlen(steps, warmup, paired_leg=True, full=True):
+    """Varlen prefill with checkpoints (one workgroup per chain, the
+    scheduled launch and, with `full`, the split launch), then with `full` the
+    resume batch."""
     import torch
     import linear_attention_recurrence_decode_amd as kda
     import workloads as wl
@@ -411,15 +461,23 @@ def bench_varlen(steps, warmup):
     stream = torch.cuda.current_stream()
     split, paired = kda.KDA_PREFILL_SPLIT, kda.KDA_PREFILL_PAIRED
     st = PrefillSetup(kda, wl, shape, inp, lengths, [0] * N, interval, [0, split, paired])
-    t_s = _time_calls(lambda: st.call(split, stream), steps, warmup, stream)
+    del inp
     t = _time_calls(lambda: st.call(0, stream), steps, warmup, stream)
-    t_p = _time_calls(lambda: st.call(paired, stream), steps, warmup, stream)
     res = {"workload": f"varlen_ckpt: {N} sequences, {sum(lengths)} tokens (lengths log-uniform in [1K, 64K]), "
                        f"H={shape.H}, dk=dv={shape.dk}, bf16, checkpoints every {interval} and at ends "
                        f"({st.nck} checkpoints)",
-           "straight": prefill_rates(st.T, shape.H, shape.dk, shape.dv, t),
-           "straight_split": prefill_rates(st.T, shape.H, shape.dk, shape.dv, t_s),
-           "straight_paired": prefill_rates(st.T, shape.H, shape.dk, shape.dv, t_p)}
+           "straight": prefill_rates(st.T, shape.H, shape.dk, shape.dv, t)}
+    if full:
+        t_s = _time_calls(lambda: st.call(split, stream), steps, warmup, stream)
+        res["straight_split"] = prefill_rates(st.T, shape.H, shape.dk, shape.dv, t_s)
+    if paired_leg:
+        t_p = _time_calls(lambda: st.call(paired, stream), steps, warmup, stream)
+        res["straight_paired"] = prefill_rates(st.T, shape.H, shape.dk, shape.dv, t_p)
+    res["value"] = max(r["value"] for key, r in res.items() if key.startswith("straight") and key != "straight_split")
+    if not full:
+        del st
+        return res
+    inp = wl.token_inputs(w["seed"], shape, sum(lengths))
     # resume batch: each sequence with an interval checkpoint restarts from a seeded one
     rng = np.random.default_rng([w["seed"], wl.TID["resume"], 0])
     rem, pos, src, idx = [], [], [], []
@@ -444,18 +502,20 @@ def bench_varlen(steps, warmup):
                    stream=stream)
     # every pass restarts from the resumed slots (the final slots are distinct)
     t_r = _time_calls(lambda: rs.call(0, stream), steps, warmup, stream)
-    t_rp = _time_calls(lambda: rs.call(paired, stream), steps, warmup, stream)
     res["resume"] = dict(prefill_rates(rs.T, shape.H, shape.dk, shape.dv, t_r),
                          sequences=n_r, tokens=int(rs.T))
-    res["resume_paired"] = prefill_rates(rs.T, shape.H, shape.dk, shape.dv, t_rp)
-    # the headline is the faster of the straight one-workgroup and scheduled calls
-    res["value"] = max(res["straight"]["value"], res["straight_paired"]["value"])
+    if paired_leg:
+        t_rp = _time_calls(lambda: rs.call(paired, stream), steps, warmup, stream)
+        res["resume_paired"] = prefill_rates(rs.T, shape.H, shape.dk, shape.dv, t_rp)
+    # the headline (value, set above) is the faster of the straight
+    # one-workgroup and scheduled calls
     return res
 
 
-def bench_long(steps, warmup):
-    """The 1M-token sequence, unsplit and split at its checkpoints, then the
-    256-sequence decode fanned out from its end state."""
+def bench_long(steps, warmup, paired_leg=True, full=True):
+    """The 1M-token sequence split at its checkpoints (the value) and with
+    its 8 chains paired; with `full` also unsplit in one workgroup per chain,
+    and the 256-sequence decode fanned out from its end state."""
     import torch
     import linear_attention_recurrence_decode_amd as kda
     import workloads as wl
@@ -467,16 +527,23 @@ def bench_long(steps, warmup):
     stream = torch.cuda.current_stream()
     split, paired = kda.KDA_PREFILL_SPLIT, kda.KDA_PREFILL_PAIRED
     st = PrefillSetup(kda, wl, shape, inp, [L], [0], interval, [0, split, paired])
+    conv_w, norm_w = st.conv_w, st.norm_w
+    del inp
     res = {"workload": f"long_1m: 1 sequence of {L} tokens, H={shape.H}, dk=dv={shape.dk}, bf16, checkpoints "
                        f"every {interval}"}
-    t_u = _time_calls(lambda: st.call(0, stream), max(1, steps // 4), min(warmup, 1), stream)
-    res["unsplit"] = prefill_rates(L, shape.H, shape.dk, shape.dv, t_u)
-    # the 8 chains paired (producer and consumer workgroups), not split
-    t_p = _time_calls(lambda: st.call(paired, stream), max(1, steps // 4), min(warmup, 1), stream)
-    res["unsplit_paired"] = prefill_rates(L, shape.H, shape.dk, shape.dv, t_p)
+    if full:
+        t_u = _time_calls(lambda: st.call(0, stream), max(1, steps // 4), min(warmup, 1), stream)
+        res["unsplit"] = prefill_rates(L, shape.H, shape.dk, shape.dv, t_u)
+    if paired_leg:
+        # the 8 chains paired (producer and consumer workgroups), not split
+        t_p = _time_calls(lambda: st.call(paired, stream), max(1, steps // 4), min(warmup, 1), stream)
+        res["unsplit_paired"] = prefill_rates(L, shape.H, shape.dk, shape.dv, t_p)
     t_s = _time_calls(lambda: st.call(split, stream), steps, warmup, stream)
     res["split"] = prefill_rates(L, shape.H, shape.dk, shape.dv, t_s)
     res["value"] = res["split"]["value"]
+    if not full:
+        del st
+        return res
     # decode fan-out: 256 slots from the end state, 512 steps
     B, nsteps = w["decode_B"], w["decode_steps"]
     cfg = st.cfg
@@ -493,7 +560,7 @@ def bench_long(steps, warmup):
 
     def decode_pass():
         for s2 in range(nsteps):
-            kda.kda_decode_step(cfg, q[s2], k[s2], v[s2], z[s2], g[s2], beta[s2], st.conv_w, st.norm_w, Sp, Xp,
+            kda.kda_decode_step(cfg, q[s2], k[s2], v[s2], z[s2], g[s2], beta[s2], conv_w, norm_w, Sp, Xp,
                                 slot, dout[s2], stream=stream)
 
     t_d = _time_calls(decode_pass, max(1, steps // 4), 1, stream)
@@ -576,12 +643,52 @@ def cpu_baseline(sample_steps: int):
     oracle.decode_steps(r(inp.q)[:n1], r(inp.k)[:n1], r(inp.v)[:n1], r(inp.z)[:n1], r(inp.g)[:n1],
                         r(inp.beta)[:n1], inp.conv_w, inp.norm_w, S[slots], X[slots], threads=1)
     dt1 = time.perf_counter() - t1
+    # the oracle keeps a thread count it is given: restore all of them
+    oracle.decode_steps(r(inp.q)[:1], r(inp.k)[:1], r(inp.v)[:1], r(inp.z)[:1], r(inp.g)[:1],
+                        r(inp.beta)[:1], inp.conv_w, inp.norm_w, S[slots], X[slots], threads=threads)
     return {"value": B * sample_steps / dt, "unit": "tok/s", "cores": threads, "kind": "oracle",
             "sample": f"decode workload, {sample_steps} of 256 steps, 64 sequences x 32 heads, "
                       f"fp64 token-by-token, {dt:.1f} s",
             "single_thread": {"value": B * n1 / dt1, "unit": "tok/s",
                               "sample": f"first {n1} steps of the same workload on one thread, {dt1:.1f} s"},
             "cpu": cpu_model()}
+
+
+def cpu_baseline_prefill(threads: int):
+    """The fp64 oracle on bounded samples of the three prefill workloads
+    (the first tokens of every sequence, all heads, checkpoints as in the
+    workload), timed on this host with `threads` threads (given explicitly:
+    a thread count passed to the oracle stays set for later calls).  The
+    oracle runs one (sequence, head) chain per thread, so the 1M-token sample
+    uses 8 threads (its 8 heads)."""
+    import oracle
+    import workloads as wl
+
+    res = {}
+
+    def sample(name, seed, shape, lengths, take, interval, what):
+        cu = wl.cu_seqlens(lengths)
+        sub = [min(take, int(L)) for L in lengths]
+        rows = np.concatenate([np.arange(cu[n], cu[n] + m) for n, m in enumerate(sub)])
+        inp = wl.token_rows(seed, shape, rows)
+        t0 = time.perf_counter()
+        oracle.run(inp.q, inp.k, inp.v, inp.z, inp.g, inp.beta, inp.conv_w, inp.norm_w, wl.cu_seqlens(sub),
+                   ckpt_interval=interval, threads=threads)
+        dt = time.perf_counter() - t0
+        tokens = int(sum(sub))
+        res[name] = {"value": tokens / dt, "unit": "tok/s", "cores": min(threads, len(sub) * shape.H),
+                     "kind": "oracle", "seconds": dt, "token_heads": tokens * shape.H,
+                     "sample": f"{what}: first {take} tokens of each of {len(sub)} sequences ({tokens} tokens), "
+                               f"all {shape.H} heads, fp64 token-by-token, {dt:.1f} s"}
+
+    w = wl.WORKLOADS["prefill_4x8k"]
+    sample("prefill_4x8k", w["seed"], w["shape"], w["lengths"], 2048, 0, "prefill_4x8k")
+    w = wl.WORKLOADS["varlen_ckpt"]
+    lengths = [int(x) for x in wl.loguniform_lengths(w["seed"], w["n"], w["lo"], w["hi"])]
+    sample("varlen_ckpt", w["seed"], w["shape"], lengths, 1024, w["interval"], "varlen_ckpt")
+    w = wl.WORKLOADS["long_1m"]
+    sample("long_1m", w["seed"], w["shape"], w["lengths"], 16384, w["interval"], "long_1m")
+    return res
 
 
 def cpu_model():
@@ -603,6 +710,8 @@ def main():
     ap.add_argument("--cpu-sample-steps", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-paired", action="store_true",
+                    help="leave out every KDA_PREFILL_PAIRED launch (a cooperative launch), e.g. under a profiler")
     ap.add_argument("--multi-token", type=int, default=1,
                     help="decode T tokens per launch with per-token states kept (speculative verify); 1 = one step")
     ap.add_argument("--state-dtype", choices=["f32", "bf16"], default="f32",
@@ -636,8 +745,8 @@ def main():
         if args.workload == "project_4x8k":
             res = bench_project(args.steps, args.warmup)
         else:
-            res = bench_varlen(args.steps, args.warmup) if args.workload == "varlen_ckpt" else \
-                bench_long(args.steps, args.warmup)
+            res = bench_varlen(args.steps, args.warmup, paired_leg=not args.no_paired) \
+                if args.workload == "varlen_ckpt" else bench_long(args.steps, args.warmup, paired_leg=not args.no_paired)
         metric = ("KDA input projections TFLOP/s (" if args.workload == "project_4x8k" else "KDA prefill tok/s (")
         line = {"metric": metric + args.workload + ")", "value": res["value"], "unit": res.get("unit", "tok/s"),
                 "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
@@ -672,11 +781,23 @@ def main():
         line["variants"] = res["variants"]
     if "slot_copies" in res:
         line["slot_copies"] = res["slot_copies"]
+    if "cold_state" in res:
+        line["cold_state"] = res["cold_state"]
     if not args.no_prefill:
-        line["prefill"] = bench_prefill(max(3, args.steps // 2), max(1, args.warmup))
+        import torch
+        line["prefill"] = bench_prefill(max(3, args.steps // 2), max(1, args.warmup), paired_leg=not args.no_paired)
+        torch.cuda.empty_cache()
+        line["varlen_ckpt"] = bench_varlen(max(3, args.steps // 2), max(1, args.warmup),
+                                           paired_leg=not args.no_paired, full=False)
+        torch.cuda.empty_cache()
+        line["long_1m"] = bench_long(max(3, args.steps // 4), 1, paired_leg=not args.no_paired, full=False)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_sample_steps} decode steps")
         line["cpu_baseline"] = cpu_baseline(args.cpu_sample_steps)
+        if not args.no_prefill:
+            log("[bench] cpu baseline: oracle on samples of the prefill workloads")
+            line["cpu_baseline"]["prefill_workloads"] = cpu_baseline_prefill(line["cpu_baseline"]["cores"])
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -158,6 +158,42 @@ def token_inputs(seed: int, shape: LayerShape, T: int, *, g_scale: float = 1.0,
     return Inputs(shape, q, k, v, z, g, beta, conv_w, nw)
 
 
+def token_rows(seed: int, shape: LayerShape, rows, *, g_scale: float = 1.0, norm_w: str = "ones",
+               conv_w_std: float = 0.5) -> Inputs:
+    """The inputs token_inputs(seed, shape, T, ...) holds at the packed token
+    indices `rows` (any T beyond max(rows)), drawing only the blocks that
+    contain them: each block is its own seeded stream and a shorter draw from
+    a stream gives its first values, so the rows are the same values."""
+    rows = np.asarray(rows, np.int64)
+    H, dk, dv = shape.H, shape.dk, shape.dv
+    rnd = round_bf16 if shape.act == "bf16" else None
+    gs = np.float32(g_scale)
+    specs = {"q": ((H, dk), rnd), "k": ((H, dk), rnd), "v": ((H, dv), rnd), "z": ((H, dv), rnd),
+             "g": ((H, dk), (lambda a: (-_softplus(a) * gs).astype(np.float32)) if g_scale != 1.0
+                   else (lambda a: -_softplus(a))),
+             "beta": ((H,), _sigmoid)}
+    blocks = rows // BLOCK_TOKENS
+    out = {}
+    for name, (inner, tf) in specs.items():
+        arr = np.empty((len(rows),) + inner, np.float32)
+        for b in np.unique(blocks):
+            sel = np.nonzero(blocks == b)[0]
+            lo = int(b) * BLOCK_TOKENS
+            n = int(rows[sel].max()) - lo + 1
+            rng = np.random.default_rng([seed, TID[name], int(b)])
+            blk = rng.standard_normal((n,) + inner, dtype=np.float32)
+            if tf is not None:
+                blk = tf(blk)
+            arr[sel] = blk[rows[sel] - lo]
+        out[name] = arr
+    conv_w = draw_plain(seed, TID["conv_w"], (H, shape.C, shape.W), std=conv_w_std)
+    if norm_w == "ones":
+        nw = np.ones((dv,), np.float32)
+    else:
+        nw = (0.5 + np.abs(draw_plain(seed, TID["norm_w"], (dv,)))).astype(np.float32)
+    return Inputs(shape, out["q"], out["k"], out["v"], out["z"], out["g"], out["beta"], conv_w, nw)
+
+
 def states(seed: int, shape: LayerShape, nslots: int, state_std: float = 0.02,
            conv_std: float = 1.0):
     """Random recurrent state (fp32) and conv state (activation dtype) pools."""

@@ -598,7 +598,11 @@ def bench_project(steps, warmup):
     # context only: the library GEMM (torch.matmul) on the same bf16 product, without the routing and gate maps
     wcol = wd.t().contiguous()
     t_lib = _time_calls(lambda: torch.matmul(xd, wcol), steps, warmup, stream)
-    del wcol, xd, wd, q, k, v, z, g, beta
+    del wcol
+    # the conv front end (the causal conv + SiLU on q, k, v in the epilogue), and the
+    # prefill of these tokens (4 sequences of 8192) after each front end
+    conv_res = conv_front_end(kda, wl, cfg, shape, xd, wd, q, k, v, z, g, beta, T, flops, steps, warmup, stream)
+    del xd, wd, q, k, v, z, g, beta
     # the output projection of the same tokens: o [T][H][dv] -> y [T][Dm]
     o, wo = wl.output_projection_inputs(w["seed"], shape, T, Dm)
     od, wod = torch.from_numpy(o).to(torch.bfloat16).cuda(), torch.from_numpy(wo).to(torch.bfloat16).cuda()
@@ -617,7 +621,47 @@ def bench_project(steps, warmup):
                                "what": "torch.matmul of the same bf16 x and W^T (plain product, no epilogue)"},
             "output_projection": {"TFLOP/s": flops_out / t_out / 1e12, "ms_per_call": t_out * 1e3,
                                   "frac": flops_out / t_out / BF16_PEAK,
-                                  "what": f"kda_project_output: o [{T}][{H * dv}] bf16 times W_o [{Dm}][{H * dv}] bf16"}}
+                                  "what": f"kda_project_output: o [{T}][{H * dv}] bf16 times W_o [{Dm}][{H * dv}] bf16"},
+            "conv_front_end": conv_res}
+
+
+def conv_front_end(kda, wl, cfg, shape, xd, wd, q, k, v, z, g, beta, T, flops, steps, warmup, stream):
+    """kda_project_inputs_conv on the same x and W (the GEMM plus the causal
+    conv and SiLU of q, k, v in its epilogue, post-conv and raw tensors
+    written), then the 4 x 8192 prefill on each front end's outputs: the
+    unfused pair (kda_project_inputs + kda_prefill_varlen) against the fused
+    one (kda_project_inputs_conv + kda_prefill_varlen with
+    KDA_PREFILL_CONV_DONE), one workgroup per chain and paired."""
+    import torch
+    H, dk, dv, C = shape.H, shape.dk, shape.dv, shape.C
+    N = 4
+    lengths = [T // N] * N
+    cu = torch.from_numpy(wl.cu_seqlens(lengths).astype(np.int32)).cuda()
+    pool = torch.zeros((1, H, C, 3), dtype=torch.bfloat16, device="cuda")
+    init = torch.full((N,), -1, dtype=torch.int32, device="cuda")
+    q2, k2 = (torch.empty((2, T, H, dk), dtype=torch.bfloat16, device="cuda") for _ in range(2))
+    v2 = torch.empty((2, T, H, dv), dtype=torch.bfloat16, device="cuda")
+    cw = torch.from_numpy(wl.token_inputs(5, shape, 1).conv_w).cuda()
+    nw = torch.ones((dv,), device="cuda")
+    t_fe = _time_calls(lambda: kda.kda_project_inputs_conv(cfg, cu, xd, wd, cw, pool, init, q2, k2, v2, z, g, beta,
+                                                           stream=stream), steps, warmup, stream)
+    S = torch.zeros((N, H, dk, dv), device="cuda")
+    X = torch.zeros((N, H, C, 3), dtype=torch.bfloat16, device="cuda")
+    fin = torch.arange(N, dtype=torch.int32, device="cuda")
+    out = torch.empty((T, H, dv), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(cfg, N, T, 0, kda.KDA_PREFILL_PAIRED), dtype=torch.uint8,
+                     device="cuda")
+    res = {"what": "kda_project_inputs_conv: the input projections with the causal conv + SiLU of q, k, v in the "
+                   "epilogue (post-conv and raw tensors written); prefill_ms: the 4 x 8192 prefill after it "
+                   "(KDA_PREFILL_CONV_DONE) and after kda_project_inputs (unfused)",
+           "ms_per_call": t_fe * 1e3, "TFLOP/s": flops / t_fe / 1e12, "prefill_ms": {}}
+    for label, (qq, kk, vv), cd in (("unfused", (q, k, v), 0), ("conv_done", (q2, k2, v2), kda.KDA_PREFILL_CONV_DONE)):
+        for mode, fl in (("one_workgroup", 0), ("paired", kda.KDA_PREFILL_PAIRED)):
+            t = _time_calls(lambda: kda.kda_prefill_varlen(cfg, cu, qq, kk, vv, z, g, beta, cw, nw, S, X, init, fin,
+                                                           out, ws, flags=fl | cd, stream=stream),
+                            max(3, steps // 2), max(1, warmup), stream)
+            res["prefill_ms"][f"{label}_{mode}"] = t * 1e3
+    return res
 
 
 def cpu_baseline(sample_steps: int):

@@ -82,8 +82,10 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 typedef enum {
     KDA_PREFILL_SPLIT = 1,    /* cut sequences into segments at checkpoint positions */
     KDA_PREFILL_PAIRED = 2,   /* two workgroups per chain: state-independent and state phases overlap */
-    KDA_PREFILL_PAIRED_POLL_ONCE = 4  /* with KDA_PREFILL_PAIRED, for tests only: every wait between
+    KDA_PREFILL_PAIRED_POLL_ONCE = 4, /* with KDA_PREFILL_PAIRED, for tests only: every wait between
                                          the two workgroups of a chain polls once before it gives up */
+    KDA_PREFILL_CONV_DONE = 8         /* q, k, v as written by kda_project_inputs_conv: the conv and
+                                         SiLU are done; bf16 activations only */
 } kda_prefill_flags;
 
 typedef struct {
@@ -196,7 +198,12 @@ kda_status kda_decode_multi(const kda_config* cfg, int32_t B, int32_t T,
  *   after a call without KDA_PREFILL_PAIRED; a call with num_seqs == 0
  *   launches nothing and leaves it untouched.
  * flags: 0, KDA_PREFILL_SPLIT or KDA_PREFILL_PAIRED (not both), and
- *   KDA_PREFILL_PAIRED_POLL_ONCE only together with KDA_PREFILL_PAIRED.
+ *   KDA_PREFILL_PAIRED_POLL_ONCE only together with KDA_PREFILL_PAIRED;
+ *   KDA_PREFILL_CONV_DONE with any of them (bf16 activations).
+ * KDA_PREFILL_CONV_DONE: q, k and v each point to two tensors back to back as
+ *   kda_project_inputs_conv writes them (post-conv activations, then the raw
+ *   inputs); the conv and SiLU are skipped and the raw inputs only feed the
+ *   conv states of checkpoints and final slots.
  * KDA_PREFILL_SPLIT (needs ckpt_interval > 0).  Without it each
  *   (sequence, head) chain runs through its chunks in order in one workgroup,
  *   so a batch of few long sequences occupies few compute units.  With it,
@@ -317,6 +324,41 @@ kda_status kda_project_inputs(const kda_config* cfg, int32_t T, int32_t Dm,
                               const void* x, const void* w,
                               void* q, void* k, void* v, void* z, float* g, float* beta,
                               void* stream);
+
+/*
+ * The input projections with the causal conv fused into the GEMM's epilogue:
+ * the front end of a chunked prefill over num_seqs packed sequences.
+ * [vLLM blog, "KDA prefill and decode": the input projections and the causal
+ *  convolution are fused around the recurrence.]
+ *
+ * Arguments as kda_project_inputs, plus cu_seqlens ([num_seqs+1] int32
+ * device array as for kda_prefill_varlen, describing the T packed tokens of
+ * x), conv_w ([H][2dk+dv][4] fp32) and the initial conv states: sequence n's
+ * left context is conv_pool[init_slot[n]] ([num_slots][H][2dk+dv][3] bf16,
+ * index 2 = the token just before the sequence), or zero when init_slot is
+ * NULL or init_slot[n] is -1 (an id outside the pool counts as -1).
+ * q, k and v each point to TWO tensors back to back ([2][T][H][dk] for q
+ * and k, [2][T][H][dv] for v, bf16):
+ *   first  the activations after the conv: RNE_bf16(SiLU(w3 r_t + w2 r_{t-1}
+ *          + w1 r_{t-2} + w0 r_{t-3})), r the raw projections rounded to bf16
+ *          (rows before a sequence's first token from its left context),
+ *          the value kda_prefill_varlen forms in fp32 from the raw inputs;
+ *   second the raw projections r themselves (what conv states hold).
+ * z, g and beta as kda_prefill_varlen takes them.  Pass q, k, v, z, g, beta
+ * to kda_prefill_varlen with KDA_PREFILL_CONV_DONE (same cu_seqlens, and the
+ * same initial conv states as its init_slot gives): it then skips the conv,
+ * and its checkpoints and final conv states hold the raw inputs as without
+ * the flag.  The one difference from the unfused pair kda_project_inputs +
+ * kda_prefill_varlen is the rounding of the post-conv activations to bf16.
+ * The GEMM runs in tiles of 256 rows that overlap by 3 (each recomputes the
+ * conv's left context of its first row): 1.2% more MFMA work.
+ */
+kda_status kda_project_inputs_conv(const kda_config* cfg, int32_t num_seqs, int32_t T, int32_t Dm,
+                                   const int32_t* cu_seqlens, const void* x, const void* w,
+                                   const float* conv_w, const void* conv_pool, int32_t num_slots,
+                                   const int32_t* init_slot,
+                                   void* q, void* k, void* v, void* z, float* g, float* beta,
+                                   void* stream);
 
 /*
  * Output projection of the layer for T tokens in one bf16 MFMA GEMM:

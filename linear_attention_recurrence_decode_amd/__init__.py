@@ -26,12 +26,14 @@ KDA_F32, KDA_BF16 = 0, 1
 KDA_PREFILL_SPLIT = 1
 KDA_PREFILL_PAIRED = 2
 KDA_PREFILL_PAIRED_POLL_ONCE = 4
+KDA_PREFILL_CONV_DONE = 8
 
 # every symbol include/kda.h declares
 EXPORTS = (
     "kda_decode_step", "kda_decode_multi", "kda_prefill_varlen", "kda_prefill_varlen_static",
     "kda_state_checkpoint", "kda_resume",
-    "kda_project_inputs", "kda_project_output", "kda_prefill_workspace_bytes", "kda_num_checkpoints", "kda_last_error",
+    "kda_project_inputs", "kda_project_inputs_conv", "kda_project_output", "kda_prefill_workspace_bytes",
+    "kda_num_checkpoints", "kda_last_error",
     # host-side prefix cache (include/kda_prefix_cache.h)
     "kda_pcache_create", "kda_pcache_destroy", "kda_pcache_lookup", "kda_pcache_release",
     "kda_pcache_reserve", "kda_pcache_insert", "kda_pcache_insert_many", "kda_pcache_unreserve",
@@ -104,6 +106,7 @@ def lib():
     L.kda_decode_multi.argtypes = [CP, I32, I32] + [P] * 8 + [P, P, I32, P, P, P, P, P]
     L.kda_project_inputs.argtypes = [CP, I32, I32] + [P] * 9
     L.kda_project_output.argtypes = [CP, I32, I32, P, P, P, P]
+    L.kda_project_inputs_conv.argtypes = [CP, I32, I32, I32, P, P, P, P, P, I32, P] + [P] * 6 + [P]
     L.kda_prefill_varlen.argtypes = ([CP, I32, I64, P, P] + [P] * 8 + [P, P, I32, P, P, I32, P, P, I32, P,
                                      I32, P, P, ctypes.c_size_t, P])
     L.kda_prefill_varlen_static.argtypes = ([CP, I32, I64, P, P] + [P] * 8 + [P, P, I32, P, P, I32, P, P, I32, P,
@@ -132,7 +135,8 @@ def lib():
               "kda_pcache_unreserve"):
         getattr(L, f).restype = I32
     for f in ("kda_decode_step", "kda_decode_multi", "kda_prefill_varlen", "kda_prefill_varlen_static",
-              "kda_state_checkpoint", "kda_resume", "kda_project_inputs", "kda_project_output"):
+              "kda_state_checkpoint", "kda_resume", "kda_project_inputs", "kda_project_inputs_conv",
+              "kda_project_output"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -248,6 +252,27 @@ def kda_project_inputs(cfg: Config, x, w, q, k, v, z, g, beta, stream=None):
                                     _ptr(z), _ptr(g), _ptr(beta), _stream(stream)))
 
 
+def kda_project_inputs_conv(cfg: Config, cu_seqlens, x, w, conv_w, conv_pool, init_slot, q, k, v, z, g, beta,
+                            stream=None):
+    """Input projections with the causal conv fused (see include/kda.h): q, k
+    [2][T][H][dk] and v [2][T][H][dv] bf16 receive the post-conv activations
+    and then the raw projections; z, g, beta as kda_project_inputs."""
+    T, Dm = x.shape
+    N = cu_seqlens.numel() - 1
+    H, dk, dv, C = cfg.num_heads, cfg.head_k, cfg.head_v, cfg.conv_channels
+    S = conv_pool.shape[0]
+    _want(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
+    _want(x, "x", torch.bfloat16, (T, Dm)); _want(w, "w", torch.bfloat16, (projection_rows(cfg), Dm))
+    _want(conv_w, "conv_w", torch.float32, (H, C, 4)); _want(conv_pool, "conv_pool", torch.bfloat16, (S, H, C, 3))
+    _want(init_slot, "init_slot", torch.int32, (N,))
+    _want(q, "q", torch.bfloat16, (2, T, H, dk)); _want(k, "k", torch.bfloat16, (2, T, H, dk))
+    _want(v, "v", torch.bfloat16, (2, T, H, dv)); _want(z, "z", torch.bfloat16, (T, H, dv))
+    _want(g, "g", torch.float32, (T, H, dk)); _want(beta, "beta", torch.float32, (T, H))
+    _check(lib().kda_project_inputs_conv(ctypes.byref(cfg.c()), N, T, Dm, _ptr(cu_seqlens), _ptr(x), _ptr(w),
+                                         _ptr(conv_w), _ptr(conv_pool), S, _ptr(init_slot), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(z), _ptr(g), _ptr(beta), _stream(stream)))
+
+
 def kda_project_output(cfg: Config, o, w_o, y, stream=None):
     """Output projection y = o W_o^T (see include/kda.h): o [T][H][dv] bf16,
     w_o [Dm][H dv] bf16, y [T][Dm] bf16."""
@@ -268,7 +293,8 @@ def kda_prefill_varlen(cfg: Config, cu_seqlens, q, k, v, z, g, beta, conv_w, nor
                        ckpt_base=None, flags: int = 0, stream=None):
     """Chunked varlen prefill (see include/kda.h)."""
     a = _prefill_args(cfg, cu_seqlens, q, k, v, z, g, beta, conv_w, norm_w, state_pool, conv_pool,
-                      init_slot, final_slot, out, start_pos, ckpt_interval, ckpt_state, ckpt_conv, ckpt_base)
+                      init_slot, final_slot, out, start_pos, ckpt_interval, ckpt_state, ckpt_conv, ckpt_base,
+                      conv_done=bool(int(flags) & KDA_PREFILL_CONV_DONE))
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if workspace is not None:
         _want(workspace, "workspace", workspace.dtype)
@@ -283,24 +309,27 @@ def kda_prefill_varlen_static(cfg: Config, cu_seqlens, q, k, v, z, g, beta, conv
     """kda_prefill_varlen with the library's static device workspace: allocates
     nothing (see include/kda.h)."""
     a = _prefill_args(cfg, cu_seqlens, q, k, v, z, g, beta, conv_w, norm_w, state_pool, conv_pool,
-                      init_slot, final_slot, out, start_pos, ckpt_interval, ckpt_state, ckpt_conv, ckpt_base)
+                      init_slot, final_slot, out, start_pos, ckpt_interval, ckpt_state, ckpt_conv, ckpt_base,
+                      conv_done=bool(int(flags) & KDA_PREFILL_CONV_DONE))
     _check(lib().kda_prefill_varlen_static(*a, int(flags), _ptr(out), _stream(stream)))
     return out
 
 
 def _prefill_args(cfg, cu_seqlens, q, k, v, z, g, beta, conv_w, norm_w, state_pool, conv_pool,
-                  init_slot, final_slot, out, start_pos, ckpt_interval, ckpt_state, ckpt_conv, ckpt_base):
+                  init_slot, final_slot, out, start_pos, ckpt_interval, ckpt_state, ckpt_conv, ckpt_base,
+                  conv_done=False):
     """Checked leading arguments shared by the two prefill entry points, up to
     ckpt_base."""
     N = cu_seqlens.numel() - 1
-    T = q.shape[0]
+    T = z.shape[0]
     H, dk, dv, C = cfg.num_heads, cfg.head_k, cfg.head_v, cfg.conv_channels
     act = cfg.torch_act
     S = state_pool.shape[0]
+    lead = (2, T) if conv_done else (T,)           # KDA_PREFILL_CONV_DONE: post-conv then raw
     _want(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
     _want(start_pos, "start_pos", torch.int64, (N,))
-    _want(q, "q", act, (T, H, dk)); _want(k, "k", act, (T, H, dk))
-    _want(v, "v", act, (T, H, dv)); _want(z, "z", act, (T, H, dv))
+    _want(q, "q", act, lead + (H, dk)); _want(k, "k", act, lead + (H, dk))
+    _want(v, "v", act, lead + (H, dv)); _want(z, "z", act, (T, H, dv))
     _want(g, "g", torch.float32, (T, H, dk)); _want(beta, "beta", torch.float32, (T, H))
     _want(conv_w, "conv_w", torch.float32, (H, C, 4)); _want(norm_w, "norm_w", torch.float32, (dv,))
     _want(state_pool, "state_pool", cfg.torch_state, (S, H, dk, dv))

@@ -218,7 +218,7 @@ kda_status check_prefill_mode(int32_t ckpt_interval, int32_t flags) {
     if (ckpt_interval < 0 || ckpt_interval % 64 != 0)
         return fail(KDA_ERR_INVALID_ARG, "ckpt_interval must be 0 or a positive multiple of 64 (got %d)",
                     ckpt_interval);
-    if (flags & ~(KDA_PREFILL_SPLIT | KDA_PREFILL_PAIRED | KDA_PREFILL_PAIRED_POLL_ONCE))
+    if (flags & ~(KDA_PREFILL_SPLIT | KDA_PREFILL_PAIRED | KDA_PREFILL_PAIRED_POLL_ONCE | KDA_PREFILL_CONV_DONE))
         return fail(KDA_ERR_INVALID_ARG, "unknown prefill flags 0x%x", flags);
     if ((flags & KDA_PREFILL_PAIRED_POLL_ONCE) && !(flags & KDA_PREFILL_PAIRED))
         return fail(KDA_ERR_INVALID_ARG, "KDA_PREFILL_PAIRED_POLL_ONCE needs KDA_PREFILL_PAIRED");
@@ -269,6 +269,8 @@ kda_status kda_prefill_varlen(const kda_config* cfg, int32_t num_seqs, int64_t t
     if (!kda::prefill_supported(cfg->head_k, cfg->head_v, cfg->act_dtype))
         return fail(KDA_ERR_UNSUPPORTED, "prefill does not support dk=%d dv=%d act_dtype=%d", cfg->head_k,
                     cfg->head_v, cfg->act_dtype);
+    if ((flags & KDA_PREFILL_CONV_DONE) && cfg->act_dtype != KDA_BF16)
+        return fail(KDA_ERR_UNSUPPORTED, "KDA_PREFILL_CONV_DONE needs bf16 activations (act_dtype = KDA_BF16)");
     if (num_seqs == 0) return ok();
     KDA_TRY(need_idx(cu_seqlens, 4, "cu_seqlens"));
     if (start_pos) KDA_TRY(need_idx(start_pos, 8, "start_pos"));
@@ -346,6 +348,7 @@ kda_status kda_prefill_varlen(const kda_config* cfg, int32_t num_seqs, int64_t t
     p.max_pairs = 0;
     p.sched_grid = 0;
     p.spin_limit = (flags & KDA_PREFILL_PAIRED_POLL_ONCE) ? 1 : kda::PAIR_SPIN_LIMIT;
+    p.conv_done = (flags & KDA_PREFILL_CONV_DONE) ? 1 : 0;
     p.status = reinterpret_cast<int32_t*>(ws + wl.status);
     if (wl.ring > 0) {
         // a scheduled launch needs a grid of at least 16 workgroups that the
@@ -400,6 +403,60 @@ kda_status kda_project_inputs(const kda_config* cfg, int32_t T, int32_t Dm, cons
     p.z = z;
     p.g = g;
     p.beta = beta;
+    return hip_status(kda::launch_project(p, static_cast<hipStream_t>(stream)), "projection launch");
+}
+
+kda_status kda_project_inputs_conv(const kda_config* cfg, int32_t num_seqs, int32_t T, int32_t Dm,
+                                   const int32_t* cu_seqlens, const void* x, const void* w, const float* conv_w,
+                                   const void* conv_pool, int32_t num_slots, const int32_t* init_slot, void* q,
+                                   void* k, void* v, void* z, float* g, float* beta, void* stream) {
+    KDA_TRY(check_cfg(cfg));
+    if (cfg->act_dtype != KDA_BF16)
+        return fail(KDA_ERR_UNSUPPORTED, "input projections need bf16 activations (act_dtype = KDA_BF16)");
+    if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 1 (got %d)", num_seqs);
+    if (T < 0) return fail(KDA_ERR_INVALID_ARG, "T must be >= 0 (got %d)", T);
+    if (num_slots < 1) return fail(KDA_ERR_INVALID_ARG, "num_slots must be >= 1 (got %d)", num_slots);
+    if (Dm < 64 || Dm % 64 != 0) return fail(KDA_ERR_INVALID_ARG, "Dm must be a positive multiple of 64 (got %d)", Dm);
+    if (Dm > (1 << 22)) return fail(KDA_ERR_INVALID_ARG, "Dm must be at most 4194304 (got %d)", Dm);
+    const int64_t N = static_cast<int64_t>(cfg->num_heads) * (3 * cfg->head_k + 2 * cfg->head_v) + cfg->num_heads;
+    if (N * Dm * 2 >= (1LL << 31) * 2 || static_cast<int64_t>(T) * Dm * 2 >= (1LL << 40))
+        return fail(KDA_ERR_INVALID_ARG, "projection sizes too large");
+    if (T == 0) return ok();
+    KDA_TRY(need_idx(cu_seqlens, 4, "cu_seqlens"));
+    KDA_TRY(need_vec(x, "x"));
+    KDA_TRY(need_vec(w, "w"));
+    KDA_TRY(need_vec(conv_w, "conv_w"));
+    KDA_TRY(need_vec(conv_pool, "conv_pool"));
+    if (init_slot) KDA_TRY(need_idx(init_slot, 4, "init_slot"));
+    KDA_TRY(need_vec(q, "q"));
+    KDA_TRY(need_vec(k, "k"));
+    KDA_TRY(need_vec(v, "v"));
+    KDA_TRY(need_vec(z, "z"));
+    KDA_TRY(need_vec(g, "g"));
+    KDA_TRY(need_idx(beta, 4, "beta"));
+    kda::ProjectParams p{};
+    p.T = T;
+    p.N = static_cast<int32_t>(N);
+    p.Dm = Dm;
+    p.mode = 0;
+    p.H = cfg->num_heads;
+    p.dk = cfg->head_k;
+    p.dv = cfg->head_v;
+    p.x = x;
+    p.w = w;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.z = z;
+    p.g = g;
+    p.beta = beta;
+    p.conv = 1;
+    p.num_seqs = num_seqs;
+    p.cu_seqlens = cu_seqlens;
+    p.init_slot = init_slot;
+    p.conv_pool = conv_pool;
+    p.num_slots = num_slots;
+    p.conv_w = conv_w;
     return hip_status(kda::launch_project(p, static_cast<hipStream_t>(stream)), "projection launch");
 }
 

@@ -76,6 +76,16 @@ template <> struct Act<bf16_t> {
 __device__ __forceinline__ float sigmoid(float y) { return __builtin_amdgcn_rcpf(1.0f + __expf(-y)); }
 __device__ __forceinline__ float silu(float y) { return y * sigmoid(y); }
 
+// One causal conv tap sum over a 4-token window a, b, c, d (oldest first;
+// w.w multiplies the newest).  The prefill and the projection's conv front
+// end both use this order, so they form the same fp32 value.
+__device__ __forceinline__ float conv4(const float4& w, float a, float b, float c, float d) {
+    float y = w.x * a;
+    y = fmaf(w.y, b, y);
+    y = fmaf(w.z, c, y);
+    return fmaf(w.w, d, y);
+}
+
 // Sum over the lanes of a wave64 whose lane ids differ only in the bits of
 // [lo_mask, 64): e.g. lo = 32 sums lane l with lane l ^ 32.
 template <int LO>

@@ -99,6 +99,7 @@ struct PrefillParams {
                         // [32]: pairs chosen at 0, chain queue at 1
     int32_t max_pairs;  // pairs the ring holds
     int32_t sched_grid; // workgroups of the scheduled launch
+    int32_t conv_done;  // q, k, v hold post-conv activations then raw inputs (bf16 only)
     int32_t spin_limit; // polls before a wait between paired workgroups gives up
     int32_t* status;    // workspace word: waits that gave up in this call (zeroed by the metadata kernel)
 };
@@ -117,6 +118,16 @@ struct ProjectParams {
     void* g;            // fp32
     void* beta;         // fp32
     void* y;            // mode 1: [T][N] bf16
+    // conv front end (input projections with the causal conv + SiLU on q, k,
+    // v): q, k, v then each point to two tensors back to back, the post-conv
+    // activations [T][H][d] and the raw projections [T][H][d]
+    int32_t conv;
+    int32_t num_seqs;
+    const int32_t* cu_seqlens;  // [num_seqs + 1]
+    const int32_t* init_slot;   // [num_seqs]: conv-state slot of each sequence's left context, -1 = zero
+    const void* conv_pool;      // [num_slots][H][2dk+dv][3] bf16
+    int32_t num_slots;
+    const float* conv_w;        // [H][2dk+dv][4]
 };
 
 // Each launcher returns hipSuccess or the launch error.

@@ -316,14 +316,6 @@ __device__ __forceinline__ void store_pool_strip(void* pool, int64_t slot_head, 
         }
 }
 
-// One causal conv tap sum over a 4-token window (w.w multiplies the newest).
-__device__ __forceinline__ float conv4(const float4& w, float a, float b, float c, float d) {
-    float y = w.x * a;
-    y = fmaf(w.y, b, y);
-    y = fmaf(w.z, c, y);
-    return fmaf(w.w, d, y);
-}
-
 // Registers holding one chunk's staged inputs between the loads and the LDS
 // stores: raw q|k|v rows (with 3 rows of left context) as 16-byte words, this
 // thread's 16 log-decay values, and (threads 0..63) one beta.
@@ -674,7 +666,12 @@ __device__ __forceinline__ bool ring_wait(const int32_t* ctr, int want, int seen
 // !OUT (segment transitions, FUSED only): trans = false gives the segment's
 // end state from a zero state (G), trans = true its transition matrix
 // (F: the state propagated from the identity with v = 0).
-template <int D, typename ACT, bool OUT, int ROLE>
+// CD (conv done): q, k and v each hold two tensors back to back, the
+// activations after the causal conv and SiLU (what phase A would compute
+// from the raw inputs, rounded to bf16) and the raw inputs; phase A then
+// takes the activations as they are, and the conv states written at
+// checkpoints and at the end still come from the raw inputs.
+template <int D, typename ACT, bool OUT, int ROLE, bool CD = false>
 __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds<D, ACT>& sm, int item, const int h,
                                               bool trans) {
     static_assert(ROLE == FUSED || OUT, "paired roles produce outputs");
@@ -807,9 +804,10 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
     const float4 wqk = *reinterpret_cast<const float4*>(p.conv_w + (static_cast<int64_t>(h) * C + cqk) * 4);
     const float4 wv = *reinterpret_cast<const float4*>(p.conv_w + (static_cast<int64_t>(h) * C + 2 * DK + jcol) * 4);
     const float nwj = p.norm_w[jcol];
-    const ACT* qin = static_cast<const ACT*>(p.q);
-    const ACT* kin = static_cast<const ACT*>(p.k);
-    const ACT* vin = static_cast<const ACT*>(p.v);
+    // raw inputs (the conv state's contents): with CD, the second tensor of each pair
+    const ACT* qin = static_cast<const ACT*>(p.q) + (CD ? p.T * H * DK : 0);
+    const ACT* kin = static_cast<const ACT*>(p.k) + (CD ? p.T * H * DK : 0);
+    const ACT* vin = static_cast<const ACT*>(p.v) + (CD ? p.T * H * DV : 0);
     const ACT* zin = static_cast<const ACT*>(p.z);
     ACT* out = static_cast<ACT*>(p.out);
     __syncthreads();
@@ -1091,6 +1089,10 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
 #pragma unroll 4
             for (int t = r0; t < r0 + 32; t++) {
                 const float w3 = A::ld(raw + (t + 3) * CR + cqk);
+                if constexpr (CD) {
+                    dst[t * FP] = t < n ? w3 : 0.f;          // the activation itself
+                    continue;
+                }
                 float y = wqk.x * w0;
                 y = fmaf(wqk.y, w1, y);
                 y = fmaf(wqk.z, w2, y);
@@ -1111,7 +1113,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const float y = conv4(wv, x[e], x[e + 1], x[e + 2], x[e + 3]);
-                    vh[tb][e] = (rb + e) < n ? silu(y) : 0.f;
+                    vh[tb][e] = (rb + e) < n ? (CD ? x[e + 3] : silu(y)) : 0.f;
                 }
             }
             if constexpr (!OUT) {
@@ -1402,7 +1404,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
                         const float y = conv4(wv, x[e], x[e + 1], x[e + 2], x[e + 3]);
-                        vh[tb][e] = (rb + e) < n ? silu(y) : 0.f;
+                        vh[tb][e] = (rb + e) < n ? (CD ? x[e + 3] : silu(y)) : 0.f;
                     }
                 }
             }
@@ -1608,7 +1610,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
 // One workgroup per chain (OUT), or per segment transition (!OUT): blocks
 // [0, items*H) give each segment's end state from a zero state (G), blocks
 // [items*H, 2*items*H) its transition matrix (F).
-template <int D, typename ACT, bool OUT>
+template <int D, typename ACT, bool OUT, bool CD>
 __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
     __shared__ PrefillLds<D, ACT> sm;
     const int h = blockIdx.x % p.H;
@@ -1618,7 +1620,7 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
         trans = item >= p.max_items;
         if (trans) item -= p.max_items;
     }
-    prefill_chain<D, ACT, OUT, FUSED>(p, sm, item, h, trans);
+    prefill_chain<D, ACT, OUT, FUSED, CD>(p, sm, item, h, trans);
 }
 
 // A resident grid of G workgroups, launched cooperatively so that all of
@@ -1634,7 +1636,7 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
 // QUEUE = false: every chain is paired (the grid holds them all), and the
 // one-workgroup code is left out of the kernel, which keeps the two roles'
 // register allocation free of it.
-template <int D, typename ACT, bool QUEUE>
+template <int D, typename ACT, bool QUEUE, bool CD>
 __global__ __launch_bounds__(4 * D) void prefill_pair_kernel(PrefillParams p) {
     __shared__ PrefillLds<D, ACT> sm;
     __shared__ int next_s;
@@ -1644,8 +1646,8 @@ __global__ __launch_bounds__(4 * D) void prefill_pair_kernel(PrefillParams p) {
     const int b = blockIdx.x;
     const int pair = 8 * (b / 16) + (b % 8);
     if (pair < K) {
-        if ((b % 16) < 8) prefill_chain<D, ACT, true, PRODUCER>(p, sm, pair / p.H, pair % p.H, false);
-        else prefill_chain<D, ACT, true, CONSUMER>(p, sm, pair / p.H, pair % p.H, false);
+        if ((b % 16) < 8) prefill_chain<D, ACT, true, PRODUCER, CD>(p, sm, pair / p.H, pair % p.H, false);
+        else prefill_chain<D, ACT, true, CONSUMER, CD>(p, sm, pair / p.H, pair % p.H, false);
         __syncthreads();
     }
     if constexpr (!QUEUE) return;
@@ -1655,7 +1657,7 @@ __global__ __launch_bounds__(4 * D) void prefill_pair_kernel(PrefillParams p) {
         const int chain = K + next_s;
         __syncthreads();
         if (chain >= NH) break;
-        prefill_chain<D, ACT, true, FUSED>(p, sm, chain / p.H, chain % p.H, false);
+        prefill_chain<D, ACT, true, FUSED, CD>(p, sm, chain / p.H, chain % p.H, false);
         __syncthreads();
     }
 }
@@ -1910,7 +1912,7 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(PrefillParams p) {
     }
 }
 
-template <int D, typename ACT>
+template <int D, typename ACT, bool CD>
 hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
     if (!p.split) {
         const int64_t blocks = static_cast<int64_t>(p.N) * p.H;
@@ -1923,11 +1925,11 @@ hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
             PrefillParams pc = p;
             void* args[] = {&pc};
             const bool all_paired = 2 * blocks <= p.sched_grid && blocks <= p.max_pairs;
-            const void* f = all_paired ? reinterpret_cast<const void*>(&prefill_pair_kernel<D, ACT, false>)
-                                       : reinterpret_cast<const void*>(&prefill_pair_kernel<D, ACT, true>);
+            const void* f = all_paired ? reinterpret_cast<const void*>(&prefill_pair_kernel<D, ACT, false, CD>)
+                                       : reinterpret_cast<const void*>(&prefill_pair_kernel<D, ACT, true, CD>);
             return hipLaunchCooperativeKernel(f, dim3(static_cast<unsigned>(p.sched_grid)), dim3(4 * D), args, 0, s);
         }
-        hipLaunchKernelGGL((prefill_kernel<D, ACT, true>), dim3(static_cast<unsigned>(blocks)), dim3(4 * D), 0, s,
+        hipLaunchKernelGGL((prefill_kernel<D, ACT, true, CD>), dim3(static_cast<unsigned>(blocks)), dim3(4 * D), 0, s,
                            p);
         return hipGetLastError();
     }
@@ -1936,13 +1938,13 @@ hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
     hipLaunchKernelGGL(prefill_split_meta_kernel, dim3(1), dim3(1024), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_kernel<D, ACT, false>), dim3(static_cast<unsigned>(2 * items)), dim3(4 * D), 0, s,
+    hipLaunchKernelGGL((prefill_kernel<D, ACT, false, CD>), dim3(static_cast<unsigned>(2 * items)), dim3(4 * D), 0, s,
                        p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(segment_scan_kernel<D>, dim3(static_cast<unsigned>(static_cast<int64_t>(p.N) * p.H * (D / 16))),
                        dim3(256), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_kernel<D, ACT, true>), dim3(static_cast<unsigned>(items)), dim3(4 * D), 0, s, p);
+    hipLaunchKernelGGL((prefill_kernel<D, ACT, true, CD>), dim3(static_cast<unsigned>(items)), dim3(4 * D), 0, s, p);
     return hipGetLastError();
 }
 
@@ -1960,11 +1962,11 @@ int64_t prefill_pair_slot_bytes(int dk, int act) {
 
 int64_t prefill_pair_capacity(int dk, int act) {
     const void* f = nullptr;
-    if (act == 1) f = dk == 32 ? reinterpret_cast<const void*>(&prefill_pair_kernel<32, bf16_t, true>)
-                    : dk == 64 ? reinterpret_cast<const void*>(&prefill_pair_kernel<64, bf16_t, true>)
-                               : reinterpret_cast<const void*>(&prefill_pair_kernel<128, bf16_t, true>);
-    else f = dk == 32 ? reinterpret_cast<const void*>(&prefill_pair_kernel<32, float, true>)
-                      : reinterpret_cast<const void*>(&prefill_pair_kernel<64, float, true>);
+    if (act == 1) f = dk == 32 ? reinterpret_cast<const void*>(&prefill_pair_kernel<32, bf16_t, true, false>)
+                    : dk == 64 ? reinterpret_cast<const void*>(&prefill_pair_kernel<64, bf16_t, true, false>)
+                               : reinterpret_cast<const void*>(&prefill_pair_kernel<128, bf16_t, true, false>);
+    else f = dk == 32 ? reinterpret_cast<const void*>(&prefill_pair_kernel<32, float, true, false>)
+                      : reinterpret_cast<const void*>(&prefill_pair_kernel<64, float, true, false>);
     int dev = 0, cus = 0, per_cu = 0, coop = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return 0;
@@ -2019,14 +2021,22 @@ PrefillWorkspace prefill_workspace(int32_t N, int32_t H, int64_t T, int dk, int 
 
 hipError_t launch_prefill(int dk, int dv, int act, const PrefillParams& p, hipStream_t s) {
     if (!prefill_supported(dk, dv, act)) return hipErrorInvalidValue;
-    if (act == 1) {
+    if (act == 1 && p.conv_done) {
         switch (dk) {
-            case 32: return launch_prefill_t<32, bf16_t>(p, s);
-            case 64: return launch_prefill_t<64, bf16_t>(p, s);
-            default: return launch_prefill_t<128, bf16_t>(p, s);
+            case 32: return launch_prefill_t<32, bf16_t, true>(p, s);
+            case 64: return launch_prefill_t<64, bf16_t, true>(p, s);
+            default: return launch_prefill_t<128, bf16_t, true>(p, s);
         }
     }
-    return dk == 32 ? launch_prefill_t<32, float>(p, s) : launch_prefill_t<64, float>(p, s);
+    if (p.conv_done) return hipErrorInvalidValue;          // the conv front end produces bf16 only
+    if (act == 1) {
+        switch (dk) {
+            case 32: return launch_prefill_t<32, bf16_t, false>(p, s);
+            case 64: return launch_prefill_t<64, bf16_t, false>(p, s);
+            default: return launch_prefill_t<128, bf16_t, false>(p, s);
+        }
+    }
+    return dk == 32 ? launch_prefill_t<32, float, false>(p, s) : launch_prefill_t<64, float, false>(p, s);
 }
 
 }  // namespace kda

@@ -48,9 +48,15 @@ __device__ __forceinline__ float softplus_f(float y) {
 // consecutive; within an XCD, groups of GROUP_M row tiles sweep all column
 // tiles so that the concurrently running tiles share panels of x and W in
 // that XCD's L2.
-template <int BM, int BN>
+// In the conv mode a tile computes BM rows but stores the last BM - HALO:
+// its first HALO rows are the conv's left context of the next, computed again
+// (the tiles overlap by HALO rows), so m0 = (BM - HALO) t - HALO.
+constexpr int HALO = 3;
+
+template <int BM, int BN, bool CONV = false>
 __device__ __forceinline__ bool tile_origin(const ProjectParams& p, int& m0, int& n0) {
-    const int tiles_m = (p.T + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+    constexpr int SM = CONV ? BM - HALO : BM;     // stored rows per tile
+    const int tiles_m = (p.T + SM - 1) / SM, tiles_n = (p.N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
     const int per_xcd = (tiles + XCDS - 1) / XCDS;
     const int b = blockIdx.x;
@@ -59,7 +65,7 @@ __device__ __forceinline__ bool tile_origin(const ProjectParams& p, int& m0, int
     const int in_group = GROUP_M * tiles_n;
     const int first_m = (t / in_group) * GROUP_M;
     const int gm = min(tiles_m - first_m, GROUP_M);
-    m0 = (first_m + (t % in_group) % gm) * BM;
+    m0 = (first_m + (t % in_group) % gm) * SM - (CONV ? HALO : 0);
     n0 = ((t % in_group) / gm) * BN;
     return true;
 }
@@ -155,6 +161,182 @@ __device__ __forceinline__ void epilogue(const ProjectParams& p, const f32x16 (&
     }
 }
 
+// Epilogue of the conv front end.  The routing and the 32-row strips are
+// those of `epilogue`; on the q, k and v columns each stored row m becomes
+//   raw(m)  = RNE_bf16(x W^T)                       (stored in the second tensor)
+//   a(m)    = RNE_bf16(SiLU(conv4(w, raw(m-3), raw(m-2), raw(m-1), raw(m))))
+// where a row before its sequence's first token is taken from that
+// sequence's initial conv state (index 2 = the token just before the start)
+// or is zero, exactly as the prefill forms its left context; z, g and beta
+// are stored as in `epilogue`.  The rows before a strip's first row come from
+// the previous strip (kept in `halo`), for the second row-wave's first strip
+// from the first row-wave's last strip, and for the tile's first strip from
+// the tile's own first HALO rows, which are computed but not stored.
+template <int BM, int BN, int WM, int WN, int TI = BM / WM / 32, int TJ = BN / WN / 32>
+__device__ __forceinline__ void epilogue_conv(const ProjectParams& p, const f32x16 (&acc)[TI][TJ], float* smem,
+                                              int m0, int n0) {
+    constexpr int RM = BM / WM, RN = BN / WN, NW = WM * WN;
+    constexpr int EP = RN + 4;
+    constexpr int GPR = RN / 4;
+    constexpr int RPI = 64 / GPR;
+    static_assert(RN % 4 == 0 && 64 % GPR == 0 && 32 % RPI == 0, "column groups must tile a wave");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lr = lane & 31;
+    const int wm = wave / WN, wn = wave % WN;
+    float* stage = smem + wave * 32 * EP;
+    float* halo_all = smem + NW * 32 * EP;                                 // [NW][HALO][EP]
+    float* halo = halo_all + wave * HALO * EP;
+    int2* rowinfo = reinterpret_cast<int2*>(halo_all + NW * HALO * EP);   // [BM]: (sequence start, sequence)
+    const int cg = lane % GPR, rsub = lane / GPR;
+
+    const int H = p.H, dk = p.dk, dv = p.dv, C = 2 * dk + dv;
+    const int64_t bq = static_cast<int64_t>(H) * dk, bv = static_cast<int64_t>(H) * dv;
+    const int64_t n = n0 + RN * wn + 4 * cg;
+    const int nv = static_cast<int>(min(static_cast<int64_t>(4), max(static_cast<int64_t>(0), p.N - n)));
+    int kind;
+    int64_t col, width;
+    if (nv == 0) { kind = -1; col = 0; width = 0; }
+    else if (n < bq) { kind = 0; col = n; width = bq; }
+    else if (n < 2 * bq) { kind = 1; col = n - bq; width = bq; }
+    else if (n < 2 * bq + bv) { kind = 2; col = n - 2 * bq; width = bv; }
+    else if (n < 2 * bq + 2 * bv) { kind = 3; col = n - 2 * bq - bv; width = bv; }
+    else if (n < 3 * bq + 2 * bv) { kind = 4; col = n - 2 * bq - 2 * bv; width = bq; }
+    else { kind = 5; col = n - 3 * bq - 2 * bv; width = H; }
+    void* dst = kind == 0 ? p.q : kind == 1 ? p.k : kind == 2 ? p.v : kind == 3 ? p.z : kind == 4 ? p.g : p.beta;
+    const int esz = kind >= 4 ? 4 : 2;
+    const bool wide = nv == 4 && width % 4 == 0 && col % 4 == 0 && reinterpret_cast<uintptr_t>(dst) % (4 * esz) == 0;
+    // conv channel and weights of this lane's columns (q, k, v only; the 4
+    // columns of a group lie in one head: the head sizes are multiples of 32)
+    const bool convk = kind >= 0 && kind <= 2;
+    const int dh = kind == 2 ? dv : dk;
+    const int head = convk ? static_cast<int>(col / dh) : 0;
+    const int cc = convk ? kind * dk + static_cast<int>(col % dh) : 0;   // first conv channel of the group
+    float4 cw[4];
+#pragma unroll
+    for (int c = 0; c < 4; c++)
+        cw[c] = (convk && c < nv) ? *reinterpret_cast<const float4*>(p.conv_w + (static_cast<int64_t>(head) * C + cc + c) * 4)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    auto rbf = [](float x) { return static_cast<float>(static_cast<__bf16>(x)); };   // RNE to bf16 and back
+
+    // sequence start and index of every tile row (largest n with cu[n] <= m)
+    for (int r = threadIdx.x; r < BM; r += 64 * NW) {
+        const int m = m0 + r;
+        int2 si = make_int2(0, -1);
+        if (m >= 0 && m < p.T) {
+            int lo = 0, hi = p.num_seqs;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (p.cu_seqlens[mid] <= m) lo = mid;
+                else hi = mid;
+            }
+            si = make_int2(p.cu_seqlens[lo], lo);
+        }
+        rowinfo[r] = si;
+    }
+
+#pragma unroll
+    for (int i = 0; i < TI; i++) {
+#pragma unroll
+        for (int j = 0; j < TJ; j++)
+#pragma unroll
+            for (int e = 0; e < 16; e++)
+                stage[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * EP + 32 * j + lr] = acc[i][j][e];
+        if (i == 0 && WM > 1 && wm == 0 && lane >= 32) {
+            // rows RM-3 .. RM-1 (the last strip's rows 29..31: e = 13..15 of
+            // the upper half-wave) are the left context of the next row-wave
+            float* dh2 = halo_all + (wave + WN) * HALO * EP;
+#pragma unroll
+            for (int j = 0; j < TJ; j++)
+#pragma unroll
+                for (int e = 13; e < 16; e++) dh2[((e & 3) - 1) * EP + 32 * j + lr] = acc[TI - 1][j][e];
+        }
+        __syncthreads();
+        const int rb = RM * wm + 32 * i;
+#pragma unroll 2
+        for (int it = 0; it < 32 / RPI; it++) {
+            const int r = it * RPI + rsub;
+            const int tr = rb + r, m = m0 + tr;
+            if (kind < 0 || m < 0 || m >= p.T || tr < HALO) continue;
+            const float4 y = *reinterpret_cast<const float4*>(&stage[r * EP + 4 * cg]);
+            const int64_t o = static_cast<int64_t>(m) * width + col;
+            float v4[4] = {y.x, y.y, y.z, y.w};
+            float a4[4];
+            if (convk) {
+                // window rows m-3 .. m-1 of the same sequence, or the initial conv state
+                const int2 si = rowinfo[tr];
+                float back[3][4];                   // back[j-1]: row m - j
+#pragma unroll
+                for (int j = 1; j <= HALO; j++) {
+                    if (m - j >= si.x) {
+                        const float* src = r - j >= 0 ? &stage[(r - j) * EP + 4 * cg] : &halo[(r - j + HALO) * EP + 4 * cg];
+                        const float4 b = *reinterpret_cast<const float4*>(src);
+                        back[j - 1][0] = rbf(b.x);
+                        back[j - 1][1] = rbf(b.y);
+                        back[j - 1][2] = rbf(b.z);
+                        back[j - 1][3] = rbf(b.w);
+                    } else {
+                        const int idx = HALO - (si.x - (m - j));          // conv-state index, 2 = just before the start
+                        const int slot = (p.init_slot && si.y >= 0) ? p.init_slot[si.y] : -1;
+#pragma unroll
+                        for (int c = 0; c < 4; c++) {
+                            float x0 = 0.f;
+                            if (slot >= 0 && slot < p.num_slots && c < nv)
+                                x0 = bf16_to_f32(static_cast<const uint16_t*>(p.conv_pool)[
+                                    ((static_cast<int64_t>(slot) * H + head) * C + cc + c) * HALO + idx]);
+                            back[j - 1][c] = x0;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < 4; c++) {
+                    v4[c] = rbf(v4[c]);
+                    a4[c] = silu(conv4(cw[c], back[2][c], back[1][c], back[0][c], v4[c]));
+                }
+            } else if (kind == 4) {
+#pragma unroll
+                for (int c = 0; c < 4; c++) v4[c] = -softplus_f(v4[c]);
+            } else if (kind == 5) {
+#pragma unroll
+                for (int c = 0; c < 4; c++) v4[c] = sigmoid(v4[c]);
+            }
+            auto put = [&](void* base, const float (&x)[4]) {
+                if (wide) {
+                    if (kind < 4) {
+                        uint2 w;
+                        w.x = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x[0]))) |
+                              (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x[1]))) << 16);
+                        w.y = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x[2]))) |
+                              (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x[3]))) << 16);
+                        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + o) = w;
+                    } else {
+                        *reinterpret_cast<float4*>(static_cast<float*>(base) + o) = make_float4(x[0], x[1], x[2], x[3]);
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 4; c++) {
+                        if (c >= nv) break;
+                        if (kind < 4) static_cast<uint16_t*>(base)[o + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x[c]));
+                        else static_cast<float*>(base)[o + c] = x[c];
+                    }
+                }
+            };
+            if (convk) {
+                put(dst, a4);                                                     // post-conv activations
+                put(static_cast<uint16_t*>(dst) + static_cast<int64_t>(p.T) * width, v4);   // raw projections
+            } else {
+                put(dst, v4);
+            }
+        }
+        // this strip's last HALO rows are the next strip's left context
+        if (i + 1 < TI) {
+            for (int e = lane; e < HALO * RN; e += 64) {
+                const int hr = e / RN, hc = e % RN;
+                halo[hr * EP + hc] = stage[(32 - HALO + hr) * EP + hc];
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // Physical 16-byte chunk of logical chunk c in row r of an unpadded LDS tile
 // with CPR chunks per row (XOR is its own inverse, so the same map takes a
 // physical chunk to its logical one).  For every aligned run of 8 rows, and
@@ -201,7 +383,7 @@ __device__ __forceinline__ i32x4 raw_rsrc(const void* p, uint32_t bytes) {
 // instruction fills 1 KiB of LDS contiguously), one step ahead, into two
 // buffers; no registers hold them.  Rows past T (or N) read the last valid
 // row instead; they only feed outputs that are never stored.
-template <int BM, int BN, int BK, int WM, int WN>
+template <int BM, int BN, int BK, int WM, int WN, bool CONV>
 __global__ __launch_bounds__(64 * WM * WN) void project_kernel(ProjectParams p) {
     constexpr int NW = WM * WN;
     constexpr int RM = BM / WM, RN = BN / WN;
@@ -215,12 +397,15 @@ __global__ __launch_bounds__(64 * WM * WN) void project_kernel(ProjectParams p) 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * SS];
 
     int m0, n0;
-    if (!tile_origin<BM, BN>(p, m0, n0)) return;
+    if (!tile_origin<BM, BN, CONV>(p, m0, n0)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int K = p.Dm;
-    const int va_rows = min(BM, p.T - m0), vb_rows = min(BN, p.N - n0);
-    const i32x4 ra = raw_rsrc(static_cast<const uint16_t*>(p.x) + static_cast<int64_t>(m0) * K,
+    // the conv mode's first tile starts HALO rows before row 0: those rows
+    // read row 0 (they only feed outputs that are never stored)
+    const int mb = CONV ? max(m0, 0) : m0, shift = CONV ? mb - m0 : 0;
+    const int va_rows = min(BM - shift, p.T - mb), vb_rows = min(BN, p.N - n0);
+    const i32x4 ra = raw_rsrc(static_cast<const uint16_t*>(p.x) + static_cast<int64_t>(mb) * K,
                               static_cast<uint32_t>(va_rows) * K * 2);
     const i32x4 rb = raw_rsrc(static_cast<const uint16_t*>(p.w) + static_cast<int64_t>(n0) * K,
                               static_cast<uint32_t>(vb_rows) * K * 2);
@@ -229,7 +414,8 @@ __global__ __launch_bounds__(64 * WM * WN) void project_kernel(ProjectParams p) 
 #pragma unroll
     for (int j = 0; j < IA; j++) {
         const int r = (wave * IA + j) * RPI + lane / CPR;
-        oa[j] = static_cast<uint32_t>((min(r, va_rows - 1) * K + 8 * swz<CPR>(r, lane % CPR)) * 2);
+        const int rx = CONV ? min(max(r - shift, 0), va_rows - 1) : min(r, va_rows - 1);
+        oa[j] = static_cast<uint32_t>((rx * K + 8 * swz<CPR>(r, lane % CPR)) * 2);
     }
 #pragma unroll
     for (int j = 0; j < IB; j++) {
@@ -310,20 +496,27 @@ __global__ __launch_bounds__(64 * WM * WN) void project_kernel(ProjectParams p) 
     }
     __syncthreads();
     static_assert(NW * 32 * (RN + 4) * 4 <= sizeof(smem), "epilogue staging exceeds the tile buffers");
-    epilogue<BM, BN, WM, WN>(p, acc, reinterpret_cast<float*>(smem), m0, n0);
+    static_assert(NW * (32 + HALO) * (RN + 4) * 4 + BM * 8 <= sizeof(smem), "conv staging exceeds the tile buffers");
+    if constexpr (CONV) epilogue_conv<BM, BN, WM, WN>(p, acc, reinterpret_cast<float*>(smem), m0, n0);
+    else epilogue<BM, BN, WM, WN>(p, acc, reinterpret_cast<float*>(smem), m0, n0);
 }
 
 }  // namespace
 
 hipError_t launch_project(const ProjectParams& p, hipStream_t s) {
     constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = 4;
-    const int64_t tiles = static_cast<int64_t>((p.T + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    const int SM = p.conv ? BM - HALO : BM;       // stored rows per tile
+    const int64_t tiles = static_cast<int64_t>((p.T + SM - 1) / SM) * ((p.N + BN - 1) / BN);
     if (tiles == 0) return hipSuccess;
     const int64_t grid = (tiles + XCDS - 1) / XCDS * XCDS;
     // tile ids and the per-lane byte offsets ((row < BM) x Dm + chunk) x 2 are 32-bit
     if (grid > INT32_MAX || (static_cast<int64_t>(BM - 1) * p.Dm + BK) * 2 > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((project_kernel<BM, BN, BK, WM, WN>), dim3(static_cast<unsigned>(grid)), dim3(64 * WM * WN), 0,
-                       s, p);
+    if (p.conv)
+        hipLaunchKernelGGL((project_kernel<BM, BN, BK, WM, WN, true>), dim3(static_cast<unsigned>(grid)),
+                           dim3(64 * WM * WN), 0, s, p);
+    else
+        hipLaunchKernelGGL((project_kernel<BM, BN, BK, WM, WN, false>), dim3(static_cast<unsigned>(grid)),
+                           dim3(64 * WM * WN), 0, s, p);
     return hipGetLastError();
 }
 

@@ -133,8 +133,11 @@ def test_prefill_validation():
     assert prefill_call(cfg(), interval=64, ckb=None) == kda.KDA_ERR_INVALID_ARG
     assert prefill_call(cfg(), interval=64, nck=0) == kda.KDA_ERR_INVALID_ARG
     assert prefill_call(cfg(), N=0, cu=None) == kda.KDA_OK                      # nothing to do
-    assert prefill_call(cfg(), flags=8) == kda.KDA_ERR_INVALID_ARG                 # unknown flag
+    assert prefill_call(cfg(), flags=16) == kda.KDA_ERR_INVALID_ARG                # unknown flag
     assert "unknown" in kda.last_error()
+    assert prefill_call(cfg(head_k=64, head_v=64, act_dtype=kda.KDA_F32),
+                        flags=kda.KDA_PREFILL_CONV_DONE) == kda.KDA_ERR_UNSUPPORTED  # the front end is bf16 only
+    assert "CONV_DONE" in kda.last_error()
     assert prefill_call(cfg(), flags=kda.KDA_PREFILL_PAIRED_POLL_ONCE) == kda.KDA_ERR_INVALID_ARG
     assert "needs KDA_PREFILL_PAIRED" in kda.last_error()
     both = kda.KDA_PREFILL_SPLIT | kda.KDA_PREFILL_PAIRED
@@ -208,3 +211,25 @@ def test_projection_validation():
     assert project_out_call(cfg(), y=FAKE + 1) == kda.KDA_ERR_INVALID_ARG
     assert project_out_call(cfg(), T=0, o=None) == kda.KDA_OK
     assert kda.last_error() == ""
+
+
+def test_project_inputs_conv_validation():
+    """The conv front end checks its arguments on the host (no GPU needed)."""
+    P = ctypes.c_void_p
+    L = kda.lib()
+
+    def call(c, N=2, T=8, Dm=128, **ptrs):
+        names = ("cu", "x", "w", "cw", "pool", "init", "q", "k", "v", "z", "g", "beta")
+        a = {n: FAKE for n in names}
+        a.update(ptrs)
+        vp = lambda x: None if x is None else P(x)
+        return L.kda_project_inputs_conv(ctypes.byref(c.c()), N, T, Dm, vp(a["cu"]), vp(a["x"]), vp(a["w"]),
+                                         vp(a["cw"]), vp(a["pool"]), 4, vp(a["init"]), vp(a["q"]), vp(a["k"]),
+                                         vp(a["v"]), vp(a["z"]), vp(a["g"]), vp(a["beta"]), None)
+
+    assert call(cfg(act_dtype=kda.KDA_F32, head_k=64, head_v=64)) == kda.KDA_ERR_UNSUPPORTED
+    assert call(cfg(), N=0) == kda.KDA_ERR_INVALID_ARG
+    assert call(cfg(), Dm=100) == kda.KDA_ERR_INVALID_ARG
+    assert call(cfg(), cu=None) == kda.KDA_ERR_INVALID_ARG
+    assert call(cfg(), q=MISALIGNED) == kda.KDA_ERR_INVALID_ARG
+    assert call(cfg(), T=0, cu=None) == kda.KDA_OK                     # nothing to do

@@ -446,3 +446,63 @@ def test_state_round_continues_from_each_checkpoint():
     plain = oracle.run(q, k, v, z, g, beta, cw, nw, [0, T], start_pos=[7], ckpt_interval=I)
     np.testing.assert_array_equal(plain.out[:cuts[1]], whole.out[:cuts[1]])
     assert not np.array_equal(plain.out[cuts[1]:], whole.out[cuts[1]:])
+
+
+# ---------------------------------------------------------------------------
+# The stand-alone conv oracle (oracle/conv.py), the reference for a fused
+# front end's post-conv activations.
+
+def _conv_case(seed=7):
+    rng = np.random.default_rng(seed)
+    H, C = 2, 6
+    lengths = [5, 1, 0, 9, 2]
+    T = sum(lengths)
+    x = rng.standard_normal((T, H, C))
+    X0 = rng.standard_normal((len(lengths), H, C, 3))
+    return x, X0, np.concatenate([[0], np.cumsum(lengths)]), H, C
+
+
+def test_conv_oracle_current_tap_is_identity():
+    """w = e3 (only the current token's tap): the pre-activation is the raw
+    input, at sequence starts too."""
+    from oracle import conv
+    x, X0, cu, H, C = _conv_case()
+    w = np.zeros((H, C, 4))
+    w[:, :, 3] = 1.0
+    np.testing.assert_array_equal(conv.preactivation(x, w, cu, X0), x)
+
+
+def test_conv_oracle_oldest_tap_reads_the_conv_state():
+    """w = e0 (the token three back): inside a sequence the raw input three
+    rows up; for its first three tokens the initial conv state, index 0 for
+    the first token, 1 for the second, 2 for the third (pins the tap order and
+    the conv-state order against a shift or a reversal)."""
+    from oracle import conv
+    x, X0, cu, H, C = _conv_case()
+    w = np.zeros((H, C, 4))
+    w[:, :, 0] = 1.0
+    y = conv.preactivation(x, w, cu, X0)
+    for n in range(len(cu) - 1):
+        for t in range(int(cu[n]), int(cu[n + 1])):
+            r = t - int(cu[n])
+            want = X0[n][:, :, r] if r < 3 else x[t - 3]
+            np.testing.assert_array_equal(y[t], want)
+
+
+def test_conv_oracle_is_linear_in_the_weights_and_silu_closed_form():
+    from oracle import conv
+    x, X0, cu, H, C = _conv_case(8)
+    rng = np.random.default_rng(9)
+    w1, w2 = rng.standard_normal((H, C, 4)), rng.standard_normal((H, C, 4))
+    y12 = conv.preactivation(x, w1 + w2, cu, X0)
+    np.testing.assert_allclose(y12, conv.preactivation(x, w1, cu, X0) + conv.preactivation(x, w2, cu, X0),
+                               rtol=0, atol=1e-12)
+    assert conv.silu(0.0) == 0.0
+    assert abs(conv.silu(1.0) - 1.0 / (1.0 + np.exp(-1.0))) < 1e-16
+    assert abs(conv.silu(-40.0)) < 1e-15 and abs(conv.silu(40.0) - 40.0) < 1e-12
+    # the layer's channel order: q, then k, then v per head
+    q, k, v = x[:, :, :2], x[:, :, 2:4], x[:, :, 4:]
+    w = np.zeros((H, C, 4))
+    w[:, :, 3] = 1.0
+    aq, ak, av = conv.activations(q, k, v, w, cu, X0)
+    np.testing.assert_allclose(np.concatenate([aq, ak, av], axis=2), conv.silu(x), rtol=0, atol=0)

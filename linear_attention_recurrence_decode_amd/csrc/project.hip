@@ -22,6 +22,8 @@
 // XCD form groups of 4 row tiles sweeping N, sharing panels of x and W in
 // that XCD's L2.  The epilogue stages the fp32 results through LDS.
 
+#include <utility>
+
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -38,9 +40,25 @@ union V16 {
     bf16x8_p v;
 };
 
+// softplus(y) = max(y, 0) + log1p(e), e = exp(-|y|) in (0, 1].  log1p(e) is
+// taken as 2 atanh(s) with s = e / (2 + e) in (0, 1/3]: the odd series
+// 2 s (1 + s^2/3 + s^4/5 + ... + s^14/15), whose first omitted term is below
+// 2^-28 of the sum.  One reciprocal and eight FMAs, about a third of the
+// instructions of a library log1pf, for a few ulp.  y = -inf gives 0, +inf
+// gives +inf, NaN stays NaN.
 __device__ __forceinline__ float softplus_f(float y) {
-    // max(y, 0) + log1p(exp(-|y|))
-    return fmaxf(y, 0.f) + log1pf(__expf(-fabsf(y)));
+    const float e = __expf(-fabsf(y));
+    const float s = e * __builtin_amdgcn_rcpf(2.0f + e);
+    const float s2 = s * s;
+    float p = 1.0f / 15.0f;
+    p = fmaf(p, s2, 1.0f / 13.0f);
+    p = fmaf(p, s2, 1.0f / 11.0f);
+    p = fmaf(p, s2, 1.0f / 9.0f);
+    p = fmaf(p, s2, 1.0f / 7.0f);
+    p = fmaf(p, s2, 1.0f / 5.0f);
+    p = fmaf(p, s2, 1.0f / 3.0f);
+    p = fmaf(p, s2, 1.0f);
+    return fmaxf(y, 0.f) + 2.0f * s * p;
 }
 
 // Output tile of this workgroup, or false past the last tile.  Workgroups are
@@ -48,15 +66,12 @@ __device__ __forceinline__ float softplus_f(float y) {
 // consecutive; within an XCD, groups of GROUP_M row tiles sweep all column
 // tiles so that the concurrently running tiles share panels of x and W in
 // that XCD's L2.
-// In the conv mode a tile computes BM rows but stores the last BM - HALO:
-// its first HALO rows are the conv's left context of the next, computed again
-// (the tiles overlap by HALO rows), so m0 = (BM - HALO) t - HALO.
+// Rows of the causal conv's window before the current token.
 constexpr int HALO = 3;
 
-template <int BM, int BN, bool CONV = false>
+template <int BM, int BN>
 __device__ __forceinline__ bool tile_origin(const ProjectParams& p, int& m0, int& n0) {
-    constexpr int SM = CONV ? BM - HALO : BM;     // stored rows per tile
-    const int tiles_m = (p.T + SM - 1) / SM, tiles_n = (p.N + BN - 1) / BN;
+    const int tiles_m = (p.T + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
     const int per_xcd = (tiles + XCDS - 1) / XCDS;
     const int b = blockIdx.x;
@@ -65,7 +80,7 @@ __device__ __forceinline__ bool tile_origin(const ProjectParams& p, int& m0, int
     const int in_group = GROUP_M * tiles_n;
     const int first_m = (t / in_group) * GROUP_M;
     const int gm = min(tiles_m - first_m, GROUP_M);
-    m0 = (first_m + (t % in_group) % gm) * SM - (CONV ? HALO : 0);
+    m0 = (first_m + (t % in_group) % gm) * BM;
     n0 = ((t % in_group) / gm) * BN;
     return true;
 }
@@ -161,32 +176,109 @@ __device__ __forceinline__ void epilogue(const ProjectParams& p, const f32x16 (&
     }
 }
 
-// Epilogue of the conv front end.  The routing and the 32-row strips are
-// those of `epilogue`; on the q, k and v columns each stored row m becomes
+// SiLU of the conv front end: exp through the hardware base-2 exponential
+// and the hardware reciprocal (a few ulp in fp32, far below the bf16 rounding
+// of the result).  y -> -inf gives exp2 -> inf, rcp -> 0 and -0; no NaN.
+__device__ __forceinline__ float front_silu(float y) {
+    return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504088896341f * y));
+}
+
+// Post-conv activation of one channel from its window of rounded raw inputs
+// (oldest first); the epilogue and the tile-top pass use this one expression,
+// so that a row gets the same bits whichever computes it.
+__device__ __forceinline__ float front_act(const float4& w, float a, float b, float c, float d) {
+    return front_silu(conv4(w, a, b, c, d));
+}
+
+template <int... I, typename F>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F&& f) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
+__device__ __forceinline__ float round_bf16(float x) { return static_cast<float>(static_cast<__bf16>(x)); }
+
+// Sequence of packed row m (0 <= m < cu[num_seqs]): the largest n with
+// cu[n] <= m, which skips empty sequences.  Returns (cu[n], n).
+__device__ __forceinline__ int2 sequence_of(const int32_t* cu, int num_seqs, int m) {
+    int lo = 0, hi = num_seqs;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cu[mid] <= m) lo = mid;
+        else hi = mid;
+    }
+    return make_int2(cu[lo], lo);
+}
+
+// Left-context value of conv channel ch of head `head` for the row `back`
+// rows before a sequence's first token (back = 1 .. 3): the sequence's
+// initial conv state (index 3 - back; 2 = the token just before the start)
+// or zero without one.
+__device__ __forceinline__ float conv_context(const ProjectParams& p, int seq, int head, int ch, int back) {
+    const int slot = (p.init_slot && seq >= 0) ? p.init_slot[seq] : -1;
+    if (slot < 0 || slot >= p.num_slots) return 0.f;
+    const int C = 2 * p.dk + p.dv;
+    return bf16_to_f32(static_cast<const uint16_t*>(p.conv_pool)[
+        ((static_cast<int64_t>(slot) * p.H + head) * C + ch) * HALO + (HALO - back)]);
+}
+
+// Store of 4 consecutive results of one row: one 8-byte (bf16) or 16-byte
+// (fp32) store when `wide`, else element by element.
+__device__ __forceinline__ void put4(void* base, int64_t o, bool wide, bool is_f32, int nv, const float (&x)[4]) {
+    if (wide) {
+        if (!is_f32) {
+            uint2 w;
+            w.x = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x[0]))) |
+                  (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x[1]))) << 16);
+            w.y = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x[2]))) |
+                  (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x[3]))) << 16);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + o) = w;
+        } else {
+            *reinterpret_cast<float4*>(static_cast<float*>(base) + o) = make_float4(x[0], x[1], x[2], x[3]);
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            if (c >= nv) break;
+            if (!is_f32) static_cast<uint16_t*>(base)[o + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x[c]));
+            else static_cast<float*>(base)[o + c] = x[c];
+        }
+    }
+}
+
+// Epilogue of the conv front end.  The routing is that of `epilogue`; on the
+// q, k and v columns each row m becomes
 //   raw(m)  = RNE_bf16(x W^T)                       (stored in the second tensor)
 //   a(m)    = RNE_bf16(SiLU(conv4(w, raw(m-3), raw(m-2), raw(m-1), raw(m))))
 // where a row before its sequence's first token is taken from that
 // sequence's initial conv state (index 2 = the token just before the start)
 // or is zero, exactly as the prefill forms its left context; z, g and beta
-// are stored as in `epilogue`.  The rows before a strip's first row come from
-// the previous strip (kept in `halo`), for the second row-wave's first strip
-// from the first row-wave's last strip, and for the tile's first strip from
-// the tile's own first HALO rows, which are computed but not stored.
+// are stored as in `epilogue`.
+// Each lane owns 4 columns of RPS consecutive rows of a 32-row strip and
+// slides the window down them: a row is read from LDS and rounded once, and
+// its three predecessors stay in registers.  A lane whose rows and window lie
+// in one sequence past its first HALO tokens takes no boundary test.  The
+// rows before a strip come from the previous strip (kept in `halo`), for the
+// second row-wave's first strip from the first row-wave's last strip; the
+// tile's first HALO rows, whose window reaches into the previous tile, get
+// their activations from conv_tile_top_kernel after the GEMM (their raw
+// inputs are stored here).
 template <int BM, int BN, int WM, int WN, int TI = BM / WM / 32, int TJ = BN / WN / 32>
 __device__ __forceinline__ void epilogue_conv(const ProjectParams& p, const f32x16 (&acc)[TI][TJ], float* smem,
                                               int m0, int n0) {
     constexpr int RM = BM / WM, RN = BN / WN, NW = WM * WN;
     constexpr int EP = RN + 4;
-    constexpr int GPR = RN / 4;
-    constexpr int RPI = 64 / GPR;
-    static_assert(RN % 4 == 0 && 64 % GPR == 0 && 32 % RPI == 0, "column groups must tile a wave");
+    constexpr int GPR = RN / 4;             // 4-column groups per row
+    constexpr int SEGS = 64 / GPR;          // row segments per strip
+    constexpr int RPS = 32 / SEGS;          // rows per segment
+    static_assert(RN % 4 == 0 && GPR * SEGS == 64 && RPS * SEGS == 32 && RPS >= HALO,
+                  "column groups and row segments must tile a wave's strip");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lr = lane & 31;
     const int wm = wave / WN, wn = wave % WN;
     float* stage = smem + wave * 32 * EP;
     float* halo_all = smem + NW * 32 * EP;                                 // [NW][HALO][EP]
     float* halo = halo_all + wave * HALO * EP;
     int2* rowinfo = reinterpret_cast<int2*>(halo_all + NW * HALO * EP);   // [BM]: (sequence start, sequence)
-    const int cg = lane % GPR, rsub = lane / GPR;
+    const int cg = lane % GPR, seg = lane / GPR;
 
     const int H = p.H, dk = p.dk, dv = p.dv, C = 2 * dk + dv;
     const int64_t bq = static_cast<int64_t>(H) * dk, bv = static_cast<int64_t>(H) * dv;
@@ -202,8 +294,9 @@ __device__ __forceinline__ void epilogue_conv(const ProjectParams& p, const f32x
     else if (n < 3 * bq + 2 * bv) { kind = 4; col = n - 2 * bq - 2 * bv; width = bq; }
     else { kind = 5; col = n - 3 * bq - 2 * bv; width = H; }
     void* dst = kind == 0 ? p.q : kind == 1 ? p.k : kind == 2 ? p.v : kind == 3 ? p.z : kind == 4 ? p.g : p.beta;
-    const int esz = kind >= 4 ? 4 : 2;
-    const bool wide = nv == 4 && width % 4 == 0 && col % 4 == 0 && reinterpret_cast<uintptr_t>(dst) % (4 * esz) == 0;
+    const bool is_f32 = kind >= 4;
+    const bool wide = nv == 4 && width % 4 == 0 && col % 4 == 0 &&
+                      reinterpret_cast<uintptr_t>(dst) % (is_f32 ? 16 : 8) == 0;
     // conv channel and weights of this lane's columns (q, k, v only; the 4
     // columns of a group lie in one head: the head sizes are multiples of 32)
     const bool convk = kind >= 0 && kind <= 2;
@@ -215,26 +308,20 @@ __device__ __forceinline__ void epilogue_conv(const ProjectParams& p, const f32x
     for (int c = 0; c < 4; c++)
         cw[c] = (convk && c < nv) ? *reinterpret_cast<const float4*>(p.conv_w + (static_cast<int64_t>(head) * C + cc + c) * 4)
                                   : make_float4(0.f, 0.f, 0.f, 0.f);
-    auto rbf = [](float x) { return static_cast<float>(static_cast<__bf16>(x)); };   // RNE to bf16 and back
+    void* raw_dst = convk ? static_cast<void*>(static_cast<uint16_t*>(dst) + static_cast<int64_t>(p.T) * width) : dst;
 
-    // sequence start and index of every tile row (largest n with cu[n] <= m)
+    // sequence start and index of every tile row; rows past T get a start no
+    // row reaches, which keeps their lanes off the fast path
     for (int r = threadIdx.x; r < BM; r += 64 * NW) {
         const int m = m0 + r;
-        int2 si = make_int2(0, -1);
-        if (m >= 0 && m < p.T) {
-            int lo = 0, hi = p.num_seqs;
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (p.cu_seqlens[mid] <= m) lo = mid;
-                else hi = mid;
-            }
-            si = make_int2(p.cu_seqlens[lo], lo);
-        }
-        rowinfo[r] = si;
+        rowinfo[r] = m < p.T ? sequence_of(p.cu_seqlens, p.num_seqs, m) : make_int2(INT32_MAX, -1);
     }
 
-#pragma unroll
-    for (int i = 0; i < TI; i++) {
+    // Strips by compile-time index, so that acc stays in registers; the row
+    // loops inside stay rolled (the epilogue runs once per tile, and fully
+    // unrolled its code would be fetched cold line after line).
+    static_for(std::make_integer_sequence<int, TI>{}, [&](auto strip) {
+        constexpr int i = decltype(strip)::value;
 #pragma unroll
         for (int j = 0; j < TJ; j++)
 #pragma unroll
@@ -250,80 +337,76 @@ __device__ __forceinline__ void epilogue_conv(const ProjectParams& p, const f32x
                 for (int e = 13; e < 16; e++) dh2[((e & 3) - 1) * EP + 32 * j + lr] = acc[TI - 1][j][e];
         }
         __syncthreads();
-        const int rb = RM * wm + 32 * i;
-#pragma unroll 2
-        for (int it = 0; it < 32 / RPI; it++) {
-            const int r = it * RPI + rsub;
-            const int tr = rb + r, m = m0 + tr;
-            if (kind < 0 || m < 0 || m >= p.T || tr < HALO) continue;
-            const float4 y = *reinterpret_cast<const float4*>(&stage[r * EP + 4 * cg]);
-            const int64_t o = static_cast<int64_t>(m) * width + col;
-            float v4[4] = {y.x, y.y, y.z, y.w};
-            float a4[4];
+        const int r0 = RPS * seg;                       // this lane's first strip row
+        const int tr0 = RM * wm + 32 * i + r0;          // ... as a tile row
+        const int mr0 = m0 + tr0;
+        int64_t o = static_cast<int64_t>(mr0) * width + col;
+        if (kind >= 0 && mr0 < p.T) {
             if (convk) {
-                // window rows m-3 .. m-1 of the same sequence, or the initial conv state
-                const int2 si = rowinfo[tr];
-                float back[3][4];                   // back[j-1]: row m - j
+                float w3[4], w2[4], w1[4];              // rounded raw rows r-3, r-2, r-1
+                auto load = [&](int r, float (&x)[4]) {
+                    const float4 y = *reinterpret_cast<const float4*>(
+                        r >= 0 ? &stage[r * EP + 4 * cg] : &halo[(r + HALO) * EP + 4 * cg]);
+                    x[0] = round_bf16(y.x);
+                    x[1] = round_bf16(y.y);
+                    x[2] = round_bf16(y.z);
+                    x[3] = round_bf16(y.w);
+                };
+                load(r0 - 3, w3);
+                load(r0 - 2, w2);
+                load(r0 - 1, w1);
+                const bool fast = rowinfo[tr0 + RPS - 1].x <= mr0 - HALO;
+#pragma unroll 1
+                for (int t = 0; t < RPS; t++) {
+                    const int m = mr0 + t;
+                    float w0[4];
+                    load(r0 + t, w0);
+                    float b3[4], b2[4], b1[4];
 #pragma unroll
-                for (int j = 1; j <= HALO; j++) {
-                    if (m - j >= si.x) {
-                        const float* src = r - j >= 0 ? &stage[(r - j) * EP + 4 * cg] : &halo[(r - j + HALO) * EP + 4 * cg];
-                        const float4 b = *reinterpret_cast<const float4*>(src);
-                        back[j - 1][0] = rbf(b.x);
-                        back[j - 1][1] = rbf(b.y);
-                        back[j - 1][2] = rbf(b.z);
-                        back[j - 1][3] = rbf(b.w);
-                    } else {
-                        const int idx = HALO - (si.x - (m - j));          // conv-state index, 2 = just before the start
-                        const int slot = (p.init_slot && si.y >= 0) ? p.init_slot[si.y] : -1;
+                    for (int c = 0; c < 4; c++) { b3[c] = w3[c]; b2[c] = w2[c]; b1[c] = w1[c]; }
+                    if (!fast && m < p.T) {
+                        // rows before the sequence's first token: its initial conv state or zero
+                        // (si.x <= m, so the context index si.x - (m - j) is 1 .. j)
+                        const int2 si = rowinfo[tr0 + t];
+                        if (m - 3 < si.x) {
 #pragma unroll
-                        for (int c = 0; c < 4; c++) {
-                            float x0 = 0.f;
-                            if (slot >= 0 && slot < p.num_slots && c < nv)
-                                x0 = bf16_to_f32(static_cast<const uint16_t*>(p.conv_pool)[
-                                    ((static_cast<int64_t>(slot) * H + head) * C + cc + c) * HALO + idx]);
-                            back[j - 1][c] = x0;
+                            for (int c = 0; c < 4; c++) {
+                                if (c >= nv) break;
+                                if (m - 1 < si.x) b1[c] = conv_context(p, si.y, head, cc + c, si.x - (m - 1));
+                                if (m - 2 < si.x) b2[c] = conv_context(p, si.y, head, cc + c, si.x - (m - 2));
+                                b3[c] = conv_context(p, si.y, head, cc + c, si.x - (m - 3));
+                            }
                         }
                     }
-                }
+                    if (m < p.T) {
+                        if (tr0 + t >= HALO) {
+                            float a4[4];
 #pragma unroll
-                for (int c = 0; c < 4; c++) {
-                    v4[c] = rbf(v4[c]);
-                    a4[c] = silu(conv4(cw[c], back[2][c], back[1][c], back[0][c], v4[c]));
-                }
-            } else if (kind == 4) {
-#pragma unroll
-                for (int c = 0; c < 4; c++) v4[c] = -softplus_f(v4[c]);
-            } else if (kind == 5) {
-#pragma unroll
-                for (int c = 0; c < 4; c++) v4[c] = sigmoid(v4[c]);
-            }
-            auto put = [&](void* base, const float (&x)[4]) {
-                if (wide) {
-                    if (kind < 4) {
-                        uint2 w;
-                        w.x = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x[0]))) |
-                              (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x[1]))) << 16);
-                        w.y = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x[2]))) |
-                              (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x[3]))) << 16);
-                        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + o) = w;
-                    } else {
-                        *reinterpret_cast<float4*>(static_cast<float*>(base) + o) = make_float4(x[0], x[1], x[2], x[3]);
+                            for (int c = 0; c < 4; c++) a4[c] = front_act(cw[c], b3[c], b2[c], b1[c], w0[c]);
+                            put4(dst, o, wide, false, nv, a4);
+                        }
+                        put4(raw_dst, o, wide, false, nv, w0);
                     }
-                } else {
 #pragma unroll
-                    for (int c = 0; c < 4; c++) {
-                        if (c >= nv) break;
-                        if (kind < 4) static_cast<uint16_t*>(base)[o + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x[c]));
-                        else static_cast<float*>(base)[o + c] = x[c];
-                    }
+                    for (int c = 0; c < 4; c++) { w3[c] = w2[c]; w2[c] = w1[c]; w1[c] = w0[c]; }
+                    o += width;
                 }
-            };
-            if (convk) {
-                put(dst, a4);                                                     // post-conv activations
-                put(static_cast<uint16_t*>(dst) + static_cast<int64_t>(p.T) * width, v4);   // raw projections
             } else {
-                put(dst, v4);
+#pragma unroll 1
+                for (int t = 0; t < RPS; t++) {
+                    if (mr0 + t < p.T) {
+                        const float4 y = *reinterpret_cast<const float4*>(&stage[(r0 + t) * EP + 4 * cg]);
+                        float v4[4] = {y.x, y.y, y.z, y.w};
+                        if (kind == 4) {
+#pragma unroll
+                            for (int c = 0; c < 4; c++) v4[c] = -softplus_f(v4[c]);
+                        } else if (kind == 5) {
+#pragma unroll
+                            for (int c = 0; c < 4; c++) v4[c] = sigmoid(v4[c]);
+                        }
+                        put4(dst, o + t * width, wide, is_f32, nv, v4);
+                    }
+                }
             }
         }
         // this strip's last HALO rows are the next strip's left context
@@ -334,7 +417,41 @@ __device__ __forceinline__ void epilogue_conv(const ProjectParams& p, const f32x
             }
         }
         __syncthreads();
+    });
+}
+
+// Activations of the first HALO rows of every BM-row tile of the conv front
+// end, whose window reaches into the tile above: one channel of one row per
+// thread, from the raw inputs the GEMM stored (the same rounded values its
+// epilogue holds) and, before a sequence's first token, its initial conv state.
+__global__ __launch_bounds__(256) void conv_tile_top_kernel(ProjectParams p, int BM) {
+    const int H = p.H, dk = p.dk, dv = p.dv, C = 2 * dk + dv;
+    const int64_t bq = static_cast<int64_t>(H) * dk, bv = static_cast<int64_t>(H) * dv;
+    const int64_t ncol = 2 * bq + bv;
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t row = e / ncol, n = e % ncol;           // row: (tile, HALO row of the tile)
+    const int m = static_cast<int>(row / HALO) * BM + static_cast<int>(row % HALO);
+    if (m >= p.T) return;
+    int kind;
+    int64_t col, width;
+    if (n < bq) { kind = 0; col = n; width = bq; }
+    else if (n < 2 * bq) { kind = 1; col = n - bq; width = bq; }
+    else { kind = 2; col = n - 2 * bq; width = bv; }
+    uint16_t* dst = static_cast<uint16_t*>(kind == 0 ? p.q : kind == 1 ? p.k : p.v);
+    const uint16_t* raw = dst + static_cast<int64_t>(p.T) * width;
+    const int dh = kind == 2 ? dv : dk;
+    const int head = static_cast<int>(col / dh), ch = kind * dk + static_cast<int>(col % dh);
+    const int2 si = sequence_of(p.cu_seqlens, p.num_seqs, m);
+    float x[HALO + 1];                                    // rows m-3 .. m
+#pragma unroll
+    for (int j = 0; j <= HALO; j++) {
+        const int mj = m - HALO + j;
+        x[j] = mj >= si.x ? bf16_to_f32(raw[static_cast<int64_t>(mj) * width + col])
+                          : conv_context(p, si.y, head, ch, si.x - mj);
     }
+    const float4 w = *reinterpret_cast<const float4*>(p.conv_w + (static_cast<int64_t>(head) * C + ch) * 4);
+    dst[static_cast<int64_t>(m) * width + col] =
+        __builtin_bit_cast(uint16_t, static_cast<__bf16>(front_act(w, x[0], x[1], x[2], x[3])));
 }
 
 // Physical 16-byte chunk of logical chunk c in row r of an unpadded LDS tile
@@ -397,15 +514,12 @@ __global__ __launch_bounds__(64 * WM * WN) void project_kernel(ProjectParams p) 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * SS];
 
     int m0, n0;
-    if (!tile_origin<BM, BN, CONV>(p, m0, n0)) return;
+    if (!tile_origin<BM, BN>(p, m0, n0)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int K = p.Dm;
-    // the conv mode's first tile starts HALO rows before row 0: those rows
-    // read row 0 (they only feed outputs that are never stored)
-    const int mb = CONV ? max(m0, 0) : m0, shift = CONV ? mb - m0 : 0;
-    const int va_rows = min(BM - shift, p.T - mb), vb_rows = min(BN, p.N - n0);
-    const i32x4 ra = raw_rsrc(static_cast<const uint16_t*>(p.x) + static_cast<int64_t>(mb) * K,
+    const int va_rows = min(BM, p.T - m0), vb_rows = min(BN, p.N - n0);
+    const i32x4 ra = raw_rsrc(static_cast<const uint16_t*>(p.x) + static_cast<int64_t>(m0) * K,
                               static_cast<uint32_t>(va_rows) * K * 2);
     const i32x4 rb = raw_rsrc(static_cast<const uint16_t*>(p.w) + static_cast<int64_t>(n0) * K,
                               static_cast<uint32_t>(vb_rows) * K * 2);
@@ -414,8 +528,7 @@ __global__ __launch_bounds__(64 * WM * WN) void project_kernel(ProjectParams p) 
 #pragma unroll
     for (int j = 0; j < IA; j++) {
         const int r = (wave * IA + j) * RPI + lane / CPR;
-        const int rx = CONV ? min(max(r - shift, 0), va_rows - 1) : min(r, va_rows - 1);
-        oa[j] = static_cast<uint32_t>((rx * K + 8 * swz<CPR>(r, lane % CPR)) * 2);
+        oa[j] = static_cast<uint32_t>((min(r, va_rows - 1) * K + 8 * swz<CPR>(r, lane % CPR)) * 2);
     }
 #pragma unroll
     for (int j = 0; j < IB; j++) {
@@ -505,18 +618,25 @@ __global__ __launch_bounds__(64 * WM * WN) void project_kernel(ProjectParams p) 
 
 hipError_t launch_project(const ProjectParams& p, hipStream_t s) {
     constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = 4;
-    const int SM = p.conv ? BM - HALO : BM;       // stored rows per tile
-    const int64_t tiles = static_cast<int64_t>((p.T + SM - 1) / SM) * ((p.N + BN - 1) / BN);
+    const int64_t tiles_m = (p.T + BM - 1) / BM;
+    const int64_t tiles = tiles_m * ((p.N + BN - 1) / BN);
     if (tiles == 0) return hipSuccess;
     const int64_t grid = (tiles + XCDS - 1) / XCDS * XCDS;
     // tile ids and the per-lane byte offsets ((row < BM) x Dm + chunk) x 2 are 32-bit
     if (grid > INT32_MAX || (static_cast<int64_t>(BM - 1) * p.Dm + BK) * 2 > INT32_MAX) return hipErrorInvalidValue;
-    if (p.conv)
+    if (p.conv) {
         hipLaunchKernelGGL((project_kernel<BM, BN, BK, WM, WN, true>), dim3(static_cast<unsigned>(grid)),
                            dim3(64 * WM * WN), 0, s, p);
-    else
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t items = tiles_m * HALO * (static_cast<int64_t>(p.H) * (2 * p.dk + p.dv));
+        const int64_t blocks = (items + 255) / 256;
+        if (blocks > INT32_MAX) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(conv_tile_top_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, BM);
+    } else {
         hipLaunchKernelGGL((project_kernel<BM, BN, BK, WM, WN, false>), dim3(static_cast<unsigned>(grid)),
                            dim3(64 * WM * WN), 0, s, p);
+    }
     return hipGetLastError();
 }
 

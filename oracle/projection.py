@@ -41,8 +41,11 @@ def softplus(x):
 
 
 def sigmoid(x):
+    """The logistic function 1 / (1 + e^-x), written with e = e^-|x| so that
+    no exponential overflows and small values keep their relative precision."""
     x = np.asarray(x, np.float64)
-    return 0.5 * (1.0 + np.tanh(0.5 * x))
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
 
 
 def project(x, w, H: int, dk: int, dv: int):

@@ -130,3 +130,38 @@ def test_projections_feed_the_prefill():
     e_y = rel_l2(y, projection.output(r.out, w_o))
     say(f"  projections -> prefill -> output projection: out {e_o:.3e} state {e_s:.3e} y {e_y:.3e}")
     assert e_o <= 1e-2 and e_s <= 5e-3 and e_y <= 1e-2
+
+
+def test_routing_and_gate_maps_elementwise():
+    """One-hot rows of x make the GEMM exact: y[m][n] = W[n][m mod Dm], one
+    bf16 product.  q, k, v and z must then equal those weights bit for bit
+    (which pins the column routing), and g and beta are checked element by
+    element against the oracle's -softplus and logistic function of exactly
+    those pre-activations.  Bound: the fp32 maps evaluate exp(-|y|) as
+    exp2(-|y| log2 e); rounding the product costs the result up to |y| 2^-24
+    relative and the fp32 constant log2 e (0.22 2^-24 off) another
+    0.22 |y| 2^-24, to which exp2, the reciprocal and the log1p series add a
+    few ulp: |got - ref| <= (1.25 |y| + 8) 2^-24 |ref|."""
+    H, d, Dm, T = 2, 32, 64, 320
+    shape = wl.LayerShape(H, d, d)
+    N = projection.rows(H, d, d)
+    rng = np.random.default_rng(31)
+    w = np.concatenate([rng.uniform(-60.0, 40.0, (N, Dm // 2)), 3.0 * rng.standard_normal((N, Dm // 2))], 1)
+    w[:, 0] = 0.0
+    w = torch.from_numpy(w.astype(np.float32)).to(torch.bfloat16).double().numpy()   # exact bf16 values
+    x = np.zeros((T, Dm))
+    x[np.arange(T), np.arange(T) % Dm] = 1.0
+    o = run_gpu(shape, x, w)
+    ref = projection.project(x, w, H, d, d)
+    for name in ("q", "k", "v", "z"):
+        got = host(o[name])
+        assert np.array_equal(got, ref[name]), name
+    y_g = x @ w[2 * H * d + 2 * H * d:3 * H * d + 2 * H * d].T                 # gate pre-activations [T][H d]
+    y_b = x @ w[3 * H * d + 2 * H * d:].T                                      # beta pre-activations [T][H]
+    for name, y in (("g", y_g.reshape(T, H, d)), ("beta", y_b)):
+        got, r = host(o[name]), ref[name]
+        err = np.abs(got - r)
+        bound = (1.25 * np.abs(y) + 8.0) * 2.0 ** -24 * np.abs(r)
+        worst = float(np.max(err / np.maximum(np.abs(r), 1e-300)))
+        say(f"  {name}: worst relative error {worst:.3e}, worst error / bound {float(np.max(err / bound)):.3f}")
+        assert np.isfinite(got).all() and (err <= bound).all(), name

@@ -17,8 +17,8 @@
 // (rg, cg) owns rows rg*RPT .. rg*RPT+RPT-1 and columns 4cg..4cg+3, i.e. RPT
 // float4 registers.  Each load instruction of a wave reads whole rows
 // (NCG lanes x 16 bytes per row).  The two dk-reductions (S'^T k and S'^T q) go
-// through the thread's rows, then lane shuffles across row groups of a wave,
-// then LDS across waves.
+// through the thread's rows, then lane moves across row groups of a wave
+// (DPP and row swaps, no LDS), then LDS across waves.
 //
 // The readout uses o = S^T q = S'^T q + u (q . k) (S' the decayed state,
 // u the delta-rule update), so the state is read once and written once.
@@ -131,9 +131,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
         pk = fmaf(ak, ak, pk);
         pqk = fmaf(aq, ak, pqk);
     }
-    pq = xor_sum_below<64>(pq);
-    pk = xor_sum_below<64>(pk);
-    pqk = xor_sum_below<64>(pqk);
+    pq = lane_sum_below<64>(pq);
+    pk = lane_sum_below<64>(pk);
+    pqk = lane_sum_below<64>(pqk);
     if (lane == 0) {
         nrm_s[wave][0] = pq;
         nrm_s[wave][1] = pk;
@@ -165,10 +165,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
         rr.x = fmaf(s[r].x, qh, rr.x); rr.y = fmaf(s[r].y, qh, rr.y);
         rr.z = fmaf(s[r].z, qh, rr.z); rr.w = fmaf(s[r].w, qh, rr.w);
     }
-    pred.x = xor_sum_from<NCG>(pred.x); pred.y = xor_sum_from<NCG>(pred.y);
-    pred.z = xor_sum_from<NCG>(pred.z); pred.w = xor_sum_from<NCG>(pred.w);
-    rr.x = xor_sum_from<NCG>(rr.x); rr.y = xor_sum_from<NCG>(rr.y);
-    rr.z = xor_sum_from<NCG>(rr.z); rr.w = xor_sum_from<NCG>(rr.w);
+    pred.x = lane_sum_from<NCG>(pred.x); pred.y = lane_sum_from<NCG>(pred.y);
+    pred.z = lane_sum_from<NCG>(pred.z); pred.w = lane_sum_from<NCG>(pred.w);
+    rr.x = lane_sum_from<NCG>(rr.x); rr.y = lane_sum_from<NCG>(rr.y);
+    rr.z = lane_sum_from<NCG>(rr.z); rr.w = lane_sum_from<NCG>(rr.w);
     if (lane < NCG) {
         *reinterpret_cast<float4*>(&red_s[wave][0][4 * cg]) = pred;
         *reinterpret_cast<float4*>(&red_s[wave][1][4 * cg]) = rr;
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
 
     // 8. gated RMSNorm over dv (every row group holds all of o)
     float ss = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
-    ss = xor_sum_below<NCG>(ss);
+    ss = lane_sum_below<NCG>(ss);
     if (rg == 0) {
         const float rinv = rsqrtf(ss * (1.0f / DV) + p.rms_eps);
         const float4 zz = A::cvt4(zraw);
@@ -217,8 +217,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams p) {
     }
 }
 
-// Non-temporal 16-byte store (cache-policy bit NT): for data written once and
-// not read again by this launch or the next (the fp32 per-token rollback
+// Non-temporal 16- and 8-byte stores (cache-policy bit NT): for data written
+// once and not read again by this launch or the next (the per-token rollback
 // states of a multi-token step).  Without the hint that stream takes the place
 // of the live state in the last-level cache and the next step reads the state
 // from HBM again.  Bit 1 of the intrinsics' cache-policy operand is NT on gfx950.
@@ -230,6 +230,12 @@ __device__ __forceinline__ void buf_st4_nt(__amdgpu_buffer_rsrc_t r, uint32_t vo
     v.z = __float_as_int(x.z);
     v.w = __float_as_int(x.w);
     __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(voff), 0, kCachePolicyNT);
+}
+__device__ __forceinline__ void buf_st8_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint2 x) {
+    i32x2 v;
+    v.x = static_cast<int>(x.x);
+    v.y = static_cast<int>(x.y);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, static_cast<int>(voff), 0, kCachePolicyNT);
 }
 
 // T decode tokens per sequence in one launch (speculative verification: the
@@ -305,13 +311,25 @@ __global__ __launch_bounds__(NT) void decode_multi_kernel(DecodeParams p) {
     __builtin_amdgcn_sched_barrier(0);
     const auto rs = make_rsrc(static_cast<ST*>(p.state) + sh * DK * DV, DK * DV * SB);
     const uint32_t voff = static_cast<uint32_t>((rg * RPT * DV + 4 * cg) * SB);
-    float4 s[RPT];
+    // the state: fp32 in s; a bf16 state stays packed in sp (after every token
+    // it is exactly its bf16 rounding) and is widened and decayed where used,
+    // which halves its registers; the values are those of the fp32 form
+    constexpr int RS = SB == 4 ? RPT : 1, RP = SB == 2 ? RPT : 1;
+    float4 s[RS];
+    uint2 sp[RP];
 #pragma unroll
     for (int r = 0; r < RPT; r++) {
         if constexpr (SB == 4) s[r] = buf_ld4(rs, voff + (r % 8) * DV * 4, (r / 8) * 8 * DV * 4);
-        else s[r] = bf16x4_to_f32(buf_ld8(rs, voff + r * DV * 2));
+        else sp[r] = buf_ld8(rs, voff + r * DV * 2);
     }
     __builtin_amdgcn_sched_barrier(0);
+    auto decayed = [&](int r, float e) -> float4 {
+        float4 x;
+        if constexpr (SB == 4) x = s[r];
+        else x = bf16x4_to_f32(sp[r]);
+        x.x *= e; x.y *= e; x.z *= e; x.w *= e;
+        return x;
+    };
 
     for (int t = 0; t < T; t++) {
         // the next token's operands are requested now and used next iteration
@@ -362,9 +380,9 @@ __global__ __launch_bounds__(NT) void decode_multi_kernel(DecodeParams p) {
             pk = fmaf(ak, ak, pk);
             pqk = fmaf(aq, ak, pqk);
         }
-        pq = xor_sum_below<64>(pq);
-        pk = xor_sum_below<64>(pk);
-        pqk = xor_sum_below<64>(pqk);
+        pq = lane_sum_below<64>(pq);
+        pk = lane_sum_below<64>(pk);
+        pqk = lane_sum_below<64>(pqk);
         if (lane == 0) {
             nrm_s[wave][0] = pq;
             nrm_s[wave][1] = pk;
@@ -390,16 +408,23 @@ __global__ __launch_bounds__(NT) void decode_multi_kernel(DecodeParams p) {
             const float e = eg_s[i];
             const float kh = a_s[DK + i] * rk;
             const float qh = a_s[i] * rq;
-            s[r].x *= e; s[r].y *= e; s[r].z *= e; s[r].w *= e;
-            pred.x = fmaf(s[r].x, kh, pred.x); pred.y = fmaf(s[r].y, kh, pred.y);
-            pred.z = fmaf(s[r].z, kh, pred.z); pred.w = fmaf(s[r].w, kh, pred.w);
-            rr.x = fmaf(s[r].x, qh, rr.x); rr.y = fmaf(s[r].y, qh, rr.y);
-            rr.z = fmaf(s[r].z, qh, rr.z); rr.w = fmaf(s[r].w, qh, rr.w);
+            const float4 x = decayed(r, e);
+            if constexpr (SB == 4) s[r] = x;
+            pred.x = fmaf(x.x, kh, pred.x); pred.y = fmaf(x.y, kh, pred.y);
+            pred.z = fmaf(x.z, kh, pred.z); pred.w = fmaf(x.w, kh, pred.w);
+            rr.x = fmaf(x.x, qh, rr.x); rr.y = fmaf(x.y, qh, rr.y);
+            rr.z = fmaf(x.z, qh, rr.z); rr.w = fmaf(x.w, qh, rr.w);
         }
-        pred.x = xor_sum_from<NCG>(pred.x); pred.y = xor_sum_from<NCG>(pred.y);
-        pred.z = xor_sum_from<NCG>(pred.z); pred.w = xor_sum_from<NCG>(pred.w);
-        rr.x = xor_sum_from<NCG>(rr.x); rr.y = xor_sum_from<NCG>(rr.y);
-        rr.z = xor_sum_from<NCG>(rr.z); rr.w = xor_sum_from<NCG>(rr.w);
+        if constexpr (SB == 2) {
+            // widen again in the update below rather than keep the decayed
+            // fp32 rows alive across the reductions (no instruction emitted)
+#pragma unroll
+            for (int r = 0; r < RPT; r++) asm volatile("" : "+v"(sp[r].x), "+v"(sp[r].y));
+        }
+        pred.x = lane_sum_from<NCG>(pred.x); pred.y = lane_sum_from<NCG>(pred.y);
+        pred.z = lane_sum_from<NCG>(pred.z); pred.w = lane_sum_from<NCG>(pred.w);
+        rr.x = lane_sum_from<NCG>(rr.x); rr.y = lane_sum_from<NCG>(rr.y);
+        rr.z = lane_sum_from<NCG>(rr.z); rr.w = lane_sum_from<NCG>(rr.w);
         if (lane < NCG) {
             *reinterpret_cast<float4*>(&red_s[wave][0][4 * cg]) = pred;
             *reinterpret_cast<float4*>(&red_s[wave][1][4 * cg]) = rr;
@@ -429,23 +454,29 @@ __global__ __launch_bounds__(NT) void decode_multi_kernel(DecodeParams p) {
                                                       ((static_cast<int64_t>(b) * T + t) * H + h) * DK * DV
                                                 : static_cast<ST*>(p.state),
                                   p.token_state ? DK * DV * SB : 0u);
+        // the row offsets are formed here from an offset the compiler cannot
+        // hoist: hoisted out of the token loop they became RPT live VGPRs,
+        // here they fold into the stores' immediate offset field
+        uint32_t vo = voff;
+        asm volatile("" : "+v"(vo));
 #pragma unroll
         for (int r = 0; r < RPT; r++) {
             const float kh = a_s[DK + rg * RPT + r] * rk;
-            s[r].x = fmaf(kh, u.x, s[r].x); s[r].y = fmaf(kh, u.y, s[r].y);
-            s[r].z = fmaf(kh, u.z, s[r].z); s[r].w = fmaf(kh, u.w, s[r].w);
+            float4 x = SB == 4 ? s[RS > 1 ? r : 0] : decayed(r, eg_s[rg * RPT + r]);
+            x.x = fmaf(kh, u.x, x.x); x.y = fmaf(kh, u.y, x.y);
+            x.z = fmaf(kh, u.z, x.z); x.w = fmaf(kh, u.w, x.w);
             if constexpr (SB == 2) {
-                const uint2 hb = f32_to_bf16x4(s[r]);
-                s[r] = bf16x4_to_f32(hb);
-                if (p.token_state) buf_st8(rt, voff + r * DV * 2, hb);
+                sp[r] = f32_to_bf16x4(x);
+                if (p.token_state) buf_st8_nt(rt, vo + r * DV * 2, sp[r]);
             } else {
-                if (p.token_state) buf_st4_nt(rt, voff + r * DV * 4, s[r]);
+                s[r] = x;
+                if (p.token_state) buf_st4_nt(rt, vo + r * DV * 4, s[r]);
             }
         }
 
         // gated RMSNorm over dv
         float ss = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
-        ss = xor_sum_below<NCG>(ss);
+        ss = lane_sum_below<NCG>(ss);
         if (rg == 0) {
             const float rinv = rsqrtf(ss * (1.0f / DV) + p.rms_eps);
             const float4 zz = A::cvt4(zraw);
@@ -468,7 +499,7 @@ __global__ __launch_bounds__(NT) void decode_multi_kernel(DecodeParams p) {
 #pragma unroll
     for (int r = 0; r < RPT; r++) {
         if constexpr (SB == 4) buf_st4(rs, voff + r * DV * 4, s[r]);
-        else buf_st8(rs, voff + r * DV * 2, f32_to_bf16x4(s[r]));
+        else buf_st8(rs, voff + r * DV * 2, sp[r]);
     }
 #pragma unroll
     for (int j = 0; j < CPT; j++) {

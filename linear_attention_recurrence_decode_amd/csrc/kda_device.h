@@ -86,23 +86,6 @@ __device__ __forceinline__ float conv4(const float4& w, float a, float b, float 
     return fmaf(w.w, d, y);
 }
 
-// Sum over the lanes of a wave64 whose lane ids differ only in the bits of
-// [lo_mask, 64): e.g. lo = 32 sums lane l with lane l ^ 32.
-template <int LO>
-__device__ __forceinline__ float xor_sum_from(float x) {
-#pragma unroll
-    for (int off = LO; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
-    return x;
-}
-
-// Sum over the lanes whose ids differ only in bits below HI (HI a power of 2).
-template <int HI>
-__device__ __forceinline__ float xor_sum_below(float x) {
-#pragma unroll
-    for (int off = 1; off < HI; off <<= 1) x += __shfl_xor(x, off, 64);
-    return x;
-}
-
 // Sum over aligned groups of G lanes (G = 1, 2, 4, 8 or 16) with DPP lane
 // moves: swap neighbours, swap pairs, mirror within 8, mirror within 16.
 // Every lane of a group ends with the group's sum.
@@ -113,6 +96,48 @@ __device__ __forceinline__ float dpp_group_sum(float x) {
     if constexpr (G >= 4) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
     if constexpr (G >= 8) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
     if constexpr (G >= 16) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));
+    return x;
+}
+
+// x plus the value of lane l ^ 8: each row of 16 lanes rotated by 8 (DPP).
+__device__ __forceinline__ float add_lane_xor8(float x) {
+    return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+
+// x plus the value of lane l ^ 16, and of lane l ^ 32: the gfx950 row swaps
+// exchange odd rows of 16 (halves of 32) of one operand with even rows
+// (halves) of the other; with x in both, one holds the even row's value and
+// the other the odd row's in every lane, so both lanes of a pair add the same
+// two values in the same order.
+__device__ __forceinline__ float add_lane_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_lane_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over aligned groups of G lanes (G = 8, 16, 32 or 64); every lane of a
+// group ends with the same bits.  No LDS traffic and no index registers.
+template <int G>
+__device__ __forceinline__ float lane_sum_below(float x) {
+    static_assert(G == 8 || G == 16 || G == 32 || G == 64, "groups of 8 to 64 lanes");
+    x = dpp_group_sum<(G < 16 ? G : 16)>(x);
+    if constexpr (G >= 32) x = add_lane_xor16(x);
+    if constexpr (G >= 64) x = add_lane_xor32(x);
+    return x;
+}
+
+// Sum over the lanes of a wave64 whose ids differ only in the bits from LO
+// up (LO = 8, 16, 32 or 64; 64 is the identity): e.g. LO = 32 adds lanes l
+// and l ^ 32.
+template <int LO>
+__device__ __forceinline__ float lane_sum_from(float x) {
+    static_assert(LO == 8 || LO == 16 || LO == 32 || LO == 64, "lane bits from 8, 16, 32 or 64");
+    if constexpr (LO <= 8) x = add_lane_xor8(x);
+    if constexpr (LO <= 16) x = add_lane_xor16(x);
+    if constexpr (LO <= 32) x = add_lane_xor32(x);
     return x;
 }
 

@@ -265,6 +265,17 @@ __global__ __launch_bounds__(NT) void decode_multi_kernel(DecodeParams p) {
     __shared__ float eg_s[DK];
     __shared__ float red_s[NW][2][DV];
     __shared__ float nrm_s[NW][3];
+    // the small per-token operands of up to TG tokens, staged together so that
+    // one memory round trip serves TG tokens (the compute of one token is
+    // shorter than a round trip to HBM): per token q | k | v | z (ACT) then
+    // g (DK fp32) and beta (fp32, padded to 16 bytes)
+    constexpr int TG = 8;
+    constexpr int QC = DK * A::kBytes / 16, VC = DV * A::kBytes / 16, GC = DK * 4 / 16;
+    constexpr int OPC = 2 * QC + 2 * VC + GC;          // 16-byte chunks of one token
+    constexpr int OPB = OPC * 16;                       // bytes of one token's operands
+    static_assert(DK * A::kBytes % 16 == 0 && DV * A::kBytes % 16 == 0, "rows must be 16-byte multiples");
+    __shared__ __attribute__((aligned(16))) char op_s[TG * OPB];
+    __shared__ float bt_s[TG];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -283,30 +294,48 @@ __global__ __launch_bounds__(NT) void decode_multi_kernel(DecodeParams p) {
     }
     const int64_t sh = static_cast<int64_t>(slot) * H + h;
 
-    // conv window (raw, oldest first), weights, and the first token's operands
+    // operands of tokens t0 .. t0 + n - 1 into op_s, straight from global
+    // memory into LDS (16 bytes per lane; a wave instruction fills 1 KiB of
+    // consecutive chunks), no registers holding them; visible after the
+    // caller's wait and barrier
+    auto stage = [&](int t0, int n, int ln) {
+        constexpr int PER = (TG * OPC + NT - 1) / NT;
+#pragma unroll
+        for (int i = 0; i < PER; i++) {
+            const int e0 = (i * NW + wave) * 64;        // first chunk of this wave instruction
+            const int e = e0 + ln;
+            if (e0 < n * OPC && e < n * OPC) {
+                const int tt = e / OPC, c = e % OPC;
+                const int64_t row = (t0 + tt) * step + bh;
+                const uint4* src =
+                    c < QC ? reinterpret_cast<const uint4*>(static_cast<const ACT*>(p.q) + row * DK) + c
+                    : c < 2 * QC ? reinterpret_cast<const uint4*>(static_cast<const ACT*>(p.k) + row * DK) + (c - QC)
+                    : c < 2 * QC + VC ? reinterpret_cast<const uint4*>(static_cast<const ACT*>(p.v) + row * DV) + (c - 2 * QC)
+                    : c < 2 * QC + 2 * VC ? reinterpret_cast<const uint4*>(static_cast<const ACT*>(p.z) + row * DV) + (c - 2 * QC - VC)
+                    : reinterpret_cast<const uint4*>(p.g + row * DK) + (c - 2 * QC - 2 * VC);
+                __builtin_amdgcn_global_load_lds(src, reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                                          reinterpret_cast<uintptr_t>(op_s + e0 * 16)),
+                                                 16, 0, 0);
+            }
+        }
+        if (tid < n) bt_s[tid] = p.beta[(t0 + tid) * step + bh];
+    };
+    stage(0, min(T, TG), lane);
+
+    // conv window (raw, oldest first) and weights
     ACT* X = static_cast<ACT*>(p.conv) + sh * C * 3;
     const float* w = p.conv_w + static_cast<int64_t>(h) * C * 4;
-    typename A::raw xin[CPT], x0[CPT], x1[CPT], x2[CPT];
+    typename A::raw x0[CPT], x1[CPT], x2[CPT];
     float4 wc[CPT];
-    auto src_of = [&](int c, int t) -> const ACT* {
-        const int64_t o = t * step;
-        return c < DK ? static_cast<const ACT*>(p.q) + (o + bh) * DK + c
-                      : (c < 2 * DK ? static_cast<const ACT*>(p.k) + (o + bh) * DK + (c - DK)
-                                    : static_cast<const ACT*>(p.v) + (o + bh) * DV + (c - 2 * DK));
-    };
 #pragma unroll
     for (int j = 0; j < CPT; j++) {
         const int c = min(tid + j * NT, C - 1);
-        xin[j] = A::ld_raw(src_of(c, 0));
         x0[j] = A::ld_raw(X + c * 3);
         x1[j] = A::ld_raw(X + c * 3 + 1);
         x2[j] = A::ld_raw(X + c * 3 + 2);
         wc[j] = *reinterpret_cast<const float4*>(w + c * 4);
     }
-    float gv = p.g[bh * DK + min(tid, DK - 1)];
-    float bt = p.beta[bh];
     const float4 nw = *reinterpret_cast<const float4*>(p.norm_w + 4 * cg);
-    typename A::raw4 zraw = A::ld4_raw(static_cast<const ACT*>(p.z) + bh * DV + 4 * cg);
 
     __builtin_amdgcn_sched_barrier(0);
     const auto rs = make_rsrc(static_cast<ST*>(p.state) + sh * DK * DV, DK * DV * SB);
@@ -332,14 +361,28 @@ __global__ __launch_bounds__(NT) void decode_multi_kernel(DecodeParams p) {
     };
 
     for (int t = 0; t < T; t++) {
-        // the next token's operands are requested now and used next iteration
-        const int tn = min(t + 1, T - 1);
-        typename A::raw xin_n[CPT];
+        if (t % TG == 0) {
+            // every wave is past the previous group's last token (its closing
+            // barrier), so its slots may be overwritten
+            if (t > 0) {
+                // the lane index made opaque here, so that the copies' address
+                // arithmetic is formed in place rather than hoisted out of the
+                // token loop into live registers (no instruction emitted)
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
+                stage(t, min(T - t, TG), ln);
+            }
+            __builtin_amdgcn_s_waitcnt(0);              // this wave's copies have landed
+            __syncthreads();
+        }
+        const char* op = op_s + (t % TG) * OPB;
+        const ACT* op_a = reinterpret_cast<const ACT*>(op);      // q | k | v | z: conv channel c at c
+        typename A::raw xin[CPT];
 #pragma unroll
-        for (int j = 0; j < CPT; j++) xin_n[j] = A::ld_raw(src_of(min(tid + j * NT, C - 1), tn));
-        const float gv_n = p.g[(tn * step + bh) * DK + min(tid, DK - 1)];
-        const float bt_n = p.beta[tn * step + bh];
-        const typename A::raw4 zraw_n = A::ld4_raw(static_cast<const ACT*>(p.z) + (tn * step + bh) * DV + 4 * cg);
+        for (int j = 0; j < CPT; j++) xin[j] = A::ld_raw(op_a + min(tid + j * NT, C - 1));
+        const float gv = reinterpret_cast<const float*>(op + (2 * QC + 2 * VC) * 16)[min(tid, DK - 1)];
+        const float bt = bt_s[t % TG];
+        const typename A::raw4 zraw = A::ld4_raw(op_a + 2 * DK + DV + 4 * cg);
 
         // conv + SiLU; the window shifts in registers
 #pragma unroll
@@ -487,11 +530,6 @@ __global__ __launch_bounds__(NT) void decode_multi_kernel(DecodeParams p) {
             y.w = o.w * rinv * nw.w * sigmoid(zz.w);
             A::st4(out + t * step * DV + 4 * cg, y);
         }
-#pragma unroll
-        for (int j = 0; j < CPT; j++) xin[j] = xin_n[j];
-        gv = gv_n;
-        bt = bt_n;
-        zraw = zraw_n;
         __syncthreads();        // a_s, eg_s and the reduction buffers are reused
     }
 

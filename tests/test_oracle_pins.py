@@ -508,46 +508,40 @@ def test_conv_oracle_is_linear_in_the_weights_and_silu_closed_form():
     np.testing.assert_allclose(np.concatenate([aq, ak, av], axis=2), conv.silu(x), rtol=0, atol=0)
 
 
-# ---------------------------------------------------------------------------
-# projection oracle (oracle/projection.py): gate maps and column routing
 
-def test_projection_gate_maps_against_scipy_and_definitions():
-    """softplus against its definition log(1 + e^y) (written with log1p,
-    accurate in fp64 up to y = 30) and against scipy's log-sigmoid
-    (softplus(y) = -log_expit(-y)) over a wide range; sigmoid against
-    scipy's expit."""
-    from scipy.special import log_expit
-    from oracle import projection
-    y = np.linspace(-700.0, 700.0, 20001)
-    np.testing.assert_allclose(projection.softplus(y), -log_expit(-y), rtol=1e-14, atol=1e-300)
-    mid = np.linspace(-30.0, 30.0, 601)
-    np.testing.assert_allclose(projection.softplus(mid), np.log1p(np.exp(mid)), rtol=1e-13)
-    np.testing.assert_allclose(projection.sigmoid(y), expit(y), rtol=1e-13, atol=1e-300)
-    # softplus(y) - softplus(-y) = y, softplus(0) = log 2
-    np.testing.assert_allclose(projection.softplus(mid) - projection.softplus(-mid), mid, rtol=0, atol=1e-12)
-    assert projection.softplus(0.0) == np.log(2.0)
+def test_conv_oracle_brute_force_every_tap():
+    """Random weights on all four taps against scalar loops: tap j multiplies
+    the raw input 3 - j tokens back; a token before the sequence's first one
+    comes from the initial conv state, slot 3 - (start - token) (slot 2 is the
+    token just before the start)."""
+    from oracle import conv
+    x, X0, cu, H, C = _conv_case(11)
+    w = np.random.default_rng(12).standard_normal((H, C, 4))
+    y = conv.preactivation(x, w, cu, X0)
+    for n in range(len(cu) - 1):
+        s0 = int(cu[n])
+        for t in range(s0, int(cu[n + 1])):
+            for h in range(H):
+                for c in range(C):
+                    acc = 0.0
+                    for j in range(4):
+                        src = t - 3 + j                       # token feeding tap j
+                        val = x[src, h, c] if src >= s0 else X0[n, h, c, 3 - (s0 - src)]
+                        acc += w[h, c, j] * val
+                    assert abs(y[t, h, c] - acc) <= 1e-12, (n, t, h, c)
 
 
-def test_projection_routes_weight_rows_to_tensors():
-    """With x the identity, y = W^T, so every output element is one weight:
-    the rows of W are q (H dk), k (H dk), v (H dv), z (H dv), g (H dk) and
-    beta (H), each block head-major."""
-    from oracle import projection
-    H, dk, dv = 2, 3, 4
-    N = projection.rows(H, dk, dv)
-    assert N == H * (3 * dk + 2 * dv) + H
-    w = np.arange(N * N, dtype=np.float64).reshape(N, N) / (N * N) - 0.5
-    out = projection.project(np.eye(N), w, H, dk, dv)
-    o = 0
-    for name, width in (("q", dk), ("k", dk), ("v", dv), ("z", dv)):
-        for h in range(H):
-            for c in range(width):
-                np.testing.assert_array_equal(out[name][:, h, c], w[o + h * width + c])
-        o += H * width
-    for h in range(H):
-        for c in range(dk):
-            np.testing.assert_allclose(out["g"][:, h, c], -np.logaddexp(0.0, w[o + h * dk + c]), rtol=1e-14)
-    o += H * dk
-    for h in range(H):
-        np.testing.assert_allclose(out["beta"][:, h], expit(w[o + h]), rtol=1e-14)
-    assert (out["g"] < 0).all() and ((out["beta"] > 0) & (out["beta"] < 1)).all()
+def test_conv_oracle_split_sequence_invariance():
+    """A sequence cut in two gives the same pre-activations when the second
+    part starts from a conv state holding the first part's last three raw
+    inputs (the state a checkpoint at the cut stores)."""
+    from oracle import conv
+    rng = np.random.default_rng(13)
+    H, C, T, cut = 2, 5, 17, 7
+    x = rng.standard_normal((T, H, C))
+    X0 = rng.standard_normal((1, H, C, 3))
+    w = rng.standard_normal((H, C, 4))
+    whole = conv.preactivation(x, w, np.array([0, T]), X0)
+    X1 = np.transpose(x[cut - 3:cut], (1, 2, 0))[None]          # [1][H][C][3], oldest first
+    tail = conv.preactivation(x[cut:], w, np.array([0, T - cut]), X1)
+    np.testing.assert_allclose(tail, whole[cut:], rtol=0, atol=1e-13)

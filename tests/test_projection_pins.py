@@ -4,6 +4,7 @@ projection's loops and selection weights."""
 import math
 
 import numpy as np
+from scipy.special import expit, log_expit
 
 from oracle import projection
 
@@ -70,3 +71,43 @@ def test_output_projection_brute_force_and_selection():
     for h in range(H):
         for j in range(dv):
             np.testing.assert_array_equal(ys[:, j * H + h], o[:, h, j])
+
+
+
+def test_projection_gate_maps_against_scipy_and_definitions():
+    """softplus against its definition log(1 + e^y) (written with log1p,
+    accurate in fp64 up to y = 30) and against scipy's log-sigmoid
+    (softplus(y) = -log_expit(-y)) over a wide range; sigmoid against
+    scipy's expit."""
+    y = np.linspace(-700.0, 700.0, 20001)
+    np.testing.assert_allclose(projection.softplus(y), -log_expit(-y), rtol=1e-14, atol=1e-300)
+    mid = np.linspace(-30.0, 30.0, 601)
+    np.testing.assert_allclose(projection.softplus(mid), np.log1p(np.exp(mid)), rtol=1e-13)
+    np.testing.assert_allclose(projection.sigmoid(y), expit(y), rtol=1e-13, atol=1e-300)
+    # softplus(y) - softplus(-y) = y, softplus(0) = log 2
+    np.testing.assert_allclose(projection.softplus(mid) - projection.softplus(-mid), mid, rtol=0, atol=1e-12)
+    assert projection.softplus(0.0) == np.log(2.0)
+
+
+def test_projection_routes_weight_rows_to_tensors():
+    """With x the identity, y = W^T, so every output element is one weight:
+    the rows of W are q (H dk), k (H dk), v (H dv), z (H dv), g (H dk) and
+    beta (H), each block head-major."""
+    H, dk, dv = 2, 3, 4
+    N = projection.rows(H, dk, dv)
+    assert N == H * (3 * dk + 2 * dv) + H
+    w = np.arange(N * N, dtype=np.float64).reshape(N, N) / (N * N) - 0.5
+    out = projection.project(np.eye(N), w, H, dk, dv)
+    o = 0
+    for name, width in (("q", dk), ("k", dk), ("v", dv), ("z", dv)):
+        for h in range(H):
+            for c in range(width):
+                np.testing.assert_array_equal(out[name][:, h, c], w[o + h * width + c])
+        o += H * width
+    for h in range(H):
+        for c in range(dk):
+            np.testing.assert_allclose(out["g"][:, h, c], -np.logaddexp(0.0, w[o + h * dk + c]), rtol=1e-14)
+    o += H * dk
+    for h in range(H):
+        np.testing.assert_allclose(out["beta"][:, h], expit(w[o + h]), rtol=1e-14)
+    assert (out["g"] < 0).all() and ((out["beta"] > 0) & (out["beta"] < 1)).all()

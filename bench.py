@@ -570,7 +570,7 @@ def bench_long(steps, warmup, paired_leg=True, full=True):
     return res
 
 
-def bench_project(steps, warmup):
+def bench_project(steps, warmup, paired_leg=True):
     """The input projections of the 4 x 8192 prefill: one bf16 GEMM per call
     (the line's value); the output projection of the same tokens is timed
     after it and reported beside it."""
@@ -601,7 +601,8 @@ def bench_project(steps, warmup):
     del wcol
     # the conv front end (the causal conv + SiLU on q, k, v in the epilogue), and the
     # prefill of these tokens (4 sequences of 8192) after each front end
-    conv_res = conv_front_end(kda, wl, cfg, shape, xd, wd, q, k, v, z, g, beta, T, flops, steps, warmup, stream)
+    conv_res = conv_front_end(kda, wl, cfg, shape, xd, wd, q, k, v, z, g, beta, T, flops, steps, warmup, stream,
+                              paired_leg)
     del xd, wd, q, k, v, z, g, beta
     # the output projection of the same tokens: o [T][H][dv] -> y [T][Dm]
     o, wo = wl.output_projection_inputs(w["seed"], shape, T, Dm)
@@ -625,7 +626,7 @@ def bench_project(steps, warmup):
             "conv_front_end": conv_res}
 
 
-def conv_front_end(kda, wl, cfg, shape, xd, wd, q, k, v, z, g, beta, T, flops, steps, warmup, stream):
+def conv_front_end(kda, wl, cfg, shape, xd, wd, q, k, v, z, g, beta, T, flops, steps, warmup, stream, paired_leg=True):
     """kda_project_inputs_conv on the same x and W (the GEMM plus the causal
     conv and SiLU of q, k, v in its epilogue, post-conv and raw tensors
     written), then the 4 x 8192 prefill on each front end's outputs: the
@@ -656,7 +657,7 @@ def conv_front_end(kda, wl, cfg, shape, xd, wd, q, k, v, z, g, beta, T, flops, s
                    "(KDA_PREFILL_CONV_DONE) and after kda_project_inputs (unfused)",
            "ms_per_call": t_fe * 1e3, "TFLOP/s": flops / t_fe / 1e12, "prefill_ms": {}}
     for label, (qq, kk, vv), cd in (("unfused", (q, k, v), 0), ("conv_done", (q2, k2, v2), kda.KDA_PREFILL_CONV_DONE)):
-        for mode, fl in (("one_workgroup", 0), ("paired", kda.KDA_PREFILL_PAIRED)):
+        for mode, fl in (("one_workgroup", 0), ("paired", kda.KDA_PREFILL_PAIRED))[:2 if paired_leg else 1]:
             t = _time_calls(lambda: kda.kda_prefill_varlen(cfg, cu, qq, kk, vv, z, g, beta, cw, nw, S, X, init, fin,
                                                            out, ws, flags=fl | cd, stream=stream),
                             max(3, steps // 2), max(1, warmup), stream)
@@ -787,7 +788,7 @@ def main():
         del src, dst
     if args.workload != "decode_b64":
         if args.workload == "project_4x8k":
-            res = bench_project(args.steps, args.warmup)
+            res = bench_project(args.steps, args.warmup, paired_leg=not args.no_paired)
         else:
             res = bench_varlen(args.steps, args.warmup, paired_leg=not args.no_paired) \
                 if args.workload == "varlen_ckpt" else bench_long(args.steps, args.warmup, paired_leg=not args.no_paired)

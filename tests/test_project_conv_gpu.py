@@ -162,3 +162,69 @@ def test_conv_done_prefill_matches_oracle_and_unfused(name, mode):
     say(f"  vs unfused pipeline: out {e_u:.3e} state {e_us:.3e}")
     assert e_u <= 1e-2 and e_us <= 5e-3
     assert np.array_equal(bits(X), bits(X_u)) and np.array_equal(bits(ckX), bits(ckX_u))
+
+
+def test_front_end_full_size_sampled_rows():
+    """The conv front end on the 4 x 8192 token projections (Dm 7168, H=32,
+    d=128) as four packed sequences: one starting from an initial conv state,
+    one with none, one from a second state, one whose slot is out of range
+    (zero context, as in the prefill).  Raw halves bit-equal to
+    kda_project_inputs on every row; activations of sampled rows (the first
+    three rows of tiles, where the tile-top pass computes them, sequence
+    starts and random rows) against the conv oracle on the projection
+    oracle's rows, rounded to bf16.  Each sampled row's window is the oracle
+    run over the rows from max(start, m - 3) to m, from the sequence's
+    initial conv state when that range begins at its start."""
+    wk = wl.WORKLOADS["project_4x8k"]
+    shape, T, Dm = wk["shape"], wk["T"], wk["Dm"]
+    H, d = shape.H, shape.dk
+    bf = torch.bfloat16
+    x, w = wl.projection_inputs(wk["seed"], shape, T, Dm)
+    lengths = [T // 4] * 4
+    cu = wl.cu_seqlens(lengths)
+    conv_w = wl.token_inputs(wk["seed"], shape, 1).conv_w
+    _, X = wl.states(wk["seed"] + 1, shape, 2, conv_std=1.0)     # two slots of conv state
+    init = np.array([0, -1, 1, 7], np.int32)                       # 7 >= 2 slots: zero context
+    cfg = kda.Config(H, d, d, kda.KDA_BF16)
+    q2, k2, v2 = (torch.empty((2, T, H, d), dtype=bf, device="cuda") for _ in range(3))
+    z = torch.empty((T, H, d), dtype=bf, device="cuda")
+    g = torch.empty((T, H, d), device="cuda")
+    beta = torch.empty((T, H), device="cuda")
+    xd, wd = dev(x, bf), dev(w, bf)
+    kda.kda_project_inputs_conv(cfg, dev(cu.astype(np.int32)), xd, wd, dev(conv_w), dev(X, bf), dev(init),
+                                q2, k2, v2, z, g, beta)
+    torch.cuda.synchronize()
+    say(f"conv front end full size: T={T} Dm={Dm} H={H}; raw halves against kda_project_inputs")
+    q1, k1, v1 = (torch.empty((T, H, d), dtype=bf, device="cuda") for _ in range(3))
+    z1 = torch.empty_like(z)
+    g1, b1 = torch.empty_like(g), torch.empty_like(beta)
+    kda.kda_project_inputs(cfg, xd, wd, q1, k1, v1, z1, g1, b1)
+    torch.cuda.synchronize()
+    for name, a, b in (("q", q2[1], q1), ("k", k2[1], k1), ("v", v2[1], v1), ("z", z, z1), ("g", g, g1),
+                       ("beta", beta, b1)):
+        assert torch.equal(a.view(torch.int16) if a.dtype == bf else a.view(torch.int32),
+                           b.view(torch.int16) if b.dtype == bf else b.view(torch.int32)), name
+    del q1, k1, v1, z1, g1, b1
+    starts = [int(s) for s in cu[:-1]]
+    rng = np.random.default_rng(wk["seed"] + 2)
+    tops = [t + j for t in (256, 512, 8192 + 256, 3 * 8192 - 256, T - 256) for j in range(3)]
+    rows = sorted(set(tops + [s + j for s in starts for j in range(4)] + list(rng.choice(T, 24, replace=False))))
+    sel = torch.tensor(rows, device="cuda")
+    got = {n: host(t[0][sel]) for n, t in (("q", q2), ("k", k2), ("v", v2))}
+    want = {n: [] for n in got}
+    for m in rows:
+        n = int(np.searchsorted(cu, m, side="right")) - 1
+        s = starts[n]
+        lo = max(s, m - 3)
+        p = projection.project(x[lo:m + 1], w, H, d, d)
+        X0 = None
+        if lo == s and 0 <= init[n] < 2:
+            X0 = X[init[n]:init[n] + 1]
+        aq, ak, av = conv.activations(r16(p["q"]), r16(p["k"]), r16(p["v"]), conv_w, np.array([0, m + 1 - lo]), X0)
+        for name, a in (("q", aq), ("k", ak), ("v", av)):
+            want[name].append(a[-1])
+    for name in ("q", "k", "v"):
+        ref = np.stack(want[name])
+        e, e_r = rel_l2(got[name], ref), per_row_max(got[name], ref)
+        say(f"  {name}: {len(rows)} rows, rel-L2 {e:.3e}, worst row {e_r:.3e}")
+        assert np.isfinite(got[name]).all() and e <= 1e-2 and e_r <= tol_row("bf16"), name

@@ -546,6 +546,7 @@ struct PrefillLds {
     ACT vwin[sizeof(ACT) == 2 ? 1 : (CH + 3) * D];   // consumer's raw v rows (fp32 activations)
     int flag;
     int local;                 // the chunk takes the block-local decay path
+    int early;                 // consumer: this chunk's slot was requested during the previous epilogue
 };
 
 // A thread's 16 consecutive entries of K-^T row c (chunk rows 16 qq ..
@@ -639,6 +640,66 @@ __device__ __forceinline__ void ring_get2(__amdgpu_buffer_rsrc_t r, uint4* lds_w
 #pragma unroll
     for (int i = 0; i < FB; i++) lds_words[B0 + i * NT + tp] = wb[i];
     if (RB > 0 && tp < RB) lds_words[B0 + FB * NT + tp] = wb[FB];
+}
+
+// One 16-byte word per lane from a buffer straight into LDS with the ring's
+// device-coherent policy (buffer load with the LDS bit: lane l writes LDS
+// bytes [lds + 16 l, lds + 16 l + 16), so a wave instruction fills 64
+// consecutive words; no register holds the data).  The copy is asynchronous:
+// the wave waits for its vector memory count to drain, and the workgroup
+// meets at a barrier, before anyone reads the words.  Written as inline
+// assembly so that the compiler, which cannot tell which LDS bytes such a
+// copy writes, does not make unrelated LDS reads wait for it.
+__device__ __forceinline__ void ring_word_to_lds(i32x4 rsrc, uint32_t lds, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen sc1 lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ i32x4 raw_rsrc(const void* p, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    i32x4 r;
+    r[0] = static_cast<int32_t>(a);
+    r[1] = static_cast<int32_t>((a >> 32) & 0xffff);
+    r[2] = static_cast<int32_t>(bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(p)));
+}
+
+// The words ring_get2 loads ([0, NA) and [B0, B0 + NB)) and the NS sv words
+// from word S0 on, copied into LDS as ring_word_to_lds does: each wave takes
+// every NWV-th block of 64 words; lanes outside the ranges write nothing.
+// The resource, the LDS bases and the wave index are made wave-uniform
+// (scalar registers), as the copy's scalar operands must be.
+template <int NA, int B0, int NB, int NS, int S0, int NWV>
+__device__ __forceinline__ void ring_get2_async(const void* slot, uint32_t slot_bytes, void* planes, void* sv,
+                                                int wave, int lane) {
+    i32x4 r = raw_rsrc(slot, slot_bytes);
+#pragma unroll
+    for (int i = 0; i < 4; i++) r[i] = __builtin_amdgcn_readfirstlane(r[i]);
+    const uint32_t lp = __builtin_amdgcn_readfirstlane(lds_addr(planes));
+    const uint32_t ls = __builtin_amdgcn_readfirstlane(lds_addr(sv));
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll 1
+    for (int b = wv; b < (NA + 63) / 64; b += NWV) {
+        const int w = 64 * b + lane;
+        if (w < NA) ring_word_to_lds(r, lp + 1024 * b, 16 * w);
+    }
+#pragma unroll 1
+    for (int b = B0 / 64 + wv; b < (B0 + NB + 63) / 64; b += NWV) {
+        const int w = 64 * b + lane;
+        if (w >= B0 && w < B0 + NB) ring_word_to_lds(r, lp + 1024 * b, 16 * w);
+    }
+#pragma unroll 1
+    for (int b = wv; b < (NS + 63) / 64; b += NWV) {
+        const int w = 64 * b + lane;
+        if (w < NS) ring_word_to_lds(r, ls + 1024 * b, 16 * (S0 + w));
+    }
 }
 
 // A ring counter read ahead of need (one lane): the read takes a memory round
@@ -871,7 +932,10 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
         stage_issue<ACT, DK, DV, NT, NTEN>(stg, p, x0_s, ctx0, tc0, n, H, h, tp);
         stage_commit<ACT, DK, DV, NT, NTEN>(stg, raw, beta_s, tp);
     }
-    if (tid == 0) sm.local = 0;
+    if (tid == 0) {
+        sm.local = 0;
+        sm.early = 0;
+    }
     __syncthreads();
 
     // ---- block-local decay path, for chunks whose decay leaves the range of
@@ -1356,9 +1420,12 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             // into LDS and the v rows into vwin
             VWin<ACT, DV, NT> vw;
             vwin_issue<ACT, DV, NT>(vw, p, ctx0, tc0, n, H, h, opq(tid));
+            const bool early = sm.early;
+            if (!early) {
             if (tid == 0) sm.flag = ring_wait(ready_ctr, chunk + 1, seen, p.spin_limit, p.status);
             __syncthreads();
-            if (!sm.flag) {
+            }
+            if (!early && !sm.flag) {
                 // the producer is gone: NaN outputs from here on, and NaN in
                 // this head's state of every checkpoint still due and of the
                 // final slot, so that none of them passes for a valid state
@@ -1386,8 +1453,13 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             }
             {
                 const int tp = opq(tid);
-                ring_get2<NPA, PB0, NPB, NT>(rr, reinterpret_cast<uint4*>(lds), tp);
-                if (tp < NSV) reinterpret_cast<uint4*>(sm.sv)[tp] = ring_ld(rr, NPW + tp);
+                if (!early) {
+                    ring_get2<NPA, PB0, NPB, NT>(rr, reinterpret_cast<uint4*>(lds), tp);
+                    if (tp < NSV) reinterpret_cast<uint4*>(sm.sv)[tp] = ring_ld(rr, NPW + tp);
+                } else {
+                    // the slot's copies, issued after the previous chunk's phase B
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                }
                 vwin_commit<ACT, DK, DV, NT>(vw, vwin, x0_s, tp);
             }
             __syncthreads();
@@ -1409,6 +1481,10 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
                 }
             }
         }
+
+        // consumer: a fresh look at the producer's counter, returned during
+        // phase B, decides whether the next slot is requested right after it
+        if (ROLE == CONSUMER && tid == 0) seen = ring_peek(ready_ctr);
 
         // ---------------- B: state-dependent part; wave = 16-column strip of S
         f32x4 accr[4];     // readouts O (rows 16tb + 4g + e, this lane's column)
@@ -1515,12 +1591,29 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
                     }
             }
         }
-        __syncthreads();
-
-        // ---------------- next chunk's inputs: loads in flight during the epilogue
         const int done_next = done + n;
         const int64_t pos_next = pos + n;
         const int n_next = done_next < L ? min(L - done_next, CH - static_cast<int>(pos_next % CH)) : 0;
+        // consumer: when the next chunk was already published at the last
+        // look at its counter, its slot is requested now, straight into the
+        // planes (free once phase B is done), and lands during the epilogue
+        if (ROLE == CONSUMER && tid == 0) sm.early = n_next > 0 && seen >= chunk + 2;
+        __syncthreads();
+
+        if constexpr (ROLE == CONSUMER) {
+            if (sm.early) {
+                constexpr int NPW2 = Sh::BYTES / 16;
+                constexpr int NPA2 = (Sh::O1 + (kOutHi ? CH * PS * 2 : Sh::R1)) / 16;
+                constexpr int PB02 = Sh::O2 / 16;
+                constexpr int NPB2 = (Sh::O5 + (kOutHi ? CH * QS * 2 : Sh::R5)) / 16 - PB02;
+                constexpr int NSV2 = (CH + 3 * DK) / 4;
+                ring_get2_async<NPA2, PB02, NPB2, NSV2, NPW2, NW>(
+                    ring + ((chunk + 1) % RING) * pair_slot_bytes<D, ACT>(),
+                    static_cast<uint32_t>(pair_slot_bytes<D, ACT>()), lds, sm.sv, wave, lane);
+            }
+        }
+
+        // ---------------- next chunk's inputs: loads in flight during the epilogue
         if constexpr (ROLE == FUSED) {
             if (n_next > 0) stage_issue<ACT, DK, DV, NT, NTEN>(stg, p, x0_s, ctx0, tok0 + done_next, n_next, H, h, opq(tid));
             else stage_clear(stg);

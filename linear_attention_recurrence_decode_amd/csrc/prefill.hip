@@ -783,6 +783,18 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
     ACT* vwin = kOutHi ? reinterpret_cast<ACT*>(qp_l) : sm.vwin;
     static_assert(!kOutHi || (CH + 3) * DV * static_cast<int>(sizeof(ACT)) <= Sh::R1 - CH * PS * 2,
                   "the v rows fit in the Q+ lo plane");
+    // 16-byte words of a ring slot: the planes phase B reads, K+ and Q+ (words
+    // [0, NPA)), K-^T, L and P (words [PB0, PB0 + NPB)) -- with bf16 outputs
+    // phase B reads only the hi planes of Q+ and P -- then sv (NSV words
+    // from NPW on)
+    constexpr int NPW = Sh::BYTES / 16;
+    constexpr int NPA = (Sh::O1 + (kOutHi ? CH * PS * 2 : Sh::R1)) / 16;
+    constexpr int PB0 = Sh::O2 / 16;
+    constexpr int NPB = (Sh::O5 + (kOutHi ? CH * QS * 2 : Sh::R5)) / 16 - PB0;
+    static_assert(Sh::BYTES % 16 == 0 && Sh::O1 % 16 == 0 && Sh::O2 % 16 == 0 && Sh::O5 % 16 == 0 &&
+                  (CH * PS * 2) % 16 == 0 && (CH * QS * 2) % 16 == 0, "16-byte plane words");
+    constexpr int NSV = (CH + 3 * DK) / 4;
+    static_assert(NSV <= NT, "one sv word per thread");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -1370,17 +1382,6 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
         __syncthreads();
         }   // phase A
 
-        // 16-byte words of the planes phase B reads: K+ and Q+ (words
-        // [0, NPA)), K-^T, L and P (words [PB0, PB0 + NPB)); with bf16 outputs
-        // phase B reads only the hi planes of Q+ and P
-        constexpr int NPW = Sh::BYTES / 16;
-        constexpr int NPA = (Sh::O1 + (kOutHi ? CH * PS * 2 : Sh::R1)) / 16;
-        constexpr int PB0 = Sh::O2 / 16;
-        constexpr int NPB = (Sh::O5 + (kOutHi ? CH * QS * 2 : Sh::R5)) / 16 - PB0;
-        static_assert(Sh::BYTES % 16 == 0 && Sh::O1 % 16 == 0 && Sh::O2 % 16 == 0 && Sh::O5 % 16 == 0 &&
-                      (CH * PS * 2) % 16 == 0 && (CH * QS * 2) % 16 == 0, "16-byte plane words");
-        constexpr int NSV = (CH + 3 * DK) / 4;               // 16-byte words of sv
-        static_assert(NSV <= NT, "one sv word per thread");
         const auto rr = make_rsrc(rslot, static_cast<uint32_t>(pair_slot_bytes<D, ACT>()));
         if constexpr (ROLE == PRODUCER) {
             // hand the chunk over: wait until the consumer has taken the
@@ -1602,12 +1603,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
 
         if constexpr (ROLE == CONSUMER) {
             if (sm.early) {
-                constexpr int NPW2 = Sh::BYTES / 16;
-                constexpr int NPA2 = (Sh::O1 + (kOutHi ? CH * PS * 2 : Sh::R1)) / 16;
-                constexpr int PB02 = Sh::O2 / 16;
-                constexpr int NPB2 = (Sh::O5 + (kOutHi ? CH * QS * 2 : Sh::R5)) / 16 - PB02;
-                constexpr int NSV2 = (CH + 3 * DK) / 4;
-                ring_get2_async<NPA2, PB02, NPB2, NSV2, NPW2, NW>(
+                ring_get2_async<NPA, PB0, NPB, NSV, NPW, NW>(
                     ring + ((chunk + 1) % RING) * pair_slot_bytes<D, ACT>(),
                     static_cast<uint32_t>(pair_slot_bytes<D, ACT>()), lds, sm.sv, wave, lane);
             }

@@ -724,17 +724,17 @@ __device__ __forceinline__ bool ring_wait(const int32_t* ctr, int want, int seen
 
 // One (sequence, head) chain, or one segment of it, in the given role.
 // OUT: outputs, checkpoints and final states of whole sequences or segments.
-// !OUT (segment transitions, FUSED only): trans = false gives the segment's
-// end state from a zero state (G), trans = true its transition matrix
-// (F: the state propagated from the identity with v = 0).
+// !OUT (segment transitions, FUSED only): the segment's end state from a
+// zero state (G) and its transition matrix (F: the state propagated from the
+// identity with v = 0), side by side, sharing each chunk's state-independent
+// part.
 // CD (conv done): q, k and v each hold two tensors back to back, the
 // activations after the causal conv and SiLU (what phase A would compute
 // from the raw inputs, rounded to bf16) and the raw inputs; phase A then
 // takes the activations as they are, and the conv states written at
 // checkpoints and at the end still come from the raw inputs.
 template <int D, typename ACT, bool OUT, int ROLE, bool CD = false>
-__device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds<D, ACT>& sm, int item, const int h,
-                                              bool trans) {
+__device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds<D, ACT>& sm, int item, const int h) {
     static_assert(ROLE == FUSED || OUT, "paired roles produce outputs");
     using Sh = PrefillShape<D, ACT>;
     constexpr int DK = Sh::DK, DV = Sh::DV, NW = Sh::NW, NT = Sh::NT, C = Sh::C;
@@ -765,6 +765,10 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
     char* reg5 = opaque_lds(lds, Sh::O5);
     float* ak_f = reinterpret_cast<float*>(reg0);                // [CH][FP] fp32
     float* aq_f = reinterpret_cast<float*>(reg1);
+    // transition pass (no outputs, so no q): SiLU(conv(v)) of each thread,
+    // [16][NT] fp32, from phase A to phase B where the Q+ planes would be
+    float* vst = reinterpret_cast<float*>(reg1);
+    static_assert(16 * NT * 4 <= Sh::R1, "the v values fit in the Q+ region");
     uint16_t* kp_h = reinterpret_cast<uint16_t*>(reg0);          // K+ planes [CH][PS]
     uint16_t* kp_l = kp_h + CH * PS;
     uint16_t* qp_h = reinterpret_cast<uint16_t*>(reg1);          // Q+ planes
@@ -831,6 +835,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
 
     // ---- chain prologue: initial state (accumulator layout), conv state, weights
     f32x4 S[IB];
+    f32x4 SF[OUT ? 1 : IB];    // F's strip (transition pass only)
     {
         const uint32_t sv = static_cast<uint32_t>((4 * g4 * DV + jcol) * 4);
         const float* s0 = nullptr;          // fp32 source
@@ -858,7 +863,13 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
 #pragma unroll
             for (int ib = 0; ib < IB; ib++)
 #pragma unroll
-                for (int e = 0; e < 4; e++) S[ib][e] = (trans && 16 * ib + 4 * g4 + e == jcol) ? 1.f : 0.f;
+                for (int e = 0; e < 4; e++) S[ib][e] = 0.f;
+        }
+        if constexpr (!OUT) {
+#pragma unroll
+            for (int ib = 0; ib < IB; ib++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) SF[ib][e] = 16 * ib + 4 * g4 + e == jcol ? 1.f : 0.f;
         }
         const int64_t hx = (static_cast<int64_t>(seq) * H + h) * C * 3;
         const ACT* x0 = seg_in ? static_cast<const ACT*>(p.seq_x0) + hx
@@ -866,7 +877,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
                                             : nullptr);
         // the zero-start pass of a sequence's first segment keeps its initial
         // conv state for the segments' output pass
-        ACT* keep = (!OUT && !trans && wk.part == 0) ? static_cast<ACT*>(p.seq_x0) + hx : nullptr;
+        ACT* keep = (!OUT && wk.part == 0) ? static_cast<ACT*>(p.seq_x0) + hx : nullptr;
         for (int e = tid; e < C * 3; e += NT) {
             if (x0) x0_s[e] = x0[e];
             else A::st(&x0_s[e], 0.f);
@@ -1003,7 +1014,8 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
 #pragma unroll
                 for (int e = 0; e < 8; e += 4) {
                     *reinterpret_cast<float4*>(kr + e) = *reinterpret_cast<const float4*>(ak_f + R * FP + c0 + e);
-                    *reinterpret_cast<float4*>(qr + e) = *reinterpret_cast<const float4*>(aq_f + R * FP + c0 + e);
+                    if constexpr (OUT) *reinterpret_cast<float4*>(qr + e) = *reinterpret_cast<const float4*>(aq_f + R * FP + c0 + e);
+                    else *reinterpret_cast<float4*>(qr + e) = float4{0.f, 0.f, 0.f, 0.f};
                     *reinterpret_cast<float4*>(pr8 + e) = *reinterpret_cast<const float4*>(pi_f + R * FP + c0 + e);
                 }
                 const float sk = rk_s[R], sq = rq_s[R], bt = beta_s[R];
@@ -1052,7 +1064,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             for (int r = 0; r < 16; r++) {
                 const int t = 16 * qqp + r;
                 const float kh = ak_f[t * FP + cgp] * rk_s[t];
-                const float qh = aq_f[t * FP + cgp] * rq_s[t];
+                const float qh = OUT ? aq_f[t * FP + cgp] * rq_s[t] : 0.f;
                 const float E = __expf(gq[r]);
                 const float sl = tau - gq[r];
                 kp[r] = kh * E;
@@ -1162,8 +1174,9 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             float w1 = A::ld(raw + (r0 + 1) * CR + cqk);
             float w2 = A::ld(raw + (r0 + 2) * CR + cqk);
             float* dst = cqk < DK ? aq_f + cqk : ak_f + (cqk - DK);
+            // the transition pass needs no q
 #pragma unroll 4
-            for (int t = r0; t < r0 + 32; t++) {
+            for (int t = r0; t < ((OUT || cqk >= DK) ? r0 + 32 : r0); t++) {
                 const float w3 = A::ld(raw + (t + 3) * CR + cqk);
                 if constexpr (CD) {
                     dst[t * FP] = t < n ? w3 : 0.f;          // the activation itself
@@ -1190,14 +1203,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
                 for (int e = 0; e < 4; e++) {
                     const float y = conv4(wv, x[e], x[e + 1], x[e + 2], x[e + 3]);
                     vh[tb][e] = (rb + e) < n ? (CD ? x[e + 3] : silu(y)) : 0.f;
-                }
-            }
-            if constexpr (!OUT) {
-                if (trans) {
-#pragma unroll
-                    for (int tb = 0; tb < 4; tb++)
-#pragma unroll
-                        for (int e = 0; e < 4; e++) vh[tb][e] = 0.f;
+                    if constexpr (!OUT) vst[(4 * tb + e) * NT + tp] = vh[tb][e];
                 }
             }
         }
@@ -1211,17 +1217,19 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             const int pair = tp / PPT, part = tp % PPT;
             const int t = pair % CH;
             const float* src = (pair < CH ? aq_f : ak_f) + t * FP + part * SPAN;
-            float ssum = 0.f;
+            if (OUT || pair >= CH) {      // whole waves: the transition pass needs no q
+                float ssum = 0.f;
 #pragma unroll
-            for (int c = 0; c < SPAN; c += 4) {
-                const float4 a4 = *reinterpret_cast<const float4*>(src + c);
-                ssum = fmaf(a4.x, a4.x, ssum);
-                ssum = fmaf(a4.y, a4.y, ssum);
-                ssum = fmaf(a4.z, a4.z, ssum);
-                ssum = fmaf(a4.w, a4.w, ssum);
+                for (int c = 0; c < SPAN; c += 4) {
+                    const float4 a4 = *reinterpret_cast<const float4*>(src + c);
+                    ssum = fmaf(a4.x, a4.x, ssum);
+                    ssum = fmaf(a4.y, a4.y, ssum);
+                    ssum = fmaf(a4.z, a4.z, ssum);
+                    ssum = fmaf(a4.w, a4.w, ssum);
+                }
+                ssum = dpp_group_sum<PPT>(ssum);
+                if (part == 0) (pair < CH ? rq_s : rk_s)[t] = rsqrtf(ssum + p.l2_eps);
             }
-            ssum = dpp_group_sum<PPT>(ssum);
-            if (part == 0) (pair < CH ? rq_s : rk_s)[t] = rsqrtf(ssum + p.l2_eps);
 #pragma unroll
             for (int r = 1; r < 16; r++) gq[r] += gq[r - 1];
             gtot_s[tp / DK][tp % DK] = gq[15];
@@ -1274,7 +1282,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
                 const float d = (gq[r] + off) - gam_r;
                 const float E = __expf(d), Ei = __expf(-d);
                 const float kh = ak_f[t * FP + cgp] * rk_s[t];
-                const float qh = aq_f[t * FP + cgp] * rq_s[t];
+                const float qh = OUT ? aq_f[t * FP + cgp] * rq_s[t] : 0.f;
                 kp[r] = kh * E;
                 km[r] = kh * Ei;
                 qp[r] = qh * E;
@@ -1506,80 +1514,113 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
                     for (int e = 0; e < 4; e++)
                         zr[tb][e] = buf_ld_act<ACT>(rz, vo + static_cast<uint32_t>((16 * tb + e) * rowb), 0);
             }
-            f32x4 accx[4];
-#pragma unroll
-            for (int tb = 0; tb < 4; tb++) {
-                accx[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                accr[tb] = accx[tb];
-            }
-            // K_g S and Q_g S: the per-channel exp(Gam_r) goes onto S's rows.  K+ keeps
-            // about fp32 accuracy; with bf16 outputs Q+ (outputs only) is rounded once
-#pragma unroll
-            for (int ks = 0; ks < KS; ks++) {
-                float x[8];
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    x[e] = eGr_s[32 * ks + 4 * gg + e] * S[2 * ks][e];
-                    x[e + 4] = eGr_s[32 * ks + 16 + 4 * gg + e] * S[2 * ks + 1][e];
-                }
-                const Frag fs = split8(x);
+            // one state strip through the chunk: S (or, for the transition pass's F, the
+            // strip propagated from the identity, with v taken as zero)
+            auto state_step = [&](f32x4 (&Sx)[IB], bool zero_v, int o) {
+                // the LDS operands at offset o (elements): an offset the optimiser cannot
+                // see keeps the second strip's loads from being merged with the first's,
+                // whose values would otherwise stay in registers across both strips
+                const float* const eGr_s_o = eGr_s + o;
+                const float* const beta_s_o = beta_s + o;
+                const float* const eGC_s_o = eGC_s + o;
+                const float* const eGCr_s_o = eGCr_s + o;
+                const uint16_t* const kp_h_o = kp_h + o;
+                const uint16_t* const kp_l_o = kp_l + o;
+                const uint16_t* const qp_h_o = qp_h + o;
+                const uint16_t* const qp_l_o = qp_l + o;
+                const uint16_t* const lp_h_o = lp_h + o;
+                const uint16_t* const lp_l_o = lp_l + o;
+                const uint16_t* const pp_h_o = pp_h + o;
+                const uint16_t* const pp_l_o = pp_l + o;
+                const uint16_t* const kt_h_o = kt_h + o;
+                const uint16_t* const kt_l_o = kt_l + o;
+                const float* const vst_o = vst + o;
+                f32x4 accx[4];
 #pragma unroll
                 for (int tb = 0; tb < 4; tb++) {
-                    const int off = (16 * tb + lc) * PS + 32 * ks + 4 * gg;
-                    accx[tb] = mfma3(ld_perm(kp_h, kp_l, off), fs, accx[tb]);
-                    if constexpr (!OUT) continue;
-                    if constexpr (kOutHi) accr[tb] = mfma2(ld_perm_hi(qp_h, off), fs, accr[tb]);
-                    else accr[tb] = mfma3(ld_perm(qp_h, qp_l, off), fs, accr[tb]);
+                    accx[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    accr[tb] = accx[tb];
                 }
-            }
-            // Y = Diag(b) (V - K_g S)
-            f32x4 y[4];
+                // K_g S and Q_g S: the per-channel exp(Gam_r) goes onto S's rows.  K+ keeps
+                // about fp32 accuracy; with bf16 outputs Q+ (outputs only) is rounded once
 #pragma unroll
-            for (int tb = 0; tb < 4; tb++)
+                for (int ks = 0; ks < KS; ks++) {
+                    float x[8];
 #pragma unroll
-                for (int e = 0; e < 4; e++) y[tb][e] = beta_s[16 * tb + 4 * gg + e] * (vh[tb][e] - accx[tb][e]);
-            // U: solve (I + L) U = Y block by block, U_a = T_aa (Y_a - sum_{c<a} L_ac U_c)
-            Frag4 fu[4];
+                    for (int e = 0; e < 4; e++) {
+                        x[e] = eGr_s_o[32 * ks + 4 * gg + e] * Sx[2 * ks][e];
+                        x[e + 4] = eGr_s_o[32 * ks + 16 + 4 * gg + e] * Sx[2 * ks + 1][e];
+                    }
+                    const Frag fs = split8(x);
 #pragma unroll
-            for (int a = 0; a < 4; a++) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int c2 = 0; c2 < a; c2++)
-                    acc = mfma3_16(ld4(lp_h, lp_l, (16 * a + lc) * QS + 16 * c2 + 4 * gg), fu[c2], acc);
-                f32x4 r;
-#pragma unroll
-                for (int e = 0; e < 4; e++) r[e] = y[a][e] - acc[e];
-                const f32x4 ua = mfma3_16(ld4(lp_h, lp_l, (16 * a + lc) * QS + 16 * a + 4 * gg), split4(r),
-                                          f32x4{0.f, 0.f, 0.f, 0.f});
-                fu[a] = split4(ua);
-            }
-            const Frag fu0 = cat(fu[0], fu[1]);
-            const Frag fu1 = cat(fu[2], fu[3]);
-            // O = Q_g S + P U (with bf16 outputs, Q+ and P are rounded once to bf16)
-#pragma unroll
-            for (int tb = 0; tb < 4; tb++) {
-                if constexpr (!OUT) break;
-                const int row = (16 * tb + lc) * QS + 4 * gg;
-                if constexpr (kOutHi) {
-                    accr[tb] = mfma2(ld_perm_hi(pp_h, row), fu0, accr[tb]);
-                    if (tb >= 2) accr[tb] = mfma2(ld_perm_hi(pp_h, row + 32), fu1, accr[tb]);
-                } else {
-                    accr[tb] = mfma3(ld_perm(pp_h, pp_l, row), fu0, accr[tb]);
-                    if (tb >= 2) accr[tb] = mfma3(ld_perm(pp_h, pp_l, row + 32), fu1, accr[tb]);
+                    for (int tb = 0; tb < 4; tb++) {
+                        const int off = (16 * tb + lc) * PS + 32 * ks + 4 * gg;
+                        accx[tb] = mfma3(ld_perm(kp_h_o, kp_l_o, off), fs, accx[tb]);
+                        if constexpr (!OUT) continue;
+                        if constexpr (kOutHi) accr[tb] = mfma2(ld_perm_hi(qp_h_o, off), fs, accr[tb]);
+                        else accr[tb] = mfma3(ld_perm(qp_h_o, qp_l_o, off), fs, accr[tb]);
+                    }
                 }
-            }
-            // S = Diag(exp Gam_end) S + Diag(exp(Gam_end - Gam_r)) K-^T U
+                // Y = Diag(b) (V - K_g S)
+                f32x4 y[4];
 #pragma unroll
-            for (int ib = 0; ib < IB; ib++) {
-                const int row = (16 * ib + lc) * QS + 4 * gg;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mfma3(ld_perm(kt_h, kt_l, row), fu0, acc);
-                acc = mfma3(ld_perm(kt_h, kt_l, row + 32), fu1, acc);
+                for (int tb = 0; tb < 4; tb++)
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int i = 16 * ib + 4 * gg + e;
-                    S[ib][e] = fmaf(eGC_s[i], S[ib][e], eGCr_s[i] * acc[e]);
+                    for (int e = 0; e < 4; e++) {
+                        const float v = zero_v ? 0.f : (OUT ? vh[tb][e] : vst_o[(4 * tb + e) * NT + tp]);
+                        y[tb][e] = beta_s_o[16 * tb + 4 * gg + e] * (v - accx[tb][e]);
+                    }
+                // U: solve (I + L) U = Y block by block, U_a = T_aa (Y_a - sum_{c<a} L_ac U_c)
+                Frag4 fu[4];
+#pragma unroll
+                for (int a = 0; a < 4; a++) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int c2 = 0; c2 < a; c2++)
+                        acc = mfma3_16(ld4(lp_h_o, lp_l_o, (16 * a + lc) * QS + 16 * c2 + 4 * gg), fu[c2], acc);
+                    f32x4 r;
+#pragma unroll
+                    for (int e = 0; e < 4; e++) r[e] = y[a][e] - acc[e];
+                    const f32x4 ua = mfma3_16(ld4(lp_h_o, lp_l_o, (16 * a + lc) * QS + 16 * a + 4 * gg), split4(r),
+                                              f32x4{0.f, 0.f, 0.f, 0.f});
+                    fu[a] = split4(ua);
                 }
+                const Frag fu0 = cat(fu[0], fu[1]);
+                const Frag fu1 = cat(fu[2], fu[3]);
+                // O = Q_g S + P U (with bf16 outputs, Q+ and P are rounded once to bf16)
+#pragma unroll
+                for (int tb = 0; tb < 4; tb++) {
+                    if constexpr (!OUT) break;
+                    const int row = (16 * tb + lc) * QS + 4 * gg;
+                    if constexpr (kOutHi) {
+                        accr[tb] = mfma2(ld_perm_hi(pp_h_o, row), fu0, accr[tb]);
+                        if (tb >= 2) accr[tb] = mfma2(ld_perm_hi(pp_h_o, row + 32), fu1, accr[tb]);
+                    } else {
+                        accr[tb] = mfma3(ld_perm(pp_h_o, pp_l_o, row), fu0, accr[tb]);
+                        if (tb >= 2) accr[tb] = mfma3(ld_perm(pp_h_o, pp_l_o, row + 32), fu1, accr[tb]);
+                    }
+                }
+                // S = Diag(exp Gam_end) S + Diag(exp(Gam_end - Gam_r)) K-^T U
+#pragma unroll
+                for (int ib = 0; ib < IB; ib++) {
+                    const int row = (16 * ib + lc) * QS + 4 * gg;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    acc = mfma3(ld_perm(kt_h_o, kt_l_o, row), fu0, acc);
+                    acc = mfma3(ld_perm(kt_h_o, kt_l_o, row + 32), fu1, acc);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const int i = 16 * ib + 4 * gg + e;
+                        Sx[ib][e] = fmaf(eGC_s_o[i], Sx[ib][e], eGCr_s_o[i] * acc[e]);
+                    }
+                }
+            };
+            state_step(S, false, 0);
+            if constexpr (!OUT) {
+                // F's strip after G's: every G value is final before F's operands
+                // are requested (asm statements keep their order)
+#pragma unroll
+                for (int ib = 0; ib < IB; ib++) asm volatile("" : "+v"(S[ib]));
+                state_step(SF, true, opq(0));
             }
             // row sums of O^2 over this wave's 16 columns
             if constexpr (OUT) {
@@ -1691,25 +1732,19 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             write_conv_state(static_cast<ACT*>(p.conv) + sh * C * 3, tok0 + L);
         }
     } else {
-        float* dst = (trans ? p.seg_F : p.seg_G) + (static_cast<int64_t>(item) * H + h) * DK * DV;
-        store_state_strip<IB, DV>(dst, S, g4, jcol, DK);
+        const int64_t sh = (static_cast<int64_t>(item) * H + h) * DK * DV;
+        store_state_strip<IB, DV>(p.seg_G + sh, S, g4, jcol, DK);
+        store_state_strip<IB, DV>(p.seg_F + sh, SF, g4, jcol, DK);
     }
 }
 
-// One workgroup per chain (OUT), or per segment transition (!OUT): blocks
-// [0, items*H) give each segment's end state from a zero state (G), blocks
-// [items*H, 2*items*H) its transition matrix (F).
+// One workgroup per chain (OUT), or per segment transition (!OUT: its G and
+// F together).
 template <int D, typename ACT, bool OUT, bool CD>
 __global__ __launch_bounds__(4 * D) void prefill_kernel(PrefillParams p) {
     __shared__ PrefillLds<D, ACT> sm;
-    const int h = blockIdx.x % p.H;
-    int item = blockIdx.x / p.H;
-    bool trans = false;
-    if constexpr (!OUT) {
-        trans = item >= p.max_items;
-        if (trans) item -= p.max_items;
-    }
-    prefill_chain<D, ACT, OUT, FUSED, CD>(p, sm, item, h, trans);
+    const int b = static_cast<int>(blockIdx.x);
+    prefill_chain<D, ACT, OUT, FUSED, CD>(p, sm, b / p.H, b % p.H);
 }
 
 // A resident grid of G workgroups, launched cooperatively so that all of
@@ -1735,8 +1770,8 @@ __global__ __launch_bounds__(4 * D) void prefill_pair_kernel(PrefillParams p) {
     const int b = blockIdx.x;
     const int pair = 8 * (b / 16) + (b % 8);
     if (pair < K) {
-        if ((b % 16) < 8) prefill_chain<D, ACT, true, PRODUCER, CD>(p, sm, pair / p.H, pair % p.H, false);
-        else prefill_chain<D, ACT, true, CONSUMER, CD>(p, sm, pair / p.H, pair % p.H, false);
+        if ((b % 16) < 8) prefill_chain<D, ACT, true, PRODUCER, CD>(p, sm, pair / p.H, pair % p.H);
+        else prefill_chain<D, ACT, true, CONSUMER, CD>(p, sm, pair / p.H, pair % p.H);
         __syncthreads();
     }
     if constexpr (!QUEUE) return;
@@ -1746,7 +1781,7 @@ __global__ __launch_bounds__(4 * D) void prefill_pair_kernel(PrefillParams p) {
         const int chain = K + next_s;
         __syncthreads();
         if (chain >= NH) break;
-        prefill_chain<D, ACT, true, FUSED, CD>(p, sm, chain / p.H, chain % p.H, false);
+        prefill_chain<D, ACT, true, FUSED, CD>(p, sm, chain / p.H, chain % p.H);
         __syncthreads();
     }
 }
@@ -2027,8 +2062,7 @@ hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
     hipLaunchKernelGGL(prefill_split_meta_kernel, dim3(1), dim3(1024), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_kernel<D, ACT, false, CD>), dim3(static_cast<unsigned>(2 * items)), dim3(4 * D), 0, s,
-                       p);
+    hipLaunchKernelGGL((prefill_kernel<D, ACT, false, CD>), dim3(static_cast<unsigned>(items)), dim3(4 * D), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(segment_scan_kernel<D>, dim3(static_cast<unsigned>(static_cast<int64_t>(p.N) * p.H * (D / 16))),
                        dim3(256), 0, s, p);

@@ -340,10 +340,14 @@ __global__ __launch_bounds__(NT) void decode_multi_kernel(DecodeParams p) {
     __builtin_amdgcn_sched_barrier(0);
     const auto rs = make_rsrc(static_cast<ST*>(p.state) + sh * DK * DV, DK * DV * SB);
     const uint32_t voff = static_cast<uint32_t>((rg * RPT * DV + 4 * cg) * SB);
-    // the state: fp32 in s; a bf16 state stays packed in sp (after every token
-    // it is exactly its bf16 rounding) and is widened and decayed where used,
-    // which halves its registers; the values are those of the fp32 form
+    // the state: fp32 in s; a bf16 state stays packed in sp between tokens
+    // (after every token it is exactly its bf16 rounding), which halves its
+    // registers.  Within a token its rows are widened and decayed in the
+    // reductions and kept in xd for the update (KEEP), or, where those 64
+    // values would cost a wave per SIMD (fp32 activations at d = 128), widened
+    // and decayed again in the update; the values are those of the fp32 form
     constexpr int RS = SB == 4 ? RPT : 1, RP = SB == 2 ? RPT : 1;
+    constexpr bool KEEP = SB == 2 && !(sizeof(ACT) == 4 && DK == 128);
     float4 s[RS];
     uint2 sp[RP];
 #pragma unroll
@@ -445,6 +449,7 @@ __global__ __launch_bounds__(NT) void decode_multi_kernel(DecodeParams p) {
 
         // decay, then the two reductions over the decayed rows
         float4 pred = make_float4(0.f, 0.f, 0.f, 0.f), rr = pred;
+        float4 xd[KEEP ? RPT : 1];
 #pragma unroll
         for (int r = 0; r < RPT; r++) {
             const int i = rg * RPT + r;
@@ -453,12 +458,13 @@ __global__ __launch_bounds__(NT) void decode_multi_kernel(DecodeParams p) {
             const float qh = a_s[i] * rq;
             const float4 x = decayed(r, e);
             if constexpr (SB == 4) s[r] = x;
+            if constexpr (KEEP) xd[r] = x;
             pred.x = fmaf(x.x, kh, pred.x); pred.y = fmaf(x.y, kh, pred.y);
             pred.z = fmaf(x.z, kh, pred.z); pred.w = fmaf(x.w, kh, pred.w);
             rr.x = fmaf(x.x, qh, rr.x); rr.y = fmaf(x.y, qh, rr.y);
             rr.z = fmaf(x.z, qh, rr.z); rr.w = fmaf(x.w, qh, rr.w);
         }
-        if constexpr (SB == 2) {
+        if constexpr (SB == 2 && !KEEP) {
             // widen again in the update below rather than keep the decayed
             // fp32 rows alive across the reductions (no instruction emitted)
 #pragma unroll
@@ -505,7 +511,7 @@ __global__ __launch_bounds__(NT) void decode_multi_kernel(DecodeParams p) {
 #pragma unroll
         for (int r = 0; r < RPT; r++) {
             const float kh = a_s[DK + rg * RPT + r] * rk;
-            float4 x = SB == 4 ? s[RS > 1 ? r : 0] : decayed(r, eg_s[rg * RPT + r]);
+            float4 x = SB == 4 ? s[RS > 1 ? r : 0] : (KEEP ? xd[KEEP ? r : 0] : decayed(r, eg_s[rg * RPT + r]));
             x.x = fmaf(kh, u.x, x.x); x.y = fmaf(kh, u.y, x.y);
             x.z = fmaf(kh, u.z, x.z); x.w = fmaf(kh, u.w, x.w);
             if constexpr (SB == 2) {

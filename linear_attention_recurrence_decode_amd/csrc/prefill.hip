@@ -438,56 +438,6 @@ __device__ __forceinline__ void stage_clear(Staged<NU>& st) {
     st.beta = 0.f;
 }
 
-// The chunk's raw v rows for a consumer: CH + 3 rows of DV values (row 0 is
-// three tokens before the chunk [tc0, tc0 + n)), 16-byte word u of the rows
-// loaded by thread u % NT.  Rows before the sequence start come from the
-// initial conv state; rows past the chunk read as zero (outside the
-// resource) and only feed masked rows.
-template <typename ACT, int DV, int NT>
-struct VWin {
-    static constexpr int VEC = 16 / static_cast<int>(sizeof(ACT));
-    static constexpr int UPR = DV / VEC;                 // words per row
-    static constexpr int UNITS = (CH + 3) * UPR;
-    static constexpr int NI = (UNITS + NT - 1) / NT;
-    uint4 w[NI];    // loaded words of this thread
-    int d0;         // rows taken from the initial conv state
-};
-
-template <typename ACT, int DV, int NT>
-__device__ __forceinline__ void vwin_issue(VWin<ACT, DV, NT>& vw, const PrefillParams& p, int64_t ctx0,
-                                           int64_t tc0, int n, int H, int h, int tp) {
-    using VW = VWin<ACT, DV, NT>;
-    const int64_t first = max(tc0 - 3, ctx0);
-    const int d0 = static_cast<int>(first - (tc0 - 3));
-    vw.d0 = d0;
-    const auto rv = make_rsrc(static_cast<const ACT*>(p.v) + (first * H + h) * DV,
-                              static_cast<uint32_t>(((tc0 + n - 1 - first) * H + 1) * DV * sizeof(ACT)));
-    const uint32_t rowb = static_cast<uint32_t>(H * DV * sizeof(ACT));
-#pragma unroll
-    for (int i = 0; i < VW::NI; i++) {
-        const int u = tp + i * NT, r = u / VW::UPR, col = (u % VW::UPR) * VW::VEC;
-        const uint32_t vo = (u < VW::UNITS && r >= d0) ? static_cast<uint32_t>(r - d0) * rowb + col * sizeof(ACT)
-                                                       : 0x80000000u;
-        const float4 x = buf_ld4(rv, vo, 0);
-        vw.w[i] = make_uint4(__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z), __float_as_uint(x.w));
-    }
-}
-
-template <typename ACT, int DK, int DV, int NT>
-__device__ __forceinline__ void vwin_commit(const VWin<ACT, DV, NT>& vw, ACT* vwin, const ACT* x0, int tp) {
-    using VW = VWin<ACT, DV, NT>;
-    const int d0 = vw.d0;
-#pragma unroll
-    for (int i = 0; i < VW::NI; i++) {
-        const int u = tp + i * NT, r = u / VW::UPR, col = (u % VW::UPR) * VW::VEC;
-        if (u < VW::UNITS && r >= d0) *reinterpret_cast<uint4*>(vwin + r * DV + col) = vw.w[i];
-    }
-    for (int e = tp; e < d0 * DV; e += NT) {
-        const int r = e / DV, c = e % DV;
-        vwin[r * DV + c] = x0[(2 * DK + c) * 3 + 3 - d0 + r];
-    }
-}
-
 // Store the staged raw rows and beta into LDS (rows of CR elements: q, k, v).
 template <typename ACT, int DK, int DV, int NT, int NTEN, int NU>
 __device__ __forceinline__ void stage_commit(const Staged<NU>& st, ACT* raw, float* beta_s, int tp) {
@@ -669,6 +619,57 @@ __device__ __forceinline__ i32x4 raw_rsrc(const void* p, uint32_t bytes) {
 
 __device__ __forceinline__ uint32_t lds_addr(void* p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(p)));
+}
+
+// One 16-byte word of an input tensor per lane into LDS (M0 = the wave's
+// 1 KiB destination, lane l at + 16 l), no registers; an offset outside the
+// resource reads as zero.
+__device__ __forceinline__ void input_word_to_lds(i32x4 rsrc, uint32_t lds, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+
+// A consumer's raw v rows of the chunk [tc0, tc0 + n): CH + 3 rows of DV
+// values in vwin (row 0 is three tokens before the chunk), copied straight
+// from global memory into LDS, 16-byte word u by lane u % 64 of wave
+// (u / 64) % NWV.  Rows before the sequence start (packed index ctx0) and
+// rows past the chunk read as zero; the former are filled from the initial
+// conv state by vwin_fix once the copy has landed, the latter only feed
+// masked rows.  Complete after the issuing wave's vmcnt(0) and a barrier.
+template <typename ACT, int DV, int NWV>
+__device__ __forceinline__ void vwin_copy(const PrefillParams& p, ACT* vwin, int64_t ctx0, int64_t tc0, int n,
+                                          int H, int h, int wave, int lane) {
+    constexpr int VEC = 16 / static_cast<int>(sizeof(ACT));
+    constexpr int UPR = DV / VEC;                      // words per row
+    constexpr int UNITS = (CH + 3) * UPR;
+    const int64_t first = max(tc0 - 3, ctx0);
+    const int d0 = static_cast<int>(first - (tc0 - 3));
+    i32x4 r = raw_rsrc(static_cast<const ACT*>(p.v) + (first * H + h) * DV,
+                       static_cast<uint32_t>(((tc0 + n - 1 - first) * H + 1) * DV * sizeof(ACT)));
+#pragma unroll
+    for (int i = 0; i < 4; i++) r[i] = __builtin_amdgcn_readfirstlane(r[i]);
+    const uint32_t lv = __builtin_amdgcn_readfirstlane(lds_addr(vwin));
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t rowb = static_cast<uint32_t>(H * DV * sizeof(ACT));
+#pragma unroll 1
+    for (int b = wv; b < (UNITS + 63) / 64; b += NWV) {
+        const int u = 64 * b + lane, row = u / UPR, col = (u % UPR) * VEC;
+        const uint32_t vo = row >= d0 ? static_cast<uint32_t>(row - d0) * rowb + col * sizeof(ACT) : 0x80000000u;
+        if (u < UNITS) input_word_to_lds(r, lv + 1024 * b, vo);
+    }
+}
+
+// Rows of vwin before the sequence start, from the initial conv state x0
+// (after the copy has landed: its zeros would overwrite them).
+template <typename ACT, int DK, int DV, int NT>
+__device__ __forceinline__ void vwin_fix(ACT* vwin, const ACT* x0, int64_t ctx0, int64_t tc0, int tp) {
+    const int d0 = static_cast<int>(max(tc0 - 3, ctx0) - (tc0 - 3));
+    for (int e = tp; e < d0 * DV; e += NT) {
+        const int r = e / DV, c = e % DV;
+        vwin[r * DV + c] = x0[(2 * DK + c) * 3 + 3 - d0 + r];
+    }
 }
 
 // The words ring_get2 loads ([0, NA) and [B0, B0 + NB)) and the NS sv words
@@ -1424,11 +1425,11 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             continue;
         }
         if constexpr (ROLE == CONSUMER) {
-            // take the chunk over: request the chunk's raw v rows (with 3
-            // rows of left context), wait for the chunk, then planes and sv
-            // into LDS and the v rows into vwin
-            VWin<ACT, DV, NT> vw;
-            vwin_issue<ACT, DV, NT>(vw, p, ctx0, tc0, n, H, h, opq(tid));
+            // take the chunk over: the chunk's raw v rows (with 3 rows of
+            // left context) were requested into vwin during the previous
+            // chunk's epilogue (the first chunk's here); wait for the chunk,
+            // then planes and sv into LDS
+            if (chunk == 0) vwin_copy<ACT, DV, NW>(p, vwin, ctx0, tc0, n, H, h, wave, lane);
             const bool early = sm.early;
             if (!early) {
             if (tid == 0) sm.flag = ring_wait(ready_ctr, chunk + 1, seen, p.spin_limit, p.status);
@@ -1438,6 +1439,8 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
                 // the producer is gone: NaN outputs from here on, and NaN in
                 // this head's state of every checkpoint still due and of the
                 // final slot, so that none of them passes for a valid state
+                // (the v-row copy into LDS lands before the workgroup ends)
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 for (int64_t e = tid; e < static_cast<int64_t>(L - done) * DV; e += NT) {
                     const int64_t t = tc0 + e / DV;
                     A::st(out + (t * H + h) * DV + e % DV, nan_f32());
@@ -1465,11 +1468,11 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
                 if (!early) {
                     ring_get2<NPA, PB0, NPB, NT>(rr, reinterpret_cast<uint4*>(lds), tp);
                     if (tp < NSV) reinterpret_cast<uint4*>(sm.sv)[tp] = ring_ld(rr, NPW + tp);
-                } else {
-                    // the slot's copies, issued after the previous chunk's phase B
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 }
-                vwin_commit<ACT, DK, DV, NT>(vw, vwin, x0_s, tp);
+                // this wave's copies into LDS (the v rows, and with an early
+                // take-over the slot, issued after the previous chunk's phase B)
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                vwin_fix<ACT, DK, DV, NT>(vwin, x0_s, ctx0, tc0, tp);
             }
             __syncthreads();
             {
@@ -1648,6 +1651,8 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
                     ring + ((chunk + 1) % RING) * pair_slot_bytes<D, ACT>(),
                     static_cast<uint32_t>(pair_slot_bytes<D, ACT>()), lds, sm.sv, wave, lane);
             }
+            // the next chunk's v rows (vwin was last read before phase B)
+            if (n_next > 0) vwin_copy<ACT, DV, NW>(p, vwin, ctx0, tok0 + done_next, n_next, H, h, wave, lane);
         }
 
         // ---------------- next chunk's inputs: loads in flight during the epilogue

@@ -1,4 +1,4 @@
-"""A seeded random sweep of small prefill calls against the fp64 oracle.
+"""Seeded random sweeps of small prefill and decode calls against the fp64 oracle.
 
 Each case draws its own head size (32, 64, 128), activation dtype (fp32 at
 d <= 64), head count, packed sequences (empty, one to three tokens, one
@@ -12,14 +12,19 @@ draws are fixed by the sweep's seed, so the list of cases never changes.
 Checks, per case: outputs, final states and every checkpoint against the
 oracle (the parity bars of the other prefill tests; bf16-stored states to
 the bf16-state bars), conv states and conv checkpoints exactly, and for the
-paired launch the one-workgroup launch's results bit for bit.
+paired launch the one-workgroup launch's results bit for bit.  The decode
+sweep draws head size, dtypes, batch, tokens per launch (1 to 8), pool size
+and gate strength, checks T single-token steps against the oracle and one
+T-token launch against those steps bit for bit.
 """
 import numpy as np
 import pytest
 import torch
 
 import linear_attention_recurrence_decode_amd as kda
+import oracle
 import workloads as wl
+from tests.test_decode_multi_gpu import multi, setup, single_steps
 from tests.helpers import TOL_STATE_PER_CHAIN, bits, host, per_chain_max, per_row_max, rel_l2, say, tol_row, tols
 from tests.prefill_runner import Run, oracle_for, states_for
 
@@ -128,3 +133,58 @@ def test_sweep_case_matches_oracle(c):
         assert np.array_equal(bits(run.Sd), bits(one.Sd)) and np.array_equal(bits(run.Xd), bits(one.Xd))
         if run.nck:
             assert np.array_equal(bits(run.ckS[:run.nck]), bits(one.ckS[:run.nck]))
+
+
+# ---- decode: single steps and multi-token launches over random configurations
+
+def draw_decode_case(i):
+    rng = np.random.default_rng([SWEEP_SEED, 1000 + i])
+    d = int(rng.choice([32, 64, 128]))
+    act = "f32" if d <= 64 and rng.random() < 0.5 else "bf16"
+    B = int(rng.integers(1, 13))
+    return dict(idx=i, d=d, act=act, H=int(rng.integers(1, 5)), B=B, T=int(rng.integers(1, 9)),
+                pool=B + int(rng.integers(0, 7)), bf16_state=bool(rng.random() < 0.3),
+                g_scale=float(rng.choice([0.0, 0.05, 0.2, 1.0, 6.0])))
+
+
+DECODE_CASES = [draw_decode_case(i) for i in range(24)]
+
+
+def decode_case_id(c):
+    return (f"{c['idx']:02d}-d{c['d']}-{c['act']}-B{c['B']}-T{c['T']}-g{c['g_scale']}"
+            f"{'-bf16state' if c['bf16_state'] else ''}")
+
+
+@pytest.mark.parametrize("c", DECODE_CASES, ids=[decode_case_id(c) for c in DECODE_CASES])
+def test_sweep_decode_matches_oracle(c):
+    """T single-token steps against the oracle, and one T-token launch against
+    those steps bit for bit (outputs, states, conv states, per-token states)."""
+    shape = wl.LayerShape(c["H"], c["d"], c["d"], act=c["act"])
+    B, T = c["B"], c["T"]
+    say(f"sweep decode {decode_case_id(c)}: H={c['H']} pool={c['pool']}")
+    sdt = kda.KDA_BF16 if c["bf16_state"] else kda.KDA_F32
+    cfg, inp, S, X, slots, t = setup(shape, SWEEP_SEED % 100000 + 500 + c["idx"], B, T, c["pool"], sdt,
+                                     g_scale=c["g_scale"])
+    o1, S1, X1, after = single_steps(cfg, S, X, slots, t, T)
+    r = lambda a: a.reshape((T, B) + a.shape[1:])
+    o_ref, S_ref, X_ref = oracle.decode_steps(r(inp.q), r(inp.k), r(inp.v), r(inp.z), r(inp.g), r(inp.beta),
+                                              inp.conv_w, inp.norm_w, S[slots], X[slots],
+                                              state_round=c["bf16_state"])
+    if c["bf16_state"]:
+        tol_o, tol_s, tol_c = TOL_BF16_STATE_OUT, TOL_BF16_STATE, TOL_BF16_STATE_CHAIN
+    else:
+        tol_o, tol_s = tols(c["act"])
+        tol_c = TOL_STATE_PER_CHAIN
+    out, Sg = host(o1), host(S1)[slots]
+    e_o, e_r = rel_l2(out, o_ref), per_row_max(out, o_ref, 3)
+    e_s, e_c = rel_l2(Sg, S_ref), per_chain_max(Sg, S_ref)
+    say(f"  steps vs oracle: out {e_o:.3e} (worst row {e_r:.3e})  state {e_s:.3e} (worst chain {e_c:.3e})")
+    assert np.isfinite(out).all() and np.isfinite(Sg).all()
+    assert e_o <= tol_o and e_r <= tol_row(c["act"]) and e_s <= tol_s and e_c <= tol_c
+    np.testing.assert_array_equal(host(X1)[slots], X_ref)
+    o2, S2, X2, ts, tc = multi(cfg, S, X, slots, t, T)
+    assert np.array_equal(bits(o1), bits(o2))
+    assert np.array_equal(bits(S1), bits(S2)) and np.array_equal(bits(X1), bits(X2))
+    for s in range(T):
+        assert np.array_equal(bits(ts[:, s]), bits(after[s][0])), f"token state {s}"
+        assert np.array_equal(bits(tc[:, s]), bits(after[s][1])), f"token conv state {s}"

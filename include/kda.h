@@ -215,8 +215,10 @@ kda_status kda_decode_multi(const kda_config* cfg, int32_t B, int32_t T,
  *   segments' F and G are computed in parallel, a scan forms every segment's
  *   initial state in fp32, and the segments then run again from those states
  *   to produce their outputs.  The scan results are the interval checkpoints.
- *   About three times the arithmetic of the unsplit run, for parallelism over
- *   segments as well as sequences and heads; worth it when sequences x heads
+ *   About two and a half times the arithmetic of the unsplit run (each
+ *   chunk's state-independent work twice, its state phase three times: G, F
+ *   and the outputs), for parallelism over segments as well as sequences and
+ *   heads; worth it when sequences x heads
  *   is well below the number of compute units [vLLM blog, introduction:
  *   contexts of up to one million tokens].  Results agree with an unsplit run
  *   to fp32 rounding.  A run resumed from one of its interval checkpoints with

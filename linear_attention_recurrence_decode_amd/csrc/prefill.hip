@@ -197,25 +197,24 @@ __device__ __forceinline__ Frag ld_nat(const uint16_t* hi, const uint16_t* lo, i
     return Frag{a.v, b.v};
 }
 
-// Elements [off, off+4) and [off+16, off+20): the permuted contraction order.
-__device__ __forceinline__ Frag ld_perm(const uint16_t* hi, const uint16_t* lo, int off) {
-    U128 a, b;
-    const uint2 a0 = *reinterpret_cast<const uint2*>(hi + off);
-    const uint2 a1 = *reinterpret_cast<const uint2*>(hi + off + 16);
-    const uint2 b0 = *reinterpret_cast<const uint2*>(lo + off);
-    const uint2 b1 = *reinterpret_cast<const uint2*>(lo + off + 16);
-    a.u = make_uint4(a0.x, a0.y, a1.x, a1.y);
-    b.u = make_uint4(b0.x, b0.y, b1.x, b1.y);
-    return Frag{a.v, b.v};
+// The hi plane only of ld_nat.
+__device__ __forceinline__ bf16x8 ld_nat_hi(const uint16_t* hi, int off) {
+    U128 a;
+    a.u = *reinterpret_cast<const uint4*>(hi + off);
+    return a.v;
 }
 
-// The hi plane only of ld_perm.
-__device__ __forceinline__ bf16x8 ld_perm_hi(const uint16_t* hi, int off) {
-    U128 a;
-    const uint2 a0 = *reinterpret_cast<const uint2*>(hi + off);
-    const uint2 a1 = *reinterpret_cast<const uint2*>(hi + off + 16);
-    a.u = make_uint4(a0.x, a0.y, a1.x, a1.y);
-    return a.v;
+// Storage order of the planes that phase B reads as MFMA A operands (K+, Q+
+// and K- along dk; P and K-^T along the chunk rows).  Phase B's B operands
+// come straight from 16x16 accumulator tiles: lane group g holds rows 4g ..
+// 4g+3 of two stacked tiles, that is contraction indices {4g..4g+3,
+// 16+4g..16+4g+3} of a group of 32.  Each group of 32 is stored in the order
+// that puts those eight side by side -- index 16h + 4g + e at 8g + 4h + e --
+// so a lane's A fragment is one 16-byte read.  The intra-chunk products
+// contract K+ and Q+ with K- over dk and read both operands in this stored
+// order, which pairs the same indices.
+__device__ __forceinline__ constexpr int pcol(int j) {
+    return (j & ~31) | (((j >> 2) & 3) << 3) | (((j >> 4) & 1) << 2) | (j & 3);
 }
 
 // 4 consecutive elements of a plane pair.
@@ -500,18 +499,19 @@ struct PrefillLds {
 };
 
 // A thread's 16 consecutive entries of K-^T row c (chunk rows 16 qq ..
-// 16 qq + 15) into the hi/lo planes: two 16-byte stores per plane.
+// 16 qq + 15) into the hi/lo planes, in pcol order: four 8-byte stores per
+// plane, at 8g + 4 (qq & 1) of the row's group of 32 for rows 4g .. 4g + 3.
 template <int QS>
 __device__ __forceinline__ void st_kt(uint16_t* kt_h, uint16_t* kt_l, int c, int qq, const float (&km)[16]) {
     uint32_t wh[8], wl[8];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) split2(km[r], km[r + 1], wh[r / 2], wl[r / 2]);
-    uint4* dh = reinterpret_cast<uint4*>(kt_h + c * QS + 16 * qq);
-    uint4* dl = reinterpret_cast<uint4*>(kt_l + c * QS + 16 * qq);
-    dh[0] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
-    dh[1] = make_uint4(wh[4], wh[5], wh[6], wh[7]);
-    dl[0] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
-    dl[1] = make_uint4(wl[4], wl[5], wl[6], wl[7]);
+    const int o = c * QS + pcol(16 * qq);
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+        *reinterpret_cast<uint2*>(kt_h + o + 8 * g) = make_uint2(wh[2 * g], wh[2 * g + 1]);
+        *reinterpret_cast<uint2*>(kt_l + o + 8 * g) = make_uint2(wl[2 * g], wl[2 * g + 1]);
+    }
 }
 
 // Roles of a chain's workgroup.  FUSED runs both phases of every chunk.  In a
@@ -1040,7 +1040,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
                     if (part == 0) {
                         const float kn = rk_s[S2];
                         ld_s[a][rl][sl] = sl < rl ? bt * (m * sk * kn) : 0.f;
-                        if constexpr (OUT) st_split1(pp_h, plo, R * QS + S2, pp * sq * kn);
+                        if constexpr (OUT) st_split1(pp_h, plo, R * QS + pcol(S2), pp * sq * kn);
                     }
                 }
             }
@@ -1050,7 +1050,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
                 const int rl = first ? pr : 15 - pr;
                 const int sl = first ? pr + 1 + e : 1 + e;
                 ld_s[a][rl][sl] = 0.f;
-                if constexpr (OUT) st_split1(pp_h, plo, (16 * a + rl) * QS + 16 * a + sl, 0.f);
+                if constexpr (OUT) st_split1(pp_h, plo, (16 * a + rl) * QS + pcol(16 * a + sl), 0.f);
             }
         }
         __syncthreads();
@@ -1081,7 +1081,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             __syncthreads();
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
-                const int idx = (16 * qqp + r) * PS + cgp;
+                const int idx = (16 * qqp + r) * PS + pcol(cgp);
                 st_split2(kp_h, kp_l, idx, PS, kp[r], kp[r + 1]);
                 if constexpr (OUT) st_split2(qp_h, qp_l, idx, PS, qp[r], qp[r + 1]);
                 st_split2(km_h, km_l, idx, PS, kb[r], kb[r + 1]);
@@ -1102,7 +1102,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
                 if constexpr (OUT) {
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
-                        const int idx = (16 * a + 4 * gg + e) * QS + 16 * b + lc;
+                        const int idx = (16 * a + 4 * gg + e) * QS + pcol(16 * b + lc);
                         pp_h[idx] = 0;
                         if constexpr (!kOutHi) pp_l[idx] = 0;
                     }
@@ -1117,7 +1117,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
                     float d[8];
 #pragma unroll
                     for (int e = 0; e < 8; e++) {
-                        const int c = 32 * ks + 8 * gg + e;
+                        const int c = 32 * ks + 16 * (e >> 2) + 4 * gg + (e & 3);   // channel at 8 gg + e (pcol order)
                         float s2 = gtot_s[b + 1][c];
                         if (a == b + 3) s2 += gtot_s[b + 2][c];
                         d[e] = __expf(s2);
@@ -1129,13 +1129,13 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             }
 #pragma unroll
             for (int e = 0; e < 4; e += 2) {
-                const int t = 16 * a + 4 * gg + e, s2 = 16 * b + lc;
+                const int t = 16 * a + 4 * gg + e, s2 = 16 * b + lc, s2p = pcol(s2);
                 if constexpr (OUT && kOutHi) {
                     const uint32_t hw = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{ap[e], ap[e + 1]}, bf16x2));
-                    pp_h[t * QS + s2] = static_cast<uint16_t>(hw);
-                    pp_h[(t + 1) * QS + s2] = static_cast<uint16_t>(hw >> 16);
+                    pp_h[t * QS + s2p] = static_cast<uint16_t>(hw);
+                    pp_h[(t + 1) * QS + s2p] = static_cast<uint16_t>(hw >> 16);
                 } else if constexpr (OUT) {
-                    st_split2(pp_h, pp_l, t * QS + s2, QS, ap[e], ap[e + 1]);
+                    st_split2(pp_h, pp_l, t * QS + s2p, QS, ap[e], ap[e + 1]);
                 }
                 st_split2(lp_h, lp_l, t * QS + s2, QS, beta_s[t] * am[e], beta_s[t + 1] * am[e + 1]);
             }
@@ -1151,7 +1151,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
         const float E = __expf(pre);
 #pragma unroll
         for (int r = 0; r < 16; r++) {
-            const int idx = (16 * qqp + r) * PS + cgp;
+            const int idx = (16 * qqp + r) * PS + pcol(cgp);
             st_split1(kp_h, kp_l, idx, ld_pair(kp_h, kp_l, idx) * E);
             if constexpr (OUT) st_split1(qp_h, qp_l, idx, ld_pair(qp_h, qp_l, idx) * E);
         }
@@ -1296,7 +1296,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             __syncthreads();
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
-                const int idx = (16 * qqp + r) * PS + cgp;
+                const int idx = (16 * qqp + r) * PS + pcol(cgp);
                 st_split2(kp_h, kp_l, idx, PS, kp[r], kp[r + 1]);
                 if constexpr (OUT) st_split2(qp_h, qp_l, idx, PS, qp[r], qp[r + 1]);
                 st_split2(km_h, km_l, idx, PS, km[r], km[r + 1]);
@@ -1320,7 +1320,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
                     if constexpr (OUT) {
 #pragma unroll
                         for (int e = 0; e < 4; e++) {
-                            const int idx = (16 * a + 4 * gg + e) * QS + 16 * b + lc;
+                            const int idx = (16 * a + 4 * gg + e) * QS + pcol(16 * b + lc);
                             pp_h[idx] = 0;
                             if constexpr (!kOutHi) pp_l[idx] = 0;   // with bf16 outputs only P's hi plane is read
                         }
@@ -1337,16 +1337,16 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
                 }
 #pragma unroll
                 for (int e = 0; e < 4; e += 2) {
-                    const int t = 16 * a + 4 * gg + e, s2 = 16 * b + lc;
+                    const int t = 16 * a + 4 * gg + e, s2 = 16 * b + lc, s2p = pcol(s2);
                     if constexpr (OUT && kOutHi) {
                         // hi plane only (the same rounding as split2's hi)
                         const uint32_t hw = __builtin_bit_cast(
                             uint32_t, __builtin_convertvector(f32x2{t >= s2 ? ap[e] : 0.f, t + 1 >= s2 ? ap[e + 1] : 0.f},
                                                               bf16x2));
-                        pp_h[t * QS + s2] = static_cast<uint16_t>(hw);
-                        pp_h[(t + 1) * QS + s2] = static_cast<uint16_t>(hw >> 16);
+                        pp_h[t * QS + s2p] = static_cast<uint16_t>(hw);
+                        pp_h[(t + 1) * QS + s2p] = static_cast<uint16_t>(hw >> 16);
                     } else if constexpr (OUT) {
-                        st_split2(pp_h, pp_l, t * QS + s2, QS, t >= s2 ? ap[e] : 0.f, t + 1 >= s2 ? ap[e + 1] : 0.f);
+                        st_split2(pp_h, pp_l, t * QS + s2p, QS, t >= s2 ? ap[e] : 0.f, t + 1 >= s2 ? ap[e + 1] : 0.f);
                     }
                     if (a > b) {
                         st_split2(lp_h, lp_l, t * QS + s2, QS, beta_s[t] * am[e], beta_s[t + 1] * am[e + 1]);
@@ -1557,11 +1557,11 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
                     const Frag fs = split8(x);
 #pragma unroll
                     for (int tb = 0; tb < 4; tb++) {
-                        const int off = (16 * tb + lc) * PS + 32 * ks + 4 * gg;
-                        accx[tb] = mfma3(ld_perm(kp_h_o, kp_l_o, off), fs, accx[tb]);
+                        const int off = (16 * tb + lc) * PS + 32 * ks + 8 * gg;
+                        accx[tb] = mfma3(ld_nat(kp_h_o, kp_l_o, off), fs, accx[tb]);
                         if constexpr (!OUT) continue;
-                        if constexpr (kOutHi) accr[tb] = mfma2(ld_perm_hi(qp_h_o, off), fs, accr[tb]);
-                        else accr[tb] = mfma3(ld_perm(qp_h_o, qp_l_o, off), fs, accr[tb]);
+                        if constexpr (kOutHi) accr[tb] = mfma2(ld_nat_hi(qp_h_o, off), fs, accr[tb]);
+                        else accr[tb] = mfma3(ld_nat(qp_h_o, qp_l_o, off), fs, accr[tb]);
                     }
                 }
                 // Y = Diag(b) (V - K_g S)
@@ -1594,22 +1594,22 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
 #pragma unroll
                 for (int tb = 0; tb < 4; tb++) {
                     if constexpr (!OUT) break;
-                    const int row = (16 * tb + lc) * QS + 4 * gg;
+                    const int row = (16 * tb + lc) * QS + 8 * gg;
                     if constexpr (kOutHi) {
-                        accr[tb] = mfma2(ld_perm_hi(pp_h_o, row), fu0, accr[tb]);
-                        if (tb >= 2) accr[tb] = mfma2(ld_perm_hi(pp_h_o, row + 32), fu1, accr[tb]);
+                        accr[tb] = mfma2(ld_nat_hi(pp_h_o, row), fu0, accr[tb]);
+                        if (tb >= 2) accr[tb] = mfma2(ld_nat_hi(pp_h_o, row + 32), fu1, accr[tb]);
                     } else {
-                        accr[tb] = mfma3(ld_perm(pp_h_o, pp_l_o, row), fu0, accr[tb]);
-                        if (tb >= 2) accr[tb] = mfma3(ld_perm(pp_h_o, pp_l_o, row + 32), fu1, accr[tb]);
+                        accr[tb] = mfma3(ld_nat(pp_h_o, pp_l_o, row), fu0, accr[tb]);
+                        if (tb >= 2) accr[tb] = mfma3(ld_nat(pp_h_o, pp_l_o, row + 32), fu1, accr[tb]);
                     }
                 }
                 // S = Diag(exp Gam_end) S + Diag(exp(Gam_end - Gam_r)) K-^T U
 #pragma unroll
                 for (int ib = 0; ib < IB; ib++) {
-                    const int row = (16 * ib + lc) * QS + 4 * gg;
+                    const int row = (16 * ib + lc) * QS + 8 * gg;
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                    acc = mfma3(ld_perm(kt_h_o, kt_l_o, row), fu0, acc);
-                    acc = mfma3(ld_perm(kt_h_o, kt_l_o, row + 32), fu1, acc);
+                    acc = mfma3(ld_nat(kt_h_o, kt_l_o, row), fu0, acc);
+                    acc = mfma3(ld_nat(kt_h_o, kt_l_o, row + 32), fu1, acc);
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
                         const int i = 16 * ib + 4 * gg + e;

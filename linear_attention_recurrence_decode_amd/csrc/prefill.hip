@@ -1371,11 +1371,18 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
             float xk[KPP];
 #pragma unroll
             for (int kk = 0; kk < KPP; kk++) xk[kk] = 0.f;
+            // this thread's entries of the block, all requested before the
+            // substitution so that its 16 dependent steps do not each wait for LDS
+            float lb[16][KPP];
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+#pragma unroll
+                for (int kk = 0; kk < KPP; kk++) lb[r][kk] = ld_s[blk][r][part * KPP + kk];
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 float c2 = 0.f;
 #pragma unroll
-                for (int kk = 0; kk < KPP; kk++) c2 = fmaf(ld_s[blk][r][part * KPP + kk], xk[kk], c2);
+                for (int kk = 0; kk < KPP; kk++) c2 = fmaf(lb[r][kk], xk[kk], c2);
                 const float sdot = dpp_group_sum<PARTS>(c2);
                 const float xr = r < col ? 0.f : (r == col ? 1.f : -sdot);
 #pragma unroll

@@ -41,7 +41,8 @@
 // l%16).  Contractions over a 32-index block use the permuted order
 // {4g..4g+3, 16+4g..16+4g+3} for lane group g, which is exactly what two
 // stacked accumulator tiles hold, so S, Y and U feed the MFMA B operand from
-// registers; the LDS operand reads the same permutation.  Every product uses
+// registers; the LDS operand planes are stored in that order (pcol), so a
+// lane's fragment is one 16-byte read.  Every product uses
 // three bf16 MFMAs (hi*hi + hi*lo + lo*hi), i.e. about fp32 accuracy.
 // The gated RMSNorm epilogue, checkpoint writes and the final state write are
 // fused into the same kernel.

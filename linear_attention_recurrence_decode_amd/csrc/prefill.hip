@@ -172,6 +172,24 @@ __device__ __forceinline__ void st_split2(uint16_t* hi, uint16_t* lo, int idx, i
     lo[idx + stride] = static_cast<uint16_t>(l >> 16);
 }
 
+// Rows r and r+1 (values a, b) of one channel into a plane pair whose
+// channel c and c+1 (c even) sit side by side, as 32-bit words: the lanes of
+// channels c and c+1 (lanes l and l^1) swap half words, the even lane then
+// stores row r and the odd lane row r+1 of both channels.  idx is the
+// element of (row r, this lane's channel); all lanes of the wave take part.
+__device__ __forceinline__ void st_split2_x2(uint16_t* hi, uint16_t* lo, int idx, int stride, float a, float b,
+                                            bool odd) {
+    uint32_t h, l;
+    split2(a, b, h, l);
+    const uint32_t ph = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(h), 0xB1, 0xF, 0xF, false));
+    const uint32_t pl = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(l), 0xB1, 0xF, 0xF, false));
+    // even: (own row r, partner's row r); odd: (partner's row r+1, own row r+1)
+    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+    const int at = odd ? idx + stride - 1 : idx;
+    *reinterpret_cast<uint32_t*>(hi + at) = __builtin_amdgcn_perm(ph, h, sel);
+    *reinterpret_cast<uint32_t*>(lo + at) = __builtin_amdgcn_perm(pl, l, sel);
+}
+
 // One element of a plane pair (the lo plane skipped when lo is null).
 __device__ __forceinline__ void st_split1(uint16_t* hi, uint16_t* lo, int idx, float a) {
     uint32_t h, l;
@@ -1295,12 +1313,13 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
                 eGC_s[cgp] = __expf(gam_c);
             }
             __syncthreads();
+            const bool odd = cgp & 1;
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
                 const int idx = (16 * qqp + r) * PS + pcol(cgp);
-                st_split2(kp_h, kp_l, idx, PS, kp[r], kp[r + 1]);
-                if constexpr (OUT) st_split2(qp_h, qp_l, idx, PS, qp[r], qp[r + 1]);
-                st_split2(km_h, km_l, idx, PS, km[r], km[r + 1]);
+                st_split2_x2(kp_h, kp_l, idx, PS, kp[r], kp[r + 1], odd);
+                if constexpr (OUT) st_split2_x2(qp_h, qp_l, idx, PS, qp[r], qp[r + 1], odd);
+                st_split2_x2(km_h, km_l, idx, PS, km[r], km[r + 1], odd);
             }
         }
         after_planes();

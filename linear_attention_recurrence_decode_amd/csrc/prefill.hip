@@ -373,75 +373,81 @@ struct StageMap {
     }
 };
 
-// Issue the global loads of the chunk [tc0, tc0+n) of head h (no waits).
-// Left-context rows before the sequence start (first packed token ctx0) come
-// from the initial conv state x0 (index 2 = the token just before the start).
-template <typename ACT, int DK, int DV, int NT, int NTEN, int NU>
+// Issue the global loads of the chunk [tc0, tc0+n) of head h (no waits): the
+// raw q, k (and v) rows (ROWS) and the log-decays and beta (GATES), which a
+// caller may request at different points.  Left-context rows before the
+// sequence start (first packed token ctx0) come from the initial conv state
+// x0 (index 2 = the token just before the start).
+template <typename ACT, int DK, int DV, int NT, int NTEN, bool ROWS = true, bool GATES = true, int NU>
 __device__ __forceinline__ void stage_issue(Staged<NU>& st, const PrefillParams& p, const ACT* x0,
                                             int64_t ctx0, int64_t tc0, int n, int H, int h, int tp) {
     static_assert(DK == DV, "one row layout for q, k and v");
     using M = StageMap<ACT, DK, NT, NTEN>;
     static_assert(M::NU == NU, "staging slots");
-    constexpr int D = DK;
-    const int wv = __builtin_amdgcn_readfirstlane(tp >> 6), lane = tp & 63;
-    // resources start at the first row inside the sequence; rows before it
-    // (and rows past the chunk) fall outside and read as zero
-    const int64_t first = max(tc0 - 3, ctx0);
-    const int d0 = static_cast<int>(first - (tc0 - 3));                // 0..3 rows of context from x0
-    const int64_t hoff = (first * H + h) * D;
-    const uint32_t nbytes = static_cast<uint32_t>(((tc0 + n - 1 - first) * H + 1) * D * sizeof(ACT));
-    const uint32_t rowb = static_cast<uint32_t>(H * D * sizeof(ACT));
-    const ACT* tens[3] = {static_cast<const ACT*>(p.q), static_cast<const ACT*>(p.k), static_cast<const ACT*>(p.v)};
-#pragma unroll
-    for (int j = 0; j < NU; j++) {
-        const typename M::Unit u = M::unit(j, wv, lane);
-        st.val[j] = make_uint4(0, 0, 0, 0);
-        const int tsel = __builtin_amdgcn_readfirstlane(u.tensor);
-        if (tsel < NTEN) {
-            const auto rs = make_rsrc(tens[tsel] + hoff, nbytes);
-            const int rel = u.r - d0;
-            const uint32_t vo = (u.valid && rel >= 0) ? static_cast<uint32_t>(rel) * rowb + u.col * sizeof(ACT)
-                                                      : 0x80000000u;
-            const float4 x = buf_ld4(rs, vo, 0);
-            st.val[j] = make_uint4(__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z),
-                                   __float_as_uint(x.w));
-        }
-    }
-    if (d0 > 0) {
-        // context rows before the sequence start: raw values from x0
+    if constexpr (ROWS) {
+        constexpr int D = DK;
+        const int wv = __builtin_amdgcn_readfirstlane(tp >> 6), lane = tp & 63;
+        // resources start at the first row inside the sequence; rows before it
+        // (and rows past the chunk) fall outside and read as zero
+        const int64_t first = max(tc0 - 3, ctx0);
+        const int d0 = static_cast<int>(first - (tc0 - 3));                // 0..3 rows of context from x0
+        const int64_t hoff = (first * H + h) * D;
+        const uint32_t nbytes = static_cast<uint32_t>(((tc0 + n - 1 - first) * H + 1) * D * sizeof(ACT));
+        const uint32_t rowb = static_cast<uint32_t>(H * D * sizeof(ACT));
+        const ACT* tens[3] = {static_cast<const ACT*>(p.q), static_cast<const ACT*>(p.k), static_cast<const ACT*>(p.v)};
 #pragma unroll
         for (int j = 0; j < NU; j++) {
             const typename M::Unit u = M::unit(j, wv, lane);
-            if (u.valid && u.r < d0) {
-                const int m = 3 - d0 + u.r;                 // x0 index of this token
-                const int c0 = u.tensor * D + u.col;
-                uint32_t wd[4];
+            st.val[j] = make_uint4(0, 0, 0, 0);
+            const int tsel = __builtin_amdgcn_readfirstlane(u.tensor);
+            if (tsel < NTEN) {
+                const auto rs = make_rsrc(tens[tsel] + hoff, nbytes);
+                const int rel = u.r - d0;
+                const uint32_t vo = (u.valid && rel >= 0) ? static_cast<uint32_t>(rel) * rowb + u.col * sizeof(ACT)
+                                                          : 0x80000000u;
+                const float4 x = buf_ld4(rs, vo, 0);
+                st.val[j] = make_uint4(__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z),
+                                       __float_as_uint(x.w));
+            }
+        }
+        if (d0 > 0) {
+            // context rows before the sequence start: raw values from x0
 #pragma unroll
-                for (int q4 = 0; q4 < 4; q4++) {
-                    const int c = c0 + q4 * (M::VEC / 4);
-                    if constexpr (sizeof(ACT) == 2) {
-                        wd[q4] = static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(x0)[c * 3 + m]) |
-                                 (static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(x0)[(c + 1) * 3 + m]) << 16);
-                    } else {
-                        wd[q4] = __float_as_uint(reinterpret_cast<const float*>(x0)[c * 3 + m]);
+            for (int j = 0; j < NU; j++) {
+                const typename M::Unit u = M::unit(j, wv, lane);
+                if (u.valid && u.r < d0) {
+                    const int m = 3 - d0 + u.r;                 // x0 index of this token
+                    const int c0 = u.tensor * D + u.col;
+                    uint32_t wd[4];
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; q4++) {
+                        const int c = c0 + q4 * (M::VEC / 4);
+                        if constexpr (sizeof(ACT) == 2) {
+                            wd[q4] = static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(x0)[c * 3 + m]) |
+                                     (static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(x0)[(c + 1) * 3 + m]) << 16);
+                        } else {
+                            wd[q4] = __float_as_uint(reinterpret_cast<const float*>(x0)[c * 3 + m]);
+                        }
                     }
+                    st.val[j] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
                 }
-                st.val[j] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
             }
         }
     }
-    // row t of this head at byte offset t * row_bytes; the resources end after
-    // row n-1 and the whole offset is in the range-checked per-lane offset, so
-    // rows past the chunk read as zero
-    const int cgp = tp % DK, qqp = tp / DK;
-    const auto rg = make_rsrc(p.g + (tc0 * H + h) * DK, static_cast<uint32_t>(((n - 1) * H + 1) * DK * 4));
-    const uint32_t gv = static_cast<uint32_t>((16 * qqp * H * DK + cgp) * 4);
+    if constexpr (GATES) {
+        // row t of this head at byte offset t * row_bytes; the resources end after
+        // row n-1 and the whole offset is in the range-checked per-lane offset, so
+        // rows past the chunk read as zero
+        const int cgp = tp % DK, qqp = tp / DK;
+        const auto rg = make_rsrc(p.g + (tc0 * H + h) * DK, static_cast<uint32_t>(((n - 1) * H + 1) * DK * 4));
+        const uint32_t gv = static_cast<uint32_t>((16 * qqp * H * DK + cgp) * 4);
 #pragma unroll
-    for (int r = 0; r < 16; r++) st.gq[r] = buf_ldf(rg, gv + static_cast<uint32_t>(r * H * DK * 4), 0);
-    st.beta = 0.f;
-    if (tp < CH) {
-        const auto rb = make_rsrc(p.beta + tc0 * H + h, static_cast<uint32_t>(((n - 1) * H + 1) * 4));
-        st.beta = buf_ldf(rb, static_cast<uint32_t>(tp * H * 4), 0);
+        for (int r = 0; r < 16; r++) st.gq[r] = buf_ldf(rg, gv + static_cast<uint32_t>(r * H * DK * 4), 0);
+        st.beta = 0.f;
+        if (tp < CH) {
+            const auto rb = make_rsrc(p.beta + tc0 * H + h, static_cast<uint32_t>(((n - 1) * H + 1) * 4));
+            st.beta = buf_ldf(rb, static_cast<uint32_t>(tp * H * 4), 0);
+        }
     }
 }
 
@@ -1275,7 +1281,9 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
                 }
                 const int done_next = done + n;
                 n_next_p = done_next < L ? min(L - done_next, CH - static_cast<int>((pos + n) % CH)) : 0;
-                if (n_next_p > 0) stage_issue<ACT, DK, DV, NT, NTEN>(stg, p, x0_s, ctx0, tok0 + done_next, n_next_p, H, h, opq(tid));
+                // the raw rows now, the gates before A6: requested together they
+                // stall the issue for want of room among the misses in flight
+                if (n_next_p > 0) stage_issue<ACT, DK, DV, NT, NTEN, true, false>(stg, p, x0_s, ctx0, tok0 + done_next, n_next_p, H, h, opq(tid));
                 else stage_clear(stg);
             }
         };
@@ -1386,6 +1394,10 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
         {
             const int tp = opq(tid);
             if (tp == 0) sm.local = 0;                   // read after A3: free for the next chunk
+            if constexpr (ROLE == PRODUCER) {
+                if (n_next_p > 0)
+                    stage_issue<ACT, DK, DV, NT, NTEN, false, true>(stg, p, x0_s, ctx0, tok0 + done + n, n_next_p, H, h, tp);
+            }
             constexpr int PARTS = NT / 64, KPP = 16 / PARTS;
             const int part = tp % PARTS, col = (tp / PARTS) % 16, blk = tp / (16 * PARTS);
             float xk[KPP];

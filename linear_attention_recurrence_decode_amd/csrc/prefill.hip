@@ -1394,9 +1394,15 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
         {
             const int tp = opq(tid);
             if (tp == 0) sm.local = 0;                   // read after A3: free for the next chunk
+            // the next chunk's log-decays and beta (its raw rows follow A4 in a
+            // producer, phase B in one workgroup per chain)
             if constexpr (ROLE == PRODUCER) {
                 if (n_next_p > 0)
                     stage_issue<ACT, DK, DV, NT, NTEN, false, true>(stg, p, x0_s, ctx0, tok0 + done + n, n_next_p, H, h, tp);
+            } else if constexpr (ROLE == FUSED) {
+                const int dn = done + n;
+                const int nn = dn < L ? min(L - dn, CH - static_cast<int>((pos + n) % CH)) : 0;
+                if (nn > 0) stage_issue<ACT, DK, DV, NT, NTEN, false, true>(stg, p, x0_s, ctx0, tok0 + dn, nn, H, h, tp);
             }
             constexpr int PARTS = NT / 64, KPP = 16 / PARTS;
             const int part = tp % PARTS, col = (tp / PARTS) % 16, blk = tp / (16 * PARTS);
@@ -1696,7 +1702,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams& p, PrefillLds
 
         // ---------------- next chunk's inputs: loads in flight during the epilogue
         if constexpr (ROLE == FUSED) {
-            if (n_next > 0) stage_issue<ACT, DK, DV, NT, NTEN>(stg, p, x0_s, ctx0, tok0 + done_next, n_next, H, h, opq(tid));
+            if (n_next > 0) stage_issue<ACT, DK, DV, NT, NTEN, true, false>(stg, p, x0_s, ctx0, tok0 + done_next, n_next, H, h, opq(tid));
             else stage_clear(stg);
         } else {
             // every read of this slot is complete (its values fed phase B):

@@ -31,7 +31,7 @@ from tests.prefill_runner import Run, oracle_for, states_for
 pytestmark = pytest.mark.gpu
 
 SWEEP_SEED = 20261203
-N_CASES = 48
+N_CASES = 96
 # bf16-stored states: the bars of the bf16-state tests
 TOL_BF16_STATE_OUT, TOL_BF16_STATE, TOL_BF16_STATE_CHAIN = 1e-2, 5e-3, 2e-3
 
@@ -147,7 +147,7 @@ def draw_decode_case(i):
                 g_scale=float(rng.choice([0.0, 0.05, 0.2, 1.0, 6.0])))
 
 
-DECODE_CASES = [draw_decode_case(i) for i in range(24)]
+DECODE_CASES = [draw_decode_case(i) for i in range(48)]
 
 
 def decode_case_id(c):

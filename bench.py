@@ -19,6 +19,9 @@ step).  The line also carries:
                 MiB, standing in for consecutive layers, so each launch reads
                 its state from HBM, not from the 256 MB Infinity Cache), and a
                 2 GiB read+write copy for the streaming rate this box attains
+  next_rows     the same decode workload with a bf16-stored state, and as
+                4-token launches keeping every token's state (fp32 and bf16
+                pools): tokens/s and the HBM fraction by the bytes each moves
   prefill       the chunked prefill workload (4 x 8192 tokens, one call per
                 pass): tokens/s and the algorithmic HBM and bf16-MFMA fractions
   varlen_ckpt   the varlen prefill with checkpoints (16 sequences, 262,990
@@ -28,7 +31,8 @@ step).  The line also carries:
   cpu_baseline  the fp64 oracle timed on this host on a bounded sample of the
                 decode workload, and (prefill_workloads) on samples of the
                 three prefill workloads
---no-paired leaves out every KDA_PREFILL_PAIRED (cooperative) launch.
+--no-paired leaves out every KDA_PREFILL_PAIRED (cooperative) launch; --no-next-rows the
+next_rows legs.
 With --workload the line instead reports one of the larger prefill
 workloads (inputs resident in HBM, one call per pass):
   varlen_ckpt   16 sequences of log-uniform length in [1K, 64K] (262,990
@@ -102,7 +106,23 @@ def measured_traffic(path=PROFILE_TRAFFIC, sources=DECODE_SOURCES):
     return rec.get("traffic_bytes_per_launch")
 
 
-def bench_decode(args):
+_DECODE_INPUTS = {}
+
+
+def decode_inputs(w):
+    """The decode workload's host inputs, drawn once per process."""
+    import workloads as wl
+    key = w["seed"]
+    if key not in _DECODE_INPUTS:
+        shape, B, nsteps, pool = w["shape"], w["B"], w["steps"], w["pool"]
+        log(f"[bench] generating decode inputs B={B} steps={nsteps} H={shape.H} d={shape.dk}")
+        inp = wl.token_inputs(w["seed"], shape, B * nsteps)
+        S, X = wl.states(w["seed"], shape, pool, state_std=w["state_std"], conv_std=w["conv_std"])
+        _DECODE_INPUTS[key] = (inp, S, X, wl.slot_permutation(w["seed"], pool, B))
+    return _DECODE_INPUTS[key]
+
+
+def bench_decode(args, extras=True):
     import torch
     import linear_attention_recurrence_decode_amd as kda
     import workloads as wl
@@ -113,10 +133,7 @@ def bench_decode(args):
     bf16_state = args.state_dtype == "bf16"
     cfg = kda.Config(H, dk, dv, kda.KDA_BF16, state_dtype=kda.KDA_BF16 if bf16_state else kda.KDA_F32)
     act = cfg.torch_act
-    log(f"[bench] generating decode inputs B={B} steps={nsteps} H={H} d={dk} state {args.state_dtype}")
-    inp = wl.token_inputs(w["seed"], shape, B * nsteps)
-    S, X = wl.states(w["seed"], shape, pool, state_std=w["state_std"], conv_std=w["conv_std"])
-    slots = wl.slot_permutation(w["seed"], pool, B)
+    inp, S, X, slots = decode_inputs(w)
     r = lambda a: torch.from_numpy(a.reshape((nsteps, B) + a.shape[1:]))
     q, k, v, z = (r(a).to(act).cuda() for a in (inp.q, inp.k, inp.v, inp.z))
     g, beta = r(inp.g).cuda(), r(inp.beta).cuda()
@@ -198,11 +215,33 @@ def bench_decode(args):
     }
     if variants is not None:
         res["variants"] = variants
-    if T == 1:
+    if T == 1 and extras:
         res["slot_copies"] = slot_copies(kda, cfg, Sd, Xd, slot_d, B, H, dk, dv, sb, args)
         res["cold_state"] = cold_state_decode(kda, cfg, q, k, v, z, g, beta, conv_w, norm_w, S, X, slot_d,
                                               nbytes, B, args)
     return res
+
+
+def bench_next_rows(args):
+    """The decode workload in the forms the next rows of the design add: a
+    bf16-stored state (one token per launch) and 4-token launches with
+    per-token states kept for rollback, with an fp32 and with a bf16 pool.
+    Same inputs, passes and warm-up as the headline leg."""
+    import copy
+    import torch
+    out = {}
+    for sd, T in (("bf16", 1), ("f32", 4), ("bf16", 4)):
+        a = copy.copy(args)
+        a.state_dtype, a.multi_token, a.variants = sd, T, False
+        log(f"[bench] decode with a {sd} state pool, {T} token(s) per launch")
+        r = bench_decode(a, extras=False)
+        rf = r["roofline"]
+        out[f"{sd}_state_T{T}"] = {"value": r["value"], "unit": "tok/s", "ms_per_step": r["ms_per_step"],
+                                   "hbm_frac": rf["frac"], "kernel": rf["kernel"],
+                                   "bytes_per_launch": rf["bytes_per_launch"], "mean_launch_us": rf["mean_launch_us"],
+                                   "steps": a.steps}
+        torch.cuda.empty_cache()
+    return out
 
 
 def cold_state_decode(kda, cfg, q, k, v, z, g, beta, conv_w, norm_w, S, X, slot_d, nbytes, B, args, layers=4):
@@ -755,6 +794,8 @@ def main():
     ap.add_argument("--cpu-sample-steps", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="leave out the bf16-state and multi-token decode legs of the default line")
     ap.add_argument("--no-paired", action="store_true",
                     help="leave out every KDA_PREFILL_PAIRED launch (a cooperative launch), e.g. under a profiler")
     ap.add_argument("--multi-token", type=int, default=1,
@@ -828,6 +869,8 @@ def main():
         line["slot_copies"] = res["slot_copies"]
     if "cold_state" in res:
         line["cold_state"] = res["cold_state"]
+    if not args.no_next_rows and args.state_dtype == "f32" and args.multi_token == 1:
+        line["next_rows"] = bench_next_rows(args)
     if not args.no_prefill:
         import torch
         line["prefill"] = bench_prefill(max(3, args.steps // 2), max(1, args.warmup), paired_leg=not args.no_paired)
